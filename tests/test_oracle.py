@@ -1,0 +1,386 @@
+"""Pins for the CPU oracle.  None of these expected values comes from the
+oracle itself: they come from the worked example printed on the format-survey
+page (tests/golden/five_by_five.json), from dense brute force in numpy / plain
+Python loops, or from invariants that must hold for any correct
+implementation.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st, HealthCheck
+
+import gen
+import oracle
+
+
+# --------------------------------------------------------------------------
+# helpers that do NOT use the oracle
+# --------------------------------------------------------------------------
+def dense_from_coo(m, n, row, col, val):
+    d = np.zeros((m, n), np.float64)
+    np.add.at(d, (np.asarray(row), np.asarray(col)), np.asarray(val, np.float64))
+    return d
+
+
+def dense_from_csr(m, n, row_ptr, col, val):
+    d = np.zeros((m, n), np.float64)
+    for i in range(m):
+        for p in range(row_ptr[i], row_ptr[i + 1]):
+            d[i, col[p]] += float(val[p])
+    return d
+
+
+@pytest.fixture(scope="module")
+def five(golden_dir):
+    with open(os.path.join(golden_dir, "five_by_five.json")) as f:
+        g = json.load(f)
+    v = g["value_of"]
+    g["coo_valf"] = np.array([v[s] for s in g["coo_val"]], np.float32)
+    g["csr_valf"] = np.array([v[s] for s in g["csr_val"]], np.float32)
+    # the dense matrix as the page describes it, row by row
+    dense = np.zeros((g["m"], g["n"]))
+    for i, entries in enumerate(g["rows_described"]):
+        for c, s in entries:
+            dense[i, c] = v[s]
+    g["dense"] = dense
+    return g
+
+
+# --------------------------------------------------------------------------
+# the page's worked example
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(6))
+def test_five_coo_to_csr_matches_page(five, seed):
+    rng = np.random.default_rng(seed)
+    p = rng.permutation(8) if seed else np.arange(8)
+    row = np.array(five["coo_row"])[p]
+    col = np.array(five["coo_col"])[p]
+    val = five["coo_valf"][p]
+    rp, c, v = oracle.coo_to_csr(5, 5, row, col, val)
+    assert rp.tolist() == five["csr_row_ptr"]
+    assert c.tolist() == five["csr_col"]
+    assert v.tolist() == five["csr_valf"].tolist()
+
+
+def test_five_csc_matches_dense_columns(five):
+    rp = np.array(five["csr_row_ptr"], np.int32)
+    cp, ri, cv = oracle.csr_to_csc(5, 5, rp, np.array(five["csr_col"]), five["csr_valf"])
+    # expected CSC read off the dense matrix column by column, top to bottom
+    d = five["dense"]
+    exp_ptr, exp_rows, exp_vals = [0], [], []
+    for j in range(5):
+        for i in range(5):
+            if d[i, j] != 0:
+                exp_rows.append(i)
+                exp_vals.append(d[i, j])
+        exp_ptr.append(len(exp_rows))
+    assert cp.tolist() == exp_ptr == [0, 2, 3, 5, 6, 8]
+    assert ri.tolist() == exp_rows
+    assert cv.tolist() == exp_vals
+
+
+def test_five_products_exact(five):
+    d = five["dense"]
+    rp = np.array(five["csr_row_ptr"], np.int32)
+    col = np.array(five["csr_col"], np.int32)
+    val = five["csr_valf"]
+    x = np.arange(1, 6, dtype=np.float32)
+    u = np.arange(1, 6, dtype=np.float32)
+    # brute force in plain Python loops over the page's dense matrix
+    ax = [sum(d[i, j] * x[j] for j in range(5)) for i in range(5)]
+    atu = [sum(d[i, j] * u[i] for i in range(5)) for j in range(5)]
+    y, _ = oracle.spmv(rp, col, val, x)
+    assert y.tolist() == ax == [7, 6, 54, 21, 40]
+    cp, ri, cv = oracle.csr_to_csc(5, 5, rp, col, val)
+    z, _ = oracle.spmv(cp, ri, cv, u)
+    assert z.tolist() == atu == [13, 6, 30, 15, 58]
+    zs, _ = oracle.spmv_t_scatter(5, 5, rp, col, val, u)
+    assert zs.tolist() == atu
+    assert float(np.dot(z, x)) == float(np.dot(u, y)) == 465.0
+
+
+def test_five_ell_slots(five):
+    rp = np.array(five["csr_row_ptr"], np.int32)
+    col = np.array(five["csr_col"], np.int32)
+    val = five["csr_valf"]
+    # ELL is SELL with a single slice holding every row and no sorting window
+    s = oracle.sell_build(rp, col, val, C=5, sigma=1)
+    assert s["slots"] == five["ell_total_slots"] == 15
+    assert int((s["col"] >= 0).sum()) == five["ell_valid_slots"] == 8
+    v = five["value_of"]
+    for i in range(5):
+        got_c = [int(s["col"][t * 5 + i]) for t in range(five["ell_K"])]
+        got_v = [float(s["val"][t * 5 + i]) for t in range(five["ell_K"])]
+        exp_c = [c if c is not None else -1 for c in five["ell_col_rows"][i]]
+        exp_v = [v[a] if a is not None else 0.0 for a in five["ell_val_rows"][i]]
+        assert got_c == exp_c
+        assert got_v == exp_v
+    y = oracle.sell_spmv(s, 5, np.arange(1, 6, dtype=np.float32))
+    assert y.tolist() == [7, 6, 54, 21, 40]
+
+
+# --------------------------------------------------------------------------
+# dense brute force on small random matrices
+# --------------------------------------------------------------------------
+@st.composite
+def small_coo(draw):
+    m = draw(st.integers(0, 16))
+    n = draw(st.integers(1, 16))
+    nnz = draw(st.integers(0, 60)) if m > 0 else 0
+    row = draw(st.lists(st.integers(0, max(m - 1, 0)), min_size=nnz, max_size=nnz))
+    col = draw(st.lists(st.integers(0, n - 1), min_size=nnz, max_size=nnz))
+    # distinct small integers as values: every entry is identifiable and all
+    # products/sums are exact in fp64
+    vals = draw(st.permutations(list(range(1, nnz + 1)))) if nnz else []
+    sign = draw(st.lists(st.sampled_from([-1, 1]), min_size=nnz, max_size=nnz))
+    val = np.array([s * v for s, v in zip(sign, vals)], np.float32)
+    return m, n, np.array(row, np.int32), np.array(col, np.int32), val
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(small_coo())
+def test_coo_to_csr_brute_force(case):
+    m, n, row, col, val = case
+    rp, c, v = oracle.coo_to_csr(m, n, row, col, val)
+    assert rp[0] == 0 and rp[-1] == row.size
+    assert np.all(np.diff(rp) >= 0)
+    # the same matrix, duplicates summed
+    np.testing.assert_array_equal(dense_from_csr(m, n, rp, c, v), dense_from_coo(m, n, row, col, val))
+    # order inside each row: by column, equal columns in input order
+    pos_of_val = {float(a): k for k, a in enumerate(val)}
+    for i in range(m):
+        seg = list(zip(c[rp[i]:rp[i + 1]].tolist(), [pos_of_val[float(a)] for a in v[rp[i]:rp[i + 1]]]))
+        assert seg == sorted(seg)
+        assert all(row[p] == i for _, p in seg)
+    # row lengths equal the number of COO entries of the row
+    assert np.diff(rp).tolist() == [int((row == i).sum()) for i in range(m)]
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(small_coo(), st.integers(0, 2 ** 31 - 1))
+def test_products_brute_force(case, seed):
+    m, n, row, col, val = case
+    rng = np.random.default_rng(seed)
+    rp, c, v = oracle.coo_to_csr(m, n, row, col, val)
+    d = dense_from_coo(m, n, row, col, val)
+    x = rng.integers(-4, 5, size=n).astype(np.float32)
+    u = rng.integers(-4, 5, size=m).astype(np.float32)
+    yo = rng.integers(-4, 5, size=m).astype(np.float32)
+    zo = rng.integers(-4, 5, size=n).astype(np.float32)
+    alpha, beta = float(rng.integers(-3, 4)), float(rng.integers(-3, 4))
+    # y = alpha A x + beta y
+    y, sc = oracle.spmv(rp, c, v, x, alpha, beta, yo)
+    np.testing.assert_array_equal(y, alpha * (d @ x) + beta * yo)
+    abs_d = dense_from_coo(m, n, row, col, np.abs(val))
+    np.testing.assert_array_equal(sc, abs(alpha) * (abs_d @ np.abs(x)) + abs(beta) * np.abs(yo))
+    # z = alpha A^T u + beta z through the CSC, and through the scatter route
+    cp, ri, cv = oracle.csr_to_csc(m, n, rp, c, v)
+    z, _ = oracle.spmv(cp, ri, cv, u, alpha, beta, zo)
+    zs, _ = oracle.spmv_t_scatter(m, n, rp, c, v, u, alpha, beta, zo)
+    np.testing.assert_array_equal(z, alpha * (d.T @ u) + beta * zo)
+    np.testing.assert_array_equal(zs, z)
+    # C = alpha A B + beta C
+    N = int(rng.integers(1, 5))
+    B = rng.integers(-4, 5, size=(n, N)).astype(np.float32)
+    C0 = rng.integers(-4, 5, size=(m, N)).astype(np.float32)
+    Cm, _ = oracle.spmm(rp, c, v, B, alpha, beta, C0)
+    np.testing.assert_array_equal(Cm, alpha * (d @ B) + beta * C0)
+
+
+def test_beta_zero_does_not_read_y():
+    coo = gen.ragged_coo(30, 20, seed=3)
+    rp, c, v = oracle.coo_to_csr(coo.m, coo.n, coo.row, coo.col, coo.val)
+    x = gen.dense_vector(coo.n, 4)
+    y_nan = np.full(coo.m, np.nan, np.float32)
+    y, _ = oracle.spmv(rp, c, v, x, 2.0, 0.0, y_nan)
+    assert np.all(np.isfinite(y))
+    B = gen.dense_matrix(coo.n, 3, 5)
+    C, _ = oracle.spmm(rp, c, v, B, 1.0, 0.0, np.full((coo.m, 3), np.nan, np.float32))
+    assert np.all(np.isfinite(C))
+
+
+def test_rows_subset_matches_full():
+    coo = gen.ragged_coo(50, 40, seed=7, long_rows=(35,))
+    rp, c, v = oracle.coo_to_csr(coo.m, coo.n, coo.row, coo.col, coo.val)
+    x = gen.dense_vector(coo.n, 8)
+    y0 = gen.dense_vector(coo.m, 9)
+    full, fs = oracle.spmv(rp, c, v, x, 0.5, -1.5, y0)
+    rows = np.array([49, 0, 17, 17, 3])
+    sub, ss = oracle.spmv(rp, c, v, x, 0.5, -1.5, y0, rows=rows)
+    np.testing.assert_array_equal(sub, full[rows])
+    np.testing.assert_array_equal(ss, fs[rows])
+    B = gen.dense_matrix(coo.n, 4, 10)
+    Cf, _ = oracle.spmm(rp, c, v, B)
+    Cs, _ = oracle.spmm(rp, c, v, B, rows=rows)
+    np.testing.assert_array_equal(Cs, Cf[rows])
+
+
+def test_index_errors_rejected():
+    with pytest.raises(oracle.OracleError):
+        oracle.coo_to_csr(3, 3, [0, 3], [0, 0], [1.0, 2.0])
+    with pytest.raises(oracle.OracleError):
+        oracle.coo_to_csr(3, 3, [0, 1], [0, -1], [1.0, 2.0])
+
+
+# --------------------------------------------------------------------------
+# invariants
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(5))
+def test_csc_equals_csr_of_transpose_via_coo(seed):
+    coo = gen.ragged_coo(60, 45, seed, long_rows=(44,), dup_frac=0.1)
+    rp, c, v = oracle.coo_to_csr(coo.m, coo.n, coo.row, coo.col, coo.val)
+    cp, ri, cv = oracle.csr_to_csc(coo.m, coo.n, rp, c, v)
+    # CSR(A^T) through the COO route on the swapped triples, fed in CSR order so
+    # that equal (row, col) pairs keep CSR order as their tie-break
+    row_of = np.repeat(np.arange(coo.m, dtype=np.int32), np.diff(rp))
+    tp, tc, tv = oracle.coo_to_csr(coo.n, coo.m, c, row_of, v)
+    np.testing.assert_array_equal(cp, tp)
+    np.testing.assert_array_equal(ri, tc)
+    np.testing.assert_array_equal(cv, tv)
+    # transposing twice gives the CSR back
+    bp, bc, bv = oracle.csr_to_csc(coo.n, coo.m, cp, ri, cv)
+    np.testing.assert_array_equal(bp, rp)
+    np.testing.assert_array_equal(bc, c)
+    np.testing.assert_array_equal(bv, v)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_adjoint_identity(seed):
+    coo = gen.ragged_coo(70, 55, seed, long_rows=(50,))
+    rp, c, v = oracle.coo_to_csr(coo.m, coo.n, coo.row, coo.col, coo.val)
+    cp, ri, cv = oracle.csr_to_csc(coo.m, coo.n, rp, c, v)
+    x = gen.dense_vector(coo.n, seed, 3)
+    u = gen.dense_vector(coo.m, seed, 4)
+    ax, _ = oracle.spmv(rp, c, v, x)
+    atu, _ = oracle.spmv(cp, ri, cv, u)
+    lhs = float(np.dot(atu, x.astype(np.float64)))
+    rhs = float(np.dot(u.astype(np.float64), ax))
+    assert abs(lhs - rhs) <= 1e-12 * (np.abs(atu) @ np.abs(x) + 1.0)
+
+
+@pytest.mark.parametrize("N", [1, 3, 8])
+def test_spmm_columns_are_spmv(N):
+    coo = gen.ragged_coo(40, 30, 11, long_rows=(29,))
+    rp, c, v = oracle.coo_to_csr(coo.m, coo.n, coo.row, coo.col, coo.val)
+    B = gen.dense_matrix(coo.n, N, 12)
+    C0 = gen.dense_matrix(coo.m, N, 13)
+    Cm, Cs = oracle.spmm(rp, c, v, B, 1.5, -0.5, C0)
+    for j in range(N):
+        y, s = oracle.spmv(rp, c, v, np.ascontiguousarray(B[:, j]), 1.5, -0.5, np.ascontiguousarray(C0[:, j]))
+        np.testing.assert_array_equal(Cm[:, j], y)
+        np.testing.assert_array_equal(Cs[:, j], s)
+
+
+# --------------------------------------------------------------------------
+# BSR
+# --------------------------------------------------------------------------
+def _bf16_exact(h):
+    # exact widening done with numpy bit operations (independent of the C oracle)
+    return (np.asarray(h, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_bf16_widening_exact():
+    h = np.array([0x0000, 0x8000, 0x3F80, 0xBF80, 0x4049, 0x7F7F, 0x0001, 0x3C00], np.uint16)
+    np.testing.assert_array_equal(oracle.bf16_to_float64(h), _bf16_exact(h))
+    assert oracle.bf16_to_float64(np.array([0x3F80], np.uint16))[0] == 1.0
+    assert oracle.bf16_to_float64(np.array([0xC000], np.uint16))[0] == -2.0
+
+
+def test_f32_to_bf16_rounding_pins():
+    # round-to-nearest-even at the halfway points of the bf16 grid
+    f = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -1.5, 3.0e-3], np.float32)
+    h = gen.f32_to_bf16_bits(f)
+    assert h[0] == 0x3F80
+    assert h[1] == 0x3F80      # tie, even stays
+    assert h[2] == 0x3F82      # tie, rounds up to even
+    assert h[3] == 0x3F80      # below half
+    assert h[4] == 0xBFC0
+    assert abs(_bf16_exact(h[5:])[0] - 3.0e-3) <= 2 ** -8 * 3.0e-3
+
+
+def _dense_from_bsr(b):
+    d = np.zeros((b.mb * b.bs, b.kb * b.bs))
+    for I in range(b.mb):
+        for k in range(b.brow_ptr[I], b.brow_ptr[I + 1]):
+            J = b.bcol[k]
+            d[I * b.bs:(I + 1) * b.bs, J * b.bs:(J + 1) * b.bs] = _bf16_exact(b.bval[k])
+    return d
+
+
+@pytest.mark.parametrize("bs,mb,kb,density", [(1, 12, 9, 0.3), (4, 5, 6, 0.4), (8, 3, 4, 0.5), (16, 2, 2, 1.0)])
+def test_bsr_routes_match_dense(bs, mb, kb, density):
+    b = gen.block_sparse_bsr(mb=mb, kb=kb, bs=bs, density=density, std=1.0, seed=bs)
+    N = 5
+    B = gen.bf16_matrix(kb * bs, N, seed=bs)
+    Bd = _bf16_exact(B)
+    C0 = gen.dense_matrix(mb * bs, N, 21)
+    d = _dense_from_bsr(b)
+    rp, c, v = oracle.bsr_to_csr(mb, bs, b.brow_ptr, b.bcol, b.bval)
+    Cexp = 0.75 * (d @ Bd) - 2.0 * C0
+    C1, _ = oracle.spmm_bf16(rp, c, v, B, 0.75, -2.0, C0)
+    C2 = oracle.bsr_spmm_direct(mb, bs, b.brow_ptr, b.bcol, b.bval, B, 0.75, -2.0, C0)
+    np.testing.assert_allclose(C1, Cexp, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(C2, Cexp, rtol=1e-12, atol=1e-12)
+    # expansion keeps every in-block entry
+    assert rp[-1] == b.nnzb * bs * bs
+
+
+def test_bsr_one_by_one_blocks_equal_csr():
+    b = gen.block_sparse_bsr(mb=20, kb=15, bs=1, density=0.3, std=1.0, seed=5)
+    # the same matrix as a plain fp32 CSR (bf16 values are exact in fp32)
+    vals32 = _bf16_exact(b.bval.reshape(-1)).astype(np.float32)
+    B = gen.bf16_matrix(15, 3, seed=6)
+    C_bsr = oracle.bsr_spmm_direct(20, 1, b.brow_ptr, b.bcol, b.bval, B)
+    C_csr, _ = oracle.spmm(b.brow_ptr, b.bcol, vals32, _bf16_exact(B).astype(np.float32))
+    np.testing.assert_array_equal(C_bsr, C_csr)
+
+
+def test_single_dense_block_is_gemm():
+    rng = np.random.default_rng(0)
+    blk = gen.f32_to_bf16_bits(rng.normal(size=(1, 8, 8)).astype(np.float32)).reshape(1, 8, 8)
+    B = gen.bf16_matrix(8, 4, seed=1)
+    C = oracle.bsr_spmm_direct(1, 8, np.array([0, 1]), np.array([0]), blk, B)
+    np.testing.assert_allclose(C, _bf16_exact(blk[0]) @ _bf16_exact(B), rtol=1e-13, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# profile and SELL
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(4))
+def test_row_profile_against_numpy(seed):
+    coo = gen.ragged_coo(997, 300, seed, long_rows=(250, 299))
+    rp, _, _ = oracle.coo_to_csr(coo.m, coo.n, coo.row, coo.col, coo.val)
+    p = oracle.row_profile(rp)
+    L = np.bincount(coo.row, minlength=coo.m)
+    assert p["mean"] == pytest.approx(L.mean(), rel=1e-12)
+    assert p["var"] == pytest.approx(L.var(), rel=1e-12)
+    assert p["cv"] == pytest.approx(L.std() / L.mean(), rel=1e-12)
+    assert p["p95"] == int(np.percentile(L, 95, method="inverted_cdf"))
+    assert p["p99"] == int(np.percentile(L, 99, method="inverted_cdf"))
+    assert p["max"] == L.max()
+    assert p["empty"] == int((L == 0).sum())
+
+
+@pytest.mark.parametrize("C,sigma", [(4, 1), (4, 8), (64, 256), (8, 1000)])
+def test_sell_layout_and_product(C, sigma):
+    coo = gen.ragged_coo(301, 120, 2, long_rows=(110,))
+    rp, c, v = oracle.coo_to_csr(coo.m, coo.n, coo.row, coo.col, coo.val)
+    s = oracle.sell_build(rp, c, v, C, sigma)
+    L = np.diff(rp)
+    # perm is a permutation that only moves rows inside their sigma window,
+    # ordered by decreasing length with ties by row index
+    assert sorted(s["perm"].tolist()) == list(range(coo.m))
+    for w in range(0, coo.m, sigma):
+        win = list(range(w, min(coo.m, w + sigma)))
+        assert sorted(s["perm"][win].tolist()) == win
+        assert s["perm"][win].tolist() == sorted(win, key=lambda r: (-L[r], r))
+    # slot count: every slice padded to its longest row
+    widths = [max(L[s["perm"][k]] for k in range(j, min(coo.m, j + C))) for j in range(0, coo.m, C)]
+    assert s["slots"] == C * sum(widths)
+    assert int((s["col"] >= 0).sum()) == rp[-1]
+    x = gen.dense_vector(coo.n, 3)
+    y = oracle.sell_spmv(s, C, x)
+    np.testing.assert_allclose(y, dense_from_csr(coo.m, coo.n, rp, c, v) @ x.astype(np.float64), rtol=1e-12,
+                               atol=1e-12)
