@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Throughput of the sparse x dense products on one MI355X.
+
+Default workload: CSR SpMV y = A x on the power-law matrix (2^22 x 2^22,
+lognormal row lengths plus planted hub rows, ~46.8M entries, fp32).  One step
+is one `spmv` call: every row bin of the plan (group / wave / block / split
+rows and the split reduction, with the fused axpby store).  The one-time work
+(COO -> CSR build, plan) is timed separately and reported under "setup".
+
+Prints ONE JSON line.  Other workloads (--config) exist for profiling:
+  spmv_uniform, spmv_powerlaw, stencil27 (u <- A v - a u, v <- A^T u - b v per
+  step), spmm_lognormal (--N), bsr_blocks.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+KERNEL_SOURCES = ["spmm_csr_spmv_amd/csrc/spmv.hip", "spmm_csr_spmv_amd/csrc/spmm.hip",
+                  "spmm_csr_spmv_amd/csrc/bsr.hip", "spmm_csr_spmv_amd/csrc/device_common.h"]
+
+
+# --------------------------------------------------------------------------
+# byte / flop model (algorithmic: every array the method must touch, once)
+# --------------------------------------------------------------------------
+def spmv_bytes(m, k, nnz, beta_nonzero=False):
+    """CSR SpMV: values + column indices (8 B per entry), row_ptr, x read once,
+    y written (and read when beta != 0).  The 8 B per entry is the lower bound
+    of the LSMR page's section 1."""
+    return 8 * nnz + 4 * (m + 1) + 4 * k + 4 * m + (4 * m if beta_nonzero else 0)
+
+
+def spmv_flops(m, nnz, beta_nonzero=False):
+    return 2 * nnz + (2 * m if beta_nonzero else 0)
+
+
+def spmm_bytes(m, k, nnz, N, beta_nonzero=False):
+    return 8 * nnz + 4 * (m + 1) + 4 * k * N + 4 * m * N + (4 * m * N if beta_nonzero else 0)
+
+
+def bsr_bytes(mb, kb, bs, nnzb, N, beta_nonzero=False):
+    return 2 * nnzb * bs * bs + 4 * (nnzb + mb + 1) + 2 * kb * bs * N + 4 * mb * bs * N * (2 if beta_nonzero else 1)
+
+
+def bsr_flops(nnzb, bs, N):
+    return 2 * nnzb * bs * bs * N
+
+
+def csr_storage_bytes(m, nnz, val_bytes=8, idx_bytes=4):
+    """Bytes of a CSR (values, column indices, row pointer of m+1 entries)."""
+    return nnz * (val_bytes + idx_bytes) + (m + 1) * idx_bytes
+
+
+def coo_storage_bytes(nnz, val_bytes=8, idx_bytes=4):
+    return nnz * (val_bytes + 2 * idx_bytes)
+
+
+def dual_storage_bytes(m, n, nnz):
+    """CSR + CSC of an fp32/int32 matrix (LSMR page, section 4)."""
+    return 2 * (8 * nnz + 4 * (m + n + 2))
+
+
+def block_index_bytes_per_value(bs, idx_bytes=4):
+    return idx_bytes / float(bs * bs)
+
+
+def kernel_fingerprint():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(HERE, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, launches_bytes):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernels (same fingerprint); else None."""
+    path = os.path.join(HERE, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_fingerprint") != kernel_fingerprint():
+        return None
+    return t.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------------------
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="spmv_powerlaw",
+                    choices=["spmv_uniform", "spmv_powerlaw", "stencil27", "spmm_lognormal", "bsr_blocks"])
+    ap.add_argument("--N", type=int, default=32, help="right-hand-side columns for spmm_lognormal")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--options", default="", help="plan options, e.g. group_nnz=1024,wave_min=128")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the sparse products here are single-GPU kernels "
+              "(see the sharding paragraph of DESIGN.md); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gen
+    import spmm_csr_spmv_amd as sp
+
+    opts = {}
+    for kv in filter(None, args.options.split(",")):
+        k, v = kv.split("=")
+        opts[k] = int(v)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    setup = {}
+    cfg = args.config
+    result = dict(metric="SpMV/SpMM GFLOP/s + achieved HBM GB/s vs MI355X peak (fp32), 1 GPU", unit="GFLOP/s",
+                  n_gpus=1, steps=args.steps, warmup=args.warmup, higher_is_better=True, scaling="weak",
+                  vs_baseline=None, data="synthetic (seeded generators in gen/, seed 0)")
+
+    t0 = time.time()
+    if cfg == "bsr_blocks":
+        b = gen.block_sparse_bsr(seed=0)
+        N = 512
+        Bh = gen.bf16_matrix(b.kb * b.bs, N, seed=0)
+        d_brow, d_bcol = torch.from_numpy(b.brow_ptr).cuda(), torch.from_numpy(b.bcol).cuda()
+        d_bval = torch.from_numpy(b.bval.view(np.int16)).cuda()
+        d_B = torch.from_numpy(Bh.view(np.int16)).cuda()
+        C = torch.empty(b.mb * b.bs, N, device="cuda")
+        setup["generate_s"] = time.time() - t0
+
+        def step():
+            sp.bsr_spmm(b.mb, b.kb, b.bs, d_brow, d_bcol, d_bval, d_B, 1.0, 0.0, C)
+
+        flops = bsr_flops(b.nnzb, b.bs, N)
+        nbytes = bsr_bytes(b.mb, b.kb, b.bs, b.nnzb, N)
+        launches = 1
+        dtype = "bf16 in / f32 acc"
+        config = dict(workload=cfg, M=b.mb * b.bs, K=b.kb * b.bs, block=b.bs, nnz_blocks=b.nnzb, N=N)
+        bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
+        cpu_leg = None
+    else:
+        coo = {"spmv_uniform": lambda: gen.uniform_rows_coo(seed=0),
+               "spmv_powerlaw": lambda: gen.powerlaw_coo(seed=0),
+               "stencil27": lambda: gen.stencil27_coo(seed=0),
+               "spmm_lognormal": lambda: gen.lognormal_coo(seed=0)}[cfg]()
+        setup["generate_s"] = time.time() - t0
+        m, n, nnz = coo.m, coo.n, coo.nnz
+        d_row, d_col, d_val = (torch.from_numpy(a).cuda() for a in (coo.row, coo.col, coo.val))
+        torch.cuda.synchronize()
+        t1 = time.time()
+        rp, ci, vv = sp.csr_build_from_coo(m, n, d_row, d_col, d_val)
+        torch.cuda.synchronize()
+        setup["csr_build_from_coo_ms"] = (time.time() - t1) * 1e3
+        del d_row, d_col, d_val
+        csc = None
+        if cfg == "stencil27":
+            t1 = time.time()
+            csc = sp.csr_to_csc(m, n, rp, ci, vv)
+            torch.cuda.synchronize()
+            setup["csr_to_csc_ms"] = (time.time() - t1) * 1e3
+        N = args.N if cfg == "spmm_lognormal" else 1
+        t1 = time.time()
+        plan = sp.Plan(m, n, rp, ci, vv, csc=csc, max_N=N, **opts)
+        torch.cuda.synchronize()
+        setup["plan_ms"] = (time.time() - t1) * 1e3
+        prof = plan.profile()
+        x = torch.from_numpy(gen.dense_vector(n, 0, 1)).cuda()
+        y = torch.zeros(m, device="cuda")
+        config = dict(workload=cfg, M=m, K=n, nnz=nnz, row_len_mean=round(prof["mean"], 3), p95=prof["p95"],
+                      p99=prof["p99"], max_row=prof["max_len"],
+                      bins=dict(group_tasks=prof["group_tasks"], wave_rows=prof["wave_rows"],
+                                block_rows=prof["block_rows"], split_rows=prof["split_rows"],
+                                split_segments=prof["split_segments"]))
+        if opts:
+            config["plan_options"] = opts
+        bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
+        dtype = "f32"
+        if cfg == "stencil27":
+            u = torch.from_numpy(gen.dense_vector(m, 0, 2)).cuda()
+            v = torch.from_numpy(gen.dense_vector(n, 0, 3)).cuda()
+            u0, v0 = u.clone(), v.clone()
+            rng = np.random.default_rng(5)
+            ab = rng.uniform(0.5, 2.0, size=(1 << 16, 2)).astype(np.float32)
+            it = [0]
+
+            def step():
+                a, bt = ab[it[0] % ab.shape[0]]
+                it[0] += 1
+                sp.spmv(plan, 1.0, v, -float(a), u)
+                sp.spmv_t(plan, 1.0, u, -float(bt), v)
+
+            def restore():
+                u.copy_(u0)
+                v.copy_(v0)
+
+            flops = 2 * spmv_flops(m, nnz, True)
+            nbytes = 2 * spmv_bytes(m, n, nnz, True)  # per step (two launches)
+            launches = 2
+            config["step"] = "u <- A v - alpha u ; v <- A^T u - beta v"
+        elif cfg == "spmm_lognormal":
+            B = torch.from_numpy(gen.dense_matrix(n, N, 0)).cuda()
+            C = torch.empty(m, N, device="cuda")
+
+            def step():
+                sp.spmm(plan, 1.0, B, 0.0, C)
+
+            flops = 2 * nnz * N
+            nbytes = spmm_bytes(m, n, nnz, N)
+            launches = 1
+            config["N"] = N
+        else:
+            def step():
+                sp.spmv(plan, 1.0, x, 0.0, y)
+
+            flops = spmv_flops(m, nnz)
+            nbytes = spmv_bytes(m, n, nnz)
+            launches = 1
+        cpu_leg = (rp, ci, vv, x, m, n, nnz) if cfg in ("spmv_powerlaw", "spmv_uniform") else None
+
+    restore_fn = locals().get("restore")
+    # ---------------- warmup + timed region
+    for _ in range(args.warmup):
+        step()
+    if restore_fn:
+        restore_fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = elapsed * 1e3 / args.steps
+    launch_ms = float(np.mean(ev_ms)) / launches
+    step_flops_s = flops / (ms_per_step * 1e-3)
+    result["value"] = round(step_flops_s / 1e9, 3)
+    result["ms_per_step"] = round(ms_per_step, 5)
+    result["dtype"] = dtype
+    result["config"] = config
+    per_launch_bytes = nbytes / launches
+    per_launch_flops = flops / launches
+    if bound == "hbm":
+        achieved = per_launch_bytes / (launch_ms * 1e-3) / 1e9
+    else:
+        achieved = per_launch_flops / (launch_ms * 1e-3) / 1e12
+    traffic = load_traffic(cfg + ("_N%d" % N if cfg == "spmm_lognormal" else ""), per_launch_bytes)
+    result["roofline"] = dict(bound=bound, achieved=round(achieved, 2), peak=peak, unit=unit,
+                              frac=round(achieved / peak, 4), traffic=traffic,
+                              kernel_ms=round(launch_ms, 5), algorithmic_bytes_per_launch=int(per_launch_bytes),
+                              flops_per_launch=int(per_launch_flops), event_ms_median=round(float(np.median(ev_ms)), 5))
+    if bound == "mfma":
+        result["roofline"]["hbm_gbs"] = round(per_launch_bytes / (launch_ms * 1e-3) / 1e9, 1)
+    result["gflops_event"] = round(per_launch_flops / (launch_ms * 1e-3) / 1e9, 2)
+    result["setup"] = {k: round(v, 2) for k, v in setup.items()}
+
+    # ---------------- CPU baseline: the oracle on the host cores
+    if not args.no_cpu_baseline and cpu_leg is not None:
+        import oracle
+        rp_, ci_, vv_, x_, m_, n_, nnz_ = cpu_leg
+        h_rp, h_ci, h_vv, h_x = (t.cpu().numpy() for t in (rp_, ci_, vv_, x_))
+        reps, t_cpu = 0, 0.0
+        t0 = time.perf_counter()
+        while t_cpu < args.cpu_seconds and reps < 1000:
+            oracle.spmv(h_rp, h_ci, h_vv, h_x)
+            reps += 1
+            t_cpu = time.perf_counter() - t0
+        per = t_cpu / reps
+        result["cpu_baseline"] = dict(value=round(spmv_flops(m_, nnz_) / per / 1e9, 4), unit="GFLOP/s", cores=1,
+                                      kind="oracle",
+                                      sample="%d full passes of y = A x over the same %s matrix (fp64 accumulation, "
+                                             "single-threaded C loop), %.1f s" % (reps, cfg, t_cpu))
+    elif not args.no_cpu_baseline and cfg == "stencil27":
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

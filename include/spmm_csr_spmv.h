@@ -1,0 +1,219 @@
+/*
+ * spmm_csr_spmv -- sparse x dense products on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libspmm_csr_spmv.so.  Every pointer argument named as "device" is
+ * a device (HBM) address; every call that takes `stream` enqueues its work on
+ * that HIP stream (a hipStream_t passed as void*, NULL = the null stream) and
+ * returns without waiting, unless its comment says it synchronises.
+ *
+ * Pages the operations follow (title, then section):
+ *   [FMT]  「稀疏矩阵存储格式:COO、CSR、ELL、Hybrid 与块稀疏,SpMV 的容量与带宽账」
+ *   [LSMR] 「CUDA LSMR 专栏（二）：用 CSR/CSC 双存储压榨双向 SpMV」
+ *   [GEN]  「通用稀疏矩阵乘法CUDA算子实现」
+ *   [BCSR] 「GPU加速实战用BCSR格式优化稀疏矩阵乘法附CUDA代码」
+ *   [ASYNC] the AsyncSparse summary page (capital-peak.com, news 566)
+ *
+ * Conventions shared by all entry points
+ *   - Indices are zero-based int32 ([LSMR] §5.1 uses zero-based indices).
+ *     Sizes that do not fit int32 (m, n, nnz > INT32_MAX) are rejected with
+ *     SP_ERR_SIZE, never truncated ([LSMR] §8).
+ *   - Products use the BLAS axpby form  out = alpha * op(A) * in + beta * out
+ *     ([LSMR] §5.2 folds the previous vector into the product through beta).
+ *     beta == 0 means `out` is write-only: its old contents are not read.
+ *   - The caller owns every buffer.  The library allocates no device memory in
+ *     any call: scratch comes from a caller-provided workspace whose size is
+ *     queried first ([GEN] §6: scratch belongs to the framework allocator).
+ *   - Floating-point results are deterministic run to run: no floating-point
+ *     atomics, fixed reduction order ([GEN] §2.4).
+ *   - Errors are returned as status codes; nothing is thrown across the ABI.
+ *     A failed HIP launch is reported as SP_ERR_HIP.
+ */
+#ifndef SPMM_CSR_SPMV_H
+#define SPMM_CSR_SPMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+enum {
+    SP_OK = 0,
+    SP_ERR_NULL = 1,        /* a required pointer is NULL                    */
+    SP_ERR_SIZE = 2,        /* a size is negative, too large or inconsistent */
+    SP_ERR_INDEX = 3,       /* an input index is outside its dimension       */
+    SP_ERR_WORKSPACE = 4,   /* workspace missing or smaller than queried     */
+    SP_ERR_UNSUPPORTED = 5, /* option, shape or layout not supported         */
+    SP_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed    */
+    SP_ERR_STATE = 7        /* plan used before sp_plan_bind, or similar     */
+};
+
+/* Static string naming a status code (never NULL). */
+const char* sp_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int sp_version(void);
+
+/* --------------------------------------------------------- COO -> CSR
+ * [FMT] §3 (and §2): count the entries of every row, prefix-sum the counts
+ * into row_ptr, move each entry into its row's range; [GEN] §1.2 asks for
+ * the result ordered by (row, col).
+ *
+ * Input: coo_row/coo_col/coo_val, nnz entries each, device, in any order.
+ * Output (device, caller-allocated): row_ptr[m+1], col_idx[nnz], val[nnz].
+ * Within a row, entries are ordered by column; entries with equal (row, col)
+ * are kept as separate entries (duplicates are not summed) in their input
+ * order.  The result is therefore unique and bit-exact.
+ * work: device scratch of at least csr_build_from_coo_bufsize() bytes.
+ * Synchronises `stream` once (to report SP_ERR_INDEX and to size the sort).
+ * Errors: SP_ERR_NULL, SP_ERR_SIZE, SP_ERR_INDEX (some row not in [0,m) or
+ * col not in [0,n); outputs are then unspecified), SP_ERR_WORKSPACE, SP_ERR_HIP.
+ */
+int csr_build_from_coo_bufsize(int64_t m, int64_t n, int64_t nnz, size_t* bytes);
+int csr_build_from_coo(int64_t m, int64_t n, int64_t nnz,
+                       const int32_t* coo_row, const int32_t* coo_col, const float* coo_val,
+                       int32_t* row_ptr, int32_t* col_idx, float* val,
+                       void* work, size_t work_bytes, void* stream);
+
+/* --------------------------------------------------------- CSR -> CSC
+ * [LSMR] §2 and §4: the CSC of A is, array for array, the CSR of A^T; it is
+ * built once, when the matrix is constructed.  Reading a CSC input as the
+ * CSR of A^T and calling this again turns it back into the CSR of A.
+ *
+ * Input: CSR of an m x n matrix (device).  Output (device, caller-allocated):
+ * col_ptr[n+1], row_idx[nnz], cval[nnz].  Within a column, entries are ordered
+ * by row, and entries with equal (row, col) keep their CSR order; the result
+ * is unique and bit-exact.  nnz must equal row_ptr[m].
+ * work: at least csr_to_csc_bufsize() bytes.  Synchronises `stream` once.
+ * Errors: SP_ERR_NULL, SP_ERR_SIZE, SP_ERR_INDEX, SP_ERR_WORKSPACE, SP_ERR_HIP.
+ */
+int csr_to_csc_bufsize(int64_t m, int64_t n, int64_t nnz, size_t* bytes);
+int csr_to_csc(int64_t m, int64_t n, int64_t nnz,
+               const int32_t* row_ptr, const int32_t* col_idx, const float* val,
+               int32_t* col_ptr, int32_t* row_idx, float* cval,
+               void* work, size_t work_bytes, void* stream);
+
+/* --------------------------------------------------------- plan
+ * [GEN] §4: a light profile of the matrix, taken the first time the matrix is
+ * seen and kept with it, decides which kernel serves which rows; [LSMR] §5.3
+ * names the statistics (row length l_i = row_ptr[i+1] - row_ptr[i], its mean,
+ * variance and tail).  The plan holds the profile, the row-to-kernel
+ * assignment for A (and for A^T when a CSC is given) and pointers to the
+ * caller's arrays; it owns no device memory.
+ *
+ * Rows are assigned by length l:
+ *   l <= wave_min            consecutive rows packed into groups of at most
+ *                            group_nnz entries and 256 rows; a group is staged
+ *                            through LDS and reduced by 1..64 lanes per row
+ *                            (thread-per-row up to wave-per-row, [GEN] §2.1-2.2)
+ *   wave_min < l <= block_min    one wave64 per row ([GEN] §2.2)
+ *   block_min < l <= split_min   one 256-thread workgroup per row ([GEN] §2.3)
+ *   l > split_min            split into segments of split_seg entries, one
+ *                            workgroup each, partial sums reduced in fixed
+ *                            order by the last segment to finish ([GEN] §2.4)
+ * With use_sell != 0 the group rows are served instead from a SELL-C-sigma
+ * copy ([GEN] §1.4) built in the workspace (C = 64 lanes, window sell_sigma).
+ */
+typedef struct sp_plan sp_plan;
+
+typedef struct sp_plan_options {
+    int32_t group_nnz;   /* entries per group, 64..4096 (default 2048)        */
+    int32_t wave_min;    /* default 256; must be <= group_nnz                 */
+    int32_t block_min;   /* default 4096; >= wave_min                         */
+    int32_t split_min;   /* default 32768; >= block_min                       */
+    int32_t split_seg;   /* entries per split segment, >= 16 (default 8192)   */
+    int32_t use_sell;    /* 0 (default) or 1                                   */
+    int32_t sell_sigma;  /* sorting window in rows for SELL, >= 1 (default 1024) */
+    int32_t xcd_remap;   /* 1 (default): consecutive groups go to one XCD     */
+} sp_plan_options;
+
+/* Row-length profile and bin sizes of one direction of a plan. */
+typedef struct sp_profile {
+    int64_t rows, cols, nnz;
+    double mean, var, cv;        /* population variance, cv = sqrt(var)/mean  */
+    int64_t p95, p99, max_len;   /* nearest-rank percentiles of l_i           */
+    int64_t empty_rows;
+    int64_t group_tasks, group_rows, group_nnz;
+    int64_t wave_rows, wave_nnz;
+    int64_t block_rows, block_nnz;
+    int64_t split_rows, split_segments, split_nnz;
+    int64_t sell_slots;          /* padded SELL slots (0 without SELL)         */
+} sp_profile;
+
+/* Fills *opt with the defaults listed above. */
+int sp_plan_options_default(sp_plan_options* opt);
+
+/* Creates a plan for the m x n CSR matrix (row_ptr, col_idx, val: device).
+ * When col_ptr/row_idx/cval (the CSC, e.g. from csr_to_csc) are non-NULL the
+ * plan also serves spmv_t ([LSMR] §4: both directions run as non-transposed
+ * CSR products); otherwise spmv_t returns SP_ERR_UNSUPPORTED.  opt may be NULL
+ * (defaults).  Copies row_ptr (and col_ptr) to the host once: synchronises
+ * `stream`.  The arrays must stay alive and unchanged until sp_plan_destroy.
+ * Errors: SP_ERR_NULL, SP_ERR_SIZE, SP_ERR_UNSUPPORTED (bad option), SP_ERR_HIP. */
+int sp_plan_create(sp_plan** plan, int64_t m, int64_t n, int64_t nnz,
+                   const int32_t* row_ptr, const int32_t* col_idx, const float* val,
+                   const int32_t* col_ptr, const int32_t* row_idx, const float* cval,
+                   const sp_plan_options* opt, void* stream);
+
+/* Bytes of device workspace the plan needs to serve spmv/spmv_t and spmm with
+ * up to max_N right-hand-side columns ([LSMR] §5.1: one query covering both
+ * directions). */
+int sp_plan_workspace_size(const sp_plan* plan, int32_t max_N, size_t* bytes);
+
+/* Attaches a device workspace of at least the queried size and uploads the
+ * plan's task tables into it (enqueued on `stream`).  The workspace must stay
+ * alive until sp_plan_destroy or the next bind.  Calls that share a plan share
+ * its workspace, so they must be ordered on one stream. */
+int sp_plan_bind(sp_plan* plan, void* work, size_t work_bytes, int32_t max_N, void* stream);
+
+/* Profile of A (transposed = 0) or of A^T (transposed = 1). */
+int sp_plan_profile(const sp_plan* plan, int32_t transposed, sp_profile* out);
+
+/* Frees the host-side plan. */
+int sp_plan_destroy(sp_plan* plan);
+
+/* --------------------------------------------------------- products
+ * spmv:   y = alpha * A x + beta * y     x: n floats, y: m floats (device)
+ *         ([LSMR] §2, (Av)_i as a sum over the row's entries; [LSMR] §5.2)
+ * spmv_t: z = alpha * A^T u + beta * z   u: m floats, z: n floats (device),
+ *         computed on the CSC held by the plan ([LSMR] §2, §4)
+ * spmm:   C = alpha * A B + beta * C     B: n x N row-major with leading
+ *         dimension ldb >= N, C: m x N row-major with ldc >= N (device)
+ *         ([GEN] §3, C[i,n] sums A[i,k] B[k,n] over the row's entries)
+ * Never allocate, never synchronise.  x/u/B must not alias y/z/C.
+ * Errors: SP_ERR_NULL, SP_ERR_SIZE (N < 1, ld < N, N above the bound max_N),
+ * SP_ERR_STATE (not bound), SP_ERR_UNSUPPORTED (spmv_t without CSC), SP_ERR_HIP.
+ */
+int spmv(const sp_plan* plan, float alpha, const float* x, float beta, float* y, void* stream);
+int spmv_t(const sp_plan* plan, float alpha, const float* u, float beta, float* z, void* stream);
+int spmm(const sp_plan* plan, int32_t N, float alpha, const float* B, int64_t ldb,
+         float beta, float* C, int64_t ldc, void* stream);
+
+/* --------------------------------------------------------- BSR SpMM
+ * [BCSR] §1 and [ASYNC] §2.2.1: block row pointer brow_ptr[mb+1], block column
+ * index bcol[nnzb] (increasing within a block row), and the nnzb dense
+ * bs x bs blocks stored one after another, each row-major ([BCSR] §2.1 indexes
+ * a block as row*bs + col).  [GEN] §3.4: each non-zero block is a small dense
+ * GEMM, here on MFMA with bf16 inputs and fp32 accumulation ([GEN] §5).
+ *
+ * C (mb*bs x N fp32, row-major, ldc >= N) = alpha * A B + beta * C, with
+ * B (kb*bs x N bf16 bit patterns, row-major, ldb >= N).  Supported: bs == 64,
+ * N % 64 == 0, ldb % 8 == 0, ldc % 4 == 0, B and C 16-byte aligned.
+ * work: at least bsr_spmm_bufsize() bytes (may be 0 bytes: then NULL is fine).
+ * Never synchronises.
+ * Errors: SP_ERR_NULL, SP_ERR_SIZE, SP_ERR_UNSUPPORTED, SP_ERR_WORKSPACE, SP_ERR_HIP.
+ */
+int bsr_spmm_bufsize(int64_t mb, int64_t kb, int32_t bs, int64_t nnzb, int32_t N, size_t* bytes);
+int bsr_spmm(int64_t mb, int64_t kb, int32_t bs, int64_t nnzb,
+             const int32_t* brow_ptr, const int32_t* bcol, const uint16_t* bval,
+             int32_t N, const uint16_t* B, int64_t ldb,
+             float alpha, float beta, float* C, int64_t ldc,
+             void* work, size_t work_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPMM_CSR_SPMV_H */

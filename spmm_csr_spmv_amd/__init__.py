@@ -1,0 +1,26 @@
+"""Sparse x dense products on AMD Instinct MI355X (gfx950).
+
+Python binding of libspmm_csr_spmv.so (C ABI in include/spmm_csr_spmv.h):
+CSR SpMV y = alpha A x + beta y, its transpose through a one-time CSC,
+CSR SpMM C = alpha A B + beta C, and BSR SpMM on MFMA (bf16 in, fp32
+accumulate).  All arithmetic runs in the library's HIP kernels; this package
+only marshals torch tensors into the C calls.  There is no CPU fallback:
+without the built library every call raises.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    Plan,
+    SparseError,
+    bsr_spmm,
+    csr_build_from_coo,
+    csr_to_csc,
+    lib,
+    plan_options,
+    sp_plan_create,
+    sp_version,
+    spmm,
+    spmv,
+    spmv_t,
+    status_string,
+)

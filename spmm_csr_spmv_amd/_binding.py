@@ -1,0 +1,274 @@
+"""ctypes binding of libspmm_csr_spmv.so -- argument marshalling only.
+
+Every function here has the name of the C entry point it calls and does no
+arithmetic of its own: it checks dtypes/devices, allocates outputs and
+workspaces with torch (PyTorch is the device-memory and stream provider),
+passes raw device pointers and the current torch HIP stream, and raises
+SparseError on a non-zero status.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspmm_csr_spmv.so")
+
+SP_OK = 0
+STATUS = {0: "SP_OK", 1: "SP_ERR_NULL", 2: "SP_ERR_SIZE", 3: "SP_ERR_INDEX", 4: "SP_ERR_WORKSPACE",
+          5: "SP_ERR_UNSUPPORTED", 6: "SP_ERR_HIP", 7: "SP_ERR_STATE"}
+
+# Names declared in include/spmm_csr_spmv.h.
+EXPORTS = ("sp_status_string", "sp_version", "csr_build_from_coo_bufsize", "csr_build_from_coo",
+           "csr_to_csc_bufsize", "csr_to_csc", "sp_plan_options_default", "sp_plan_create",
+           "sp_plan_workspace_size", "sp_plan_bind", "sp_plan_profile", "sp_plan_destroy", "spmv", "spmv_t", "spmm",
+           "bsr_spmm_bufsize", "bsr_spmm")
+
+
+class SparseError(RuntimeError):
+    def __init__(self, fn, code, lib=None):
+        msg = lib.sp_status_string(code).decode() if lib is not None else STATUS.get(code, str(code))
+        super().__init__("%s failed: %s" % (fn, msg))
+        self.code = code
+        self.fn = fn
+
+
+class sp_plan_options(ctypes.Structure):
+    _fields_ = [("group_nnz", ctypes.c_int32), ("wave_min", ctypes.c_int32), ("block_min", ctypes.c_int32),
+                ("split_min", ctypes.c_int32), ("split_seg", ctypes.c_int32), ("use_sell", ctypes.c_int32),
+                ("sell_sigma", ctypes.c_int32), ("xcd_remap", ctypes.c_int32)]
+
+
+class sp_profile(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("nnz", ctypes.c_int64),
+                ("mean", ctypes.c_double), ("var", ctypes.c_double), ("cv", ctypes.c_double),
+                ("p95", ctypes.c_int64), ("p99", ctypes.c_int64), ("max_len", ctypes.c_int64),
+                ("empty_rows", ctypes.c_int64),
+                ("group_tasks", ctypes.c_int64), ("group_rows", ctypes.c_int64), ("group_nnz", ctypes.c_int64),
+                ("wave_rows", ctypes.c_int64), ("wave_nnz", ctypes.c_int64),
+                ("block_rows", ctypes.c_int64), ("block_nnz", ctypes.c_int64),
+                ("split_rows", ctypes.c_int64), ("split_segments", ctypes.c_int64), ("split_nnz", ctypes.c_int64),
+                ("sell_slots", ctypes.c_int64)]
+
+
+_lib = None
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+
+def lib():
+    """The loaded library (loads it on first use; raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libspmm_csr_spmv.so is not built (%s); run __graft_entry__.build() or "
+                              "python -m spmm_csr_spmv_amd.build" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        L.sp_status_string.argtypes = [ctypes.c_int]
+        L.sp_status_string.restype = ctypes.c_char_p
+        L.sp_version.restype = ctypes.c_int
+        L.csr_build_from_coo_bufsize.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
+        L.csr_build_from_coo.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
+        L.csr_to_csc_bufsize.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
+        L.csr_to_csc.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
+        L.sp_plan_options_default.argtypes = [ctypes.POINTER(sp_plan_options)]
+        L.sp_plan_create.argtypes = [ctypes.POINTER(_p), _i64, _i64, _i64, _p, _p, _p, _p, _p, _p,
+                                     ctypes.POINTER(sp_plan_options), _p]
+        L.sp_plan_workspace_size.argtypes = [_p, _i32, ctypes.POINTER(_sz)]
+        L.sp_plan_bind.argtypes = [_p, _p, _sz, _i32, _p]
+        L.sp_plan_profile.argtypes = [_p, _i32, ctypes.POINTER(sp_profile)]
+        L.sp_plan_destroy.argtypes = [_p]
+        L.spmv.argtypes = [_p, _f, _p, _f, _p, _p]
+        L.spmv_t.argtypes = [_p, _f, _p, _f, _p, _p]
+        L.spmm.argtypes = [_p, _i32, _f, _p, _i64, _f, _p, _i64, _p]
+        L.bsr_spmm_bufsize.argtypes = [_i64, _i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
+        L.bsr_spmm.argtypes = [_i64, _i64, _i32, _i64, _p, _p, _p, _i32, _p, _i64, _f, _f, _p, _i64, _p, _sz, _p]
+        for name in EXPORTS:
+            if name not in ("sp_status_string", "sp_version"):
+                getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(fn, code):
+    if code != SP_OK:
+        raise SparseError(fn, code, lib())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _dev(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_cuda:
+        raise TypeError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise TypeError("%s must be contiguous" % name)
+    return t
+
+
+def status_string(code):
+    return lib().sp_status_string(code).decode()
+
+
+def sp_version():
+    return lib().sp_version()
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- conversions
+def csr_build_from_coo(m, n, coo_row, coo_col, coo_val, stream=None):
+    """COO (device int32/int32/float32, any order) -> (row_ptr, col_idx, val) on the device."""
+    L = lib()
+    _dev(coo_row, torch.int32, "coo_row"), _dev(coo_col, torch.int32, "coo_col"), _dev(coo_val, torch.float32, "coo_val")
+    nnz = coo_row.numel()
+    dev = coo_row.device
+    size = _sz()
+    _check("csr_build_from_coo_bufsize", L.csr_build_from_coo_bufsize(m, n, nnz, ctypes.byref(size)))
+    work = _workspace(size.value, dev)
+    row_ptr = torch.empty(m + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(nnz, dtype=torch.int32, device=dev)
+    val = torch.empty(nnz, dtype=torch.float32, device=dev)
+    _check("csr_build_from_coo",
+           L.csr_build_from_coo(m, n, nnz, _ptr(coo_row), _ptr(coo_col), _ptr(coo_val), _ptr(row_ptr), _ptr(col_idx),
+                                _ptr(val), _ptr(work), size.value, _stream(stream)))
+    return row_ptr, col_idx, val
+
+
+def csr_to_csc(m, n, row_ptr, col_idx, val, stream=None):
+    """CSR of an m x n matrix -> (col_ptr, row_idx, cval), the CSR of its transpose."""
+    L = lib()
+    _dev(row_ptr, torch.int32, "row_ptr"), _dev(col_idx, torch.int32, "col_idx"), _dev(val, torch.float32, "val")
+    nnz = col_idx.numel()
+    dev = row_ptr.device
+    size = _sz()
+    _check("csr_to_csc_bufsize", L.csr_to_csc_bufsize(m, n, nnz, ctypes.byref(size)))
+    work = _workspace(size.value, dev)
+    col_ptr = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    row_idx = torch.empty(nnz, dtype=torch.int32, device=dev)
+    cval = torch.empty(nnz, dtype=torch.float32, device=dev)
+    _check("csr_to_csc", L.csr_to_csc(m, n, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(val), _ptr(col_ptr),
+                                      _ptr(row_idx), _ptr(cval), _ptr(work), size.value, _stream(stream)))
+    return col_ptr, row_idx, cval
+
+
+# ---------------------------------------------------------------- plan
+def plan_options(**kw):
+    o = sp_plan_options()
+    _check("sp_plan_options_default", lib().sp_plan_options_default(ctypes.byref(o)))
+    for k, v in kw.items():
+        if not hasattr(o, k):
+            raise KeyError(k)
+        setattr(o, k, int(v))
+    return o
+
+
+class Plan:
+    """sp_plan of an m x n CSR matrix (and of its CSC when given), bound to a
+    torch-allocated workspace.  Holds references to the arrays it points to."""
+
+    def __init__(self, m, n, row_ptr, col_idx, val, csc=None, max_N=1, stream=None, **options):
+        L = lib()
+        self._arrays = (row_ptr, col_idx, val) + (tuple(csc) if csc is not None else ())
+        _dev(row_ptr, torch.int32, "row_ptr"), _dev(col_idx, torch.int32, "col_idx"), _dev(val, torch.float32, "val")
+        cp, ri, cv = csc if csc is not None else (None, None, None)
+        self.m, self.n, self.nnz = m, n, col_idx.numel()
+        self.opt = plan_options(**options)
+        h = ctypes.c_void_p()
+        _check("sp_plan_create",
+               L.sp_plan_create(ctypes.byref(h), m, n, self.nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(val),
+                                _ptr(cp) if cp is not None else None, _ptr(ri) if ri is not None else None,
+                                _ptr(cv) if cv is not None else None, ctypes.byref(self.opt), _stream(stream)))
+        self.handle = h
+        self.max_N = int(max_N)
+        size = _sz()
+        _check("sp_plan_workspace_size", L.sp_plan_workspace_size(h, self.max_N, ctypes.byref(size)))
+        self.workspace_bytes = size.value
+        self.work = _workspace(size.value, row_ptr.device)
+        _check("sp_plan_bind", L.sp_plan_bind(h, _ptr(self.work), size.value, self.max_N, _stream(stream)))
+
+    def profile(self, transposed=False):
+        p = sp_profile()
+        _check("sp_plan_profile", lib().sp_plan_profile(self.handle, 1 if transposed else 0, ctypes.byref(p)))
+        return {k: getattr(p, k) for k, _ in sp_profile._fields_}
+
+    def destroy(self):
+        if self.handle is not None and self.handle.value:
+            lib().sp_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def sp_plan_create(m, n, row_ptr, col_idx, val, csc=None, max_N=1, **options):
+    return Plan(m, n, row_ptr, col_idx, val, csc=csc, max_N=max_N, **options)
+
+
+# ---------------------------------------------------------------- products
+def spmv(plan, alpha, x, beta, y, stream=None):
+    """y = alpha * A x + beta * y (in place on y)."""
+    _dev(x, torch.float32, "x"), _dev(y, torch.float32, "y")
+    if x.numel() != plan.n or y.numel() != plan.m:
+        raise ValueError("x must have n entries and y m entries")
+    _check("spmv", lib().spmv(plan.handle, float(alpha), _ptr(x), float(beta), _ptr(y), _stream(stream)))
+    return y
+
+
+def spmv_t(plan, alpha, u, beta, z, stream=None):
+    """z = alpha * A^T u + beta * z (in place on z), through the plan's CSC."""
+    _dev(u, torch.float32, "u"), _dev(z, torch.float32, "z")
+    if u.numel() != plan.m or z.numel() != plan.n:
+        raise ValueError("u must have m entries and z n entries")
+    _check("spmv_t", lib().spmv_t(plan.handle, float(alpha), _ptr(u), float(beta), _ptr(z), _stream(stream)))
+    return z
+
+
+def spmm(plan, alpha, B, beta, C, stream=None):
+    """C = alpha * A B + beta * C (in place on C); B is n x N, C is m x N, row-major."""
+    _dev(B, torch.float32, "B"), _dev(C, torch.float32, "C")
+    N = B.shape[1]
+    if B.shape[0] != plan.n or C.shape[0] != plan.m or C.shape[1] != N:
+        raise ValueError("shape mismatch")
+    _check("spmm", lib().spmm(plan.handle, N, float(alpha), _ptr(B), N, float(beta), _ptr(C), N, _stream(stream)))
+    return C
+
+
+def bsr_spmm(mb, kb, bs, brow_ptr, bcol, bval, B, alpha, beta, C, stream=None, work=None):
+    """C = alpha * A B + beta * C with A in BSR (bf16 blocks as int16/uint16 bits or bfloat16),
+    B bf16 (kb*bs x N), C fp32 (mb*bs x N)."""
+    L = lib()
+    _dev(brow_ptr, torch.int32, "brow_ptr"), _dev(bcol, torch.int32, "bcol")
+    for name, t in (("bval", bval), ("B", B)):
+        if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+            raise TypeError("%s must hold bf16 bit patterns" % name)
+        if not t.is_cuda or not t.is_contiguous():
+            raise TypeError("%s must be a contiguous device tensor" % name)
+    _dev(C, torch.float32, "C")
+    nnzb = bcol.numel()
+    N = B.shape[1]
+    size = _sz()
+    _check("bsr_spmm_bufsize", L.bsr_spmm_bufsize(mb, kb, bs, nnzb, N, ctypes.byref(size)))
+    if size.value > 0 and work is None:
+        work = _workspace(size.value, C.device)
+    wbytes = size.value if work is not None else 0
+    _check("bsr_spmm", L.bsr_spmm(mb, kb, bs, nnzb, _ptr(brow_ptr), _ptr(bcol), _ptr(bval), N, _ptr(B), N,
+                                  float(alpha), float(beta), _ptr(C), N, _ptr(work) if work is not None else None,
+                                  wbytes, _stream(stream)))
+    return C

@@ -1,0 +1,558 @@
+// extern "C" entry points of libspmm_csr_spmv.so and the host side of the plan.
+//
+// The plan is built once per matrix (「通用稀疏矩阵乘法CUDA算子实现」 §4: a light
+// profile taken the first time the matrix is seen and cached with it): row
+// lengths l_i = row_ptr[i+1] - row_ptr[i] with their mean, variance and tail
+// (「CUDA LSMR 专栏（二）」 §5.3), then the row-to-kernel assignment.  Products
+// only read the plan; they never allocate or synchronise.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "internal.h"
+#include "spmm_csr_spmv.h"
+
+namespace spx {
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+hipError_t launch_check_indices(const int32_t* idx, int64_t nnz, int32_t n, int32_t* flag, hipStream_t s);
+}
+
+using spx::DirDevice;
+
+namespace {
+
+constexpr int64_t kI32Max = 2147483647;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Dir {
+    bool present = false;
+    int32_t rows = 0, cols = 0;
+    int64_t nnz = 0;
+    const int32_t* ptr = nullptr;
+    const int32_t* idx = nullptr;
+    const float* val = nullptr;
+    // host task tables, in launch order
+    std::vector<int4> tasks;       // split | block | wave | group
+    std::vector<int4> split_rows;  // {row, partial_base, nseg, 0}
+    int32_t n_split = 0, n_block = 0, n_wave = 0, n_group = 0;
+    int64_t n_partials = 0;        // total split segments
+    // SELL (host side)
+    std::vector<int64_t> sell_slice_ptr;
+    std::vector<int32_t> sell_perm, sell_len;
+    int64_t sell_slots = 0;
+    sp_profile prof{};
+    DirDevice dev{};
+    // workspace offsets (byte offsets into the bound workspace)
+    mutable size_t off_tasks = 0, off_split_rows = 0, off_partials = 0, off_counters = 0;
+    mutable size_t off_sell_ptr = 0, off_sell_perm = 0, off_sell_len = 0, off_sell_col = 0, off_sell_val = 0;
+};
+
+}  // namespace
+
+struct sp_plan {
+    int64_t m = 0, n = 0, nnz = 0;
+    sp_plan_options opt{};
+    Dir fwd, tr;
+    bool bound = false;
+    int32_t bound_max_N = 0;
+};
+
+namespace {
+
+// Nearest-rank percentile of the sorted lengths: smallest L such that at least
+// q percent of the rows have length <= L.
+int64_t nearest_rank(std::vector<int32_t>& len, int q) {
+    const int64_t m = (int64_t)len.size();
+    const int64_t k = (q * m + 99) / 100 - 1;
+    std::nth_element(len.begin(), len.begin() + k, len.end());
+    return len[(size_t)k];
+}
+
+void profile_rows(const std::vector<int32_t>& hptr, Dir& d) {
+    sp_profile& p = d.prof;
+    std::memset(&p, 0, sizeof p);
+    p.rows = d.rows;
+    p.cols = d.cols;
+    p.nnz = d.nnz;
+    const int64_t m = d.rows;
+    if (m == 0) return;
+    std::vector<int32_t> len((size_t)m);
+    double sum = 0.0;
+    int64_t mx = 0, empty = 0;
+    for (int64_t i = 0; i < m; ++i) {
+        len[(size_t)i] = hptr[(size_t)i + 1] - hptr[(size_t)i];
+        sum += len[(size_t)i];
+        mx = std::max<int64_t>(mx, len[(size_t)i]);
+        empty += len[(size_t)i] == 0;
+    }
+    const double mean = sum / (double)m;
+    double var = 0.0;
+    for (int64_t i = 0; i < m; ++i) var += (len[(size_t)i] - mean) * (len[(size_t)i] - mean);
+    var /= (double)m;
+    p.mean = mean;
+    p.var = var;
+    p.cv = mean > 0.0 ? std::sqrt(var) / mean : 0.0;
+    p.max_len = mx;
+    p.empty_rows = empty;
+    p.p95 = nearest_rank(len, 95);
+    p.p99 = nearest_rank(len, 99);
+}
+
+// Row-to-bin assignment (see the sp_plan_options comment in the public header).
+void assign_bins(const std::vector<int32_t>& hptr, const sp_plan_options& o, Dir& d) {
+    std::vector<int4> split, block, wave, group;
+    sp_profile& p = d.prof;
+    d.split_rows.clear();
+    d.n_partials = 0;
+    int32_t g_r0 = 0, g_rows = 0;
+    int64_t g_nnz = 0;
+    auto close_group = [&](int32_t next_row) {
+        if (g_rows > 0) {
+            group.push_back(make_int4(g_r0, g_r0 + g_rows, hptr[(size_t)g_r0], hptr[(size_t)(g_r0 + g_rows)]));
+            p.group_tasks += 1;
+            p.group_rows += g_rows;
+            p.group_nnz += g_nnz;
+        }
+        g_r0 = next_row;
+        g_rows = 0;
+        g_nnz = 0;
+    };
+    for (int32_t r = 0; r < d.rows; ++r) {
+        const int32_t b = hptr[(size_t)r], e = hptr[(size_t)r + 1];
+        const int32_t l = e - b;
+        if (l > o.split_min) {
+            close_group(r + 1);
+            const int32_t nseg = (int32_t)((l + (int64_t)o.split_seg - 1) / o.split_seg);
+            const int32_t id = (int32_t)d.split_rows.size();
+            d.split_rows.push_back(make_int4(r, (int32_t)d.n_partials, nseg, 0));
+            for (int32_t s = 0; s < nseg; ++s) {
+                const int32_t sb = b + s * o.split_seg;
+                const int32_t se = std::min<int64_t>(e, (int64_t)sb + o.split_seg);
+                split.push_back(make_int4(id, s, sb, se));
+            }
+            d.n_partials += nseg;
+            p.split_rows += 1;
+            p.split_segments += nseg;
+            p.split_nnz += l;
+        } else if (l > o.block_min) {
+            close_group(r + 1);
+            block.push_back(make_int4(r, b, e, 0));
+            p.block_rows += 1;
+            p.block_nnz += l;
+        } else if (l > o.wave_min) {
+            close_group(r + 1);
+            wave.push_back(make_int4(r, b, e, 0));
+            p.wave_rows += 1;
+            p.wave_nnz += l;
+        } else {
+            if (g_rows > 0 && (g_nnz + l > o.group_nnz || g_rows == spx::kGroupMaxRows)) close_group(r);
+            if (g_rows == 0) g_r0 = r;
+            g_rows += 1;
+            g_nnz += l;
+        }
+    }
+    close_group(d.rows);
+    d.tasks.clear();
+    d.tasks.reserve(split.size() + block.size() + wave.size() + group.size());
+    d.tasks.insert(d.tasks.end(), split.begin(), split.end());
+    d.tasks.insert(d.tasks.end(), block.begin(), block.end());
+    d.tasks.insert(d.tasks.end(), wave.begin(), wave.end());
+    d.tasks.insert(d.tasks.end(), group.begin(), group.end());
+    d.n_split = (int32_t)split.size();
+    d.n_block = (int32_t)block.size();
+    d.n_wave = (int32_t)wave.size();
+    d.n_group = (int32_t)group.size();
+}
+
+// SELL-C-sigma layout of the group rows (C = 64): windows of sigma rows sorted
+// by decreasing length (ties by row index); rows served by another bin keep
+// their place in the window order with length -1 (sorted after every group
+// row) and contribute no slots.
+void build_sell(const std::vector<int32_t>& hptr, const sp_plan_options& o, Dir& d) {
+    const int64_t m = d.rows;
+    std::vector<int32_t> len((size_t)m);
+    for (int64_t i = 0; i < m; ++i) {
+        const int32_t l = hptr[(size_t)i + 1] - hptr[(size_t)i];
+        len[(size_t)i] = l <= o.wave_min ? l : -1;
+    }
+    d.sell_perm.resize((size_t)m);
+    for (int64_t i = 0; i < m; ++i) d.sell_perm[(size_t)i] = (int32_t)i;
+    for (int64_t w = 0; w < m; w += o.sell_sigma) {
+        const int64_t e = std::min<int64_t>(m, w + o.sell_sigma);
+        std::stable_sort(d.sell_perm.begin() + w, d.sell_perm.begin() + e,
+                         [&](int32_t a, int32_t b) { return len[(size_t)a] > len[(size_t)b]; });
+    }
+    d.sell_len.resize((size_t)m);
+    for (int64_t k = 0; k < m; ++k) d.sell_len[(size_t)k] = len[(size_t)d.sell_perm[(size_t)k]];
+    const int64_t slices = (m + 63) / 64;
+    d.sell_slice_ptr.assign((size_t)slices + 1, 0);
+    int64_t slots = 0;
+    for (int64_t s = 0; s < slices; ++s) {
+        int32_t width = 0;
+        for (int64_t k = s * 64; k < std::min<int64_t>(m, s * 64 + 64); ++k) width = std::max(width, d.sell_len[(size_t)k]);
+        d.sell_slice_ptr[(size_t)s] = slots;
+        slots += (int64_t)width * 64;
+    }
+    d.sell_slice_ptr[(size_t)slices] = slots;
+    d.sell_slots = slots;
+    d.prof.sell_slots = slots;
+}
+
+size_t dir_layout(const Dir& d, const sp_plan_options& o, int32_t max_N, size_t base) {
+    size_t off = base;
+    d.off_tasks = off;
+    off = align256(off + d.tasks.size() * sizeof(int4));
+    d.off_split_rows = off;
+    off = align256(off + d.split_rows.size() * sizeof(int4));
+    d.off_partials = off;
+    off = align256(off + (size_t)d.n_partials * (size_t)std::max(1, max_N) * sizeof(float));
+    const int64_t max_tiles = std::max<int64_t>(1, (max_N + 63) / 64);
+    d.off_counters = off;
+    off = align256(off + d.split_rows.size() * (size_t)max_tiles * sizeof(int32_t));
+    if (o.use_sell) {
+        d.off_sell_ptr = off;
+        off = align256(off + d.sell_slice_ptr.size() * sizeof(int64_t));
+        d.off_sell_perm = off;
+        off = align256(off + d.sell_perm.size() * sizeof(int32_t));
+        d.off_sell_len = off;
+        off = align256(off + d.sell_len.size() * sizeof(int32_t));
+        d.off_sell_col = off;
+        off = align256(off + (size_t)d.sell_slots * sizeof(int32_t));
+        d.off_sell_val = off;
+        off = align256(off + (size_t)d.sell_slots * sizeof(float));
+    }
+    return off;
+}
+
+// The first 256 bytes of the workspace hold the index-check flag of bind.
+constexpr size_t kMiscBytes = 256;
+
+size_t plan_layout(const sp_plan* p, int32_t max_N) {
+    size_t off = kMiscBytes;
+    if (p->fwd.present) off = dir_layout(p->fwd, p->opt, max_N, off);
+    if (p->tr.present) off = dir_layout(p->tr, p->opt, max_N, off);
+    return off < 256 ? 256 : off;
+}
+
+int check_options(const sp_plan_options& o) {
+    if (o.group_nnz < 64 || o.group_nnz > spx::kGroupMaxNnz) return SP_ERR_UNSUPPORTED;
+    if (o.wave_min < 0 || o.wave_min > o.group_nnz) return SP_ERR_UNSUPPORTED;
+    if (o.block_min < o.wave_min || o.split_min < o.block_min) return SP_ERR_UNSUPPORTED;
+    if (o.split_seg < 16) return SP_ERR_UNSUPPORTED;
+    if (o.use_sell != 0 && o.use_sell != 1) return SP_ERR_UNSUPPORTED;
+    if (o.sell_sigma < 1) return SP_ERR_UNSUPPORTED;
+    if (o.xcd_remap != 0 && o.xcd_remap != 1) return SP_ERR_UNSUPPORTED;
+    return SP_OK;
+}
+
+int setup_dir(Dir& d, int64_t rows, int64_t cols, int64_t nnz, const int32_t* ptr, const int32_t* idx, const float* val,
+              const sp_plan_options& o, hipStream_t s) {
+    d.present = true;
+    d.rows = (int32_t)rows;
+    d.cols = (int32_t)cols;
+    d.nnz = nnz;
+    d.ptr = ptr;
+    d.idx = idx;
+    d.val = val;
+    std::vector<int32_t> hptr((size_t)rows + 1);
+    if (hipMemcpyAsync(hptr.data(), ptr, ((size_t)rows + 1) * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return SP_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return SP_ERR_HIP;
+    if (hptr[0] != 0 || (int64_t)hptr[(size_t)rows] != nnz) return SP_ERR_SIZE;
+    for (int64_t i = 0; i < rows; ++i)
+        if (hptr[(size_t)i + 1] < hptr[(size_t)i]) return SP_ERR_SIZE;
+    profile_rows(hptr, d);
+    assign_bins(hptr, o, d);
+    if (o.use_sell) build_sell(hptr, o, d);
+    return SP_OK;
+}
+
+int upload_dir(Dir& d, char* ws, const sp_plan_options& o, hipStream_t s) {
+    DirDevice& v = d.dev;
+    v = DirDevice{};
+    v.rows = d.rows;
+    v.cols = d.cols;
+    v.ptr = d.ptr;
+    v.idx = d.idx;
+    v.val = d.val;
+    v.tasks = reinterpret_cast<const int4*>(ws + d.off_tasks);
+    v.n_split = d.n_split;
+    v.n_block = d.n_block;
+    v.n_wave = d.n_wave;
+    v.n_group = d.n_group;
+    v.split_rows = reinterpret_cast<const int4*>(ws + d.off_split_rows);
+    v.n_split_rows = (int32_t)d.split_rows.size();
+    v.partials = reinterpret_cast<float*>(ws + d.off_partials);
+    v.counters = reinterpret_cast<int32_t*>(ws + d.off_counters);
+    v.xcd_remap = o.xcd_remap;
+    v.group_cap = o.group_nnz;
+    if (!d.tasks.empty() &&
+        hipMemcpyAsync(ws + d.off_tasks, d.tasks.data(), d.tasks.size() * sizeof(int4), hipMemcpyHostToDevice, s) !=
+            hipSuccess)
+        return SP_ERR_HIP;
+    if (!d.split_rows.empty() &&
+        hipMemcpyAsync(ws + d.off_split_rows, d.split_rows.data(), d.split_rows.size() * sizeof(int4),
+                       hipMemcpyHostToDevice, s) != hipSuccess)
+        return SP_ERR_HIP;
+    if (o.use_sell) {
+        v.use_sell = 1;
+        v.sell_slices = (int32_t)(d.sell_slice_ptr.size() - 1);
+        v.sell_slice_ptr = reinterpret_cast<const int64_t*>(ws + d.off_sell_ptr);
+        v.sell_perm = reinterpret_cast<const int32_t*>(ws + d.off_sell_perm);
+        v.sell_len = reinterpret_cast<const int32_t*>(ws + d.off_sell_len);
+        v.sell_col = reinterpret_cast<const int32_t*>(ws + d.off_sell_col);
+        v.sell_val = reinterpret_cast<const float*>(ws + d.off_sell_val);
+        if (hipMemcpyAsync(ws + d.off_sell_ptr, d.sell_slice_ptr.data(), d.sell_slice_ptr.size() * sizeof(int64_t),
+                           hipMemcpyHostToDevice, s) != hipSuccess)
+            return SP_ERR_HIP;
+        if (d.rows > 0 &&
+            (hipMemcpyAsync(ws + d.off_sell_perm, d.sell_perm.data(), d.sell_perm.size() * sizeof(int32_t),
+                            hipMemcpyHostToDevice, s) != hipSuccess ||
+             hipMemcpyAsync(ws + d.off_sell_len, d.sell_len.data(), d.sell_len.size() * sizeof(int32_t),
+                            hipMemcpyHostToDevice, s) != hipSuccess))
+            return SP_ERR_HIP;
+        if (spx::launch_sell_fill(v, d.sell_slots, reinterpret_cast<int32_t*>(ws + d.off_sell_col),
+                                  reinterpret_cast<float*>(ws + d.off_sell_val), s) != hipSuccess)
+            return SP_ERR_HIP;
+    }
+    return SP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sp_status_string(int status) {
+    switch (status) {
+        case SP_OK: return "SP_OK";
+        case SP_ERR_NULL: return "SP_ERR_NULL: a required pointer is NULL";
+        case SP_ERR_SIZE: return "SP_ERR_SIZE: a size is negative, too large or inconsistent";
+        case SP_ERR_INDEX: return "SP_ERR_INDEX: an index is outside its dimension";
+        case SP_ERR_WORKSPACE: return "SP_ERR_WORKSPACE: workspace missing or too small";
+        case SP_ERR_UNSUPPORTED: return "SP_ERR_UNSUPPORTED: option, shape or layout not supported";
+        case SP_ERR_HIP: return "SP_ERR_HIP: a HIP call or kernel launch failed";
+        case SP_ERR_STATE: return "SP_ERR_STATE: plan not bound to a workspace";
+        default: return "unknown status";
+    }
+}
+
+int sp_version(void) { return 100; }
+
+// ------------------------------------------------------------------ conversions
+static int check_dims(int64_t m, int64_t n, int64_t nnz) {
+    if (m < 0 || n < 0 || nnz < 0 || m > kI32Max || n > kI32Max || nnz > kI32Max) return SP_ERR_SIZE;
+    // row_ptr entries and positions must fit int32 (m + 1 included)
+    if (m + 1 > kI32Max || n + 1 > kI32Max) return SP_ERR_SIZE;
+    return SP_OK;
+}
+
+int csr_build_from_coo_bufsize(int64_t m, int64_t n, int64_t nnz, size_t* bytes) {
+    if (!bytes) return SP_ERR_NULL;
+    const int rc = check_dims(m, n, nnz);
+    if (rc) return rc;
+    *bytes = spx::coo_build_bytes(m, n, nnz);
+    return SP_OK;
+}
+
+int csr_build_from_coo(int64_t m, int64_t n, int64_t nnz, const int32_t* coo_row, const int32_t* coo_col,
+                       const float* coo_val, int32_t* row_ptr, int32_t* col_idx, float* val, void* work,
+                       size_t work_bytes, void* stream) {
+    int rc = check_dims(m, n, nnz);
+    if (rc) return rc;
+    if (!row_ptr || (nnz > 0 && (!coo_row || !coo_col || !coo_val || !col_idx || !val))) return SP_ERR_NULL;
+    if (!work) return SP_ERR_WORKSPACE;
+    return spx::coo_to_csr_device(m, n, nnz, coo_row, coo_col, coo_val, row_ptr, col_idx, val, work, work_bytes,
+                                  (hipStream_t)stream);
+}
+
+int csr_to_csc_bufsize(int64_t m, int64_t n, int64_t nnz, size_t* bytes) {
+    if (!bytes) return SP_ERR_NULL;
+    const int rc = check_dims(m, n, nnz);
+    if (rc) return rc;
+    *bytes = spx::csc_build_bytes(m, n, nnz);
+    return SP_OK;
+}
+
+int csr_to_csc(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx, const float* val,
+               int32_t* col_ptr, int32_t* row_idx, float* cval, void* work, size_t work_bytes, void* stream) {
+    int rc = check_dims(m, n, nnz);
+    if (rc) return rc;
+    if (!row_ptr || !col_ptr || (nnz > 0 && (!col_idx || !val || !row_idx || !cval))) return SP_ERR_NULL;
+    if (!work) return SP_ERR_WORKSPACE;
+    return spx::csr_to_csc_device(m, n, nnz, row_ptr, col_idx, val, col_ptr, row_idx, cval, work, work_bytes,
+                                  (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------------ plan
+int sp_plan_options_default(sp_plan_options* o) {
+    if (!o) return SP_ERR_NULL;
+    o->group_nnz = 2048;
+    o->wave_min = 256;
+    o->block_min = 4096;
+    o->split_min = 32768;
+    o->split_seg = 8192;
+    o->use_sell = 0;
+    o->sell_sigma = 1024;
+    o->xcd_remap = 1;
+    return SP_OK;
+}
+
+int sp_plan_create(sp_plan** plan, int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                   const float* val, const int32_t* col_ptr, const int32_t* row_idx, const float* cval,
+                   const sp_plan_options* opt, void* stream) {
+    if (!plan) return SP_ERR_NULL;
+    *plan = nullptr;
+    int rc = check_dims(m, n, nnz);
+    if (rc) return rc;
+    if (!row_ptr || (nnz > 0 && (!col_idx || !val))) return SP_ERR_NULL;
+    const bool has_t = col_ptr != nullptr;
+    if (has_t && nnz > 0 && (!row_idx || !cval)) return SP_ERR_NULL;
+    sp_plan_options o;
+    if (opt) {
+        o = *opt;
+    } else {
+        sp_plan_options_default(&o);
+    }
+    rc = check_options(o);
+    if (rc) return rc;
+    // the kernels stream indices and values with 16-byte loads
+    auto misaligned = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) != 0; };
+    if (misaligned(col_idx) || misaligned(val) || (has_t && (misaligned(row_idx) || misaligned(cval))))
+        return SP_ERR_UNSUPPORTED;
+    sp_plan* p = new (std::nothrow) sp_plan;
+    if (!p) return SP_ERR_SIZE;
+    p->m = m;
+    p->n = n;
+    p->nnz = nnz;
+    p->opt = o;
+    hipStream_t s = (hipStream_t)stream;
+    rc = setup_dir(p->fwd, m, n, nnz, row_ptr, col_idx, val, o, s);
+    if (rc == SP_OK && has_t) rc = setup_dir(p->tr, n, m, nnz, col_ptr, row_idx, cval, o, s);
+    if (rc != SP_OK) {
+        delete p;
+        return rc;
+    }
+    *plan = p;
+    return SP_OK;
+}
+
+int sp_plan_workspace_size(const sp_plan* plan, int32_t max_N, size_t* bytes) {
+    if (!plan || !bytes) return SP_ERR_NULL;
+    if (max_N < 1) return SP_ERR_SIZE;
+    *bytes = plan_layout(plan, max_N);
+    return SP_OK;
+}
+
+int sp_plan_bind(sp_plan* plan, void* work, size_t work_bytes, int32_t max_N, void* stream) {
+    if (!plan) return SP_ERR_NULL;
+    if (max_N < 1) return SP_ERR_SIZE;
+    const size_t need = plan_layout(plan, max_N);
+    if (!work || work_bytes < need) return SP_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = static_cast<char*>(work);
+    plan->bound = false;
+    // every stored index must lie inside its dimension before any product runs
+    int32_t* flag = reinterpret_cast<int32_t*>(ws);
+    if (spx::launch_fill_i32(flag, 1, 0, s) != hipSuccess) return SP_ERR_HIP;
+    for (const Dir* d : {&plan->fwd, &plan->tr}) {
+        if (d->present && spx::launch_check_indices(d->idx, d->nnz, d->cols, flag, s) != hipSuccess)
+            return SP_ERR_HIP;
+    }
+    int32_t bad = 0;
+    if (hipMemcpyAsync(&bad, flag, sizeof bad, hipMemcpyDeviceToHost, s) != hipSuccess) return SP_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return SP_ERR_HIP;
+    if (bad) return SP_ERR_INDEX;
+    int rc = SP_OK;
+    if (plan->fwd.present) rc = upload_dir(plan->fwd, ws, plan->opt, s);
+    if (rc == SP_OK && plan->tr.present) rc = upload_dir(plan->tr, ws, plan->opt, s);
+    if (rc != SP_OK) return rc;
+    // arrival counters start at zero; the kernels put them back to zero
+    for (Dir* d : {&plan->fwd, &plan->tr}) {
+        if (!d->present || d->split_rows.empty()) continue;
+        const int64_t max_tiles = std::max<int64_t>(1, (max_N + 63) / 64);
+        if (spx::launch_fill_i32(d->dev.counters, (int64_t)d->split_rows.size() * max_tiles, 0, s) != hipSuccess)
+            return SP_ERR_HIP;
+    }
+    plan->bound = true;
+    plan->bound_max_N = max_N;
+    return SP_OK;
+}
+
+int sp_plan_profile(const sp_plan* plan, int32_t transposed, sp_profile* out) {
+    if (!plan || !out) return SP_ERR_NULL;
+    const Dir& d = transposed ? plan->tr : plan->fwd;
+    if (!d.present) return SP_ERR_UNSUPPORTED;
+    *out = d.prof;
+    return SP_OK;
+}
+
+int sp_plan_destroy(sp_plan* plan) {
+    delete plan;
+    return SP_OK;
+}
+
+// ------------------------------------------------------------------ products
+int spmv(const sp_plan* plan, float alpha, const float* x, float beta, float* y, void* stream) {
+    if (!plan) return SP_ERR_NULL;
+    if (!plan->bound) return SP_ERR_STATE;
+    if ((plan->n > 0 && !x) || (plan->m > 0 && !y)) return SP_ERR_NULL;
+    if (plan->m == 0) return SP_OK;
+    return spx::launch_spmv(plan->fwd.dev, alpha, x, beta, y, (hipStream_t)stream) == hipSuccess ? SP_OK : SP_ERR_HIP;
+}
+
+int spmv_t(const sp_plan* plan, float alpha, const float* u, float beta, float* z, void* stream) {
+    if (!plan) return SP_ERR_NULL;
+    if (!plan->tr.present) return SP_ERR_UNSUPPORTED;
+    if (!plan->bound) return SP_ERR_STATE;
+    if ((plan->m > 0 && !u) || (plan->n > 0 && !z)) return SP_ERR_NULL;
+    if (plan->n == 0) return SP_OK;
+    return spx::launch_spmv(plan->tr.dev, alpha, u, beta, z, (hipStream_t)stream) == hipSuccess ? SP_OK : SP_ERR_HIP;
+}
+
+int spmm(const sp_plan* plan, int32_t N, float alpha, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
+         void* stream) {
+    if (!plan) return SP_ERR_NULL;
+    if (!plan->bound) return SP_ERR_STATE;
+    if (N < 1 || ldb < N || ldc < N) return SP_ERR_SIZE;
+    if (!plan->fwd.split_rows.empty() && N > plan->bound_max_N) return SP_ERR_SIZE;
+    if ((plan->n > 0 && !B) || (plan->m > 0 && !C)) return SP_ERR_NULL;
+    if (plan->m == 0) return SP_OK;
+    return spx::launch_spmm(plan->fwd.dev, N, alpha, B, ldb, beta, C, ldc, (hipStream_t)stream) == hipSuccess
+               ? SP_OK
+               : SP_ERR_HIP;
+}
+
+// ------------------------------------------------------------------ BSR
+int bsr_spmm_bufsize(int64_t mb, int64_t kb, int32_t bs, int64_t nnzb, int32_t N, size_t* bytes) {
+    if (!bytes) return SP_ERR_NULL;
+    if (mb < 0 || kb < 0 || nnzb < 0 || N < 0 || mb > kI32Max || kb > kI32Max || nnzb > kI32Max) return SP_ERR_SIZE;
+    if (bs != 64) return SP_ERR_UNSUPPORTED;
+    *bytes = spx::bsr_work_bytes(mb, kb, bs, nnzb, N);
+    return SP_OK;
+}
+
+int bsr_spmm(int64_t mb, int64_t kb, int32_t bs, int64_t nnzb, const int32_t* brow_ptr, const int32_t* bcol,
+             const uint16_t* bval, int32_t N, const uint16_t* B, int64_t ldb, float alpha, float beta, float* C,
+             int64_t ldc, void* work, size_t work_bytes, void* stream) {
+    if (mb < 0 || kb < 0 || nnzb < 0 || N < 0 || mb > kI32Max || kb > kI32Max || nnzb > kI32Max) return SP_ERR_SIZE;
+    if (bs != 64) return SP_ERR_UNSUPPORTED;
+    if (mb * 64 > kI32Max || kb * 64 > kI32Max) return SP_ERR_SIZE;
+    if (ldb < N || ldc < N) return SP_ERR_SIZE;
+    if (N % 64 != 0 || ldb % 8 != 0 || ldc % 4 != 0) return SP_ERR_UNSUPPORTED;
+    if (mb > 0 && N > 0 && (!brow_ptr || !C)) return SP_ERR_NULL;
+    if (nnzb > 0 && N > 0 && (!bcol || !bval || !B)) return SP_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(B) & 15) || (reinterpret_cast<uintptr_t>(C) & 15) ||
+        (reinterpret_cast<uintptr_t>(bval) & 15))
+        return SP_ERR_UNSUPPORTED;
+    const size_t need = spx::bsr_work_bytes(mb, kb, bs, nnzb, N);
+    if (need > 0 && (!work || work_bytes < need)) return SP_ERR_WORKSPACE;
+    return spx::bsr_spmm_device(mb, kb, bs, nnzb, brow_ptr, bcol, bval, N, B, ldb, alpha, beta, C, ldc, work,
+                                work_bytes, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,248 @@
+// CSR SpMV  y = alpha * A x + beta * y  for gfx950.
+//
+// One launch serves every row bin of a plan (「通用稀疏矩阵乘法CUDA算子实现」 §2:
+// the parallel grain must follow the row length, §4: the bins come from a
+// cached profile).  The grid is the concatenation
+//     [split segments | block rows | wave rows (4 per workgroup) | groups]
+// so the longest tasks are dispatched first, and the bin of a workgroup is a
+// uniform branch on blockIdx.  The same kernel computes A^T u on the CSC
+// (「CUDA LSMR 专栏（二）」 §2, §4: the CSC arrays are the CSR of A^T).
+//
+// Every bin streams values and column indices with 16-byte loads, gathers x,
+// and fuses the axpby epilogue y = alpha*acc + beta*y into its single store
+// (「CUDA LSMR 专栏（二）」 §5.2); beta == 0 never reads y.
+#include "device_common.h"
+
+namespace spx {
+
+namespace {
+
+// Products val[q] * x[idx[q]] for q in [b, e), 4-aligned 16-byte loads for the
+// interior and guarded scalar loads at the ragged ends.  `emit(q, prod)`
+// receives each product; lanes step by 4*stride entries.
+template <class Emit>
+__device__ __forceinline__ void stream_products(const int32_t* __restrict__ idx, const float* __restrict__ val,
+                                                const float* __restrict__ x, int b, int e, int lane, int stride,
+                                                Emit emit) {
+    const int base = b & ~3;
+    for (int v = base + 4 * lane; v < e; v += 4 * stride) {
+        if (v >= b && v + 4 <= e) {
+            const int4 c = ldg4_nt(idx + v);
+            const float4 a = ldg4_nt(val + v);
+            const float x0 = x[c.x], x1 = x[c.y], x2 = x[c.z], x3 = x[c.w];
+            emit(v + 0, a.x * x0);
+            emit(v + 1, a.y * x1);
+            emit(v + 2, a.z * x2);
+            emit(v + 3, a.w * x3);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int q = v + j;
+                if (q >= b && q < e) emit(q, val[q] * x[idx[q]]);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void store_axpby(float* __restrict__ y, int row, float acc, float alpha, float beta) {
+    float o = alpha * acc;
+    if (beta != 0.0f) o = fmaf(beta, y[row], o);
+    y[row] = o;
+}
+
+// Threads per row for a group of `nrows` rows: the largest power of two
+// (at most 64) with g * nrows <= 256.
+__device__ __forceinline__ int group_lanes(int nrows) {
+    int g = 64;
+    while (g > 1 && g * nrows > kBlock) g >>= 1;
+    return g;
+}
+
+// ---- group: consecutive short rows staged through LDS --------------------
+__device__ void group_task(const int4 t, const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+                           const float* __restrict__ val, const float* __restrict__ x, float alpha, float beta,
+                           float* __restrict__ y, float* lds) {
+    const int r0 = t.x, r1 = t.y, b = t.z, e = t.w;
+    const int tid = threadIdx.x;
+    stream_products(idx, val, x, b, e, tid, kBlock, [&](int q, float p) { lds[q - b] = p; });
+    __syncthreads();
+    const int nrows = r1 - r0;
+    const int g = group_lanes(nrows);
+    const int slot = tid / g, lane = tid - slot * g;
+    const int row = r0 + slot;
+    const bool active = slot < nrows;
+    float s = 0.0f;
+    if (active) {
+        const int rb = ptr[row] - b, re = ptr[row + 1] - b;
+        for (int k = rb + lane; k < re; k += g) s += lds[k];
+    }
+    s = group_sum(s, g);
+    if (active && lane == 0) store_axpby(y, row, s, alpha, beta);
+}
+
+// ---- wave: one row per wave64 ----------------------------------------------
+__device__ void wave_task(const int4 t, const int32_t* __restrict__ idx, const float* __restrict__ val,
+                          const float* __restrict__ x, float alpha, float beta, float* __restrict__ y, bool valid) {
+    const int lane = threadIdx.x & 63;
+    float s = 0.0f;
+    if (valid) stream_products(idx, val, x, t.y, t.z, lane, 64, [&](int, float p) { s += p; });
+    s = wave_sum(s);
+    if (valid && lane == 0) store_axpby(y, t.x, s, alpha, beta);
+}
+
+// Sum of a 256-thread workgroup over [b, e) (valid in thread 0).
+__device__ __forceinline__ float block_reduce_range(const int32_t* __restrict__ idx, const float* __restrict__ val,
+                                                    const float* __restrict__ x, int b, int e, float* lds) {
+    const int tid = threadIdx.x;
+    float s = 0.0f;
+    stream_products(idx, val, x, b, e, tid, kBlock, [&](int, float p) { s += p; });
+    s = wave_sum(s);
+    if ((tid & 63) == 0) lds[tid >> 6] = s;
+    __syncthreads();
+    float r = 0.0f;
+    if (tid == 0) r = (lds[0] + lds[1]) + (lds[2] + lds[3]);
+    return r;
+}
+
+// ---- block: one row per workgroup ---------------------------------------------
+__device__ void block_task(const int4 t, const int32_t* __restrict__ idx, const float* __restrict__ val,
+                           const float* __restrict__ x, float alpha, float beta, float* __restrict__ y, float* lds) {
+    const float s = block_reduce_range(idx, val, x, t.y, t.z, lds);
+    if (threadIdx.x == 0) store_axpby(y, t.x, s, alpha, beta);
+}
+
+// ---- split: one segment of a very long row per workgroup ------------------
+// The segment's sum goes to partials[]; the workgroup that finishes last
+// (integer arrival counter) adds the row's partials in segment order, so the
+// result does not depend on arrival order.  The counter is put back to 0 by
+// that last workgroup, ready for the next launch.
+__device__ void split_task(const int4 t, const int4* __restrict__ split_rows, const int32_t* __restrict__ idx,
+                           const float* __restrict__ val, const float* __restrict__ x, float alpha, float beta,
+                           float* __restrict__ y, float* partials, int32_t* counters, float* lds) {
+    const int4 sr = split_rows[t.x];  // {row, partial_base, nseg, 0}
+    const float s = block_reduce_range(idx, val, x, t.z, t.w, lds);
+    if (threadIdx.x == 0) {
+        atomic_store_f(partials + sr.y + t.y, s);
+        const int arrived = __hip_atomic_fetch_add(counters + t.x, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (arrived == sr.z - 1) {
+            float acc = 0.0f;
+            for (int k = 0; k < sr.z; ++k) acc += atomic_load_f(partials + sr.y + k);
+            store_axpby(y, sr.x, acc, alpha, beta);
+            __hip_atomic_store(counters + t.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void spmv_bins_kernel(
+    const int4* __restrict__ tasks, int n_split, int n_block, int n_wave, int n_group, int xcd_remap,
+    const int4* __restrict__ split_rows, const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+    const float* __restrict__ val, const float* __restrict__ x, float alpha, float beta, float* __restrict__ y,
+    float* partials, int32_t* counters) {
+    extern __shared__ float lds[];
+    int b = blockIdx.x;
+    if (b < n_split) {
+        split_task(tasks[b], split_rows, idx, val, x, alpha, beta, y, partials, counters, lds);
+        return;
+    }
+    b -= n_split;
+    if (b < n_block) {
+        block_task(tasks[n_split + b], idx, val, x, alpha, beta, y, lds);
+        return;
+    }
+    b -= n_block;
+    const int n_wave_wg = (n_wave + 3) / 4;
+    if (b < n_wave_wg) {
+        const int w = 4 * b + (threadIdx.x >> 6);
+        const bool valid = w < n_wave;
+        const int4 t = valid ? tasks[n_split + n_block + w] : make_int4(0, 0, 0, 0);
+        wave_task(t, idx, val, x, alpha, beta, y, valid);
+        return;
+    }
+    b -= n_wave_wg;
+    const int first = n_split + n_block + n_wave_wg;
+    const int g = xcd_remap ? xcd_contiguous(blockIdx.x, first, n_group) : b;
+    group_task(tasks[n_split + n_block + n_wave + g], ptr, idx, val, x, alpha, beta, y, lds);
+}
+
+// ---- SELL-C-sigma, C = 64: one wave per slice, one lane per row -----------
+// (「通用稀疏矩阵乘法CUDA算子实现」 §1.4; the slot layout of
+// 「稀疏矩阵存储格式…」 §4 with slot t of all lanes adjacent.)  Lanes whose
+// row is served by another bin (length -1) do nothing; padding is skipped by
+// the length test, never multiplied.
+__global__ __launch_bounds__(kBlock) void spmv_sell_kernel(
+    int rows, int slices, const int64_t* __restrict__ slice_ptr, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ len, const int32_t* __restrict__ col, const float* __restrict__ val,
+    const float* __restrict__ x, float alpha, float beta, float* __restrict__ y) {
+    const int slice = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (slice >= slices) return;
+    const int lane = threadIdx.x & 63;
+    const int k = slice * 64 + lane;
+    if (k >= rows) return;
+    const int L = len[k];
+    if (L < 0) return;
+    const int64_t base = slice_ptr[slice] + lane;
+    float s = 0.0f;
+    for (int t = 0; t < L; ++t) {
+        const int64_t q = base + (int64_t)t * 64;
+        s += __builtin_nontemporal_load(val + q) * x[__builtin_nontemporal_load(col + q)];
+    }
+    store_axpby(y, perm[k], s, alpha, beta);
+}
+
+// Fill the SELL slot arrays from the CSR (padding: column -1, value 0).
+__global__ __launch_bounds__(kBlock) void sell_fill_kernel(
+    int rows, int slices, const int64_t* __restrict__ slice_ptr, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ len, const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+    const float* __restrict__ val, int32_t* __restrict__ scol, float* __restrict__ sval) {
+    const int slice = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (slice >= slices) return;
+    const int lane = threadIdx.x & 63;
+    const int k = slice * 64 + lane;
+    const int64_t base = slice_ptr[slice];
+    const int width = (int)((slice_ptr[slice + 1] - base) / 64);
+    const int L = k < rows ? len[k] : -1;
+    const int p0 = (k < rows && L > 0) ? ptr[perm[k]] : 0;
+    for (int t = 0; t < width; ++t) {
+        const int64_t q = base + (int64_t)t * 64 + lane;
+        if (t < L) {
+            scol[q] = idx[p0 + t];
+            sval[q] = val[p0 + t];
+        } else {
+            scol[q] = -1;
+            sval[q] = 0.0f;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_spmv(const DirDevice& d, float alpha, const float* x, float beta, float* y, hipStream_t s) {
+    const int n_wave_wg = (d.n_wave + 3) / 4;
+    const int64_t grid = (int64_t)d.n_split + d.n_block + n_wave_wg + (d.use_sell ? 0 : d.n_group);
+    if (grid > 0) {
+        const size_t lds = (size_t)(d.group_cap > 16 ? d.group_cap : 16) * sizeof(float);
+        hipLaunchKernelGGL(spmv_bins_kernel, dim3((unsigned)grid), dim3(kBlock), lds, s, d.tasks, d.n_split,
+                           d.n_block, d.n_wave, d.use_sell ? 0 : d.n_group, d.xcd_remap, d.split_rows, d.ptr,
+                           d.idx, d.val, x, alpha, beta, y, d.partials, d.counters);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    if (d.use_sell && d.sell_slices > 0) {
+        hipLaunchKernelGGL(spmv_sell_kernel, dim3((unsigned)((d.sell_slices + 3) / 4)), dim3(kBlock), 0, s, d.rows,
+                           d.sell_slices, d.sell_slice_ptr, d.sell_perm, d.sell_len, d.sell_col, d.sell_val, x,
+                           alpha, beta, y);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_sell_fill(const DirDevice& d, int64_t slots, int32_t* sell_col, float* sell_val, hipStream_t s) {
+    (void)slots;
+    if (d.sell_slices <= 0) return hipSuccess;
+    hipLaunchKernelGGL(sell_fill_kernel, dim3((unsigned)((d.sell_slices + 3) / 4)), dim3(kBlock), 0, s, d.rows,
+                       d.sell_slices, d.sell_slice_ptr, d.sell_perm, d.sell_len, d.ptr, d.idx, d.val, sell_col,
+                       sell_val);
+    return hipGetLastError();
+}
+
+}  // namespace spx

@@ -1,0 +1,135 @@
+"""Host-only checks of the C ABI: the library loads, exports every function the
+public header declares, and rejects bad arguments before touching a GPU.
+No call here launches a kernel or reaches the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import spmm_csr_spmv_amd as sp
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "spmm_csr_spmv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("csr_build_from_coo", "csr_to_csc", "spmv", "spmv_t", "spmm", "bsr_spmm"):
+        assert required in names
+    assert sorted(sp.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(sp.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version():
+    for code in range(8):
+        s = sp.status_string(code)
+        assert s.startswith("SP_")
+    assert sp.status_string(99) == "unknown status"
+    assert sp.sp_version() >= 100
+
+
+def test_option_defaults():
+    o = sp.plan_options()
+    assert (o.group_nnz, o.wave_min, o.block_min, o.split_min, o.split_seg) == (2048, 256, 4096, 32768, 8192)
+    assert (o.use_sell, o.sell_sigma, o.xcd_remap) == (0, 1024, 1)
+
+
+SZ = ctypes.c_size_t
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below returns before using it
+
+
+@pytest.mark.parametrize("m,n,nnz", [(-1, 4, 4), (4, -1, 4), (4, 4, -1), (2 ** 31, 4, 4), (4, 4, 2 ** 31),
+                                     (2 ** 31 - 1, 4, 4)])
+def test_bufsize_rejects_bad_sizes(m, n, nnz):
+    L = sp.lib()
+    b = SZ()
+    assert L.csr_build_from_coo_bufsize(m, n, nnz, ctypes.byref(b)) == 2
+    assert L.csr_to_csc_bufsize(m, n, nnz, ctypes.byref(b)) == 2
+
+
+def test_bufsize_null_and_growth():
+    L = sp.lib()
+    assert L.csr_build_from_coo_bufsize(4, 4, 4, None) == 1
+    a, b = SZ(), SZ()
+    assert L.csr_build_from_coo_bufsize(1000, 1000, 10_000, ctypes.byref(a)) == 0
+    assert L.csr_build_from_coo_bufsize(1000, 1000, 20_000, ctypes.byref(b)) == 0
+    assert b.value > a.value >= 8 * 2 * 10_000
+
+
+def test_conversion_argument_errors():
+    L = sp.lib()
+    # NULL outputs
+    assert L.csr_build_from_coo(4, 4, 3, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    assert L.csr_to_csc(4, 4, 3, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    # missing workspace
+    assert L.csr_build_from_coo(4, 4, 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 4
+    assert L.csr_to_csc(4, 4, 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 4
+    # sizes
+    assert L.csr_build_from_coo(-2, 4, 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 2
+
+
+@pytest.mark.parametrize("field,value", [("group_nnz", 32), ("group_nnz", 8192), ("wave_min", 5000),
+                                         ("block_min", 10), ("split_min", 100), ("split_seg", 8),
+                                         ("use_sell", 2), ("sell_sigma", 0), ("xcd_remap", 3)])
+def test_plan_rejects_bad_options(field, value):
+    L = sp.lib()
+    o = sp.plan_options()
+    setattr(o, field, value)
+    h = ctypes.c_void_p()
+    assert L.sp_plan_create(ctypes.byref(h), 8, 8, 8, FAKE, FAKE, FAKE, None, None, None, ctypes.byref(o),
+                            None) == 5
+    assert not h.value
+
+
+def test_plan_argument_errors():
+    L = sp.lib()
+    h = ctypes.c_void_p()
+    assert L.sp_plan_create(None, 8, 8, 8, FAKE, FAKE, FAKE, None, None, None, None, None) == 1
+    assert L.sp_plan_create(ctypes.byref(h), 8, 8, 8, None, FAKE, FAKE, None, None, None, None, None) == 1
+    assert L.sp_plan_create(ctypes.byref(h), 8, 8, 8, FAKE, None, FAKE, None, None, None, None, None) == 1
+    assert L.sp_plan_create(ctypes.byref(h), 8, 8, 8, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None) == 1
+    assert L.sp_plan_create(ctypes.byref(h), 2 ** 31, 8, 8, FAKE, FAKE, FAKE, None, None, None, None, None) == 2
+    b = SZ()
+    assert L.sp_plan_workspace_size(None, 1, ctypes.byref(b)) == 1
+    assert L.sp_plan_bind(None, FAKE, 100, 1, None) == 1
+    assert L.sp_plan_profile(None, 0, None) == 1
+    assert L.sp_plan_destroy(None) == 0
+    assert L.spmv(None, 1.0, FAKE, 0.0, FAKE, None) == 1
+    assert L.spmv_t(None, 1.0, FAKE, 0.0, FAKE, None) == 1
+    assert L.spmm(None, 4, 1.0, FAKE, 4, 0.0, FAKE, 4, None) == 1
+
+
+def test_bsr_argument_errors():
+    L = sp.lib()
+    b = SZ()
+    assert L.bsr_spmm_bufsize(4, 4, 32, 8, 64, ctypes.byref(b)) == 5
+    assert L.bsr_spmm_bufsize(4, 4, 64, 8, 64, ctypes.byref(b)) == 0
+    assert L.bsr_spmm_bufsize(-1, 4, 64, 8, 64, ctypes.byref(b)) == 2
+    args = dict(mb=4, kb=4, bs=64, nnzb=8, brow=FAKE, bcol=FAKE, bval=FAKE, N=128, B=FAKE, ldb=128, alpha=1.0,
+                beta=0.0, C=FAKE, ldc=128)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.bsr_spmm(a["mb"], a["kb"], a["bs"], a["nnzb"], a["brow"], a["bcol"], a["bval"], a["N"], a["B"],
+                          a["ldb"], a["alpha"], a["beta"], a["C"], a["ldc"], None, 0, None)
+
+    assert call(bs=16) == 5
+    assert call(N=96, ldb=96, ldc=96) == 5        # N not a multiple of 64
+    assert call(ldb=132) == 5                     # ldb not a multiple of 8
+    assert call(ldb=100) == 2                     # ldb < N
+    assert call(ldc=64) == 2                      # ldc < N
+    assert call(B=None) == 1
+    assert call(C=ctypes.c_void_p(0x1004)) == 5   # misaligned C
+    assert call(mb=2 ** 31) == 2
