@@ -95,9 +95,10 @@ def _triples_from_lengths(rng, m, n, lens, distinct, chunk_rows=1 << 20):
     for r0 in range(0, m, chunk_rows):
         r1 = min(m, r0 + chunk_rows)
         ln = lens[r0:r1].copy()
-        # Rows that fill more than 1/8 of the columns are drawn exactly without
-        # replacement one by one (rejection would rarely succeed for them).
-        dense_rows = np.flatnonzero(ln * 8 > n) + r0 if distinct else np.empty(0, np.int64)
+        # Rows long enough that a with-replacement draw of them usually repeats a
+        # column (l^2 > n/4, the birthday bound) are drawn exactly without
+        # replacement one by one; rejection would rarely succeed for them.
+        dense_rows = np.flatnonzero(ln * ln * 4 > n) + r0 if distinct else np.empty(0, np.int64)
         ln[dense_rows - r0] = 0
         rows = np.repeat(np.arange(r0, r1, dtype=np.int64), ln)
         cols = rng.integers(0, n, size=rows.size, dtype=np.int64)

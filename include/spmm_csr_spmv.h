@@ -113,8 +113,12 @@ int csr_to_csc(int64_t m, int64_t n, int64_t nnz,
  *   l > split_min            split into segments of split_seg entries, one
  *                            workgroup each, partial sums reduced in fixed
  *                            order by the last segment to finish ([GEN] §2.4)
- * With use_sell != 0 the group rows are served instead from a SELL-C-sigma
- * copy ([GEN] §1.4) built in the workspace (C = 64 lanes, window sell_sigma).
+ * With use_sell = 1 the group rows are served instead from a SELL-C-sigma
+ * copy ([GEN] §1.4) built in the workspace (C = 64 lanes, window sell_sigma);
+ * use_sell = -1 (the default) picks SELL when every row has at most 64
+ * entries, rows average at least 4 entries and the padded slots exceed the
+ * entries by at most 20 % ([GEN] §4 rule table: short regular rows, padding
+ * checked first); use_sell = 0 never uses it.
  */
 typedef struct sp_plan sp_plan;
 
@@ -124,7 +128,7 @@ typedef struct sp_plan_options {
     int32_t block_min;   /* default 4096; >= wave_min                         */
     int32_t split_min;   /* default 32768; >= block_min                       */
     int32_t split_seg;   /* entries per split segment, >= 16 (default 8192)   */
-    int32_t use_sell;    /* 0 (default) or 1                                   */
+    int32_t use_sell;    /* -1 auto (default), 0 off, 1 on                     */
     int32_t sell_sigma;  /* sorting window in rows for SELL, >= 1 (default 1024) */
     int32_t xcd_remap;   /* 1 (default): consecutive groups go to one XCD     */
 } sp_plan_options;

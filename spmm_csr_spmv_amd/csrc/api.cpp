@@ -42,6 +42,7 @@ struct Dir {
     int32_t n_split = 0, n_block = 0, n_wave = 0, n_group = 0;
     int64_t n_partials = 0;        // total split segments
     // SELL (host side)
+    bool use_sell = false;
     std::vector<int64_t> sell_slice_ptr;
     std::vector<int32_t> sell_perm, sell_len;
     int64_t sell_slots = 0;
@@ -214,7 +215,7 @@ size_t dir_layout(const Dir& d, const sp_plan_options& o, int32_t max_N, size_t 
     const int64_t max_tiles = std::max<int64_t>(1, (max_N + 63) / 64);
     d.off_counters = off;
     off = align256(off + d.split_rows.size() * (size_t)max_tiles * sizeof(int32_t));
-    if (o.use_sell) {
+    if (d.use_sell) {
         d.off_sell_ptr = off;
         off = align256(off + d.sell_slice_ptr.size() * sizeof(int64_t));
         d.off_sell_perm = off;
@@ -244,7 +245,7 @@ int check_options(const sp_plan_options& o) {
     if (o.wave_min < 0 || o.wave_min > o.group_nnz) return SP_ERR_UNSUPPORTED;
     if (o.block_min < o.wave_min || o.split_min < o.block_min) return SP_ERR_UNSUPPORTED;
     if (o.split_seg < 16) return SP_ERR_UNSUPPORTED;
-    if (o.use_sell != 0 && o.use_sell != 1) return SP_ERR_UNSUPPORTED;
+    if (o.use_sell < -1 || o.use_sell > 1) return SP_ERR_UNSUPPORTED;
     if (o.sell_sigma < 1) return SP_ERR_UNSUPPORTED;
     if (o.xcd_remap != 0 && o.xcd_remap != 1) return SP_ERR_UNSUPPORTED;
     return SP_OK;
@@ -268,7 +269,27 @@ int setup_dir(Dir& d, int64_t rows, int64_t cols, int64_t nnz, const int32_t* pt
         if (hptr[(size_t)i + 1] < hptr[(size_t)i]) return SP_ERR_SIZE;
     profile_rows(hptr, d);
     assign_bins(hptr, o, d);
-    if (o.use_sell) build_sell(hptr, o, d);
+    d.use_sell = o.use_sell == 1;
+    if (o.use_sell < 0) {
+        // SELL-C-sigma pays when rows are short and similar in length
+        // (「通用稀疏矩阵乘法CUDA算子实现」 §4 rule table: check the padding first).
+        // Rule: no row above 64 entries among the rows it would serve, and the
+        // padded slots exceed the real entries by at most 20 %.
+        if (d.prof.p99 <= 64 && d.prof.max_len <= o.wave_min && d.prof.mean >= 4.0) {
+            build_sell(hptr, o, d);
+            int64_t sell_nnz = d.prof.group_nnz;
+            d.use_sell = d.sell_slots <= sell_nnz + sell_nnz / 5;
+        }
+    }
+    if (d.use_sell) {
+        if (d.sell_perm.empty() && d.rows > 0) build_sell(hptr, o, d);
+    } else {
+        d.sell_perm.clear();
+        d.sell_len.clear();
+        d.sell_slice_ptr.clear();
+        d.sell_slots = 0;
+        d.prof.sell_slots = 0;
+    }
     return SP_OK;
 }
 
@@ -299,7 +320,7 @@ int upload_dir(Dir& d, char* ws, const sp_plan_options& o, hipStream_t s) {
         hipMemcpyAsync(ws + d.off_split_rows, d.split_rows.data(), d.split_rows.size() * sizeof(int4),
                        hipMemcpyHostToDevice, s) != hipSuccess)
         return SP_ERR_HIP;
-    if (o.use_sell) {
+    if (d.use_sell) {
         v.use_sell = 1;
         v.sell_slices = (int32_t)(d.sell_slice_ptr.size() - 1);
         v.sell_slice_ptr = reinterpret_cast<const int64_t*>(ws + d.off_sell_ptr);
@@ -396,7 +417,7 @@ int sp_plan_options_default(sp_plan_options* o) {
     o->block_min = 4096;
     o->split_min = 32768;
     o->split_seg = 8192;
-    o->use_sell = 0;
+    o->use_sell = -1;
     o->sell_sigma = 1024;
     o->xcd_remap = 1;
     return SP_OK;

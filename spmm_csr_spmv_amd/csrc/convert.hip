@@ -124,15 +124,29 @@ __global__ __launch_bounds__(kBlock) void scan_add(int32_t* __restrict__ a, int6
 __global__ __launch_bounds__(kBlock) void classify(int32_t nseg, const int32_t* __restrict__ ptr,
                                                    int32_t* __restrict__ cursor, int32_t* __restrict__ small,
                                                    int32_t* __restrict__ large, int32_t* __restrict__ misc) {
-    for (int32_t s = blockIdx.x * kBlock + threadIdx.x; s < nseg; s += gridDim.x * kBlock) {
-        const int32_t b = ptr[s], len = ptr[s + 1] - b;
-        cursor[s] = b;
-        if (len >= 2 && len <= kSmallSeg) {
-            small[atomicAdd(misc + kCntSmall, 1)] = s;
-        } else if (len > kSmallSeg) {
-            large[atomicAdd(misc + kCntLarge, 1)] = s;
+    // One atomic per wave and list: the wave's lanes take consecutive slots
+    // (list order does not matter, every listed segment is sorted on its own).
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = (1ull << lane) - 1;
+    for (int32_t s0 = blockIdx.x * kBlock; s0 < nseg; s0 += gridDim.x * kBlock) {
+        const int32_t s = s0 + threadIdx.x;
+        const bool in = s < nseg;
+        const int32_t b = in ? ptr[s] : 0, len = in ? ptr[s + 1] - b : 0;
+        if (in) cursor[s] = b;
+        const bool is_small = len >= 2 && len <= kSmallSeg, is_large = len > kSmallSeg;
+        const uint64_t ms = __ballot(is_small), ml = __ballot(is_large);
+        int32_t base_s = 0, base_l = 0;
+        if (lane == 0) {
+            if (ms) base_s = atomicAdd(misc + kCntSmall, (int)__popcll(ms));
+            if (ml) base_l = atomicAdd(misc + kCntLarge, (int)__popcll(ml));
         }
-        if (len > 0) atomicMax(misc + kMaxLen, len);
+        base_s = __shfl(base_s, 0, 64);
+        base_l = __shfl(base_l, 0, 64);
+        if (is_small) small[base_s + __popcll(ms & below)] = s;
+        if (is_large) large[base_l + __popcll(ml & below)] = s;
+        int32_t mx = len;
+        for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
+        if (lane == 0 && mx > 0) atomicMax(misc + kMaxLen, mx);
     }
 }
 

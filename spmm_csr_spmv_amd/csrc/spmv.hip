@@ -17,29 +17,53 @@ namespace spx {
 
 namespace {
 
-// Products val[q] * x[idx[q]] for q in [b, e), 4-aligned 16-byte loads for the
-// interior and guarded scalar loads at the ragged ends.  `emit(q, prod)`
-// receives each product; lanes step by 4*stride entries.
-template <class Emit>
+// Products val[q] * x[idx[q]] for q in [b, e).  Lane `lane` of `stride`
+// lanes owns the 4-entry chunks starting at (b & ~3) + 4*lane + 4*stride*k.
+// Chunks are taken U at a time: the U column/value loads (16-byte loads for
+// full chunks, guarded scalar loads at the ragged ends) are all issued before
+// the gathers of x, and all gathers before any product, so every lane keeps
+// up to 8U independent memory requests in flight.  `emit(q, prod)` receives
+// each valid product; slots outside [b, e) are never read nor multiplied.
+template <int U, class Emit>
 __device__ __forceinline__ void stream_products(const int32_t* __restrict__ idx, const float* __restrict__ val,
                                                 const float* __restrict__ x, int b, int e, int lane, int stride,
                                                 Emit emit) {
     const int base = b & ~3;
-    for (int v = base + 4 * lane; v < e; v += 4 * stride) {
-        if (v >= b && v + 4 <= e) {
-            const int4 c = ldg4_nt(idx + v);
-            const float4 a = ldg4_nt(val + v);
-            const float x0 = x[c.x], x1 = x[c.y], x2 = x[c.z], x3 = x[c.w];
-            emit(v + 0, a.x * x0);
-            emit(v + 1, a.y * x1);
-            emit(v + 2, a.z * x2);
-            emit(v + 3, a.w * x3);
-        } else {
+    for (int v0 = base + 4 * lane; v0 < e; v0 += 4 * stride * U) {
+        int c[U][4];
+        float a[U][4];
+        bool ok[U][4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int q = v + j;
-                if (q >= b && q < e) emit(q, val[q] * x[idx[q]]);
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + 4 * stride * u;
+            if (v >= b && v + 4 <= e) {
+                const int4 ci = ldg4_nt(idx + v);
+                const float4 ai = ldg4_nt(val + v);
+                c[u][0] = ci.x; c[u][1] = ci.y; c[u][2] = ci.z; c[u][3] = ci.w;
+                a[u][0] = ai.x; a[u][1] = ai.y; a[u][2] = ai.z; a[u][3] = ai.w;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ok[u][j] = true;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int q = v + j;
+                    ok[u][j] = q >= b && q < e;
+                    c[u][j] = ok[u][j] ? idx[q] : 0;
+                    a[u][j] = ok[u][j] ? val[q] : 0.0f;
+                }
             }
+        }
+        float xv[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xv[u][j] = ok[u][j] ? x[c[u][j]] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + 4 * stride * u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (ok[u][j]) emit(v + j, a[u][j] * xv[u][j]);
         }
     }
 }
@@ -50,34 +74,62 @@ __device__ __forceinline__ void store_axpby(float* __restrict__ y, int row, floa
     y[row] = o;
 }
 
-// Threads per row for a group of `nrows` rows: the largest power of two
-// (at most 64) with g * nrows <= 256.
-__device__ __forceinline__ int group_lanes(int nrows) {
-    int g = 64;
-    while (g > 1 && g * nrows > kBlock) g >>= 1;
-    return g;
+// Row sums of R consecutive rows whose E products sit in LDS (prod[0..E)),
+// with row i covering prod[rs[i] .. rs[i+1]) (rs in LDS, rs[R] = E).
+// The products are split evenly: thread t reads chunk [tC, tC + C) with
+// C = ceil(E / 256), whatever the row lengths.  Thread t owns the rows that
+// start in [tC, (t+1)C) (thread 255 also owns rows starting later, i.e. empty
+// rows at the end).  A thread first stores in head[t] the part of its chunk
+// that belongs to a row started in an earlier chunk; after a barrier, each
+// owner adds its own part and then head[t+1], head[t+2], ... for a row that
+// runs past its chunk.  The order of additions is fixed by E and rs, so the
+// result is reproducible bit for bit.  out(i, sum) is called once per row.
+template <class Out>
+__device__ __forceinline__ void balanced_row_sums(const float* prod, int E, const int* rs, int R, float* head,
+                                                  Out out) {
+    const int t = threadIdx.x;
+    const int C = E > 0 ? (E + kBlock - 1) / kBlock : 1;
+    const int lo_s = t * C;
+    const int hi_s = t == kBlock - 1 ? 0x7fffffff : lo_s + C;
+    const int c0 = min(lo_s, E), c1 = min(lo_s + C, E);
+    int lo = 0, hi = R;  // first row starting at or after lo_s
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (rs[mid] < lo_s) lo = mid + 1; else hi = mid;
+    }
+    const int first = lo;
+    const int head_end = first < R ? min(c1, rs[first]) : c1;
+    float h = 0.0f;
+    for (int k = c0; k < head_end; ++k) h += prod[k];
+    head[t] = h;
+    __syncthreads();
+    for (int i = first; i < R && rs[i] < hi_s; ++i) {
+        const int beg = rs[i], end = rs[i + 1];
+        float s = 0.0f;
+        for (int k = beg; k < min(end, c1); ++k) s += prod[k];
+        if (end > c1) {
+            const int last_chunk = (end - 1) / C;
+            for (int tt = t + 1; tt <= last_chunk; ++tt) s += head[tt];
+        }
+        out(i, s);
+    }
 }
 
 // ---- group: consecutive short rows staged through LDS --------------------
+// LDS: products [group_cap] | row starts [257] | heads [256]
 __device__ void group_task(const int4 t, const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
                            const float* __restrict__ val, const float* __restrict__ x, float alpha, float beta,
-                           float* __restrict__ y, float* lds) {
+                           float* __restrict__ y, float* lds, int group_cap) {
     const int r0 = t.x, r1 = t.y, b = t.z, e = t.w;
+    const int R = r1 - r0;
     const int tid = threadIdx.x;
-    stream_products(idx, val, x, b, e, tid, kBlock, [&](int q, float p) { lds[q - b] = p; });
+    int* rs = reinterpret_cast<int*>(lds + group_cap);
+    float* head = lds + group_cap + (kGroupMaxRows + 1);
+    for (int i = tid; i <= R; i += kBlock) rs[i] = ptr[r0 + i] - b;
+    stream_products<kGroupMaxNnz / (4 * kBlock)>(idx, val, x, b, e, tid, kBlock,
+                                                  [&](int q, float p) { lds[q - b] = p; });
     __syncthreads();
-    const int nrows = r1 - r0;
-    const int g = group_lanes(nrows);
-    const int slot = tid / g, lane = tid - slot * g;
-    const int row = r0 + slot;
-    const bool active = slot < nrows;
-    float s = 0.0f;
-    if (active) {
-        const int rb = ptr[row] - b, re = ptr[row + 1] - b;
-        for (int k = rb + lane; k < re; k += g) s += lds[k];
-    }
-    s = group_sum(s, g);
-    if (active && lane == 0) store_axpby(y, row, s, alpha, beta);
+    balanced_row_sums(lds, e - b, rs, R, head, [&](int i, float s) { store_axpby(y, r0 + i, s, alpha, beta); });
 }
 
 // ---- wave: one row per wave64 ----------------------------------------------
@@ -85,7 +137,7 @@ __device__ void wave_task(const int4 t, const int32_t* __restrict__ idx, const f
                           const float* __restrict__ x, float alpha, float beta, float* __restrict__ y, bool valid) {
     const int lane = threadIdx.x & 63;
     float s = 0.0f;
-    if (valid) stream_products(idx, val, x, t.y, t.z, lane, 64, [&](int, float p) { s += p; });
+    if (valid) stream_products<4>(idx, val, x, t.y, t.z, lane, 64, [&](int, float p) { s += p; });
     s = wave_sum(s);
     if (valid && lane == 0) store_axpby(y, t.x, s, alpha, beta);
 }
@@ -95,7 +147,7 @@ __device__ __forceinline__ float block_reduce_range(const int32_t* __restrict__ 
                                                     const float* __restrict__ x, int b, int e, float* lds) {
     const int tid = threadIdx.x;
     float s = 0.0f;
-    stream_products(idx, val, x, b, e, tid, kBlock, [&](int, float p) { s += p; });
+    stream_products<4>(idx, val, x, b, e, tid, kBlock, [&](int, float p) { s += p; });
     s = wave_sum(s);
     if ((tid & 63) == 0) lds[tid >> 6] = s;
     __syncthreads();
@@ -137,7 +189,7 @@ __global__ __launch_bounds__(kBlock) void spmv_bins_kernel(
     const int4* __restrict__ tasks, int n_split, int n_block, int n_wave, int n_group, int xcd_remap,
     const int4* __restrict__ split_rows, const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
     const float* __restrict__ val, const float* __restrict__ x, float alpha, float beta, float* __restrict__ y,
-    float* partials, int32_t* counters) {
+    float* partials, int32_t* counters, int group_cap) {
     extern __shared__ float lds[];
     int b = blockIdx.x;
     if (b < n_split) {
@@ -161,7 +213,7 @@ __global__ __launch_bounds__(kBlock) void spmv_bins_kernel(
     b -= n_wave_wg;
     const int first = n_split + n_block + n_wave_wg;
     const int g = xcd_remap ? xcd_contiguous(blockIdx.x, first, n_group) : b;
-    group_task(tasks[n_split + n_block + n_wave + g], ptr, idx, val, x, alpha, beta, y, lds);
+    group_task(tasks[n_split + n_block + n_wave + g], ptr, idx, val, x, alpha, beta, y, lds, group_cap);
 }
 
 // ---- SELL-C-sigma, C = 64: one wave per slice, one lane per row -----------
@@ -180,12 +232,25 @@ __global__ __launch_bounds__(kBlock) void spmv_sell_kernel(
     if (k >= rows) return;
     const int L = len[k];
     if (L < 0) return;
-    const int64_t base = slice_ptr[slice] + lane;
+    const int32_t* cp = col + slice_ptr[slice] + lane;
+    const float* vp = val + slice_ptr[slice] + lane;
     float s = 0.0f;
-    for (int t = 0; t < L; ++t) {
-        const int64_t q = base + (int64_t)t * 64;
-        s += __builtin_nontemporal_load(val + q) * x[__builtin_nontemporal_load(col + q)];
+    int t = 0;
+    // 8 slots at a time: all loads, then all gathers, then the sums in slot order
+    for (; t + 8 <= L; t += 8) {
+        int c[8];
+        float a[8], xv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            c[u] = __builtin_nontemporal_load(cp + (int64_t)(t + u) * 64);
+            a[u] = __builtin_nontemporal_load(vp + (int64_t)(t + u) * 64);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) xv[u] = x[c[u]];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += a[u] * xv[u];
     }
+    for (; t < L; ++t) s += __builtin_nontemporal_load(vp + (int64_t)t * 64) * x[__builtin_nontemporal_load(cp + (int64_t)t * 64)];
     store_axpby(y, perm[k], s, alpha, beta);
 }
 
@@ -220,10 +285,10 @@ hipError_t launch_spmv(const DirDevice& d, float alpha, const float* x, float be
     const int n_wave_wg = (d.n_wave + 3) / 4;
     const int64_t grid = (int64_t)d.n_split + d.n_block + n_wave_wg + (d.use_sell ? 0 : d.n_group);
     if (grid > 0) {
-        const size_t lds = (size_t)(d.group_cap > 16 ? d.group_cap : 16) * sizeof(float);
+        const size_t lds = (size_t)(d.group_cap + 2 * kGroupMaxRows + 1) * sizeof(float);
         hipLaunchKernelGGL(spmv_bins_kernel, dim3((unsigned)grid), dim3(kBlock), lds, s, d.tasks, d.n_split,
                            d.n_block, d.n_wave, d.use_sell ? 0 : d.n_group, d.xcd_remap, d.split_rows, d.ptr,
-                           d.idx, d.val, x, alpha, beta, y, d.partials, d.counters);
+                           d.idx, d.val, x, alpha, beta, y, d.partials, d.counters, d.group_cap);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }

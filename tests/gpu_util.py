@@ -16,6 +16,7 @@ TOL_BF16 = 2e-2
 # all kernels at small sizes.
 BINS = {
     "default": {},
+    "group": dict(use_sell=0),
     "all_wave": dict(wave_min=0, block_min=2 ** 30, split_min=2 ** 30),
     "all_block": dict(wave_min=0, block_min=0, split_min=2 ** 30),
     "all_split": dict(wave_min=0, block_min=0, split_min=0, split_seg=16),
