@@ -36,7 +36,7 @@ class SparseError(RuntimeError):
 class sp_plan_options(ctypes.Structure):
     _fields_ = [("group_nnz", ctypes.c_int32), ("wave_min", ctypes.c_int32), ("block_min", ctypes.c_int32),
                 ("split_min", ctypes.c_int32), ("split_seg", ctypes.c_int32), ("use_sell", ctypes.c_int32),
-                ("sell_sigma", ctypes.c_int32), ("xcd_remap", ctypes.c_int32)]
+                ("sell_sigma", ctypes.c_int32), ("xcd_remap", ctypes.c_int32), ("col_panels", ctypes.c_int32)]
 
 
 class sp_profile(ctypes.Structure):
@@ -48,7 +48,7 @@ class sp_profile(ctypes.Structure):
                 ("wave_rows", ctypes.c_int64), ("wave_nnz", ctypes.c_int64),
                 ("block_rows", ctypes.c_int64), ("block_nnz", ctypes.c_int64),
                 ("split_rows", ctypes.c_int64), ("split_segments", ctypes.c_int64), ("split_nnz", ctypes.c_int64),
-                ("sell_slots", ctypes.c_int64)]
+                ("sell_slots", ctypes.c_int64), ("col_panels", ctypes.c_int64)]
 
 
 _lib = None

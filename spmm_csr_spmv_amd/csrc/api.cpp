@@ -46,11 +46,16 @@ struct Dir {
     std::vector<int64_t> sell_slice_ptr;
     std::vector<int32_t> sell_perm, sell_len;
     int64_t sell_slots = 0;
+    // column panels: the panel groups, appended to a copy of the long-row tasks
+    int32_t npanels = 0, panel_width = 0;
+    std::vector<int4> ptasks;  // split | block | wave | panel groups
+    int32_t n_pgroup = 0;
     sp_profile prof{};
     DirDevice dev{};
     // workspace offsets (byte offsets into the bound workspace)
     mutable size_t off_tasks = 0, off_split_rows = 0, off_partials = 0, off_counters = 0;
     mutable size_t off_sell_ptr = 0, off_sell_perm = 0, off_sell_len = 0, off_sell_col = 0, off_sell_val = 0;
+    mutable size_t off_pcol = 0, off_pval = 0, off_pstart = 0, off_poff = 0, off_ypart = 0, off_ptasks = 0;
 };
 
 }  // namespace
@@ -108,6 +113,9 @@ void profile_rows(const std::vector<int32_t>& hptr, Dir& d) {
 void assign_bins(const std::vector<int32_t>& hptr, const sp_plan_options& o, Dir& d) {
     std::vector<int4> split, block, wave, group;
     sp_profile& p = d.prof;
+    p.group_tasks = p.group_rows = p.group_nnz = 0;
+    p.wave_rows = p.wave_nnz = p.block_rows = p.block_nnz = 0;
+    p.split_rows = p.split_segments = p.split_nnz = 0;
     d.split_rows.clear();
     d.n_partials = 0;
     int32_t g_r0 = 0, g_rows = 0;
@@ -215,6 +223,20 @@ size_t dir_layout(const Dir& d, const sp_plan_options& o, int32_t max_N, size_t 
     const int64_t max_tiles = std::max<int64_t>(1, (max_N + 63) / 64);
     d.off_counters = off;
     off = align256(off + d.split_rows.size() * (size_t)max_tiles * sizeof(int32_t));
+    if (d.npanels > 0) {
+        d.off_pcol = off;
+        off = align256(off + (size_t)d.nnz * sizeof(int32_t));
+        d.off_pval = off;
+        off = align256(off + (size_t)d.nnz * sizeof(float));
+        d.off_ptasks = off;
+        off = align256(off + d.ptasks.size() * sizeof(int4));
+        d.off_pstart = off;
+        off = align256(off + (size_t)d.n_pgroup * (size_t)(d.npanels + 1) * sizeof(int32_t));
+        d.off_poff = off;
+        off = align256(off + (size_t)d.npanels * (size_t)d.rows * sizeof(uint16_t));
+        d.off_ypart = off;
+        off = align256(off + (size_t)d.npanels * (size_t)d.rows * sizeof(float));
+    }
     if (d.use_sell) {
         d.off_sell_ptr = off;
         off = align256(off + d.sell_slice_ptr.size() * sizeof(int64_t));
@@ -247,7 +269,39 @@ int check_options(const sp_plan_options& o) {
     if (o.split_seg < 16) return SP_ERR_UNSUPPORTED;
     if (o.use_sell < -1 || o.use_sell > 1) return SP_ERR_UNSUPPORTED;
     if (o.sell_sigma < 1) return SP_ERR_UNSUPPORTED;
+    if (o.col_panels != -1 && o.col_panels != 0 && o.col_panels != 2 && o.col_panels != 4 && o.col_panels != 8)
+        return SP_ERR_UNSUPPORTED;
     if (o.xcd_remap != 0 && o.xcd_remap != 1) return SP_ERR_UNSUPPORTED;
+    return SP_OK;
+}
+
+// Auto rule for column panels: x must exceed 8 MiB (two L2s' worth), and a
+// sample of up to 64 evenly spaced group tasks must show columns spread over
+// more than a quarter of the column range (median over the sample of
+// max col - min col).  Reads the sampled column ranges back: synchronises.
+int scattered_columns(const Dir& d, hipStream_t s, int32_t* P) {
+    *P = 0;
+    if ((int64_t)d.cols * 4 <= (int64_t)8 << 20) return SP_OK;
+    const int32_t first = d.n_split + d.n_block + d.n_wave;
+    const int32_t nsample = std::min<int32_t>(64, d.n_group);
+    std::vector<std::vector<int32_t>> cols((size_t)nsample);
+    for (int32_t k = 0; k < nsample; ++k) {
+        const int4 t = d.tasks[(size_t)first + (size_t)((int64_t)k * d.n_group / nsample)];
+        cols[(size_t)k].resize((size_t)(t.w - t.z));
+        if (t.w > t.z && hipMemcpyAsync(cols[(size_t)k].data(), d.idx + t.z, (size_t)(t.w - t.z) * sizeof(int32_t),
+                                        hipMemcpyDeviceToHost, s) != hipSuccess)
+            return SP_ERR_HIP;
+    }
+    if (hipStreamSynchronize(s) != hipSuccess) return SP_ERR_HIP;
+    std::vector<int64_t> spans;
+    for (const auto& c : cols) {
+        if (c.empty()) continue;
+        const auto mm = std::minmax_element(c.begin(), c.end());
+        spans.push_back((int64_t)*mm.second - *mm.first);
+    }
+    if (spans.empty()) return SP_OK;
+    std::nth_element(spans.begin(), spans.begin() + spans.size() / 2, spans.end());
+    if (spans[spans.size() / 2] * 4 > d.cols) *P = 4;
     return SP_OK;
 }
 
@@ -290,10 +344,53 @@ int setup_dir(Dir& d, int64_t rows, int64_t cols, int64_t nnz, const int32_t* pt
         d.sell_slots = 0;
         d.prof.sell_slots = 0;
     }
+    d.npanels = 0;
+    d.panel_width = 0;
+    if (!d.use_sell && o.col_panels != 0 && d.n_group > 0) {
+        int32_t P = o.col_panels;
+        if (P < 0) {
+            int rc = scattered_columns(d, s, &P);
+            if (rc != SP_OK) return rc;
+        }
+        if (P > 0) {
+            // Panel groups: consecutive group rows (length <= wave_min), at most
+            // kGroupMaxRows rows and P * kGroupMaxNnz / 2 entries, so that a
+            // panel block of scattered columns averages half the LDS capacity.
+            d.ptasks.assign(d.tasks.begin(), d.tasks.begin() + (d.n_split + d.n_block + d.n_wave));
+            const int64_t cap = (int64_t)P * spx::kGroupMaxNnz / 2;
+            int32_t r0 = 0, nr = 0;
+            int64_t nz = 0;
+            auto close = [&](int32_t next) {
+                if (nr > 0)
+                    d.ptasks.push_back(make_int4(r0, r0 + nr, hptr[(size_t)r0], hptr[(size_t)(r0 + nr)]));
+                r0 = next;
+                nr = 0;
+                nz = 0;
+            };
+            for (int32_t r = 0; r < d.rows; ++r) {
+                const int32_t l = hptr[(size_t)r + 1] - hptr[(size_t)r];
+                if (l > o.wave_min) {
+                    close(r + 1);
+                    continue;
+                }
+                if (nr > 0 && (nz + l > cap || nr == spx::kGroupMaxRows)) close(r);
+                if (nr == 0) r0 = r;
+                nr += 1;
+                nz += l;
+            }
+            close(d.rows);
+            d.n_pgroup = (int32_t)(d.ptasks.size() - (size_t)(d.n_split + d.n_block + d.n_wave));
+            int64_t w = (d.cols + P - 1) / P;
+            w = (w + 31) / 32 * 32;  // whole 128-byte lines of x per panel
+            d.npanels = P;
+            d.panel_width = (int32_t)std::max<int64_t>(w, 32);
+        }
+    }
+    d.prof.col_panels = d.npanels;
     return SP_OK;
 }
 
-int upload_dir(Dir& d, char* ws, const sp_plan_options& o, hipStream_t s) {
+int upload_dir(Dir& d, char* ws, const sp_plan_options& o, int32_t* panel_flag, hipStream_t s) {
     DirDevice& v = d.dev;
     v = DirDevice{};
     v.rows = d.rows;
@@ -320,6 +417,21 @@ int upload_dir(Dir& d, char* ws, const sp_plan_options& o, hipStream_t s) {
         hipMemcpyAsync(ws + d.off_split_rows, d.split_rows.data(), d.split_rows.size() * sizeof(int4),
                        hipMemcpyHostToDevice, s) != hipSuccess)
         return SP_ERR_HIP;
+    v.npanels = d.npanels;
+    v.panel_width = d.panel_width;
+    if (d.npanels > 0) {
+        v.pcol = reinterpret_cast<int32_t*>(ws + d.off_pcol);
+        v.pval = reinterpret_cast<float*>(ws + d.off_pval);
+        v.pstart = reinterpret_cast<int32_t*>(ws + d.off_pstart);
+        v.poff = reinterpret_cast<uint16_t*>(ws + d.off_poff);
+        v.ypart = reinterpret_cast<float*>(ws + d.off_ypart);
+        v.ptasks = reinterpret_cast<const int4*>(ws + d.off_ptasks);
+        v.n_pgroup = d.n_pgroup;
+        if (!d.ptasks.empty() && hipMemcpyAsync(ws + d.off_ptasks, d.ptasks.data(), d.ptasks.size() * sizeof(int4),
+                                                hipMemcpyHostToDevice, s) != hipSuccess)
+            return SP_ERR_HIP;
+        if (spx::launch_panel_build(v, panel_flag, s) != hipSuccess) return SP_ERR_HIP;
+    }
     if (d.use_sell) {
         v.use_sell = 1;
         v.sell_slices = (int32_t)(d.sell_slice_ptr.size() - 1);
@@ -418,6 +530,7 @@ int sp_plan_options_default(sp_plan_options* o) {
     o->split_min = 32768;
     o->split_seg = 8192;
     o->use_sell = -1;
+    o->col_panels = -1;
     o->sell_sigma = 1024;
     o->xcd_remap = 1;
     return SP_OK;
@@ -478,8 +591,9 @@ int sp_plan_bind(sp_plan* plan, void* work, size_t work_bytes, int32_t max_N, vo
     char* ws = static_cast<char*>(work);
     plan->bound = false;
     // every stored index must lie inside its dimension before any product runs
+    // misc words: [0] index check, [1] / [2] panel-block overflow of A / A^T
     int32_t* flag = reinterpret_cast<int32_t*>(ws);
-    if (spx::launch_fill_i32(flag, 1, 0, s) != hipSuccess) return SP_ERR_HIP;
+    if (spx::launch_fill_i32(flag, 4, 0, s) != hipSuccess) return SP_ERR_HIP;
     for (const Dir* d : {&plan->fwd, &plan->tr}) {
         if (d->present && spx::launch_check_indices(d->idx, d->nnz, d->cols, flag, s) != hipSuccess)
             return SP_ERR_HIP;
@@ -489,9 +603,22 @@ int sp_plan_bind(sp_plan* plan, void* work, size_t work_bytes, int32_t max_N, vo
     if (hipStreamSynchronize(s) != hipSuccess) return SP_ERR_HIP;
     if (bad) return SP_ERR_INDEX;
     int rc = SP_OK;
-    if (plan->fwd.present) rc = upload_dir(plan->fwd, ws, plan->opt, s);
-    if (rc == SP_OK && plan->tr.present) rc = upload_dir(plan->tr, ws, plan->opt, s);
+    if (plan->fwd.present) rc = upload_dir(plan->fwd, ws, plan->opt, flag + 1, s);
+    if (rc == SP_OK && plan->tr.present) rc = upload_dir(plan->tr, ws, plan->opt, flag + 2, s);
     if (rc != SP_OK) return rc;
+    if (plan->fwd.npanels > 0 || plan->tr.npanels > 0) {
+        // a panel block larger than the panel kernel's LDS: serve that direction without panels
+        int32_t over[2] = {0, 0};
+        if (hipMemcpyAsync(over, flag + 1, sizeof over, hipMemcpyDeviceToHost, s) != hipSuccess) return SP_ERR_HIP;
+        if (hipStreamSynchronize(s) != hipSuccess) return SP_ERR_HIP;
+        Dir* dirs[2] = {&plan->fwd, &plan->tr};
+        for (int k = 0; k < 2; ++k) {
+            if (over[k]) {
+                dirs[k]->dev.npanels = 0;
+                dirs[k]->prof.col_panels = 0;
+            }
+        }
+    }
     // arrival counters start at zero; the kernels put them back to zero
     for (Dir* d : {&plan->fwd, &plan->tr}) {
         if (!d->present || d->split_rows.empty()) continue;

@@ -12,7 +12,7 @@ namespace spx {
 
 constexpr int kBlock = 256;          // threads per workgroup for every kernel
 constexpr int kGroupMaxNnz = 4096;   // LDS capacity of a group task (entries)
-constexpr int kGroupMaxRows = 256;   // rows per group task (one per thread)
+constexpr int kGroupMaxRows = 1024;  // rows per group task
 constexpr int kXcds = 8;             // MI355X: workgroups go round-robin to 8 XCDs
 
 // Task tables of one direction (A or A^T), laid out in device memory as one
@@ -35,6 +35,16 @@ struct DirDevice {
     int32_t* counters;      // device, arrival counters (self-resetting)
     int32_t xcd_remap;
     int32_t group_cap;      // LDS entries reserved for a group task
+    // optional column panels of the group rows (see spmv.hip)
+    int32_t npanels;                 // 0 = off
+    const int4* ptasks;              // [split | block | wave | panel groups]
+    int32_t n_pgroup;
+    int32_t panel_width;             // columns per panel
+    int32_t* pcol;                   // [nnz] panel-major copy (group ranges only)
+    float* pval;                     // [nnz]
+    int32_t* pstart;                 // [n_group * (npanels + 1)]
+    uint16_t* poff;                  // [npanels * rows] row offset inside its panel block
+    float* ypart;                    // [npanels * rows]
     // optional SELL-C-sigma copy of the group rows
     int32_t use_sell;
     int32_t sell_slices;
@@ -52,6 +62,7 @@ hipError_t launch_spmm(const DirDevice& d, int32_t N, float alpha, const float* 
                        float beta, float* C, int64_t ldc, hipStream_t s);
 hipError_t launch_sell_fill(const DirDevice& d, int64_t slots, int32_t* sell_col, float* sell_val,
                             hipStream_t s);
+hipError_t launch_panel_build(const DirDevice& d, int32_t* flag, hipStream_t s);
 
 // Conversions: workspace sizes and the two builders (host driver in convert.hip).
 size_t coo_build_bytes(int64_t m, int64_t n, int64_t nnz);

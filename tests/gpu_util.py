@@ -23,6 +23,9 @@ BINS = {
     "mixed_small": dict(group_nnz=64, wave_min=8, block_min=40, split_min=100, split_seg=32),
     "sell": dict(use_sell=1, sell_sigma=128),
     "no_xcd": dict(xcd_remap=0),
+    "panels8": dict(use_sell=0, col_panels=8),
+    "panels2_small": dict(use_sell=0, col_panels=2, group_nnz=64, wave_min=8, block_min=40, split_min=100,
+                          split_seg=32),
 }
 
 
