@@ -108,7 +108,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--options", default="", help="plan options, e.g. group_nnz=1024,wave_min=128")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 256 MiB device copy (5 launches) to calibrate HBM byte counters")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = 64 << 20  # floats: 256 MiB per buffer
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty(n, device="cuda")
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps(dict(copy_bytes_read=4 * n, copy_bytes_written=4 * n, launches=5)))
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the sparse products here are single-GPU kernels "
               "(see the sharding paragraph of DESIGN.md); --gpus %d is not supported" % args.gpus, file=sys.stderr)
