@@ -218,6 +218,9 @@ int spmm(const sp_plan* plan, int32_t N, float alpha, const float* B, int64_t ld
  * B (kb*bs x N bf16 bit patterns, row-major, ldb >= N).  Supported: bs == 64,
  * N % 64 == 0, ldb % 8 == 0, ldc % 4 == 0, B and C 16-byte aligned.
  * work: at least bsr_spmm_bufsize() bytes (may be 0 bytes: then NULL is fine).
+ * The block structure is not validated (no synchronisation): block pointers
+ * are clamped to [0, nnzb], and a block whose column index lies outside
+ * [0, kb) contributes nothing; B is never read through such an index.
  * Never synchronises.
  * Errors: SP_ERR_NULL, SP_ERR_SIZE, SP_ERR_UNSUPPORTED, SP_ERR_WORKSPACE, SP_ERR_HIP.
  */

@@ -7,13 +7,14 @@
 // bf16 storage, fp32 accumulation.  The AsyncSparse page (§2.2.1, §3, §6.1)
 // uses 64 x 64 blocks and one output tile per (block row, column slice).
 //
-// Workgroup = 4 waves, output tile 64 rows x NT columns; the tile is computed
-// with v_mfma_f32_32x32x16_bf16.  Per block: the 64 x 64 A block goes to LDS
-// row-major (rows padded by 16 B so the 16-byte fragment reads of 32 rows hit
-// distinct banks); the 64 x NT slice of B goes to LDS with pairs of k rows
-// interleaved, word (p, n) = {B[2p][n], B[2p+1][n]}, which is the register
-// image of two consecutive k of one column in an MFMA B operand, so a lane's
-// 8-element B operand is four 32-bit LDS reads.
+// One workgroup per (block row, column tile of C); all tiles are computed with
+// v_mfma_f32_32x32x16_bf16 on fp32 accumulators.  Three kernels by width:
+//   N % 256 == 0: copy-engine kernel (global_load_lds into a four-stage LDS
+//                 ring, B operands by LDS transpose reads, copy waves apart
+//                 from MFMA waves);
+//   N % 128 == 0: register-prefetch kernel, B repacked into k-pair words;
+//   N % 64 == 0:  plain kernel, one 64 x 64 tile, no prefetch.
+// Each block contributes A_blk B[J*64 : J*64+64, tile] to its block row's tile.
 #include "device_common.h"
 
 namespace spx {
@@ -103,7 +104,8 @@ __global__ __launch_bounds__(kBlock) void bsr_spmm_n64(const int32_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined kernel for N % NT == 0, NT = 128 or 256.  Wave w owns columns
+// Pipelined kernel for N % NT == 0 with NT = 128 (widths that the copy-engine
+// kernel does not take; the template also builds NT = 256).  Wave w owns columns
 // [w NT/4, (w+1) NT/4) of the tile as 2 x (NT/128) MFMA tiles of 32 x 32, so
 // every A operand read from LDS feeds NT/128 MFMAs and every B operand two.
 // The next block's A and B are loaded into registers while the current
@@ -252,6 +254,232 @@ __global__ __launch_bounds__(kBlock) void bsr_spmm_pipelined(const int32_t* __re
     }
 }
 
+// ---------------------------------------------------------------------------
+// Copy-engine kernel for N % 256 == 0 (gfx950).
+//
+// Tile 64 x NT (NT = 256) per workgroup of eight waves.  Waves 0..3 compute:
+// wave w owns columns [w NT/4, (w+1) NT/4) as 2 x (NT/128) MFMA tiles of
+// 32 x 32.  Waves 4..7 only copy.  The k dimension advances in stages of half
+// a block (32 k); four stages are in flight.  A stage is filled by
+// global_load_lds (16 bytes per lane straight into LDS, no registers, no
+// repacking).  The copy waves stall whenever the memory pipeline is full; as
+// they issue no MFMAs, the compute waves keep the matrix cores fed meanwhile.
+// With 80 KB of LDS per workgroup two workgroups share a CU.
+//
+// LDS layouts (16-byte chunks, XOR-swizzled so the operand reads spread over
+// the banks; a copy instruction fills 1 KB of consecutive chunks and each
+// lane picks the source chunk that belongs at its position):
+//   A stage: row r (64 rows) x 4 chunks of 8 k;  chunk c of row r at 4 r + (c ^ fa(r)).
+//   B stage: row k (32 rows) x NT/8 chunks of 8 columns, B's own row-major
+//            order;  chunk c of row k at k NT/8 + (c ^ gb(k)).
+// A operands are one 16-byte LDS read per lane.  B operands come from
+// ds_read_b64_tr_b16: within each 16-lane group it returns to lane 4a + b,
+// element e, the b-th 16-bit value of the 8-byte row addressed by lane
+// a + 4e.  Addressing lane L at row 4 i + 8 (L / 32) + (L % 16) / 4 and
+// column 16 ((L / 16) % 2) + 4 (L % 4) therefore gives lane L the values
+// B[8 (L / 32) + 4 i + e][L % 32], e = 0..3: half i of the MFMA B operand.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kKh = 32;      // k rows per stage
+constexpr int kStages = 4;   // stages in flight
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding and leaves the other counters alone (vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int NT>
+struct DmaShape {
+    static constexpr int kABytes = kBs * kKh * 2;                 // 4 KB
+    static constexpr int kBBytes = kKh * NT * 2;                  // 16 or 32 KB
+    static constexpr int kBChunks = NT / 8;                       // chunks per B row
+    static constexpr int kBCopies = kBBytes / (kBlock * 16);      // B copy instructions per thread
+    static constexpr int kPerStage = 1 + kBCopies;                // copy instructions per thread per stage
+    static constexpr int kUC = NT / 128;                          // 32-column MFMA tiles per wave
+};
+
+__device__ __forceinline__ int dma_fa(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int dma_gb(int k) { return (k & 3) << 2; }
+
+// Issue the copies of stage h (block kb0 + h/2 with column index J0, k half
+// h%2) into (la, lb); w is the copying wave's index (0..3).  A block with an
+// out-of-range column index still copies (from block column 0) so that the
+// count of copies per stage is fixed; its product is masked by the consumers.
+template <int NT>
+__device__ __forceinline__ void dma_copy(uint8_t* la, uint8_t* lb, int h, int kb0, int J0,
+                                         const uint16_t* __restrict__ bval, const uint16_t* __restrict__ B,
+                                         int64_t ldb, int n_base, int kb_count, int w, int l) {
+    using S = DmaShape<NT>;
+    const int kb = kb0 + (h >> 1), kh = h & 1;
+    const int J = (J0 >= 0 && J0 < kb_count) ? J0 : 0;
+    {
+        const int p = w * 64 + l;  // chunk position in the A stage
+        const int r = p >> 2, c = (p & 3) ^ dma_fa(r);
+        const uint16_t* src = bval + (int64_t)kb * (kBs * kBs) + r * kBs + kh * kKh + c * 8;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(la + w * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < S::kBCopies; ++j) {
+        const int q = (j * 4 + w) * 64 + l;  // chunk position in the B stage
+        const int k = q / S::kBChunks, c = (q % S::kBChunks) ^ dma_gb(k);
+        const uint16_t* src = B + ((int64_t)J * kBs + kh * kKh + k) * ldb + n_base + c * 8;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(lb + (j * 4 + w) * 1024), 16, 0, 0);
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void dma_compute(const uint8_t* la, const uint8_t* lb, f32x16 (&acc)[2][DmaShape<NT>::kUC],
+                                            bool ok, int w, int l) {
+    using S = DmaShape<NT>;
+#pragma unroll
+    for (int ks = 0; ks < kKh / 16; ++ks) {
+        bf16x8 aop[2], bop[S::kUC];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int r = 32 * t + (l & 31), c = 2 * ks + (l >> 5);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(la + (r * 4 + (c ^ dma_fa(r))) * 16);
+            // a block with an out-of-range column contributes nothing (selected,
+            // not branched, so the accumulators stay in place)
+            aop[t] = __builtin_bit_cast(bf16x8, ok ? v : u32x4{0u, 0u, 0u, 0u});
+        }
+#pragma unroll
+        for (int u = 0; u < S::kUC; ++u) {
+            s16x4 half[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int k = 16 * ks + 8 * (l >> 5) + 4 * i + ((l & 15) >> 2);
+                const int n = w * (NT / 4) + 32 * u + 16 * ((l >> 4) & 1) + 4 * (l & 3);
+                const uint8_t* p = lb + (k * S::kBChunks + ((n >> 3) ^ dma_gb(k))) * 16 + (n & 7) * 2;
+                half[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+            }
+            const s16x4 lo = half[0], hi = half[1];
+            const short __attribute__((ext_vector_type(8))) both = {lo[0], lo[1], lo[2], lo[3],
+                                                                    hi[0], hi[1], hi[2], hi[3]};
+            bop[u] = __builtin_bit_cast(bf16x8, both);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int u = 0; u < S::kUC; ++u)
+                acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[t], bop[u], acc[t][u], 0, 0, 0);
+    }
+}
+
+template <int NT>
+__global__ __launch_bounds__(2 * kBlock) void bsr_spmm_dma(const int32_t* __restrict__ brow_ptr,
+                                                           const int32_t* __restrict__ bcol,
+                                                           const uint16_t* __restrict__ bval,
+                                                           const uint16_t* __restrict__ B, int64_t ldb, float alpha,
+                                                           float beta, float* __restrict__ C, int64_t ldc, int nnzb,
+                                                           int kb_count, int mb, int ntiles) {
+    static_assert(NT == 256, "tile width (two workgroups of 80 KB LDS per CU)");
+    using S = DmaShape<NT>;
+    // one array per stage, so that the wait-count logic can tell the copies
+    // into one stage from the operand reads of another
+    __shared__ __attribute__((aligned(1024))) uint8_t a0[S::kABytes], a1[S::kABytes], a2[S::kABytes], a3[S::kABytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t b0[S::kBBytes], b1[S::kBBytes], b2[S::kBBytes], b3[S::kBBytes];
+
+    const int I = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
+    if (I >= mb) return;
+    const int n_base = tile * NT;
+    // waves 0..3 run the MFMAs, waves 4..7 issue the copies: a copy instruction
+    // that waits for the memory pipeline then never holds back an MFMA
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+    const bool producer = wave >= 4;
+    const int w = wave & 3;
+
+    f32x16 acc[2][S::kUC];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < S::kUC; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[t][u][r] = 0.0f;
+
+    // out-of-range block pointers are clamped; with no block columns at all B
+    // has no rows and nothing is read
+    const int kb0 = max(brow_ptr[I], 0);
+    const int kb1 = kb_count > 0 ? min(brow_ptr[I + 1], nnzb) : kb0;
+    const int T = kb1 > kb0 ? 2 * (kb1 - kb0) : 0;  // stages
+
+    bool ok0 = false, ok1 = false, ok2 = false, ok3 = false;
+#define SPX_ISSUE(h, la, lb, okv, J)                                                         \
+    {                                                                                         \
+        okv = (J) >= 0 && (J) < kb_count;                                                     \
+        if (producer) dma_copy<NT>(la, lb, h, kb0, J, bval, B, ldb, n_base, kb_count, w, l);  \
+    }
+    // column index of the next stage to issue, read one stage ahead of its use
+    const int last = kb1 - 1;
+    int jn = 0;
+    if (T > 0) {
+        const int j0 = bcol[kb0];
+        jn = bcol[min(kb0 + 1, last)];
+        SPX_ISSUE(0, a0, b0, ok0, j0);
+        SPX_ISSUE(1, a1, b1, ok1, j0);
+        SPX_ISSUE(2, a2, b2, ok2, jn);
+    }
+
+    // Stage h: the producers wait until its copies have landed (copies of at
+    // most two later stages may still be in flight); barrier; the producers
+    // refill the buffer consumed at h - 1 with stage h + 3 while the consumers
+    // run the MFMAs of stage h.  The consumers' operand reads of stage h - 1
+    // completed before they reached the barrier (the MFMAs consumed them).
+#define SPX_STEP(h, la, lb, okv, nla, nlb, nokv)                                   \
+    {                                                                               \
+        if (producer) {                                                             \
+            const int ahead = min(T - 1 - (h), 2);                                  \
+            if (ahead == 2)                                                         \
+                __builtin_amdgcn_s_waitcnt(vm_wait(2 * S::kPerStage));              \
+            else if (ahead == 1)                                                    \
+                __builtin_amdgcn_s_waitcnt(vm_wait(S::kPerStage));                  \
+            else                                                                    \
+                __builtin_amdgcn_s_waitcnt(vm_wait(0));                             \
+        }                                                                           \
+        asm volatile("s_barrier" ::: "memory");                                     \
+        if ((h) + 3 < T) SPX_ISSUE((h) + 3, nla, nlb, nokv, jn);                    \
+        jn = bcol[min(kb0 + (((h) + 4) >> 1), last)];                               \
+        if (!producer) dma_compute<NT>(la, lb, acc, okv, w, l);                     \
+    }
+    for (int h = 0; h < T; h += 4) {
+        SPX_STEP(h, a0, b0, ok0, a3, b3, ok3);
+        if (h + 1 < T) SPX_STEP(h + 1, a1, b1, ok1, a0, b0, ok0);
+        if (h + 2 < T) SPX_STEP(h + 2, a2, b2, ok2, a1, b1, ok1);
+        if (h + 3 < T) SPX_STEP(h + 3, a3, b3, ok3, a2, b2, ok2);
+    }
+#undef SPX_STEP
+#undef SPX_ISSUE
+    if (producer) return;
+
+    // D layout of the 32x32 MFMA: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int u = 0; u < S::kUC; ++u) {
+            const int col = n_base + w * (NT / 4) + 32 * u + (l & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = I * kBs + 32 * t + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+                float* c = C + (int64_t)row * ldc + col;
+                float o = alpha * acc[t][u][r];
+                if (beta != 0.0f) o = fmaf(beta, *c, o);
+                *c = o;
+            }
+        }
+    }
+}
+
+template <int NT>
+hipError_t launch_dma(int64_t mb, int64_t kb, int64_t nnzb, const int32_t* brow_ptr, const int32_t* bcol,
+                      const uint16_t* bval, int32_t N, const uint16_t* B, int64_t ldb, float alpha, float beta,
+                      float* C, int64_t ldc, hipStream_t s) {
+    const int ntiles = N / NT;
+    hipLaunchKernelGGL(bsr_spmm_dma<NT>, dim3((unsigned)(mb * ntiles)), dim3(2 * kBlock), 0, s, brow_ptr, bcol, bval, B,
+                       ldb, alpha, beta, C, ldc, (int)nnzb, (int)kb, (int)mb, ntiles);
+    return hipGetLastError();
+}
+
 template <int NT>
 hipError_t launch_pipelined(int64_t mb, int64_t kb, int64_t nnzb, const int32_t* brow_ptr, const int32_t* bcol,
                             const uint16_t* bval, int32_t N, const uint16_t* B, int64_t ldb, float alpha, float beta,
@@ -269,9 +497,6 @@ hipError_t launch_pipelined(int64_t mb, int64_t kb, int64_t nnzb, const int32_t*
 
 size_t bsr_work_bytes(int64_t, int64_t, int32_t, int64_t, int32_t) { return 0; }
 
-// Tile width of the pipelined kernel for wide N (128 or 256).
-constexpr int kBsrTile = 256;
-
 int bsr_spmm_device(int64_t mb, int64_t kb, int32_t bs, int64_t nnzb, const int32_t* brow_ptr, const int32_t* bcol,
                     const uint16_t* bval, int32_t N, const uint16_t* B, int64_t ldb, float alpha, float beta,
                     float* C, int64_t ldc, void* work, size_t work_bytes, hipStream_t s) {
@@ -280,8 +505,8 @@ int bsr_spmm_device(int64_t mb, int64_t kb, int32_t bs, int64_t nnzb, const int3
     (void)bs;
     if (mb == 0 || N == 0) return SP_OK;
     hipError_t err;
-    if (N % kBsrTile == 0) {
-        err = launch_pipelined<kBsrTile>(mb, kb, nnzb, brow_ptr, bcol, bval, N, B, ldb, alpha, beta, C, ldc, s);
+    if (N % 256 == 0) {
+        err = launch_dma<256>(mb, kb, nnzb, brow_ptr, bcol, bval, N, B, ldb, alpha, beta, C, ldc, s);
     } else if (N % 128 == 0) {
         err = launch_pipelined<128>(mb, kb, nnzb, brow_ptr, bcol, bval, N, B, ldb, alpha, beta, C, ldc, s);
     } else {

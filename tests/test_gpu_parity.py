@@ -233,7 +233,11 @@ def test_spmm_n1_equals_spmv():
 
 # ------------------------------------------------------------------ BSR
 @pytest.mark.parametrize("mb,kb,N,density", [(3, 4, 64, 0.5), (8, 6, 128, 0.3), (5, 9, 192, 0.25),
-                                             (16, 16, 512, 0.1), (4, 4, 256, 1.0), (6, 3, 128, 0.0)])
+                                             (16, 16, 512, 0.1), (4, 4, 256, 1.0), (6, 3, 128, 0.0),
+                                             # long block rows: 94..96 half-block stages, every tail length
+                                             (4, 48, 512, 0.98), (4, 47, 256, 1.0),
+                                             # several column tiles per block row
+                                             (3, 5, 768, 0.6), (2, 7, 1024, 1.0)])
 def test_bsr_spmm(mb, kb, N, density):
     say("bsr", mb, kb, N, density)
     b = gen.block_sparse_bsr(mb=mb, kb=kb, bs=64, density=density, std=0.02, seed=mb * 100 + kb)
@@ -249,3 +253,27 @@ def test_bsr_spmm(mb, kb, N, density):
         assert_close(got, ref, scale, tol=TOL_BF16, what="bsr a=%g b=%g" % (alpha, beta))
         # fp32 accumulation of exact bf16 products: far inside the bf16 tolerance
         assert_close(got, ref, scale, tol=1e-5, what="bsr fp32-accumulation bound")
+
+
+@pytest.mark.parametrize("N", [64, 128, 256, 512])
+def test_bsr_out_of_range_columns(N):
+    """Blocks whose column index lies outside [0, kb) contribute nothing."""
+    say("bsr bad columns", N)
+    mb, kb = 5, 6
+    b = gen.block_sparse_bsr(mb=mb, kb=kb, bs=64, density=0.7, std=0.02, seed=77)
+    bad = b.bcol.copy()
+    rng = np.random.default_rng(5)
+    hit = rng.random(bad.size) < 0.3
+    bad[hit] = np.where(rng.random(int(hit.sum())) < 0.5, -1, kb + 3)
+    keep = ~hit
+    # reference: the same matrix with those blocks removed
+    counts = np.array([keep[b.brow_ptr[i]:b.brow_ptr[i + 1]].sum() for i in range(mb)])
+    rp_k = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    bval_k = np.ascontiguousarray(b.bval[keep])
+    rp, col, v64 = oracle.bsr_to_csr(mb, 64, rp_k, b.bcol[keep], bval_k)
+    B = gen.bf16_matrix(kb * 64, N, seed=4)
+    C = torch.full((mb * 64, N), float("nan"), device="cuda")
+    sp.bsr_spmm(mb, kb, 64, dev(b.brow_ptr), dev(bad), dev(b.bval.view(np.int16)), dev(B.view(np.int16)),
+                1.0, 0.0, C)
+    ref, scale = oracle.spmm_bf16(rp, col, v64, B, 1.0, 0.0, gen.dense_matrix(mb * 64, N, 4))
+    assert_close(host(C), ref, scale, tol=1e-5, what="bsr with skipped blocks")
