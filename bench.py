@@ -23,8 +23,14 @@ sys.path.insert(0, HERE)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-KERNEL_SOURCES = ["spmm_csr_spmv_amd/csrc/spmv.hip", "spmm_csr_spmv_amd/csrc/spmm.hip",
-                  "spmm_csr_spmv_amd/csrc/bsr.hip", "spmm_csr_spmv_amd/csrc/device_common.h"]
+# Sources whose code decides the kernels each workload runs (a committed
+# traffic summary is used only while these are unchanged).
+_CSRC = "spmm_csr_spmv_amd/csrc/"
+KERNEL_SOURCES = {
+    "spmv": [_CSRC + f for f in ("spmv.hip", "pstream.hip", "device_common.h", "internal.h", "api.cpp")],
+    "spmm": [_CSRC + f for f in ("spmm.hip", "device_common.h", "internal.h", "api.cpp")],
+    "bsr": [_CSRC + f for f in ("bsr.hip", "device_common.h", "internal.h")],
+}
 
 
 # --------------------------------------------------------------------------
@@ -71,9 +77,13 @@ def block_index_bytes_per_value(bs, idx_bytes=4):
     return idx_bytes / float(bs * bs)
 
 
-def kernel_fingerprint():
+def kernel_family(workload):
+    return "bsr" if workload.startswith("bsr") else ("spmm" if workload.startswith("spmm") else "spmv")
+
+
+def kernel_fingerprint(workload):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel_family(workload)]:
         with open(os.path.join(HERE, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -87,7 +97,7 @@ def load_traffic(workload, launches_bytes):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_fingerprint") != kernel_fingerprint():
+    if t.get("kernel_fingerprint") != kernel_fingerprint(workload):
         return None
     return t.get("bytes_per_launch")
 

@@ -120,15 +120,21 @@ int csr_to_csc(int64_t m, int64_t n, int64_t nnz,
  * entries by at most 20 % ([GEN] §4 rule table: short regular rows, padding
  * checked first); use_sell = 0 never uses it.
  *
- * Column panels ([GEN] §2.5: random x gathers are the real cost once x is
- * much larger than the cache): with col_panels = P the columns are cut into
- * P equal ranges and panel p of every group is served by the XCD p (mod 8),
- * so its gathers stay inside one L2-sized slice of x; the per-panel row sums
- * are added in panel order.  Group rows then hold at most 255 entries.  The
- * default (-1) uses 4 panels when x exceeds 8 MiB and a sample of groups
- * shows columns spread over more than a quarter of the column range; SELL
- * and panels exclude each other.  Panels cost a copy of the group entries
- * (8 bytes each) plus 6 bytes per row and panel in the workspace.
+ * Column-panel stream ([GEN] §2.5: random x gathers are the real cost once
+ * x is much larger than the cache; §2.4: split long rows, reduce the pieces in
+ * a fixed order): with col_panels = P in {1, 2, 4, 8} spmv and spmv_t use,
+ * instead of the bins above, a copy of the matrix built at bind in which
+ * the columns are cut into P panels of a power-of-two width and every row of
+ * at most min(split_min, 4032) entries is stored panel by panel, cut into
+ * row-aligned chunks of at most 4096 entries.  Panel p is served only by the
+ * XCDs p, p + P, ..., so its gathers stay in one L2-sized slice of x; the
+ * per-panel row sums are added in panel order.  Longer rows are summed in
+ * segments of split_seg entries whose partials are added in segment order.
+ * The default (-1) uses 8 panels when x exceeds 8 MiB and a sample of groups
+ * shows columns spread over more than a quarter of the column range, else
+ * none; SELL and panels exclude each other.  The copy costs 8 bytes per
+ * entry plus 4 bytes per row and panel of workspace, and sp_plan_create
+ * reads the column indices back to the host once to cut the chunks.
  */
 typedef struct sp_plan sp_plan;
 
@@ -141,7 +147,7 @@ typedef struct sp_plan_options {
     int32_t use_sell;    /* -1 auto (default), 0 off, 1 on                     */
     int32_t sell_sigma;  /* sorting window in rows for SELL, >= 1 (default 1024) */
     int32_t xcd_remap;   /* 1 (default): consecutive groups go to one XCD     */
-    int32_t col_panels;  /* -1 auto (default), 0 off, or 2, 4, 8 panels       */
+    int32_t col_panels;  /* -1 auto (default), 0 off, or 1, 2, 4, 8 panels    */
 } sp_plan_options;
 
 /* Row-length profile and bin sizes of one direction of a plan. */
@@ -155,7 +161,7 @@ typedef struct sp_profile {
     int64_t block_rows, block_nnz;
     int64_t split_rows, split_segments, split_nnz;
     int64_t sell_slots;          /* padded SELL slots (0 without SELL)         */
-    int64_t col_panels;          /* column panels in use (0 = none)            */
+    int64_t col_panels;          /* panels of the column-panel stream (0: off)  */
 } sp_profile;
 
 /* Fills *opt with the defaults listed above. */

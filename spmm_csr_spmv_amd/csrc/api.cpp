@@ -46,16 +46,21 @@ struct Dir {
     std::vector<int64_t> sell_slice_ptr;
     std::vector<int32_t> sell_perm, sell_len;
     int64_t sell_slots = 0;
-    // column panels: the panel groups, appended to a copy of the long-row tasks
-    int32_t npanels = 0, panel_width = 0;
-    std::vector<int4> ptasks;  // split | block | wave | panel groups
-    int32_t n_pgroup = 0;
+    // column-panel stream (host side; see pstream.hip)
+    int32_t ps_P = 0, ps_cb = 0;
+    std::vector<int4> ps_chunks;       // panel-major
+    int32_t ps_coff[spx::kXcds + 1] = {};
+    std::vector<int32_t> ps_start;     // [P][rows] stream position of row r's panel-p entries
+    int64_t ps_total = 0;              // stream entries, padding included
+    std::vector<int4> ps_split_tasks;  // {partial index, 0, nz_begin, nz_end}
+    std::vector<int4> ps_split_rows;   // {row, partial_base, nseg, 0}
     sp_profile prof{};
     DirDevice dev{};
     // workspace offsets (byte offsets into the bound workspace)
     mutable size_t off_tasks = 0, off_split_rows = 0, off_partials = 0, off_counters = 0;
     mutable size_t off_sell_ptr = 0, off_sell_perm = 0, off_sell_len = 0, off_sell_col = 0, off_sell_val = 0;
-    mutable size_t off_pcol = 0, off_pval = 0, off_pstart = 0, off_poff = 0, off_ypart = 0, off_ptasks = 0;
+    mutable size_t off_ps_chunks = 0, off_ps_pk = 0, off_ps_pv = 0, off_ps_ypart = 0, off_ps_split_tasks = 0;
+    mutable size_t off_ps_split_rows = 0, off_ps_partials = 0;
 };
 
 }  // namespace
@@ -212,6 +217,8 @@ void build_sell(const std::vector<int32_t>& hptr, const sp_plan_options& o, Dir&
     d.prof.sell_slots = slots;
 }
 
+int64_t ps_ystride(int64_t rows) { return (rows + 63) / 64 * 64; }
+
 size_t dir_layout(const Dir& d, const sp_plan_options& o, int32_t max_N, size_t base) {
     size_t off = base;
     d.off_tasks = off;
@@ -223,19 +230,22 @@ size_t dir_layout(const Dir& d, const sp_plan_options& o, int32_t max_N, size_t 
     const int64_t max_tiles = std::max<int64_t>(1, (max_N + 63) / 64);
     d.off_counters = off;
     off = align256(off + d.split_rows.size() * (size_t)max_tiles * sizeof(int32_t));
-    if (d.npanels > 0) {
-        d.off_pcol = off;
-        off = align256(off + (size_t)d.nnz * sizeof(int32_t));
-        d.off_pval = off;
-        off = align256(off + (size_t)d.nnz * sizeof(float));
-        d.off_ptasks = off;
-        off = align256(off + d.ptasks.size() * sizeof(int4));
-        d.off_pstart = off;
-        off = align256(off + (size_t)d.n_pgroup * (size_t)(d.npanels + 1) * sizeof(int32_t));
-        d.off_poff = off;
-        off = align256(off + (size_t)d.npanels * (size_t)d.rows * sizeof(uint16_t));
-        d.off_ypart = off;
-        off = align256(off + (size_t)d.npanels * (size_t)d.rows * sizeof(float));
+    if (d.ps_P > 0) {
+        d.off_ps_chunks = off;
+        off = align256(off + d.ps_chunks.size() * sizeof(int4));
+        d.off_ps_pk = off;
+        off = align256(off + (size_t)d.ps_total * sizeof(uint32_t));
+        d.off_ps_pv = off;
+        off = align256(off + (size_t)d.ps_total * sizeof(float));
+        // panel row sums; at bind it first holds the [P][rows] stream starts
+        d.off_ps_ypart = off;
+        off = align256(off + (size_t)d.ps_P * (size_t)ps_ystride(d.rows) * sizeof(float));
+        d.off_ps_split_tasks = off;
+        off = align256(off + d.ps_split_tasks.size() * sizeof(int4));
+        d.off_ps_split_rows = off;
+        off = align256(off + d.ps_split_rows.size() * sizeof(int4));
+        d.off_ps_partials = off;
+        off = align256(off + d.ps_split_tasks.size() * sizeof(float));
     }
     if (d.use_sell) {
         d.off_sell_ptr = off;
@@ -269,16 +279,18 @@ int check_options(const sp_plan_options& o) {
     if (o.split_seg < 16) return SP_ERR_UNSUPPORTED;
     if (o.use_sell < -1 || o.use_sell > 1) return SP_ERR_UNSUPPORTED;
     if (o.sell_sigma < 1) return SP_ERR_UNSUPPORTED;
-    if (o.col_panels != -1 && o.col_panels != 0 && o.col_panels != 2 && o.col_panels != 4 && o.col_panels != 8)
+    if (o.col_panels != -1 && o.col_panels != 0 && o.col_panels != 1 && o.col_panels != 2 && o.col_panels != 4 &&
+        o.col_panels != 8)
         return SP_ERR_UNSUPPORTED;
     if (o.xcd_remap != 0 && o.xcd_remap != 1) return SP_ERR_UNSUPPORTED;
     return SP_OK;
 }
 
-// Auto rule for column panels: x must exceed 8 MiB (two L2s' worth), and a
-// sample of up to 64 evenly spaced group tasks must show columns spread over
-// more than a quarter of the column range (median over the sample of
-// max col - min col).  Reads the sampled column ranges back: synchronises.
+// Auto rule for the column-panel stream (8 panels, one per XCD): x must
+// exceed 8 MiB (two L2s' worth), and a sample of up to 64 evenly spaced group
+// tasks must show columns spread over more than a quarter of the column range
+// (median over the sample of max col - min col).  Reads the sampled column
+// ranges back: synchronises.
 int scattered_columns(const Dir& d, hipStream_t s, int32_t* P) {
     *P = 0;
     if ((int64_t)d.cols * 4 <= (int64_t)8 << 20) return SP_OK;
@@ -301,7 +313,96 @@ int scattered_columns(const Dir& d, hipStream_t s, int32_t* P) {
     }
     if (spans.empty()) return SP_OK;
     std::nth_element(spans.begin(), spans.begin() + spans.size() / 2, spans.end());
-    if (spans[spans.size() / 2] * 4 > d.cols) *P = 4;
+    if (spans[spans.size() / 2] * 4 > d.cols) *P = 8;
+    return SP_OK;
+}
+
+// Column-panel stream (pstream.hip): panel width W = 2^cb, the smallest power
+// of two >= cols / P (at least 32); rows longer than S = min(split_min,
+// kPsEntries - 64) are cut out and split into segments of split_seg entries.
+// Each panel's rows are packed greedily into chunks of at most kPsEntries
+// entries (chunk starts padded to multiples of 4) and at most
+// min(kPsMaxRows, 2^(32 - cb)) rows, a long row ending the chunk before it.
+// Needs the column indices on the host: copies them once (synchronises).
+// Leaves d.ps_P = 0 (no stream) when the panel width would exceed 2^22
+// columns or the stream would not fit int32 positions.
+int build_pstream(const std::vector<int32_t>& hptr, const sp_plan_options& o, int32_t P, Dir& d, hipStream_t s) {
+    d.ps_P = 0;
+    d.ps_chunks.clear();
+    d.ps_start.clear();
+    d.ps_split_tasks.clear();
+    d.ps_split_rows.clear();
+    const int64_t rows = d.rows;
+    int64_t w = std::max<int64_t>(32, ((int64_t)d.cols + P - 1) / P);
+    int cb = 0;
+    while (((int64_t)1 << cb) < w) ++cb;
+    if (cb > 22) return SP_OK;
+    const int64_t rmax = std::min<int64_t>(spx::kPsMaxRows, (int64_t)1 << (32 - cb));
+    const int64_t S = std::min<int64_t>(o.split_min, spx::kPsEntries - 64);
+    std::vector<int32_t> hidx((size_t)d.nnz);
+    if (d.nnz > 0) {
+        if (hipMemcpyAsync(hidx.data(), d.idx, (size_t)d.nnz * sizeof(int32_t), hipMemcpyDeviceToHost, s) !=
+            hipSuccess)
+            return SP_ERR_HIP;
+        if (hipStreamSynchronize(s) != hipSuccess) return SP_ERR_HIP;
+    }
+    // entries of each stream row in each panel (a stream row has at most S <= 4032 entries)
+    std::vector<uint16_t> cnt((size_t)P * (size_t)rows, 0);
+    std::vector<char> longrow((size_t)rows, 0);
+    int64_t n_partials = 0;
+    for (int64_t r = 0; r < rows; ++r) {
+        const int32_t b = hptr[(size_t)r], e = hptr[(size_t)r + 1];
+        if (e - b > S) {
+            longrow[(size_t)r] = 1;
+            const int32_t nseg = (int32_t)(((int64_t)(e - b) + o.split_seg - 1) / o.split_seg);
+            d.ps_split_rows.push_back(make_int4((int32_t)r, (int32_t)n_partials, nseg, 0));
+            for (int32_t k = 0; k < nseg; ++k) {
+                const int32_t sb = b + k * o.split_seg;
+                const int32_t se = (int32_t)std::min<int64_t>(e, (int64_t)sb + o.split_seg);
+                d.ps_split_tasks.push_back(make_int4((int32_t)(n_partials + k), 0, sb, se));
+            }
+            n_partials += nseg;
+            continue;
+        }
+        for (int32_t k = b; k < e; ++k) {
+            const int32_t p = hidx[(size_t)k] >> cb;
+            cnt[(size_t)p * (size_t)rows + (size_t)r] += 1;
+        }
+    }
+    d.ps_start.assign((size_t)P * (size_t)rows, 0);
+    int64_t pos = 0;
+    for (int32_t p = 0; p < P; ++p) {
+        d.ps_coff[p] = (int32_t)d.ps_chunks.size();
+        int64_t rb = -1, n = 0;
+        auto close = [&](int64_t re) {
+            if (rb >= 0) {
+                d.ps_chunks.push_back(make_int4((int32_t)pos, (int32_t)(pos + n), (int32_t)rb, (int32_t)re));
+                pos += (n + 3) & ~(int64_t)3;
+            }
+            rb = -1;
+            n = 0;
+        };
+        const uint16_t* cp = cnt.data() + (size_t)p * (size_t)rows;
+        int32_t* sp = d.ps_start.data() + (size_t)p * (size_t)rows;
+        for (int64_t r = 0; r < rows; ++r) {
+            if (longrow[(size_t)r]) {
+                close(r);
+                continue;
+            }
+            const int64_t c = cp[r];
+            if (rb >= 0 && (r - rb + 1 > rmax || ((n + c + 3) & ~(int64_t)3) > spx::kPsEntries)) close(r);
+            if (rb < 0) rb = r;
+            if (pos + n > kI32Max) return SP_OK;
+            sp[r] = (int32_t)(pos + n);
+            n += c;
+        }
+        close(rows);
+        if (pos > kI32Max) return SP_OK;
+    }
+    for (int32_t p = P; p <= spx::kXcds; ++p) d.ps_coff[p] = (int32_t)d.ps_chunks.size();
+    d.ps_total = pos;
+    d.ps_P = P;
+    d.ps_cb = cb;
     return SP_OK;
 }
 
@@ -344,53 +445,23 @@ int setup_dir(Dir& d, int64_t rows, int64_t cols, int64_t nnz, const int32_t* pt
         d.sell_slots = 0;
         d.prof.sell_slots = 0;
     }
-    d.npanels = 0;
-    d.panel_width = 0;
-    if (!d.use_sell && o.col_panels != 0 && d.n_group > 0) {
+    d.ps_P = 0;
+    if (!d.use_sell && o.col_panels != 0 && d.rows > 0) {
         int32_t P = o.col_panels;
         if (P < 0) {
-            int rc = scattered_columns(d, s, &P);
+            const int rc = scattered_columns(d, s, &P);
             if (rc != SP_OK) return rc;
         }
         if (P > 0) {
-            // Panel groups: consecutive group rows (length <= wave_min), at most
-            // kGroupMaxRows rows and P * kGroupMaxNnz / 2 entries, so that a
-            // panel block of scattered columns averages half the LDS capacity.
-            d.ptasks.assign(d.tasks.begin(), d.tasks.begin() + (d.n_split + d.n_block + d.n_wave));
-            const int64_t cap = (int64_t)P * spx::kGroupMaxNnz / 2;
-            int32_t r0 = 0, nr = 0;
-            int64_t nz = 0;
-            auto close = [&](int32_t next) {
-                if (nr > 0)
-                    d.ptasks.push_back(make_int4(r0, r0 + nr, hptr[(size_t)r0], hptr[(size_t)(r0 + nr)]));
-                r0 = next;
-                nr = 0;
-                nz = 0;
-            };
-            for (int32_t r = 0; r < d.rows; ++r) {
-                const int32_t l = hptr[(size_t)r + 1] - hptr[(size_t)r];
-                if (l > o.wave_min) {
-                    close(r + 1);
-                    continue;
-                }
-                if (nr > 0 && (nz + l > cap || nr == spx::kGroupMaxRows)) close(r);
-                if (nr == 0) r0 = r;
-                nr += 1;
-                nz += l;
-            }
-            close(d.rows);
-            d.n_pgroup = (int32_t)(d.ptasks.size() - (size_t)(d.n_split + d.n_block + d.n_wave));
-            int64_t w = (d.cols + P - 1) / P;
-            w = (w + 31) / 32 * 32;  // whole 128-byte lines of x per panel
-            d.npanels = P;
-            d.panel_width = (int32_t)std::max<int64_t>(w, 32);
+            const int rc = build_pstream(hptr, o, P, d, s);
+            if (rc != SP_OK) return rc;
         }
     }
-    d.prof.col_panels = d.npanels;
+    d.prof.col_panels = d.ps_P;
     return SP_OK;
 }
 
-int upload_dir(Dir& d, char* ws, const sp_plan_options& o, int32_t* panel_flag, hipStream_t s) {
+int upload_dir(Dir& d, char* ws, const sp_plan_options& o, hipStream_t s) {
     DirDevice& v = d.dev;
     v = DirDevice{};
     v.rows = d.rows;
@@ -417,20 +488,31 @@ int upload_dir(Dir& d, char* ws, const sp_plan_options& o, int32_t* panel_flag, 
         hipMemcpyAsync(ws + d.off_split_rows, d.split_rows.data(), d.split_rows.size() * sizeof(int4),
                        hipMemcpyHostToDevice, s) != hipSuccess)
         return SP_ERR_HIP;
-    v.npanels = d.npanels;
-    v.panel_width = d.panel_width;
-    if (d.npanels > 0) {
-        v.pcol = reinterpret_cast<int32_t*>(ws + d.off_pcol);
-        v.pval = reinterpret_cast<float*>(ws + d.off_pval);
-        v.pstart = reinterpret_cast<int32_t*>(ws + d.off_pstart);
-        v.poff = reinterpret_cast<uint16_t*>(ws + d.off_poff);
-        v.ypart = reinterpret_cast<float*>(ws + d.off_ypart);
-        v.ptasks = reinterpret_cast<const int4*>(ws + d.off_ptasks);
-        v.n_pgroup = d.n_pgroup;
-        if (!d.ptasks.empty() && hipMemcpyAsync(ws + d.off_ptasks, d.ptasks.data(), d.ptasks.size() * sizeof(int4),
-                                                hipMemcpyHostToDevice, s) != hipSuccess)
+    v.ps_P = d.ps_P;
+    if (d.ps_P > 0) {
+        v.ps_cb = d.ps_cb;
+        for (int k = 0; k <= spx::kXcds; ++k) v.ps_coff[k] = d.ps_coff[k];
+        v.ps_chunks = reinterpret_cast<const int4*>(ws + d.off_ps_chunks);
+        v.ps_pk = reinterpret_cast<uint32_t*>(ws + d.off_ps_pk);
+        v.ps_pv = reinterpret_cast<float*>(ws + d.off_ps_pv);
+        v.ps_ypart = reinterpret_cast<float*>(ws + d.off_ps_ypart);
+        v.ps_ystride = ps_ystride(d.rows);
+        v.ps_n_split_tasks = (int32_t)d.ps_split_tasks.size();
+        v.ps_split_tasks = reinterpret_cast<const int4*>(ws + d.off_ps_split_tasks);
+        v.ps_n_split_rows = (int32_t)d.ps_split_rows.size();
+        v.ps_split_rows = reinterpret_cast<const int4*>(ws + d.off_ps_split_rows);
+        v.ps_partials = reinterpret_cast<float*>(ws + d.off_ps_partials);
+        auto up = [&](size_t off, const void* src, size_t bytes) {
+            return bytes == 0 || hipMemcpyAsync(ws + off, src, bytes, hipMemcpyHostToDevice, s) == hipSuccess;
+        };
+        // the stream starts go to the panel-sum area, which the build kernel reads before any product runs
+        if (!up(d.off_ps_chunks, d.ps_chunks.data(), d.ps_chunks.size() * sizeof(int4)) ||
+            !up(d.off_ps_split_tasks, d.ps_split_tasks.data(), d.ps_split_tasks.size() * sizeof(int4)) ||
+            !up(d.off_ps_split_rows, d.ps_split_rows.data(), d.ps_split_rows.size() * sizeof(int4)) ||
+            !up(d.off_ps_ypart, d.ps_start.data(), d.ps_start.size() * sizeof(int32_t)))
             return SP_ERR_HIP;
-        if (spx::launch_panel_build(v, panel_flag, s) != hipSuccess) return SP_ERR_HIP;
+        if (spx::launch_pstream_build(v, reinterpret_cast<const int32_t*>(ws + d.off_ps_ypart), s) != hipSuccess)
+            return SP_ERR_HIP;
     }
     if (d.use_sell) {
         v.use_sell = 1;
@@ -591,7 +673,6 @@ int sp_plan_bind(sp_plan* plan, void* work, size_t work_bytes, int32_t max_N, vo
     char* ws = static_cast<char*>(work);
     plan->bound = false;
     // every stored index must lie inside its dimension before any product runs
-    // misc words: [0] index check, [1] / [2] panel-block overflow of A / A^T
     int32_t* flag = reinterpret_cast<int32_t*>(ws);
     if (spx::launch_fill_i32(flag, 4, 0, s) != hipSuccess) return SP_ERR_HIP;
     for (const Dir* d : {&plan->fwd, &plan->tr}) {
@@ -603,22 +684,9 @@ int sp_plan_bind(sp_plan* plan, void* work, size_t work_bytes, int32_t max_N, vo
     if (hipStreamSynchronize(s) != hipSuccess) return SP_ERR_HIP;
     if (bad) return SP_ERR_INDEX;
     int rc = SP_OK;
-    if (plan->fwd.present) rc = upload_dir(plan->fwd, ws, plan->opt, flag + 1, s);
-    if (rc == SP_OK && plan->tr.present) rc = upload_dir(plan->tr, ws, plan->opt, flag + 2, s);
+    if (plan->fwd.present) rc = upload_dir(plan->fwd, ws, plan->opt, s);
+    if (rc == SP_OK && plan->tr.present) rc = upload_dir(plan->tr, ws, plan->opt, s);
     if (rc != SP_OK) return rc;
-    if (plan->fwd.npanels > 0 || plan->tr.npanels > 0) {
-        // a panel block larger than the panel kernel's LDS: serve that direction without panels
-        int32_t over[2] = {0, 0};
-        if (hipMemcpyAsync(over, flag + 1, sizeof over, hipMemcpyDeviceToHost, s) != hipSuccess) return SP_ERR_HIP;
-        if (hipStreamSynchronize(s) != hipSuccess) return SP_ERR_HIP;
-        Dir* dirs[2] = {&plan->fwd, &plan->tr};
-        for (int k = 0; k < 2; ++k) {
-            if (over[k]) {
-                dirs[k]->dev.npanels = 0;
-                dirs[k]->prof.col_panels = 0;
-            }
-        }
-    }
     // arrival counters start at zero; the kernels put them back to zero
     for (Dir* d : {&plan->fwd, &plan->tr}) {
         if (!d->present || d->split_rows.empty()) continue;

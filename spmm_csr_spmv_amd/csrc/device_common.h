@@ -81,6 +81,7 @@ __device__ __forceinline__ float4 ldg4(const float* p) { return *reinterpret_cas
 // arrays are read exactly once per product).
 typedef int32_t v4i32 __attribute__((ext_vector_type(4)));
 typedef float v4f32 __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int4 ldg4_nt(const int32_t* p) {
     const v4i32 v = __builtin_nontemporal_load(reinterpret_cast<const v4i32*>(p));
     return make_int4(v.x, v.y, v.z, v.w);
@@ -95,6 +96,64 @@ __device__ __forceinline__ float atomic_load_f(const float* p) {
 }
 __device__ __forceinline__ void atomic_store_f(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------- streamed products
+// Products val[q] * x[idx[q]] for q in [b, e).  Lane `lane` of `stride`
+// lanes owns the 4-entry chunks starting at (b & ~3) + 4*lane + 4*stride*k.
+// Chunks are taken U at a time: the U column/value loads (16-byte loads for
+// full chunks, guarded scalar loads at the ragged ends) are all issued before
+// the gathers of x, and all gathers before any product, so every lane keeps
+// up to 8U independent memory requests in flight.  `emit(q, prod)` receives
+// each valid product; slots outside [b, e) are never read nor multiplied.
+template <int U, class Emit>
+__device__ __forceinline__ void stream_products(const int32_t* __restrict__ idx, const float* __restrict__ val,
+                                                const float* __restrict__ x, int b, int e, int lane, int stride,
+                                                Emit emit) {
+    const int base = b & ~3;
+    for (int v0 = base + 4 * lane; v0 < e; v0 += 4 * stride * U) {
+        int c[U][4];
+        float a[U][4];
+        bool ok[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + 4 * stride * u;
+            if (v >= b && v + 4 <= e) {
+                const int4 ci = ldg4_nt(idx + v);
+                const float4 ai = ldg4_nt(val + v);
+                c[u][0] = ci.x; c[u][1] = ci.y; c[u][2] = ci.z; c[u][3] = ci.w;
+                a[u][0] = ai.x; a[u][1] = ai.y; a[u][2] = ai.z; a[u][3] = ai.w;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ok[u][j] = true;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int q = v + j;
+                    ok[u][j] = q >= b && q < e;
+                    c[u][j] = ok[u][j] ? idx[q] : 0;
+                    a[u][j] = ok[u][j] ? val[q] : 0.0f;
+                }
+            }
+        }
+        float xv[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xv[u][j] = ok[u][j] ? x[c[u][j]] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + 4 * stride * u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (ok[u][j]) emit(v + j, a[u][j] * xv[u][j]);
+        }
+    }
+}
+
+__device__ __forceinline__ void store_axpby(float* __restrict__ y, int row, float acc, float alpha, float beta) {
+    float o = alpha * acc;
+    if (beta != 0.0f) o = fmaf(beta, y[row], o);
+    y[row] = o;
 }
 
 }  // namespace spx

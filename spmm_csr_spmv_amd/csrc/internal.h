@@ -14,6 +14,8 @@ constexpr int kBlock = 256;          // threads per workgroup for every kernel
 constexpr int kGroupMaxNnz = 4096;   // LDS capacity of a group task (entries)
 constexpr int kGroupMaxRows = 1024;  // rows per group task
 constexpr int kXcds = 8;             // MI355X: workgroups go round-robin to 8 XCDs
+constexpr int kPsEntries = 4096;     // column-panel stream: entries per chunk (16 per thread)
+constexpr int kPsMaxRows = 2048;     // column-panel stream: rows per chunk (LDS row sums)
 
 // Task tables of one direction (A or A^T), laid out in device memory as one
 // int4 array: [split tasks | block tasks | wave tasks | group tasks].
@@ -35,16 +37,20 @@ struct DirDevice {
     int32_t* counters;      // device, arrival counters (self-resetting)
     int32_t xcd_remap;
     int32_t group_cap;      // LDS entries reserved for a group task
-    // optional column panels of the group rows (see spmv.hip)
-    int32_t npanels;                 // 0 = off
-    const int4* ptasks;              // [split | block | wave | panel groups]
-    int32_t n_pgroup;
-    int32_t panel_width;             // columns per panel
-    int32_t* pcol;                   // [nnz] panel-major copy (group ranges only)
-    float* pval;                     // [nnz]
-    int32_t* pstart;                 // [n_group * (npanels + 1)]
-    uint16_t* poff;                  // [npanels * rows] row offset inside its panel block
-    float* ypart;                    // [npanels * rows]
+    // optional column-panel stream of all rows up to ps split length (pstream.hip)
+    int32_t ps_P;                    // 0 = off; else 1, 2, 4 or 8 panels
+    int32_t ps_cb;                   // column bits: panel width 1 << ps_cb
+    int32_t ps_coff[kXcds + 1];      // first chunk of each panel
+    const int4* ps_chunks;           // {q_begin, q_end, row_begin, row_end}
+    uint32_t* ps_pk;                 // (row - row_begin) << cb | column in panel
+    float* ps_pv;
+    float* ps_ypart;                 // [P][ps_ystride] panel row sums
+    int64_t ps_ystride;
+    int32_t ps_n_split_tasks;        // long rows, segments over the CSR
+    const int4* ps_split_tasks;      // {partial index, 0, nz_begin, nz_end}
+    int32_t ps_n_split_rows;
+    const int4* ps_split_rows;       // {row, partial_base, nseg, 0}
+    float* ps_partials;
     // optional SELL-C-sigma copy of the group rows
     int32_t use_sell;
     int32_t sell_slices;
@@ -62,7 +68,11 @@ hipError_t launch_spmm(const DirDevice& d, int32_t N, float alpha, const float* 
                        float beta, float* C, int64_t ldc, hipStream_t s);
 hipError_t launch_sell_fill(const DirDevice& d, int64_t slots, int32_t* sell_col, float* sell_val,
                             hipStream_t s);
-hipError_t launch_panel_build(const DirDevice& d, int32_t* flag, hipStream_t s);
+hipError_t launch_spmv_pstream(const DirDevice& d, float alpha, const float* x, float beta, float* y,
+                               hipStream_t s);
+// Writes the panel stream of d from start[p * rows + r] (position of row r's
+// first panel-p entry), which the caller uploaded to device memory.
+hipError_t launch_pstream_build(const DirDevice& d, const int32_t* start, hipStream_t s);
 
 // Conversions: workspace sizes and the two builders (host driver in convert.hip).
 size_t coo_build_bytes(int64_t m, int64_t n, int64_t nnz);

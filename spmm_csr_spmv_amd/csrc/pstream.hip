@@ -1,0 +1,389 @@
+// Column-panel entry stream for CSR SpMV on matrices whose columns scatter
+// over an x much larger than one XCD's L2.
+//
+// 「通用稀疏矩阵乘法CUDA算子实现」 §2.5 names the random reads of x as the real
+// cost of SpMV once x no longer fits in cache, and §2.4 asks for an entry-
+// balanced split of long rows with a deterministic second stage.  Here the
+// columns are cut into P panels of W = 2^cb columns and panel p is served
+// only by the XCDs whose index is p mod P (workgroup id mod 8 is the XCD),
+// so every gather of x falls in a W-float slice held by that XCD's L2.
+//
+// Layout (built once, at bind, in the plan workspace):
+//   * every row with at most `S` entries contributes its panel-p entries to
+//     the stream of panel p, rows ascending, columns ascending within a row;
+//   * each panel's stream is cut into chunks at row boundaries, a chunk holding
+//     at most kPsEntries entries (its start padded to a multiple of 4) and at
+//     most 2^(32-cb) (and kPsMaxRows) rows; a chunk is {q_begin, q_end,
+//     row_begin, row_end} and covers every row of [row_begin, row_end),
+//     rows without panel-p entries included;
+//   * an entry is one 32-bit word, column within the panel in the low cb bits
+//     and row - row_begin in the high bits, plus its fp32 value;
+//   * rows longer than S are cut out of the stream (they end chunks) and
+//     served from the CSR in segments of split_seg entries over the whole x.
+//
+// spmv_pstream_kernel: one workgroup per chunk (and per split segment).  The
+// chunk's entries are read with coalesced 16-byte loads (lane t of the
+// workgroup holds the four runs of four entries starting at 4t, 1024 + 4t,
+// 2048 + 4t, 3072 + 4t), x is gathered, and the row sums are formed by a
+// segmented reduction over the 1024 runs: a suffix scan over (sum, link)
+// pairs inside each wave, the same scan over the 16 wave blocks, then the run
+// holding the first entry of a row writes the row's sum to LDS.  The sums are
+// added in an order fixed by the layout alone, so results are reproducible
+// bit for bit.  Rows of the chunk then go to ypart[p] (P > 1) or, with one
+// panel, straight to y with the axpby epilogue.
+//
+// spmv_pstream_reduce_kernel: y = alpha * (ypart[0] + ... + ypart[P-1]) +
+// beta * y for the stream rows (panel order fixed), and
+// y = alpha * (sum of segment partials in segment order) + beta * y for the
+// split rows.
+#include <algorithm>
+
+#include "device_common.h"
+
+namespace spx {
+
+namespace {
+
+constexpr int kRuns = kPsEntries / 4;  // 1024 runs of 4 entries per chunk
+
+struct PanelOffsets {
+    int v[kXcds + 1];  // first chunk of each panel, v[P] = number of chunks
+};
+
+struct PsArgs {
+    const int4* chunks;  // all panels, panel-major
+    int coff[kXcds + 1]; // first chunk of each panel
+    int P;               // panels (1, 2, 4 or 8)
+    int G;               // XCDs per panel (8 / P)
+    int cb;              // column bits: W = 1 << cb
+    const uint32_t* pk;  // packed (row offset, column in panel)
+    const float* pv;     // values
+    float* ypart;        // [P][ystride] (P > 1)
+    int64_t ystride;
+    int n_split;         // split segments (first workgroups of the grid)
+    int n_split_pad;     // n_split rounded up to a multiple of 8
+    const int4* split_tasks;  // {partial index, 0, nz_begin, nz_end}
+    const int32_t* idx;  // CSR arrays (split segments)
+    const float* val;
+    float* partials;
+    float* y;            // output when P == 1
+    float alpha, beta;
+};
+
+// Sum of val[q] * x[idx[q]] over [b, e) by the whole workgroup (valid in thread 0).
+__device__ float segment_sum(const int32_t* __restrict__ idx, const float* __restrict__ val,
+                             const float* __restrict__ x, int b, int e, float* red) {
+    const int tid = threadIdx.x;
+    float s = 0.0f;
+    stream_products<4>(idx, val, x, b, e, tid, kBlock, [&](int, float p) { s += p; });
+    s = wave_sum(s);
+    if ((tid & 63) == 0) red[tid >> 6] = s;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// One run of four consecutive stream entries: rows ro[j] are non-decreasing
+// over the valid prefix j < nv.
+struct Run {
+    int fr, lr;     // first and last row offset (-1: no valid entry)
+    float hsum;     // sum of the entries of row fr
+    float tsum;     // sum of the entries of row lr
+};
+
+__device__ __forceinline__ Run make_run(const int (&ro)[4], const float (&pr)[4], int nv) {
+    Run r;
+    r.fr = nv > 0 ? ro[0] : -1;
+    r.lr = nv > 0 ? ro[nv - 1] : -1;
+    float h = 0.0f, t = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j < nv && ro[j] == r.fr) h += pr[j];
+        if (j < nv && ro[j] == r.lr) t += pr[j];
+    }
+    r.hsum = h;
+    r.tsum = t;
+    return r;
+}
+
+// Rows strictly between fr and lr start and end inside the run: write them.
+__device__ __forceinline__ void write_middle(const int (&ro)[4], const float (&pr)[4], int nv, const Run& r,
+                                             float* ysh) {
+    if (nv < 3 || r.fr == r.lr) return;
+    // candidates: entries 1 and 2 (entry 0 has row fr, entry nv-1 row lr)
+    int cur = -1;
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 1; j < 3; ++j) {
+        const bool mid = j < nv - 1 && ro[j] != r.fr && ro[j] != r.lr;
+        if (mid) {
+            if (ro[j] != cur) {
+                if (cur >= 0) ysh[cur] = s;
+                cur = ro[j];
+                s = 0.0f;
+            }
+            s += pr[j];
+        }
+    }
+    if (cur >= 0) ysh[cur] = s;
+}
+
+__global__ __launch_bounds__(kBlock) void spmv_pstream_kernel(const PsArgs a, const float* __restrict__ x) {
+    __shared__ float ysh[kPsMaxRows];
+    __shared__ int16_t frs[kRuns + 1];
+    __shared__ int16_t lrs[kRuns];
+    __shared__ float agg_h[16];
+    __shared__ int agg_m[16];
+    __shared__ float cf[17];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    int b = blockIdx.x;
+    if (b < a.n_split) {
+        const int4 t = a.split_tasks[b];
+        const float s = segment_sum(a.idx, a.val, x, t.z, t.w, agg_h);
+        if (tid == 0) a.partials[t.x] = s;
+        return;
+    }
+    if (b < a.n_split_pad) return;  // idle slots that align the chunks to XCD 0
+    b -= a.n_split_pad;
+    const int xcd = b & (kXcds - 1);
+    const int p = xcd & (a.P - 1);
+    const int i = (b >> 3) * a.G + xcd / a.P;
+    const int c0 = a.coff[p];
+    if (i >= a.coff[p + 1] - c0) return;
+    const int4 c = a.chunks[c0 + i];
+    const int qb = c.x, qe = c.y, R = c.w - c.z;
+    const float* __restrict__ xp = x + ((int64_t)p << a.cb);
+    const uint32_t cmask = (1u << a.cb) - 1u;
+
+    // ---- loads: run u of this thread holds entries [qb + 1024u + 4 tid, +4)
+    uint32_t pk[4][4];
+    float pv[4][4];
+    int nv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int q = qb + 1024 * u + 4 * tid;
+        nv[u] = min(max(qe - q, 0), 4);
+        if (nv[u] > 0) {
+            const v4u32 k4 = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(a.pk + q));
+            const v4f32 v4 = __builtin_nontemporal_load(reinterpret_cast<const v4f32*>(a.pv + q));
+            pk[u][0] = k4.x; pk[u][1] = k4.y; pk[u][2] = k4.z; pk[u][3] = k4.w;
+            pv[u][0] = v4.x; pv[u][1] = v4.y; pv[u][2] = v4.z; pv[u][3] = v4.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pk[u][j] = 0u;
+                pv[u][j] = 0.0f;
+            }
+        }
+    }
+    // rows without entries in this chunk keep the zero written here
+    for (int k = tid; k < R; k += kBlock) ysh[k] = 0.0f;
+    if (tid == 0) frs[kRuns] = -1;
+    __syncthreads();
+    // ---- gathers of x (all issued before any product)
+    float xv[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xv[u][j] = j < nv[u] ? xp[pk[u][j] & cmask] : 0.0f;
+    int ro[4][4];
+    float pr[4][4];
+    Run run[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            ro[u][j] = (int)(pk[u][j] >> a.cb);
+            pr[u][j] = pv[u][j] * xv[u][j];
+        }
+        run[u] = make_run(ro[u], pr[u], nv[u]);
+        write_middle(ro[u], pr[u], nv[u], run[u], ysh);
+        frs[256 * u + tid] = (int16_t)run[u].fr;
+        lrs[256 * u + tid] = (int16_t)run[u].lr;
+    }
+    __syncthreads();  // run rows published
+
+    // ---- segmented suffix scan: C_v = hsum_v + m_v * C_{v+1}, where
+    // m_v = (run v is one row) and (run v+1 starts with that row).
+    float H[4];
+    int M[4];
+    bool link[4], cont[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int v = 256 * u + tid;
+        link[u] = run[u].lr >= 0 && frs[v + 1] == run[u].lr;
+        cont[u] = v > 0 && run[u].fr >= 0 && lrs[v - 1] == run[u].fr;
+        H[u] = run[u].hsum;
+        M[u] = (run[u].fr == run[u].lr && link[u]) ? 1 : 0;
+    }
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float h2 = __shfl_down(H[u], k, 64);
+            const int m2 = __shfl_down(M[u], k, 64);
+            if (lane + k < 64 && M[u]) {
+                H[u] += h2;
+                M[u] = m2;
+            }
+        }
+    }
+    // block B = 4u + w holds runs [64B, 64B + 64); lane 0 has its aggregate
+    if (lane == 0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            agg_h[4 * u + w] = H[u];
+            agg_m[4 * u + w] = M[u];
+        }
+    }
+    __syncthreads();
+    if (w == 0) {
+        // the same suffix scan over the 16 block aggregates, in lanes 0..15
+        float h = lane < 16 ? agg_h[lane] : 0.0f;
+        int m = lane < 16 ? agg_m[lane] : 0;
+#pragma unroll
+        for (int k = 1; k < 16; k <<= 1) {
+            const float h2 = __shfl_down(h, k, 64);
+            const int m2 = __shfl_down(m, k, 64);
+            if (lane + k < 16 && m) {
+                h += h2;
+                m = m2;
+            }
+        }
+        if (lane < 16) cf[lane] = h;
+        if (lane == 16) cf[16] = 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int B = 4 * u + w;
+        const float after = cf[B + 1];
+        const float C = M[u] ? H[u] + after : H[u];  // C_v
+        float Cn = __shfl_down(C, 1, 64);             // C_{v+1}
+        if (lane == 63) Cn = after;
+        const Run& r = run[u];
+        if (r.fr >= 0) {
+            if (!cont[u]) ysh[r.fr] = C;                               // head row starts here
+            if (r.lr != r.fr) ysh[r.lr] = link[u] ? r.tsum + Cn : r.tsum;  // tail row starts here
+        }
+    }
+    __syncthreads();
+    // ---- rows of the chunk: panel partials, or y itself with one panel
+    const int rb = c.z;
+    if (a.P == 1) {
+        for (int k = tid; k < R; k += kBlock) store_axpby(a.y, rb + k, ysh[k], a.alpha, a.beta);
+    } else {
+        float* out = a.ypart + (int64_t)p * a.ystride + rb;
+        for (int k = tid; k < R; k += kBlock) out[k] = ysh[k];
+    }
+}
+
+// Rows of panel 0's chunks (which cover every stream row), then the split
+// rows, one thread each.
+__global__ __launch_bounds__(kBlock) void spmv_pstream_reduce_kernel(
+    const int4* __restrict__ chunks0, int n_chunks0, int P, const float* __restrict__ ypart, int64_t ystride,
+    int n_split_rows, const int4* __restrict__ split_rows, const float* __restrict__ partials, float alpha,
+    float beta, float* __restrict__ y) {
+    const int b = blockIdx.x;
+    if (b < n_chunks0) {
+        const int4 c = chunks0[b];
+        for (int r = c.z + (int)threadIdx.x; r < c.w; r += kBlock) {
+            float s = ypart[r];
+            for (int p = 1; p < P; ++p) s += ypart[(int64_t)p * ystride + r];
+            store_axpby(y, r, s, alpha, beta);
+        }
+        return;
+    }
+    const int j = (b - n_chunks0) * kBlock + (int)threadIdx.x;
+    if (j >= n_split_rows) return;
+    const int4 sr = split_rows[j];  // {row, partial_base, nseg, 0}
+    float s = 0.0f;
+    for (int k = 0; k < sr.z; ++k) s += partials[sr.y + k];
+    store_axpby(y, sr.x, s, alpha, beta);
+}
+
+// Bind time: one workgroup per chunk writes the chunk's entries (row by row,
+// from start[p * rows + r]) and zero padding up to the next multiple of 4.
+__global__ __launch_bounds__(kBlock) void ps_build_kernel(
+    const int4* __restrict__ chunks, int n_chunks, const PanelOffsets coff, int P, int cb,
+    const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx, const float* __restrict__ val,
+    const int32_t* __restrict__ start, int64_t rows, uint32_t* __restrict__ pk, float* __restrict__ pv) {
+    const int ci = blockIdx.x;
+    if (ci >= n_chunks) return;
+    int p = 0;
+    while (p + 1 < P && ci >= coff.v[p + 1]) ++p;
+    const int4 c = chunks[ci];
+    const int rb = c.z;
+    for (int r = rb + (int)threadIdx.x; r < c.w; r += kBlock) {
+        int s = start[(int64_t)p * rows + r];
+        const uint32_t rowbits = (uint32_t)(r - rb) << cb;
+        for (int k = ptr[r]; k < ptr[r + 1]; ++k) {
+            const int col = idx[k];
+            if ((col >> cb) == p) {
+                pk[s] = rowbits | ((uint32_t)col & ((1u << cb) - 1u));
+                pv[s] = val[k];
+                ++s;
+            }
+        }
+    }
+    const int pad_end = (c.y + 3) & ~3;
+    if ((int)threadIdx.x < pad_end - c.y) {
+        pk[c.y + threadIdx.x] = 0u;
+        pv[c.y + threadIdx.x] = 0.0f;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_pstream_build(const DirDevice& d, const int32_t* start, hipStream_t s) {
+    const int n = d.ps_coff[d.ps_P];
+    if (n == 0) return hipSuccess;
+    PanelOffsets coff{};
+    for (int k = 0; k <= kXcds; ++k) coff.v[k] = d.ps_coff[std::min(k, (int)d.ps_P)];
+    hipLaunchKernelGGL(ps_build_kernel, dim3((unsigned)n), dim3(kBlock), 0, s, d.ps_chunks, n, coff, d.ps_P,
+                       d.ps_cb, d.ptr, d.idx, d.val, start, (int64_t)d.rows, d.ps_pk, d.ps_pv);
+    return hipGetLastError();
+}
+
+hipError_t launch_spmv_pstream(const DirDevice& d, float alpha, const float* x, float beta, float* y,
+                               hipStream_t s) {
+    PsArgs a{};
+    a.chunks = d.ps_chunks;
+    for (int k = 0; k <= kXcds; ++k) a.coff[k] = k <= d.ps_P ? d.ps_coff[k] : d.ps_coff[d.ps_P];
+    a.P = d.ps_P;
+    a.G = kXcds / d.ps_P;
+    a.cb = d.ps_cb;
+    a.pk = d.ps_pk;
+    a.pv = d.ps_pv;
+    a.ypart = d.ps_ypart;
+    a.ystride = d.ps_ystride;
+    a.n_split = d.ps_n_split_tasks;
+    a.n_split_pad = (d.ps_n_split_tasks + kXcds - 1) / kXcds * kXcds;
+    a.split_tasks = d.ps_split_tasks;
+    a.idx = d.idx;
+    a.val = d.val;
+    a.partials = d.ps_partials;
+    a.y = y;
+    a.alpha = alpha;
+    a.beta = beta;
+    int max_chunks = 0;
+    for (int p = 0; p < d.ps_P; ++p) max_chunks = std::max(max_chunks, d.ps_coff[p + 1] - d.ps_coff[p]);
+    const int64_t slots = (int64_t)kXcds * ((max_chunks + a.G - 1) / a.G);
+    const int64_t grid = a.n_split_pad + slots;
+    if (grid > 0) {
+        hipLaunchKernelGGL(spmv_pstream_kernel, dim3((unsigned)grid), dim3(kBlock), 0, s, a, x);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    const int n_chunks0 = d.ps_P > 1 ? d.ps_coff[1] : 0;
+    const int64_t rgrid = n_chunks0 + (d.ps_n_split_rows + kBlock - 1) / kBlock;
+    if (rgrid > 0) {
+        hipLaunchKernelGGL(spmv_pstream_reduce_kernel, dim3((unsigned)rgrid), dim3(kBlock), 0, s, d.ps_chunks,
+                           n_chunks0, d.ps_P, d.ps_ypart, d.ps_ystride, d.ps_n_split_rows, d.ps_split_rows,
+                           d.ps_partials, alpha, beta, y);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+}  // namespace spx

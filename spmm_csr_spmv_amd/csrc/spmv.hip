@@ -17,63 +17,6 @@ namespace spx {
 
 namespace {
 
-// Products val[q] * x[idx[q]] for q in [b, e).  Lane `lane` of `stride`
-// lanes owns the 4-entry chunks starting at (b & ~3) + 4*lane + 4*stride*k.
-// Chunks are taken U at a time: the U column/value loads (16-byte loads for
-// full chunks, guarded scalar loads at the ragged ends) are all issued before
-// the gathers of x, and all gathers before any product, so every lane keeps
-// up to 8U independent memory requests in flight.  `emit(q, prod)` receives
-// each valid product; slots outside [b, e) are never read nor multiplied.
-template <int U, class Emit>
-__device__ __forceinline__ void stream_products(const int32_t* __restrict__ idx, const float* __restrict__ val,
-                                                const float* __restrict__ x, int b, int e, int lane, int stride,
-                                                Emit emit) {
-    const int base = b & ~3;
-    for (int v0 = base + 4 * lane; v0 < e; v0 += 4 * stride * U) {
-        int c[U][4];
-        float a[U][4];
-        bool ok[U][4];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int v = v0 + 4 * stride * u;
-            if (v >= b && v + 4 <= e) {
-                const int4 ci = ldg4_nt(idx + v);
-                const float4 ai = ldg4_nt(val + v);
-                c[u][0] = ci.x; c[u][1] = ci.y; c[u][2] = ci.z; c[u][3] = ci.w;
-                a[u][0] = ai.x; a[u][1] = ai.y; a[u][2] = ai.z; a[u][3] = ai.w;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) ok[u][j] = true;
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int q = v + j;
-                    ok[u][j] = q >= b && q < e;
-                    c[u][j] = ok[u][j] ? idx[q] : 0;
-                    a[u][j] = ok[u][j] ? val[q] : 0.0f;
-                }
-            }
-        }
-        float xv[U][4];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) xv[u][j] = ok[u][j] ? x[c[u][j]] : 0.0f;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int v = v0 + 4 * stride * u;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (ok[u][j]) emit(v + j, a[u][j] * xv[u][j]);
-        }
-    }
-}
-
-__device__ __forceinline__ void store_axpby(float* __restrict__ y, int row, float acc, float alpha, float beta) {
-    float o = alpha * acc;
-    if (beta != 0.0f) o = fmaf(beta, y[row], o);
-    y[row] = o;
-}
-
 // Row sums of R consecutive rows whose E products sit in LDS (prod[0..E)),
 // with row i covering prod[rs[i] .. rs[i+1]) (rs in LDS, rs[R] = E).
 // The products are split evenly: thread t reads chunk [tC, tC + C) with
@@ -130,160 +73,6 @@ __device__ void group_task(const int4 t, const int32_t* __restrict__ ptr, const 
                                                   [&](int q, float p) { lds[q - b] = p; });
     __syncthreads();
     balanced_row_sums(lds, e - b, rs, R, head, [&](int i, float s) { store_axpby(y, r0 + i, s, alpha, beta); });
-}
-
-// Exclusive prefix sum of one int per thread over the 256-thread workgroup
-// (Hillis-Steele in LDS, sh: 256 ints); *total receives the sum.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) {
-    const int tid = threadIdx.x;
-    sh[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kBlock; off <<= 1) {
-        const int add = tid >= off ? sh[tid - off] : 0;
-        __syncthreads();
-        sh[tid] += add;
-        __syncthreads();
-    }
-    const int incl = sh[tid];
-    *total = sh[kBlock - 1];
-    __syncthreads();
-    return incl - v;
-}
-
-// ---- column panels -----------------------------------------------------------
-// For matrices whose columns scatter over an x much larger than one XCD's L2,
-// the columns are cut into P panels of width W and panel p is served only by
-// XCD p (workgroup id mod 8 = XCD): every gather of x then falls in a W-float
-// slice that stays in that XCD's L2.  Each group's entries are copied once, at
-// bind time, in (panel, row, column) order inside the group's own range
-// [nz_begin, nz_end) of the copy; poff[p * rows + r] is the offset of row r's
-// first entry inside the block of panel p of its group (16 bits: a panel group
-// holds at most 1024 rows and P * 2048 entries, well below 65536) and
-// pstart[g * (P + 1) + p] the offset of panel p inside group g, so a
-// row's panel entries need no search.  Panel groups are their own grouping
-// (larger than the LDS-staged groups: each (group, panel) block is sized to
-// fill the LDS of one workgroup about half way).  The panel
-// kernel writes ypart[p * rows + r] = sum of row r over panel p; the bins
-// kernel then forms y = alpha * (ypart[0] + ... + ypart[P-1]) + beta * y in
-// that fixed order.
-
-// One workgroup per panel group: builds the panel-major copy, the row offsets
-// and the block starts.  Runs once per bind; reads the columns from global
-// memory.  flag[0] is raised when a panel block exceeds `cap` entries (the
-// LDS capacity of the panel kernel); the plan then does not use panels.
-__global__ __launch_bounds__(kBlock) void panel_build_kernel(
-    const int4* __restrict__ gtasks, int rows, const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
-    const float* __restrict__ val, int P, int W, int cap, int32_t* __restrict__ pcol, float* __restrict__ pval,
-    int32_t* __restrict__ pstart, uint16_t* __restrict__ poff, int32_t* __restrict__ flag) {
-    __shared__ int rowoff[8][kBlock];
-    __shared__ int scan[kBlock];
-    __shared__ int pst[9];
-    __shared__ int carry[8];
-    const int4 t = gtasks[blockIdx.x];
-    const int r0 = t.x, R = t.y - t.x, b = t.z, E = t.w - t.z;
-    const int tid = threadIdx.x;
-    if (tid < 8) carry[tid] = 0;
-    // pass 1: entries per panel -> block starts (exclusive over panels)
-    int tot[8];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) tot[p] = 0;
-    for (int q = tid; q < E; q += kBlock) {
-        const int p = idx[b + q] / W;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) tot[k] += (k == p);
-    }
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        if (p < P) {  // P is uniform: every thread takes the same branches
-            int total;
-            block_exclusive_scan(tot[p], scan, &total);
-            if (tid == 0) pst[p] = total;
-            __syncthreads();
-        }
-    }
-    if (tid == 0) {
-        int s = 0;
-        for (int p = 0; p < P; ++p) {
-            const int n = pst[p];
-            if (n > cap) atomicOr(flag, 1);
-            pst[p] = s;
-            pstart[(int64_t)blockIdx.x * (P + 1) + p] = s;
-            s += n;
-        }
-        pst[P] = s;
-        pstart[(int64_t)blockIdx.x * (P + 1) + P] = s;
-    }
-    __syncthreads();
-    // pass 2, per chunk of 256 rows: offsets of each row inside each panel
-    // block (running offsets carried across chunks), then the copy
-    for (int c0 = 0; c0 < R; c0 += kBlock) {
-        const int row = c0 + tid;
-        const bool in = row < R;
-        const int rb = in ? ptr[r0 + row] : 0, re = in ? ptr[r0 + row + 1] : 0;
-        int c[8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) c[p] = 0;
-        for (int k = rb; k < re; ++k) {
-            const int p = idx[k] / W;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) c[q] += (q == p);
-        }
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            if (p < P) {
-                int total;
-                const int ex = block_exclusive_scan(c[p], scan, &total);
-                rowoff[p][tid] = carry[p] + ex;
-                __syncthreads();
-                if (tid == 0) carry[p] += total;
-            }
-        }
-        if (in) {
-            int pos[8];
-#pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                pos[p] = p < P ? rowoff[p][tid] : 0;
-                if (p < P) poff[(int64_t)p * rows + r0 + row] = (uint16_t)min(pos[p], 65535);
-                pos[p] += p < P ? b + pst[p] : 0;
-            }
-            for (int k = rb; k < re; ++k) {
-                const int col = idx[k];
-                const int p = col / W;
-                int d = 0;
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    if (q == p) d = pos[q]++;
-                pcol[d] = col;
-                pval[d] = val[k];
-            }
-        }
-        __syncthreads();
-    }
-}
-
-// One workgroup per (group, panel); panel = workgroup id mod P, so with P = 8
-// panel p runs on XCD p.  LDS: products [group_cap] | row starts [257] |
-// heads [256].
-__global__ __launch_bounds__(kBlock) void spmv_panel_kernel(
-    const int4* __restrict__ gtasks, int rows, int P, const int32_t* __restrict__ pcol,
-    const float* __restrict__ pval, const int32_t* __restrict__ pstart, const uint16_t* __restrict__ poff,
-    const float* __restrict__ x, float* __restrict__ ypart, int group_cap) {
-    extern __shared__ float lds[];
-    int* rs = reinterpret_cast<int*>(lds + group_cap);
-    float* head = lds + group_cap + (kGroupMaxRows + 1);
-    const int p = blockIdx.x % P, g = blockIdx.x / P;
-    const int4 t = gtasks[g];
-    const int r0 = t.x, R = t.y - t.x;
-    const int tid = threadIdx.x;
-    const int qb = t.z + pstart[(int64_t)g * (P + 1) + p];
-    const int qe = t.z + pstart[(int64_t)g * (P + 1) + p + 1];
-    for (int i = tid; i < R; i += kBlock) rs[i] = poff[(int64_t)p * rows + r0 + i];
-    if (tid == 0) rs[R] = qe - qb;
-    stream_products<kGroupMaxNnz / (4 * kBlock)>(pcol, pval, x, qb, qe, tid, kBlock,
-                                                  [&](int q, float v) { lds[q - qb] = v; });
-    __syncthreads();
-    float* out = ypart + (int64_t)p * rows + r0;
-    balanced_row_sums(lds, qe - qb, rs, R, head, [&](int i, float s) { out[i] = s; });
 }
 
 // ---- wave: one row per wave64 ----------------------------------------------
@@ -343,7 +132,7 @@ __global__ __launch_bounds__(kBlock) void spmv_bins_kernel(
     const int4* __restrict__ tasks, int n_split, int n_block, int n_wave, int n_group, int xcd_remap,
     const int4* __restrict__ split_rows, const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
     const float* __restrict__ val, const float* __restrict__ x, float alpha, float beta, float* __restrict__ y,
-    float* partials, int32_t* counters, int group_cap, const float* __restrict__ ypart, int npanels, int rows) {
+    float* partials, int32_t* counters, int group_cap) {
     extern __shared__ float lds[];
     int b = blockIdx.x;
     if (b < n_split) {
@@ -368,15 +157,6 @@ __global__ __launch_bounds__(kBlock) void spmv_bins_kernel(
     const int first = n_split + n_block + n_wave_wg;
     const int g = xcd_remap ? xcd_contiguous(blockIdx.x, first, n_group) : b;
     const int4 t = tasks[n_split + n_block + n_wave + g];
-    if (npanels > 0) {
-        // the group's rows were summed per column panel: add the panels in order
-        for (int r = t.x + (int)threadIdx.x; r < t.y; r += kBlock) {
-            float s = 0.0f;
-            for (int p = 0; p < npanels; ++p) s += ypart[(int64_t)p * rows + r];
-            store_axpby(y, r, s, alpha, beta);
-        }
-        return;
-    }
     group_task(t, ptr, idx, val, x, alpha, beta, y, lds, group_cap);
 }
 
@@ -446,27 +226,16 @@ __global__ __launch_bounds__(kBlock) void sell_fill_kernel(
 }  // namespace
 
 hipError_t launch_spmv(const DirDevice& d, float alpha, const float* x, float beta, float* y, hipStream_t s) {
+    if (d.ps_P > 0) return launch_spmv_pstream(d, alpha, x, beta, y, s);
     const int n_wave_wg = (d.n_wave + 3) / 4;
-    const bool panels = d.npanels > 0;
-    // with panels the group part of the bins launch runs over the panel groups
-    const int4* tasks = panels ? d.ptasks : d.tasks;
-    const int n_group = d.use_sell ? 0 : (panels ? d.n_pgroup : d.n_group);
+    const int n_group = d.use_sell ? 0 : d.n_group;
     const int64_t grid = (int64_t)d.n_split + d.n_block + n_wave_wg + n_group;
-    // products | row starts | heads (group and panel tasks)
-    const size_t lds = (size_t)(kGroupMaxNnz + (kGroupMaxRows + 1) + kBlock) * sizeof(float);
-    if (panels && d.n_pgroup > 0) {
-        const int4* gtasks = d.ptasks + d.n_split + d.n_block + d.n_wave;
-        hipLaunchKernelGGL(spmv_panel_kernel, dim3((unsigned)((int64_t)d.n_pgroup * d.npanels)), dim3(kBlock), lds,
-                           s, gtasks, d.rows, d.npanels, d.pcol, d.pval, d.pstart, d.poff, x, d.ypart,
-                           kGroupMaxNnz);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
-    }
     if (grid > 0) {
+        // products | row starts | heads (group tasks)
         const size_t lds_bins = (size_t)(d.group_cap + (kGroupMaxRows + 1) + kBlock) * sizeof(float);
-        hipLaunchKernelGGL(spmv_bins_kernel, dim3((unsigned)grid), dim3(kBlock), lds_bins, s, tasks, d.n_split,
+        hipLaunchKernelGGL(spmv_bins_kernel, dim3((unsigned)grid), dim3(kBlock), lds_bins, s, d.tasks, d.n_split,
                            d.n_block, d.n_wave, n_group, d.xcd_remap, d.split_rows, d.ptr, d.idx, d.val, x, alpha,
-                           beta, y, d.partials, d.counters, d.group_cap, d.ypart, d.npanels, d.rows);
+                           beta, y, d.partials, d.counters, d.group_cap);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -477,14 +246,6 @@ hipError_t launch_spmv(const DirDevice& d, float alpha, const float* x, float be
         return hipGetLastError();
     }
     return hipSuccess;
-}
-
-hipError_t launch_panel_build(const DirDevice& d, int32_t* flag, hipStream_t s) {
-    if (d.npanels <= 0 || d.n_pgroup <= 0) return hipSuccess;
-    const int4* gtasks = d.ptasks + d.n_split + d.n_block + d.n_wave;
-    hipLaunchKernelGGL(panel_build_kernel, dim3((unsigned)d.n_pgroup), dim3(kBlock), 0, s, gtasks, d.rows, d.ptr,
-                       d.idx, d.val, d.npanels, d.panel_width, kGroupMaxNnz, d.pcol, d.pval, d.pstart, d.poff, flag);
-    return hipGetLastError();
 }
 
 hipError_t launch_sell_fill(const DirDevice& d, int64_t slots, int32_t* sell_col, float* sell_val, hipStream_t s) {

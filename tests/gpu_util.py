@@ -23,9 +23,11 @@ BINS = {
     "mixed_small": dict(group_nnz=64, wave_min=8, block_min=40, split_min=100, split_seg=32),
     "sell": dict(use_sell=1, sell_sigma=128),
     "no_xcd": dict(xcd_remap=0),
-    "panels8": dict(use_sell=0, col_panels=8),
-    "panels2_small": dict(use_sell=0, col_panels=2, group_nnz=64, wave_min=8, block_min=40, split_min=100,
-                          split_seg=32),
+    # column-panel stream (every row up to the split length in one balanced stream)
+    "ps1": dict(use_sell=0, col_panels=1),
+    "ps2_split": dict(use_sell=0, col_panels=2, wave_min=8, block_min=40, split_min=100, split_seg=32),
+    "ps4": dict(use_sell=0, col_panels=4),
+    "ps8_split": dict(use_sell=0, col_panels=8, wave_min=8, block_min=20, split_min=40, split_seg=16),
 }
 
 

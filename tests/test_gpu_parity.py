@@ -140,7 +140,7 @@ def test_spmv_and_transpose(name, bins):
         assert_close(host(z), ref_t, scale_t, what="spmv_t %s %s a=%g b=%g" % (name, bins, alpha, beta))
 
 
-@pytest.mark.parametrize("bins", ["default", "all_split", "mixed_small", "sell"])
+@pytest.mark.parametrize("bins", ["default", "all_split", "mixed_small", "sell", "ps4", "ps8_split"])
 def test_spmv_bitwise_deterministic(bins):
     say("determinism", bins)
     coo, _, _ = case("ragged_long")
@@ -171,32 +171,25 @@ def test_profile_matches_oracle(name):
         assert got["group_nnz"] + got["wave_nnz"] + got["block_nnz"] + got["split_nnz"] == ptr[-1]
 
 
-def test_panels_fall_back_when_columns_concentrate():
-    """Forced panels on a matrix whose columns all sit in the first panel: the
-    panel blocks overflow the LDS capacity, so bind drops panels; results stay
-    exact."""
-    say("panel overflow fallback")
+def test_panels_with_concentrated_columns():
+    """Forced panels on a matrix whose columns all sit in the first panel (the
+    other panels hold no entries, only zero row sums), then on spread columns:
+    both stay exact."""
+    say("panels, concentrated and spread columns")
     rng = np.random.default_rng(3)
     m, n = 20000, 100000
     row = np.repeat(np.arange(m, dtype=np.int32), 20)
-    col = rng.integers(0, 1000, size=row.size).astype(np.int32)
     val = rng.uniform(-1, 1, size=row.size).astype(np.float32)
-    rp, c, v = oracle.coo_to_csr(m, n, row, col, val)
-    plan = sp.Plan(m, n, dev(rp), dev(c), dev(v), use_sell=0, col_panels=4)
-    assert plan.profile()["col_panels"] == 0
     x = gen.dense_vector(n, 5)
-    y = torch.zeros(m, device="cuda")
-    sp.spmv(plan, 1.0, dev(x), 0.0, y)
-    ref, scale = oracle.spmv(rp, c, v, x)
-    assert_close(host(y), ref, scale, what="fallback")
-    # spread columns: panels stay on
-    col2 = rng.integers(0, n, size=row.size).astype(np.int32)
-    rp2, c2, v2 = oracle.coo_to_csr(m, n, row, col2, val)
-    plan2 = sp.Plan(m, n, dev(rp2), dev(c2), dev(v2), use_sell=0, col_panels=4)
-    assert plan2.profile()["col_panels"] == 4
-    sp.spmv(plan2, 1.0, dev(x), 0.0, y)
-    ref, scale = oracle.spmv(rp2, c2, v2, x)
-    assert_close(host(y), ref, scale, what="panels")
+    for hi in (1000, n):
+        col = rng.integers(0, hi, size=row.size).astype(np.int32)
+        rp, c, v = oracle.coo_to_csr(m, n, row, col, val)
+        plan = sp.Plan(m, n, dev(rp), dev(c), dev(v), use_sell=0, col_panels=4)
+        assert plan.profile()["col_panels"] == 4
+        y = torch.zeros(m, device="cuda")
+        sp.spmv(plan, 1.0, dev(x), 0.0, y)
+        ref, scale = oracle.spmv(rp, c, v, x)
+        assert_close(host(y), ref, scale, what="panels, columns below %d" % hi)
 
 
 # ------------------------------------------------------------------ SpMM
