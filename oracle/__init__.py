@@ -19,6 +19,9 @@ from .oracle import (  # noqa: F401
     bsr_to_csr,
     spmm_bf16,
     bsr_spmm_direct,
+    csr_to_bsr,
+    f32_to_bf16,
+    bsr_spmv,
     row_profile,
     sell_build,
     sell_spmv,

@@ -12,6 +12,7 @@
  *   [LSMR] 「CUDA LSMR 专栏（二）：用 CSR/CSC 双存储压榨双向 SpMV」
  *   [GEN]  「通用稀疏矩阵乘法CUDA算子实现」
  *   [BCSR] 「GPU加速实战用BCSR格式优化稀疏矩阵乘法附CUDA代码」
+ *   [ASYNC] the AsyncSparse summary page (capital-peak.com, news 566)
  *
  * Readings taken where the pages are silent (each is listed in the design
  * notes of the repository as well):
@@ -22,6 +23,8 @@
  *     CSR order.
  *   - y = alpha*A*x + beta*y; when beta == 0 the old y is not read.
  *   - BSR blocks are stored row-major inside each block.
+ *   - CSR -> BSR: entries that share an element position are summed in CSR
+ *     order in fp32; bf16 blocks are that sum rounded once to nearest-even.
  *   - SELL-C-sigma: windows of sigma rows sorted by decreasing length (ties by
  *     row index), slices of C rows padded to the slice's longest row, slot k of
  *     lane j stored at slice_ptr[s] + k*C + j; padded slots hold column -1.
@@ -314,6 +317,134 @@ void oracle_bsr_spmm_direct(int64_t mb, int64_t bs, const int32_t* brow_ptr, con
             if (beta != 0.0) y += beta * (double)C_in[i * ldc + c];
             C_out[k * N + c] = y;
         }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* CSR -> BSR with square bs x bs blocks ([BCSR] §1: only blocks holding at   */
+/* least one entry are stored; block row pointer, block column index and the */
+/* dense blocks one after another, each row-major).  mb = ceil(m / bs) block  */
+/* rows, kb = ceil(n / bs) block columns; the last block row / column is     */
+/* padded.  Blocks of a block row are ordered by block column.  The value at */
+/* in-block position (r, c) of block (I, J) is the sum of the CSR entries at */
+/* element (I*bs + r, J*bs + c) taken in CSR order and added left to right in */
+/* fp32, starting from the first of them; positions without entries hold +0. */
+/* ------------------------------------------------------------------------ */
+
+/* Number of stored blocks per block row, as a row pointer brow_ptr[mb + 1];
+ * returns nnzb. */
+int64_t oracle_csr_to_bsr_count(int64_t m, int64_t n, const int32_t* row_ptr, const int32_t* col, int64_t bs,
+                                int32_t* brow_ptr)
+{
+    int64_t mb = (m + bs - 1) / bs, kb = (n + bs - 1) / bs;
+    char* seen = (char*)calloc((size_t)(kb > 0 ? kb : 1), 1);
+    int64_t total = 0;
+    brow_ptr[0] = 0;
+    for (int64_t I = 0; I < mb; ++I) {
+        int64_t i_end = (I + 1) * bs < m ? (I + 1) * bs : m;
+        int64_t count = 0;
+        for (int64_t i = I * bs; i < i_end; ++i)
+            for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p)
+                if (!seen[col[p] / bs]) {
+                    seen[col[p] / bs] = 1;
+                    ++count;
+                }
+        for (int64_t i = I * bs; i < i_end; ++i)
+            for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p) seen[col[p] / bs] = 0;
+        total += count;
+        brow_ptr[I + 1] = (int32_t)total;
+    }
+    free(seen);
+    return total;
+}
+
+static int cmp_i32(const void* a, const void* b)
+{
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return (x > y) - (x < y);
+}
+
+/* Block columns and fp32 block values for the row pointer from
+ * oracle_csr_to_bsr_count. */
+void oracle_csr_to_bsr_fill(int64_t m, const int32_t* row_ptr, const int32_t* col, const float* val, int64_t bs,
+                            const int32_t* brow_ptr, int32_t* bcol, float* bval)
+{
+    int64_t mb = (m + bs - 1) / bs;
+    int64_t nnzb = brow_ptr[mb];
+    char* filled = (char*)calloc((size_t)(nnzb * bs * bs > 0 ? nnzb * bs * bs : 1), 1);
+    for (int64_t q = 0; q < nnzb * bs * bs; ++q) bval[q] = 0.0f;
+    for (int64_t I = 0; I < mb; ++I) {
+        int64_t i_end = (I + 1) * bs < m ? (I + 1) * bs : m;
+        /* the distinct block columns of the block row, ascending */
+        int64_t ne = row_ptr[i_end] - row_ptr[I * bs];
+        int32_t* js = (int32_t*)malloc((size_t)(ne > 0 ? ne : 1) * sizeof(int32_t));
+        for (int64_t p = row_ptr[I * bs]; p < row_ptr[i_end]; ++p) js[p - row_ptr[I * bs]] = col[p] / (int32_t)bs;
+        qsort(js, (size_t)ne, sizeof(int32_t), cmp_i32);
+        int64_t k = brow_ptr[I];
+        for (int64_t e = 0; e < ne; ++e)
+            if (e == 0 || js[e] != js[e - 1]) bcol[k++] = js[e];
+        free(js);
+        /* values, entry by entry in CSR order */
+        for (int64_t i = I * bs; i < i_end; ++i) {
+            for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p) {
+                int32_t J = col[p] / (int32_t)bs;
+                int64_t lo = brow_ptr[I], hi = brow_ptr[I + 1] - 1;
+                while (lo < hi) {
+                    int64_t mid = (lo + hi) / 2;
+                    if (bcol[mid] < J) lo = mid + 1; else hi = mid;
+                }
+                int64_t slot = (lo * bs + (i - I * bs)) * bs + col[p] % bs;
+                if (!filled[slot]) {
+                    bval[slot] = val[p];
+                    filled[slot] = 1;
+                } else {
+                    bval[slot] = bval[slot] + val[p];
+                }
+            }
+        }
+    }
+    free(filled);
+}
+
+/* fp32 -> bf16 bit pattern, round to nearest, ties to even: add 0x7fff plus
+ * the lowest kept bit to the 32-bit pattern and keep the upper half (a
+ * carry into the exponent is the correct rounding, up to infinity).  NaN
+ * keeps its sign and upper payload and is made quiet. */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+/* BSR SpMV with fp32 blocks: y_i = alpha * sum over the blocks b of block
+ * row i / bs and in-block columns c of A_b[i % bs][c] * x[bcol_b * bs + c]
+ * + beta * y_i, for element rows i < m; columns >= n (padding) are skipped.
+ * Sums in fp64; scale_i = |alpha| sum |A x| + |beta| |y_i| as in oracle_spmv. */
+void oracle_bsr_spmv(int64_t m, int64_t n, int64_t bs, const int32_t* brow_ptr, const int32_t* bcol,
+                     const float* bval, const float* x, double alpha, double beta, const float* y_in,
+                     double* y_out, double* scale_out)
+{
+    for (int64_t i = 0; i < m; ++i) {
+        int64_t I = i / bs, r = i % bs;
+        double s = 0.0, a = 0.0;
+        for (int64_t b = brow_ptr[I]; b < brow_ptr[I + 1]; ++b) {
+            for (int64_t c = 0; c < bs; ++c) {
+                int64_t j = (int64_t)bcol[b] * bs + c;
+                if (j >= n) continue;
+                double t = (double)bval[(b * bs + r) * bs + c] * (double)x[j];
+                s += t;
+                a += fabs(t);
+            }
+        }
+        double y = alpha * s, sc = fabs(alpha) * a;
+        if (beta != 0.0) {
+            y += beta * (double)y_in[i];
+            sc += fabs(beta) * fabs((double)y_in[i]);
+        }
+        y_out[i] = y;
+        if (scale_out) scale_out[i] = sc;
     }
 }
 

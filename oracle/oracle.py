@@ -70,6 +70,14 @@ def _declare(lib):
     lib.oracle_bsr_spmm_direct.argtypes = [_i64, _i64, _p, _p, _p, _i64, _p, _i64, _d, _d, _p, _i64, _p,
                                            _i64, _p]
     lib.oracle_bsr_spmm_direct.restype = None
+    lib.oracle_csr_to_bsr_count.argtypes = [_i64, _i64, _p, _p, _i64, _p]
+    lib.oracle_csr_to_bsr_count.restype = _i64
+    lib.oracle_csr_to_bsr_fill.argtypes = [_i64, _p, _p, _p, _i64, _p, _p, _p]
+    lib.oracle_csr_to_bsr_fill.restype = None
+    lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_bsr_spmv.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _d, _d, _p, _p, _p]
+    lib.oracle_bsr_spmv.restype = None
     lib.oracle_row_profile.argtypes = [_i64, _p, _p]
     lib.oracle_row_profile.restype = None
     lib.oracle_sell_build.argtypes = [_i64, _p, _p, _p, _i64, _i64, _p, _p, _p, _p, _p]
@@ -223,6 +231,45 @@ def bsr_spmm_direct(mb, bs, brow_ptr, bcol, bval, B, alpha=1.0, beta=0.0, C=None
     lib.oracle_bsr_spmm_direct(mb, bs, _ptr(brow_ptr), _ptr(bcol), _ptr(bval), N, _ptr(B), N, float(alpha),
                                float(beta), _ptr(C_in), N, _ptr(r), nr, _ptr(out))
     return out
+
+
+def csr_to_bsr(m, n, row_ptr, col, val, bs, out="f32"):
+    """CSR -> BSR with bs x bs blocks: (brow_ptr int32[mb+1], bcol int32[nnzb],
+    blocks float32[nnzb, bs, bs] (out="f32") or their bf16 bit patterns
+    uint16[nnzb, bs, bs] (out="bf16"))."""
+    lib = _load()
+    row_ptr, col, val = _c(row_ptr, np.int32), _c(col, np.int32), _c(val, np.float32)
+    mb = (m + bs - 1) // bs
+    brow_ptr = np.empty(mb + 1, np.int32)
+    nnzb = lib.oracle_csr_to_bsr_count(m, n, _ptr(row_ptr), _ptr(col), bs, _ptr(brow_ptr))
+    bcol = np.empty(nnzb, np.int32)
+    bval = np.empty((nnzb, bs, bs), np.float32)
+    lib.oracle_csr_to_bsr_fill(m, _ptr(row_ptr), _ptr(col), _ptr(val), bs, _ptr(brow_ptr), _ptr(bcol), _ptr(bval))
+    if out == "bf16":
+        bval = f32_to_bf16(bval)
+    return brow_ptr, bcol, bval
+
+
+def f32_to_bf16(a):
+    """float32 -> bf16 bit patterns (uint16), element by element through the C oracle."""
+    lib = _load()
+    a = np.asarray(a, dtype=np.float32)
+    flat = a.ravel()
+    out = np.fromiter((lib.oracle_f32_to_bf16(float(v)) for v in flat), dtype=np.uint16, count=flat.size)
+    return out.reshape(a.shape)
+
+
+def bsr_spmv(m, n, bs, brow_ptr, bcol, bval, x, alpha=1.0, beta=0.0, y=None):
+    """fp64 BSR SpMV with fp32 blocks over element rows < m and columns < n: (y, scale)."""
+    lib = _load()
+    brow_ptr, bcol, bval = _c(brow_ptr, np.int32), _c(bcol, np.int32), _c(bval, np.float32)
+    x = _c(x, np.float32)
+    y_in = _c(y, np.float32) if beta != 0.0 else None
+    out = np.empty(m, np.float64)
+    scale = np.empty(m, np.float64)
+    lib.oracle_bsr_spmv(m, n, bs, _ptr(brow_ptr), _ptr(bcol), _ptr(bval), _ptr(x), float(alpha), float(beta),
+                        _ptr(y_in), _ptr(out), _ptr(scale))
+    return out, scale
 
 
 def row_profile(row_ptr):

@@ -384,3 +384,101 @@ def test_sell_layout_and_product(C, sigma):
     y = oracle.sell_spmv(s, C, x)
     np.testing.assert_allclose(y, dense_from_csr(coo.m, coo.n, rp, c, v) @ x.astype(np.float64), rtol=1e-12,
                                atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# CSR -> BSR and BSR SpMV with fp32 blocks
+# --------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def five_bsr2(golden_dir):
+    with open(os.path.join(golden_dir, "five_by_five_bsr2.json")) as f:
+        return json.load(f)
+
+
+def test_five_csr_to_bsr2_matches_hand_derivation(five, five_bsr2):
+    g = five_bsr2
+    v = five["value_of"]
+    brp, bcol, bval = oracle.csr_to_bsr(5, 5, five["csr_row_ptr"], five["csr_col"], five["csr_valf"], 2)
+    assert brp.tolist() == g["brow_ptr"]
+    assert bcol.tolist() == g["bcol"]
+    blocks = np.array([[[v[e] if isinstance(e, str) else e for e in row] for row in blk] for blk in g["blocks"]],
+                      np.float32)
+    np.testing.assert_array_equal(bval, blocks)
+    assert g["nnz"] / (bcol.size * 2 * 2) == pytest.approx(1.0 / 3.0)
+    # the page's product, exact in fp32 and fp64
+    y, _ = oracle.bsr_spmv(5, 5, 2, brp, bcol, bval, np.arange(1, 6, dtype=np.float32))
+    assert y.tolist() == [7, 6, 54, 21, 40]
+    y, _ = oracle.bsr_spmv(5, 5, 2, brp, bcol, bval, np.arange(1, 6, dtype=np.float32), 2.0, -1.0,
+                           np.ones(5, np.float32))
+    assert y.tolist() == [13, 11, 107, 41, 79]
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(small_coo(), st.sampled_from([1, 2, 3, 4, 5, 8]), st.integers(0, 2 ** 31 - 1))
+def test_csr_to_bsr_brute_force(case, bs, seed):
+    m, n, row, col, val = case
+    rp, c, v = oracle.coo_to_csr(m, n, row, col, val)
+    brp, bcol, bval = oracle.csr_to_bsr(m, n, rp, c, v, bs)
+    mb, kb = (m + bs - 1) // bs, (n + bs - 1) // bs
+    # the stored blocks are exactly the distinct (row // bs, col // bs) pairs, block columns ascending
+    pairs = sorted(set(zip((row // bs).tolist(), (col // bs).tolist())))
+    assert brp.tolist() == [sum(1 for I, _ in pairs if I < k) for k in range(mb + 1)]
+    assert bcol.tolist() == [J for _, J in pairs]
+    # expanding the blocks (cropped to m x n) gives the dense matrix, duplicates summed in fp32
+    d32 = np.zeros((m, n), np.float32)
+    for i in range(m):
+        for p in range(rp[i], rp[i + 1]):
+            d32[i, c[p]] = d32[i, c[p]] + v[p]
+    e = np.zeros((mb * bs, kb * bs), np.float32)
+    for I in range(mb):
+        for k in range(brp[I], brp[I + 1]):
+            e[I * bs:(I + 1) * bs, bcol[k] * bs:(bcol[k] + 1) * bs] = bval[k]
+    np.testing.assert_array_equal(e[:m, :n], d32)
+    assert not e[m:, :].any() and not e[:, n:].any()
+    # BSR SpMV equals the dense product (exact: small integers)
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-4, 5, size=n).astype(np.float32)
+    yo = rng.integers(-4, 5, size=m).astype(np.float32)
+    alpha, beta = float(rng.integers(-3, 4)), float(rng.integers(-3, 4))
+    y, sc = oracle.bsr_spmv(m, n, bs, brp, bcol, bval, x, alpha, beta, yo)
+    np.testing.assert_array_equal(y, alpha * (d32.astype(np.float64) @ x) + beta * yo)
+    np.testing.assert_array_equal(sc, abs(alpha) * (np.abs(e[:m, :n]).astype(np.float64) @ np.abs(x)) +
+                                  abs(beta) * np.abs(yo))
+
+
+def test_csr_to_bsr_one_by_one_is_csr():
+    coo = gen.ragged_coo(40, 30, seed=9, max_len=12)
+    rp, c, v = oracle.coo_to_csr(coo.m, coo.n, coo.row, coo.col, coo.val)
+    brp, bcol, bval = oracle.csr_to_bsr(coo.m, coo.n, rp, c, v, 1)
+    np.testing.assert_array_equal(brp, rp)
+    np.testing.assert_array_equal(bcol, c)
+    np.testing.assert_array_equal(bval.reshape(-1), v)
+
+
+def test_csr_to_bsr_duplicates_summed_in_csr_order():
+    # three entries at one position: ((a + b) + c) in fp32, a value that differs from (a + (b + c))
+    a, b, c3 = np.float32(1.0), np.float32(2.0 ** -24), np.float32(2.0 ** -24)
+    rp = np.array([0, 3], np.int32)
+    col = np.array([1, 1, 1], np.int32)
+    brp, bcol, bval = oracle.csr_to_bsr(1, 2, rp, col, np.array([a, b, c3], np.float32), 2)
+    assert bval[0, 0, 1] == (a + b) + c3 == np.float32(1.0)
+    assert (a + (b + c3)) != np.float32(1.0)
+    # a lone -0.0 is kept, an untouched position is +0.0
+    brp, bcol, bval = oracle.csr_to_bsr(1, 2, np.array([0, 1], np.int32), np.array([0], np.int32),
+                                        np.array([-0.0], np.float32), 2)
+    assert np.signbit(bval[0, 0, 0]) and not np.signbit(bval[0, 0, 1])
+
+
+def test_oracle_bf16_rounding_matches_generator_and_pins():
+    # two independent round-to-nearest-even implementations (the generator's numpy
+    # version and the oracle's C version) agree, and the halfway cases are pinned
+    rng = np.random.default_rng(4)
+    f = np.concatenate([rng.normal(size=2000).astype(np.float32),
+                        np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 3.0e38, -0.0, 0.0],
+                                 np.float32)])
+    np.testing.assert_array_equal(oracle.f32_to_bf16(f), gen.f32_to_bf16_bits(f))
+    h = oracle.f32_to_bf16(np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, np.inf, -np.inf, np.float32(3.4e38)],
+                                    np.float32))
+    assert h.tolist() == [0x3F80, 0x3F82, 0x7F80, 0xFF80, 0x7F80]
+    nan = oracle.f32_to_bf16(np.array([np.nan], np.float32))[0]
+    assert (nan & 0x7F80) == 0x7F80 and (nan & 0x7F) != 0
