@@ -30,6 +30,7 @@ KERNEL_SOURCES = {
     "spmv": [_CSRC + f for f in ("spmv.hip", "pstream.hip", "device_common.h", "internal.h", "api.cpp")],
     "spmm": [_CSRC + f for f in ("spmm.hip", "device_common.h", "internal.h", "api.cpp")],
     "bsr": [_CSRC + f for f in ("bsr.hip", "device_common.h", "internal.h")],
+    "bsr_spmv": [_CSRC + f for f in ("bsr_convert.hip", "device_common.h", "internal.h")],
 }
 
 
@@ -59,6 +60,13 @@ def bsr_flops(nnzb, bs, N):
     return 2 * nnzb * bs * bs * N
 
 
+def bsr_spmv_bytes(m, n, bs, nnzb, beta_nonzero=False):
+    """BSR SpMV with fp32 blocks: every stored block (4 bs^2 B), block column
+    indices and block row pointer, x and y once."""
+    mb = (m + bs - 1) // bs
+    return 4 * nnzb * bs * bs + 4 * (nnzb + mb + 1) + 4 * n + 4 * m + (4 * m if beta_nonzero else 0)
+
+
 def csr_storage_bytes(m, nnz, val_bytes=8, idx_bytes=4):
     """Bytes of a CSR (values, column indices, row pointer of m+1 entries)."""
     return nnz * (val_bytes + idx_bytes) + (m + 1) * idx_bytes
@@ -78,6 +86,8 @@ def block_index_bytes_per_value(bs, idx_bytes=4):
 
 
 def kernel_family(workload):
+    if workload == "bsr_spmv":
+        return "bsr_spmv"
     return "bsr" if workload.startswith("bsr") else ("spmm" if workload.startswith("spmm") else "spmv")
 
 
@@ -113,8 +123,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="spmv_powerlaw",
-                    choices=["spmv_uniform", "spmv_powerlaw", "stencil27", "spmm_lognormal", "bsr_blocks"])
+                    choices=["spmv_uniform", "spmv_powerlaw", "stencil27", "spmm_lognormal", "bsr_blocks", "bsr_spmv"])
     ap.add_argument("--N", type=int, default=32, help="right-hand-side columns for spmm_lognormal")
+    ap.add_argument("--graph-batch", type=int, default=-1,
+                    help="steps per replay of a captured HIP graph in the timed region (0: one plain launch per "
+                         "step; -1: up to 20 for workloads whose step is a single short kernel, else 0)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--options", default="", help="plan options, e.g. group_nnz=1024,wave_min=128")
@@ -168,6 +181,8 @@ def main():
         def step():
             sp.bsr_spmm(b.mb, b.kb, b.bs, d_brow, d_bcol, d_bval, d_B, 1.0, 0.0, C)
 
+        out_tensor = C
+
         flops = bsr_flops(b.nnzb, b.bs, N)
         nbytes = bsr_bytes(b.mb, b.kb, b.bs, b.nnzb, N)
         launches = 1
@@ -175,6 +190,45 @@ def main():
         config = dict(workload=cfg, M=b.mb * b.bs, K=b.kb * b.bs, block=b.bs, nnz_blocks=b.nnzb, N=N)
         bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
         cpu_leg = None
+    elif cfg == "bsr_spmv":
+        bs = 64
+        coo = gen.block_sparse_coo(seed=0)
+        setup["generate_s"] = time.time() - t0
+        m, n = coo.m, coo.n
+        d_row, d_col, d_val = (torch.from_numpy(a).cuda() for a in (coo.row, coo.col, coo.val))
+        torch.cuda.synchronize()
+        t1 = time.time()
+        rp, ci, vv = sp.csr_build_from_coo(m, n, d_row, d_col, d_val)
+        torch.cuda.synchronize()
+        setup["csr_build_from_coo_ms"] = (time.time() - t1) * 1e3
+        del d_row, d_col, d_val
+        t1 = time.time()
+        brp, bcol, bval, fill = sp.csr_to_bsr(m, n, rp, ci, vv, bs, min_fill=0.5)
+        torch.cuda.synchronize()
+        setup["csr_to_bsr_ms"] = (time.time() - t1) * 1e3
+        nnzb = bcol.numel()
+        x = torch.from_numpy(gen.dense_vector(n, 0, 1)).cuda()
+        y = torch.zeros(m, device="cuda")
+
+        def step():
+            sp.bsr_spmv(m, n, bs, brp, bcol, bval, 1.0, x, 0.0, y)
+
+        out_tensor = y
+
+        flops = 2 * nnzb * bs * bs
+        nbytes = bsr_spmv_bytes(m, n, bs, nnzb)
+        launches = 1
+        dtype = "f32"
+        config = dict(workload=cfg, M=m, K=n, block=bs, nnz=coo.nnz, nnz_blocks=nnzb, fill_ratio=fill)
+        bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
+        h_brp, h_bcol, h_bval, h_x = (t.cpu().numpy() for t in (brp, bcol, bval, x))
+
+        def cpu_call():
+            import oracle
+            oracle.bsr_spmv(m, n, bs, h_brp, h_bcol, h_bval, h_x)
+
+        cpu_leg = (cpu_call, flops, "full passes of y = A x over the same 64 x 64-block BSR (fp32 blocks, fp64 "
+                                    "accumulation, single-threaded C loop)")
     else:
         coo = {"spmv_uniform": lambda: gen.uniform_rows_coo(seed=0),
                "spmv_powerlaw": lambda: gen.powerlaw_coo(seed=0),
@@ -241,6 +295,8 @@ def main():
             def step():
                 sp.spmm(plan, 1.0, B, 0.0, C)
 
+            out_tensor = C
+
             flops = 2 * nnz * N
             nbytes = spmm_bytes(m, n, nnz, N)
             launches = 1
@@ -249,10 +305,21 @@ def main():
             def step():
                 sp.spmv(plan, 1.0, x, 0.0, y)
 
+            out_tensor = y
+
             flops = spmv_flops(m, nnz)
             nbytes = spmv_bytes(m, n, nnz)
             launches = 1
-        cpu_leg = (rp, ci, vv, x, m, n, nnz) if cfg in ("spmv_powerlaw", "spmv_uniform") else None
+        cpu_leg = None
+        if cfg in ("spmv_powerlaw", "spmv_uniform"):
+            h_rp, h_ci, h_vv, h_x = (t.cpu().numpy() for t in (rp, ci, vv, x))
+
+            def cpu_call():
+                import oracle
+                oracle.spmv(h_rp, h_ci, h_vv, h_x)
+
+            cpu_leg = (cpu_call, spmv_flops(m, nnz), "full passes of y = A x over the same %s matrix (fp64 "
+                                                     "accumulation, single-threaded C loop)" % cfg)
 
     restore_fn = locals().get("restore")
     # ---------------- warmup + timed region
@@ -261,17 +328,43 @@ def main():
     if restore_fn:
         restore_fn()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # Short single-kernel steps are timed as replays of a captured HIP graph of
+    # G back-to-back steps, so that the events measure the kernels and not the
+    # host's launch rate; G divides the step count.
+    G = args.graph_batch
+    if G < 0:
+        G = 20 if cfg in ("spmv_uniform", "bsr_spmv", "bsr_blocks") else 0
+    if G > 0:
+        G = max(g for g in range(1, min(G, args.steps) + 1) if args.steps % g == 0)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(G):
+                step()
+        torch.cuda.synchronize()
+    nrec = args.steps // G if G > 0 else args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(nrec)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(nrec)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(nrec):
         starts[i].record(stream)
-        step()
+        if G > 0:
+            graph.replay()
+        else:
+            step()
         ends[i].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ev_ms = [s.elapsed_time(e) / (G if G > 0 else 1) for s, e in zip(starts, ends)]
+    if G > 0:
+        # the graph's result equals an eager step's, bit for bit (deterministic kernels)
+        out = locals().get("out_tensor")
+        if out is not None:
+            got = out.clone()
+            step()
+            torch.cuda.synchronize()
+            result["graph_replay_matches_eager"] = bool(torch.equal(got, out))
+        result["graph_batch"] = G
     ms_per_step = elapsed * 1e3 / args.steps
     launch_ms = float(np.mean(ev_ms)) / launches
     step_flops_s = flops / (ms_per_step * 1e-3)
@@ -297,21 +390,17 @@ def main():
 
     # ---------------- CPU baseline: the oracle on the host cores
     if not args.no_cpu_baseline and cpu_leg is not None:
-        import oracle
-        rp_, ci_, vv_, x_, m_, n_, nnz_ = cpu_leg
-        h_rp, h_ci, h_vv, h_x = (t.cpu().numpy() for t in (rp_, ci_, vv_, x_))
+        cpu_call, cpu_flops, cpu_desc = cpu_leg
         reps, t_cpu = 0, 0.0
         t0 = time.perf_counter()
         while t_cpu < args.cpu_seconds and reps < 1000:
-            oracle.spmv(h_rp, h_ci, h_vv, h_x)
+            cpu_call()
             reps += 1
             t_cpu = time.perf_counter() - t0
         per = t_cpu / reps
-        result["cpu_baseline"] = dict(value=round(spmv_flops(m_, nnz_) / per / 1e9, 4), unit="GFLOP/s", cores=1,
-                                      kind="oracle",
-                                      sample="%d full passes of y = A x over the same %s matrix (fp64 accumulation, "
-                                             "single-threaded C loop), %.1f s" % (reps, cfg, t_cpu))
-    elif not args.no_cpu_baseline and cfg == "stencil27":
+        result["cpu_baseline"] = dict(value=round(cpu_flops / per / 1e9, 4), unit="GFLOP/s", cores=1, kind="oracle",
+                                      sample="%d %s, %.1f s" % (reps, cpu_desc, t_cpu))
+    elif not args.no_cpu_baseline:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
 

@@ -18,6 +18,7 @@ from .workloads import (  # noqa: F401
     stencil27_coo,
     lognormal_coo,
     block_sparse_bsr,
+    block_sparse_coo,
     bf16_matrix,
     ragged_coo,
     dense_vector,

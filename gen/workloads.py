@@ -18,6 +18,9 @@ Each function documents the distribution it draws.  The five named workloads
                   positions (6554) drawn without replacement, every block dense
                   with N(0, 0.02) values rounded to bf16; B is 16384 x 512 bf16
                   drawn N(0, 1).
+  bsr_spmv        the bsr_blocks block positions as an fp32 COO (every element
+                  of every block, N(0, 0.02)), converted on the GPU to 64 x 64
+                  BSR; x in U[-1, 1].
 """
 from dataclasses import dataclass
 
@@ -205,6 +208,23 @@ def block_sparse_bsr(mb=256, kb=256, bs=64, density=0.1, std=0.02, seed=0):
     brow_ptr[1:] = np.cumsum(counts)
     vals = rng.normal(0.0, std, size=(nblocks, bs, bs)).astype(np.float32)
     return Bsr(mb, kb, bs, brow_ptr.astype(np.int32), bcol, f32_to_bf16_bits(vals).reshape(nblocks, bs, bs))
+
+
+def block_sparse_coo(mb=256, kb=256, bs=64, density=0.1, std=0.02, seed=0):
+    """The block positions of block_sparse_bsr (same draw), every element of
+    every block present, values N(0, std) in fp32; COO ordered by block, then
+    row-major inside the block."""
+    rng = _rng(seed, 50)
+    nblocks = int(round(density * mb * kb))
+    pos = np.sort(rng.choice(mb * kb, size=nblocks, replace=False))
+    brow = (pos // kb).astype(np.int64)
+    bcol = (pos % kb).astype(np.int64)
+    r_in = np.repeat(np.arange(bs, dtype=np.int64), bs)
+    c_in = np.tile(np.arange(bs, dtype=np.int64), bs)
+    row = (brow[:, None] * bs + r_in[None, :]).reshape(-1).astype(np.int32)
+    col = (bcol[:, None] * bs + c_in[None, :]).reshape(-1).astype(np.int32)
+    val = _rng(seed, 52).normal(0.0, std, size=row.size).astype(np.float32)
+    return Coo(mb * bs, kb * bs, row, col, val)
 
 
 def bf16_matrix(rows, cols, seed, stream=51, std=1.0):

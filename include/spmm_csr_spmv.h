@@ -47,7 +47,8 @@ enum {
     SP_ERR_WORKSPACE = 4,   /* workspace missing or smaller than queried     */
     SP_ERR_UNSUPPORTED = 5, /* option, shape or layout not supported         */
     SP_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed    */
-    SP_ERR_STATE = 7        /* plan used before sp_plan_bind, or similar     */
+    SP_ERR_STATE = 7,       /* plan used before sp_plan_bind, or similar     */
+    SP_ERR_FILL = 8         /* block fill ratio below the requested minimum  */
 };
 
 /* Static string naming a status code (never NULL). */
@@ -212,6 +213,57 @@ int spmv(const sp_plan* plan, float alpha, const float* x, float beta, float* y,
 int spmv_t(const sp_plan* plan, float alpha, const float* u, float beta, float* z, void* stream);
 int spmm(const sp_plan* plan, int32_t N, float alpha, const float* B, int64_t ldb,
          float beta, float* C, int64_t ldc, void* stream);
+
+/* --------------------------------------------------------- CSR -> BSR
+ * [BCSR] §1: a block is stored when it holds at least one entry; the format is
+ * brow_ptr[mb+1] (block row pointer), bcol[nnzb] (block column of each stored
+ * block, increasing within a block row) and the nnzb dense bs x bs blocks one
+ * after another, each row-major ([BCSR] §2.1).  [ASYNC] §2.2.1 measures the
+ * layout's waste by the fill ratio nnz / (nnzb * bs * bs); [GEN] §6 warns that
+ * a conversion only pays when it is reused, so the analysis step reports the
+ * fill ratio and can refuse the conversion.
+ *
+ * Square blocks, bs in {1, 2, 4, 8, 16, 32, 64}; mb = ceil(m / bs),
+ * kb = ceil(n / bs) (the last block row / column is padded with zeros).
+ * Input: a CSR whose rows are sorted by column (as csr_build_from_coo
+ * returns it), device arrays.  The value at in-block position (r, c) of block
+ * (I, J) is the sum of the CSR entries at element (I*bs + r, J*bs + c), added
+ * in CSR order in fp32 starting from the first; other positions are +0.
+ * bf16 output is that sum rounded once to nearest-even.  Bit-exact and unique.
+ *
+ * csr_to_bsr_analyze: writes brow_ptr (device, mb+1 entries), returns nnzb and
+ * the fill ratio (host; 1.0 when nnzb == 0) and synchronises `stream` once.
+ * work: at least csr_to_bsr_bufsize() bytes.  Errors: SP_ERR_NULL,
+ * SP_ERR_SIZE (row_ptr[m] != nnz, sizes beyond int32), SP_ERR_INDEX (a column
+ * outside [0, n)), SP_ERR_UNSUPPORTED (bs not supported, or a row not sorted),
+ * SP_ERR_WORKSPACE, SP_ERR_FILL (fill ratio < min_fill: *nnzb and *fill are
+ * still set, brow_ptr is written), SP_ERR_HIP.
+ * csr_to_bsr_fill: writes bcol (device, nnzb) and bval (device, nnzb*bs*bs
+ * fp32, or bf16 bit patterns when out_bf16 = 1) for the brow_ptr of the
+ * analysis; fp32 output needs bval 16-byte aligned when bs % 4 == 0.  Never
+ * synchronises; never writes outside the ranges brow_ptr gives.
+ */
+int csr_to_bsr_bufsize(int64_t m, int64_t n, int64_t nnz, int32_t bs, size_t* bytes);
+int csr_to_bsr_analyze(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                       int32_t bs, double min_fill, int32_t* brow_ptr, int64_t* nnzb, double* fill,
+                       void* work, size_t work_bytes, void* stream);
+int csr_to_bsr_fill(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                    const float* val, int32_t bs, const int32_t* brow_ptr, int64_t nnzb, int32_t* bcol,
+                    void* bval, int32_t out_bf16, void* stream);
+
+/* --------------------------------------------------------- BSR SpMV
+ * [BCSR] §2 (block sparse matrix-vector product over the BCSR layout above):
+ * y = alpha * A x + beta * y for the m x n matrix A given as bs x bs fp32
+ * blocks (layout of csr_to_bsr), x: n floats, y: m floats (device).  Element
+ * rows >= m and columns >= n of the padded last block row / column are not
+ * read through x nor written.  A block whose column index lies outside
+ * [0, kb) contributes nothing; block pointers are clamped to [0, nnzb].
+ * bval must be 16-byte aligned, and x too when bs >= 4.  bs in {1, 2, 4, 8,
+ * 16, 32, 64}.  Never allocates, never synchronises; deterministic.
+ * Errors: SP_ERR_NULL, SP_ERR_SIZE, SP_ERR_UNSUPPORTED, SP_ERR_HIP.
+ */
+int bsr_spmv(int64_t m, int64_t n, int32_t bs, int64_t nnzb, const int32_t* brow_ptr, const int32_t* bcol,
+             const float* bval, float alpha, const float* x, float beta, float* y, void* stream);
 
 /* --------------------------------------------------------- BSR SpMM
  * [BCSR] §1 and [ASYNC] §2.2.1: block row pointer brow_ptr[mb+1], block column

@@ -2,9 +2,10 @@
 
 Python binding of libspmm_csr_spmv.so (C ABI in include/spmm_csr_spmv.h):
 CSR SpMV y = alpha A x + beta y, its transpose through a one-time CSC,
-CSR SpMM C = alpha A B + beta C, and BSR SpMM on MFMA (bf16 in, fp32
-accumulate).  All arithmetic runs in the library's HIP kernels; this package
-only marshals torch tensors into the C calls.  There is no CPU fallback:
+CSR SpMM C = alpha A B + beta C, BSR SpMM on MFMA (bf16 in, fp32
+accumulate), CSR -> BSR with a fill-ratio gate and BSR SpMV.  All
+arithmetic runs in the library's HIP kernels; this package only marshals
+torch tensors into the C calls.  There is no CPU fallback:
 without the built library every call raises.
 """
 from ._binding import (  # noqa: F401
@@ -13,7 +14,9 @@ from ._binding import (  # noqa: F401
     Plan,
     SparseError,
     bsr_spmm,
+    bsr_spmv,
     csr_build_from_coo,
+    csr_to_bsr,
     csr_to_csc,
     lib,
     plan_options,

@@ -16,13 +16,13 @@ LIB_PATH = os.path.join(_HERE, "libspmm_csr_spmv.so")
 
 SP_OK = 0
 STATUS = {0: "SP_OK", 1: "SP_ERR_NULL", 2: "SP_ERR_SIZE", 3: "SP_ERR_INDEX", 4: "SP_ERR_WORKSPACE",
-          5: "SP_ERR_UNSUPPORTED", 6: "SP_ERR_HIP", 7: "SP_ERR_STATE"}
+          5: "SP_ERR_UNSUPPORTED", 6: "SP_ERR_HIP", 7: "SP_ERR_STATE", 8: "SP_ERR_FILL"}
 
 # Names declared in include/spmm_csr_spmv.h.
 EXPORTS = ("sp_status_string", "sp_version", "csr_build_from_coo_bufsize", "csr_build_from_coo",
            "csr_to_csc_bufsize", "csr_to_csc", "sp_plan_options_default", "sp_plan_create",
            "sp_plan_workspace_size", "sp_plan_bind", "sp_plan_profile", "sp_plan_destroy", "spmv", "spmv_t", "spmm",
-           "bsr_spmm_bufsize", "bsr_spmm")
+           "csr_to_bsr_bufsize", "csr_to_bsr_analyze", "csr_to_bsr_fill", "bsr_spmv", "bsr_spmm_bufsize", "bsr_spmm")
 
 
 class SparseError(RuntimeError):
@@ -84,6 +84,11 @@ def lib():
         L.spmv.argtypes = [_p, _f, _p, _f, _p, _p]
         L.spmv_t.argtypes = [_p, _f, _p, _f, _p, _p]
         L.spmm.argtypes = [_p, _i32, _f, _p, _i64, _f, _p, _i64, _p]
+        L.csr_to_bsr_bufsize.argtypes = [_i64, _i64, _i64, _i32, ctypes.POINTER(_sz)]
+        L.csr_to_bsr_analyze.argtypes = [_i64, _i64, _i64, _p, _p, _i32, ctypes.c_double, _p,
+                                         ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double), _p, _sz, _p]
+        L.csr_to_bsr_fill.argtypes = [_i64, _i64, _i64, _p, _p, _p, _i32, _p, _i64, _p, _p, _i32, _p]
+        L.bsr_spmv.argtypes = [_i64, _i64, _i32, _i64, _p, _p, _p, _f, _p, _f, _p, _p]
         L.bsr_spmm_bufsize.argtypes = [_i64, _i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
         L.bsr_spmm.argtypes = [_i64, _i64, _i32, _i64, _p, _p, _p, _i32, _p, _i64, _f, _f, _p, _i64, _p, _sz, _p]
         for name in EXPORTS:
@@ -163,6 +168,31 @@ def csr_to_csc(m, n, row_ptr, col_idx, val, stream=None):
     _check("csr_to_csc", L.csr_to_csc(m, n, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(val), _ptr(col_ptr),
                                       _ptr(row_idx), _ptr(cval), _ptr(work), size.value, _stream(stream)))
     return col_ptr, row_idx, cval
+
+
+def csr_to_bsr(m, n, row_ptr, col_idx, val, bs, min_fill=0.0, out="f32", stream=None):
+    """CSR (rows sorted by column) -> BSR with bs x bs blocks: (brow_ptr, bcol, blocks, fill).
+    blocks is float32 [nnzb, bs, bs] (out="f32") or bf16 bit patterns as int16 (out="bf16").
+    Raises SparseError with code SP_ERR_FILL when the fill ratio is below min_fill."""
+    L = lib()
+    _dev(row_ptr, torch.int32, "row_ptr"), _dev(col_idx, torch.int32, "col_idx"), _dev(val, torch.float32, "val")
+    nnz = col_idx.numel()
+    dev = row_ptr.device
+    size = _sz()
+    _check("csr_to_bsr_bufsize", L.csr_to_bsr_bufsize(m, n, nnz, bs, ctypes.byref(size)))
+    work = _workspace(size.value, dev)
+    mb = (m + bs - 1) // bs
+    brow_ptr = torch.empty(mb + 1, dtype=torch.int32, device=dev)
+    nnzb, fill = _i64(), ctypes.c_double()
+    _check("csr_to_bsr_analyze",
+           L.csr_to_bsr_analyze(m, n, nnz, _ptr(row_ptr), _ptr(col_idx), bs, float(min_fill), _ptr(brow_ptr),
+                                ctypes.byref(nnzb), ctypes.byref(fill), _ptr(work), size.value, _stream(stream)))
+    bcol = torch.empty(nnzb.value, dtype=torch.int32, device=dev)
+    bval = torch.empty((nnzb.value, bs, bs), dtype=torch.int16 if out == "bf16" else torch.float32, device=dev)
+    _check("csr_to_bsr_fill",
+           L.csr_to_bsr_fill(m, n, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(val), bs, _ptr(brow_ptr), nnzb.value,
+                             _ptr(bcol), _ptr(bval), 1 if out == "bf16" else 0, _stream(stream)))
+    return brow_ptr, bcol, bval, fill.value
 
 
 # ---------------------------------------------------------------- plan
@@ -248,6 +278,17 @@ def spmm(plan, alpha, B, beta, C, stream=None):
         raise ValueError("shape mismatch")
     _check("spmm", lib().spmm(plan.handle, N, float(alpha), _ptr(B), N, float(beta), _ptr(C), N, _stream(stream)))
     return C
+
+
+def bsr_spmv(m, n, bs, brow_ptr, bcol, bval, alpha, x, beta, y, stream=None):
+    """y = alpha * A x + beta * y (in place on y) with A in BSR, fp32 bs x bs blocks."""
+    _dev(brow_ptr, torch.int32, "brow_ptr"), _dev(bcol, torch.int32, "bcol"), _dev(bval, torch.float32, "bval")
+    _dev(x, torch.float32, "x"), _dev(y, torch.float32, "y")
+    if x.numel() != n or y.numel() != m:
+        raise ValueError("x must have n entries and y m entries")
+    _check("bsr_spmv", lib().bsr_spmv(m, n, bs, bcol.numel(), _ptr(brow_ptr), _ptr(bcol), _ptr(bval), float(alpha),
+                                      _ptr(x), float(beta), _ptr(y), _stream(stream)))
+    return y
 
 
 def bsr_spmm(mb, kb, bs, brow_ptr, bcol, bval, B, alpha, beta, C, stream=None, work=None):

@@ -552,6 +552,7 @@ const char* sp_status_string(int status) {
         case SP_ERR_UNSUPPORTED: return "SP_ERR_UNSUPPORTED: option, shape or layout not supported";
         case SP_ERR_HIP: return "SP_ERR_HIP: a HIP call or kernel launch failed";
         case SP_ERR_STATE: return "SP_ERR_STATE: plan not bound to a workspace";
+        case SP_ERR_FILL: return "SP_ERR_FILL: block fill ratio below the requested minimum";
         default: return "unknown status";
     }
 }
@@ -741,6 +742,71 @@ int spmm(const sp_plan* plan, int32_t N, float alpha, const float* B, int64_t ld
     return spx::launch_spmm(plan->fwd.dev, N, alpha, B, ldb, beta, C, ldc, (hipStream_t)stream) == hipSuccess
                ? SP_OK
                : SP_ERR_HIP;
+}
+
+// ------------------------------------------------------------------ CSR -> BSR, BSR SpMV
+static bool bsr_block_ok(int32_t bs) { return bs == 1 || bs == 2 || bs == 4 || bs == 8 || bs == 16 || bs == 32 || bs == 64; }
+
+int csr_to_bsr_bufsize(int64_t m, int64_t n, int64_t nnz, int32_t bs, size_t* bytes) {
+    if (!bytes) return SP_ERR_NULL;
+    const int rc = check_dims(m, n, nnz);
+    if (rc) return rc;
+    if (!bsr_block_ok(bs)) return SP_ERR_UNSUPPORTED;
+    *bytes = spx::bsr_convert_work_bytes(m, bs);
+    return SP_OK;
+}
+
+int csr_to_bsr_analyze(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx, int32_t bs,
+                       double min_fill, int32_t* brow_ptr, int64_t* nnzb, double* fill, void* work, size_t work_bytes,
+                       void* stream) {
+    int rc = check_dims(m, n, nnz);
+    if (rc) return rc;
+    if (!bsr_block_ok(bs)) return SP_ERR_UNSUPPORTED;
+    if (!row_ptr || !brow_ptr || !nnzb || !fill || (nnz > 0 && !col_idx)) return SP_ERR_NULL;
+    if (!work || work_bytes < spx::bsr_convert_work_bytes(m, bs)) return SP_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    int32_t flags = 0;
+    rc = spx::csr_to_bsr_analyze_device(m, n, row_ptr, col_idx, bs, brow_ptr, work, s, &flags);
+    if (rc != SP_OK) return rc;
+    const int64_t mb = (m + bs - 1) / bs;
+    int32_t tail[2] = {0, 0};
+    if (hipMemcpyAsync(&tail[0], brow_ptr + mb, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipMemcpyAsync(&tail[1], row_ptr + m, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return SP_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return SP_ERR_HIP;
+    if (flags & 1) return SP_ERR_INDEX;
+    if (flags & 2) return SP_ERR_UNSUPPORTED;
+    if ((int64_t)tail[1] != nnz) return SP_ERR_SIZE;
+    *nnzb = tail[0];
+    *fill = tail[0] > 0 ? (double)nnz / ((double)tail[0] * bs * bs) : 1.0;
+    if (*fill < min_fill) return SP_ERR_FILL;
+    return SP_OK;
+}
+
+int csr_to_bsr_fill(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx, const float* val,
+                    int32_t bs, const int32_t* brow_ptr, int64_t nnzb, int32_t* bcol, void* bval, int32_t out_bf16,
+                    void* stream) {
+    int rc = check_dims(m, n, nnz);
+    if (rc) return rc;
+    if (!bsr_block_ok(bs) || (out_bf16 != 0 && out_bf16 != 1)) return SP_ERR_UNSUPPORTED;
+    if (nnzb < 0 || nnzb > kI32Max || nnzb * bs * bs > ((int64_t)1 << 40)) return SP_ERR_SIZE;
+    if (!row_ptr || !brow_ptr || (nnz > 0 && (!col_idx || !val)) || (nnzb > 0 && (!bcol || !bval))) return SP_ERR_NULL;
+    if (!out_bf16 && bs % 4 == 0 && (reinterpret_cast<uintptr_t>(bval) & 15)) return SP_ERR_UNSUPPORTED;
+    return spx::csr_to_bsr_fill_device(m, n, row_ptr, col_idx, val, bs, brow_ptr, bcol, bval, out_bf16,
+                                       (hipStream_t)stream);
+}
+
+int bsr_spmv(int64_t m, int64_t n, int32_t bs, int64_t nnzb, const int32_t* brow_ptr, const int32_t* bcol,
+             const float* bval, float alpha, const float* x, float beta, float* y, void* stream) {
+    int rc = check_dims(m, n, 0);
+    if (rc) return rc;
+    if (!bsr_block_ok(bs)) return SP_ERR_UNSUPPORTED;
+    if (nnzb < 0 || nnzb > kI32Max) return SP_ERR_SIZE;
+    if (m == 0) return SP_OK;
+    if (!brow_ptr || !y || (nnzb > 0 && (!bcol || !bval || (n > 0 && !x)))) return SP_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(bval) & 15) return SP_ERR_UNSUPPORTED;
+    if (bs >= 4 && (reinterpret_cast<uintptr_t>(x) & 15)) return SP_ERR_UNSUPPORTED;
+    return spx::bsr_spmv_device(m, n, bs, nnzb, brow_ptr, bcol, bval, alpha, x, beta, y, (hipStream_t)stream);
 }
 
 // ------------------------------------------------------------------ BSR

@@ -387,6 +387,10 @@ hipError_t launch_check_indices(const int32_t* idx, int64_t nnz, int32_t n, int3
     return hipGetLastError();
 }
 
+size_t scan_work_bytes(int64_t n) { return align256((size_t)((n + kScanTile - 1) / kScanTile + 1) * 4); }
+
+int scan_inclusive_i32(int32_t* a, int64_t n, int32_t* sums, hipStream_t s) { return scan_inplace(a, n, sums, s); }
+
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(fill_i32, dim3(grid_for(n)), dim3(kBlock), 0, s, p, n, v);

@@ -84,6 +84,21 @@ int csr_to_csc_device(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr,
                       const float* val, int32_t* col_ptr, int32_t* row_idx, float* cval, void* work,
                       size_t work_bytes, hipStream_t s);
 
+// Inclusive prefix sum of a[0..n) in place; sums is scratch of scan_work_bytes(n) (convert.hip).
+size_t scan_work_bytes(int64_t n);
+int scan_inclusive_i32(int32_t* a, int64_t n, int32_t* sums, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
+// CSR -> BSR and BSR SpMV with fp32 blocks (bsr_convert.hip).
+size_t bsr_convert_work_bytes(int64_t m, int32_t bs);
+int csr_to_bsr_analyze_device(int64_t m, int64_t n, const int32_t* row_ptr, const int32_t* col_idx, int32_t bs,
+                              int32_t* brow_ptr, void* work, hipStream_t s, int32_t* flags_host);
+int csr_to_bsr_fill_device(int64_t m, int64_t n, const int32_t* row_ptr, const int32_t* col_idx, const float* val,
+                           int32_t bs, const int32_t* brow_ptr, int32_t* bcol, void* bval, int32_t out_bf16,
+                           hipStream_t s);
+int bsr_spmv_device(int64_t m, int64_t n, int32_t bs, int64_t nnzb, const int32_t* brow_ptr, const int32_t* bcol,
+                    const float* bval, float alpha, const float* x, float beta, float* y, hipStream_t s);
+
 // BSR SpMM (bsr.hip).
 size_t bsr_work_bytes(int64_t mb, int64_t kb, int32_t bs, int64_t nnzb, int32_t N);
 int bsr_spmm_device(int64_t mb, int64_t kb, int32_t bs, int64_t nnzb, const int32_t* brow_ptr,

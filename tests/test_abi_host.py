@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    for code in range(8):
+    for code in range(9):
         s = sp.status_string(code)
         assert s.startswith("SP_")
     assert sp.status_string(99) == "unknown status"
@@ -134,3 +134,31 @@ def test_bsr_argument_errors():
     assert call(B=None) == 1
     assert call(C=ctypes.c_void_p(0x1004)) == 5   # misaligned C
     assert call(mb=2 ** 31) == 2
+
+
+def test_csr_to_bsr_and_bsr_spmv_argument_errors():
+    L = sp.lib()
+    b = SZ()
+    assert L.csr_to_bsr_bufsize(100, 100, 50, 3, ctypes.byref(b)) == 5      # block size not supported
+    assert L.csr_to_bsr_bufsize(100, 100, 50, 8, ctypes.byref(b)) == 0 and b.value > 0
+    assert L.csr_to_bsr_bufsize(-1, 100, 50, 8, ctypes.byref(b)) == 2
+    assert L.csr_to_bsr_bufsize(100, 100, 50, 8, None) == 1
+    nnzb, fill = ctypes.c_int64(), ctypes.c_double()
+    # analyze: missing outputs, missing or small workspace, bad block size (no GPU work is reached)
+    assert L.csr_to_bsr_analyze(10, 10, 5, FAKE, FAKE, 2, 0.0, None, ctypes.byref(nnzb), ctypes.byref(fill),
+                                FAKE, 1 << 20, None) == 1
+    assert L.csr_to_bsr_analyze(10, 10, 5, FAKE, FAKE, 2, 0.0, FAKE, ctypes.byref(nnzb), ctypes.byref(fill),
+                                None, 0, None) == 4
+    assert L.csr_to_bsr_analyze(10, 10, 5, FAKE, FAKE, 5, 0.0, FAKE, ctypes.byref(nnzb), ctypes.byref(fill),
+                                FAKE, 1 << 20, None) == 5
+    # fill: bad output type, missing arrays, misaligned fp32 blocks
+    assert L.csr_to_bsr_fill(10, 10, 5, FAKE, FAKE, FAKE, 4, FAKE, 3, FAKE, FAKE, 2, None) == 5
+    assert L.csr_to_bsr_fill(10, 10, 5, FAKE, FAKE, FAKE, 4, FAKE, 3, None, FAKE, 0, None) == 1
+    assert L.csr_to_bsr_fill(10, 10, 5, FAKE, FAKE, FAKE, 4, FAKE, 3, FAKE, ctypes.c_void_p(0x1004), 0, None) == 5
+    # bsr_spmv: empty output is a no-op, then argument checks
+    assert L.bsr_spmv(0, 10, 4, 0, None, None, None, 1.0, None, 0.0, None, None) == 0
+    assert L.bsr_spmv(10, 10, 3, 2, FAKE, FAKE, FAKE, 1.0, FAKE, 0.0, FAKE, None) == 5
+    assert L.bsr_spmv(10, 10, 4, 2, FAKE, FAKE, FAKE, 1.0, FAKE, 0.0, None, None) == 1
+    assert L.bsr_spmv(10, 10, 4, 2, FAKE, FAKE, ctypes.c_void_p(0x1004), 1.0, FAKE, 0.0, FAKE, None) == 5
+    assert L.bsr_spmv(10, 10, 4, 2, FAKE, FAKE, FAKE, 1.0, ctypes.c_void_p(0x1004), 0.0, FAKE, None) == 5
+    assert L.bsr_spmv(2 ** 31, 10, 4, 2, FAKE, FAKE, FAKE, 1.0, FAKE, 0.0, FAKE, None) == 2

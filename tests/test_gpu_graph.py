@@ -1,0 +1,84 @@
+"""The products captured in a HIP graph (torch.cuda.CUDAGraph around the C ABI
+calls) and replayed several times, with eager work and synchronisations
+between the replays: every replay must equal the eager result bit for bit
+(the kernels are deterministic and allocate nothing while running)."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+import spmm_csr_spmv_amd as sp
+from gpu_util import dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _replays_match(run, outs, replays=3):
+    """run() issues the products into `outs`; capture it, then compare each
+    replay with an eager run made between the replays."""
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for k in range(replays):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [o.clone() for o in outs]
+        for o in outs:
+            o.fill_(float("nan"))
+        run()  # eager
+        torch.cuda.synchronize()
+        for a, b in zip(got, outs):
+            assert torch.equal(a, b), "replay %d differs from the eager result" % k
+
+
+@pytest.mark.parametrize("bins", [dict(), dict(use_sell=0, col_panels=4, wave_min=8, block_min=20, split_min=40,
+                                               split_seg=16), dict(use_sell=1, sell_sigma=64),
+                                  dict(wave_min=0, block_min=0, split_min=0, split_seg=16)])
+def test_spmv_spmv_t_spmm_graph_replays(bins):
+    say("graph replays", bins)
+    coo = gen.ragged_coo(1500, 900, seed=2, max_len=30, long_rows=(300, 800, 257))
+    rp, c, v = sp.csr_build_from_coo(coo.m, coo.n, dev(coo.row), dev(coo.col), dev(coo.val))
+    csc = sp.csr_to_csc(coo.m, coo.n, rp, c, v)
+    plan = sp.Plan(coo.m, coo.n, rp, c, v, csc=csc, max_N=8, **bins)
+    x = dev(gen.dense_vector(coo.n, 1))
+    u = dev(gen.dense_vector(coo.m, 2))
+    B = dev(gen.dense_matrix(coo.n, 8, 3))
+    y = torch.empty(coo.m, device="cuda")
+    z = torch.empty(coo.n, device="cuda")
+    C = torch.empty(coo.m, 8, device="cuda")
+
+    def run():
+        sp.spmv(plan, 1.0, x, 0.0, y)
+        sp.spmv_t(plan, 2.0, u, 0.0, z)
+        sp.spmm(plan, 1.0, B, 0.0, C)
+
+    _replays_match(run, [y, z, C])
+    # and the replayed result is the right one
+    hrp, hc, hv = oracle.coo_to_csr(coo.m, coo.n, coo.row, coo.col, coo.val)
+    ref, scale = oracle.spmv(hrp, hc, hv, x.cpu().numpy())
+    assert np.all(np.abs(y.cpu().numpy() - ref) <= 1e-5 * scale + 1e-30)
+
+
+def test_bsr_spmv_and_bsr_spmm_graph_replays():
+    say("graph replays, BSR")
+    coo = gen.block_sparse_coo(mb=6, kb=5, bs=64, density=0.4, std=1.0, seed=7)
+    rp, c, v = sp.csr_build_from_coo(coo.m, coo.n, dev(coo.row), dev(coo.col), dev(coo.val))
+    brp, bcol, bval, _ = sp.csr_to_bsr(coo.m, coo.n, rp, c, v, 64)
+    _, _, bval16, _ = sp.csr_to_bsr(coo.m, coo.n, rp, c, v, 64, out="bf16")
+    x = dev(gen.dense_vector(coo.n, 4))
+    B = dev(gen.bf16_matrix(coo.n, 256, seed=5).view(np.int16))
+    y = torch.empty(coo.m, device="cuda")
+    C = torch.empty(coo.m, 256, device="cuda")
+
+    def run():
+        sp.bsr_spmv(coo.m, coo.n, 64, brp, bcol, bval, 1.0, x, 0.0, y)
+        sp.bsr_spmm(6, 5, 64, brp, bcol, bval16, B, 1.0, 0.0, C)
+
+    _replays_match(run, [y, C])
