@@ -131,6 +131,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--options", default="", help="plan options, e.g. group_nnz=1024,wave_min=128")
+    ap.add_argument("--autotune", action="store_true",
+                    help="SpMV workloads: time the default candidate plans (sp_autotune_spmv), then build the plan "
+                         "from the tuning cache; the candidates' times are reported under 'autotune'")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (5 launches) to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -250,8 +253,20 @@ def main():
             torch.cuda.synchronize()
             setup["csr_to_csc_ms"] = (time.time() - t1) * 1e3
         N = args.N if cfg == "spmm_lognormal" else 1
+        tune = None
+        if args.autotune and cfg != "spmm_lognormal":
+            x_t = torch.from_numpy(gen.dense_vector(n, 0, 1)).cuda()
+            t1 = time.time()
+            best, ms, best_opts = sp.autotune_spmv(m, n, rp, ci, vv, x_t, reps=10)
+            setup["autotune_ms"] = (time.time() - t1) * 1e3
+            tune = dict(candidates=[dict(c) for c in sp.DEFAULT_CANDIDATES], ms_per_call=[round(t, 5) for t in ms],
+                        best=best)
+            del x_t
         t1 = time.time()
-        plan = sp.Plan(m, n, rp, ci, vv, csc=csc, max_N=N, **opts)
+        if tune is not None:
+            plan = sp.Plan(m, n, rp, ci, vv, csc=csc, max_N=N, tuned=True)
+        else:
+            plan = sp.Plan(m, n, rp, ci, vv, csc=csc, max_N=N, **opts)
         torch.cuda.synchronize()
         setup["plan_ms"] = (time.time() - t1) * 1e3
         prof = plan.profile()
@@ -264,6 +279,9 @@ def main():
                                 split_segments=prof["split_segments"]))
         if opts:
             config["plan_options"] = opts
+        if tune is not None:
+            result["autotune"] = tune
+            config["col_panels"] = prof["col_panels"]
         bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
         dtype = "f32"
         if cfg == "stencil27":

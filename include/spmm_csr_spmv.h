@@ -169,6 +169,8 @@ typedef struct sp_profile {
 int sp_plan_options_default(sp_plan_options* opt);
 
 /* Creates a plan for the m x n CSR matrix (row_ptr, col_idx, val: device).
+ * opt == NULL: the defaults, or the options the tuning cache holds for this
+ * matrix's dispatch key (see sp_autotune_spmv below).
  * When col_ptr/row_idx/cval (the CSC, e.g. from csr_to_csc) are non-NULL the
  * plan also serves spmv_t ([LSMR] §4: both directions run as non-transposed
  * CSR products); otherwise spmv_t returns SP_ERR_UNSUPPORTED.  opt may be NULL
@@ -196,6 +198,57 @@ int sp_plan_profile(const sp_plan* plan, int32_t transposed, sp_profile* out);
 
 /* Frees the host-side plan. */
 int sp_plan_destroy(sp_plan* plan);
+
+/* --------------------------------------------------------- dispatch key, tuning cache, autotune
+ * [GEN] §4: the first time a matrix is seen, a light profile gives a stable
+ * dispatch key; a small autotune times 2-4 candidate kernels with events on
+ * the stream, caches the fastest configuration and never benchmarks on every
+ * call; a version number invalidates the cache for a matrix that changes.
+ *
+ * The key: format (0 = CSR), dtype (0 = fp32 values), index_bits (32),
+ * transposed (0: A, 1: A^T through the CSC), rows, cols, nnz, N (right-hand
+ * sides; 1 = SpMV), arch (950 = gfx950), the row-length profile quantised as
+ * floor(4 log2(1 + v)) for the mean, p95 and maximum row length and
+ * floor(8 cv) for the coefficient of variation, and the caller's version.
+ * Keys compare field by field (the struct is zero-filled by the library).
+ *
+ * The cache is process-wide (all devices, all threads; a mutex guards it) and
+ * maps a key to plan options.  sp_plan_create with opt == NULL builds the key
+ * of A (N = 1, version 0) and, when the cache holds options for it, uses them
+ * for both directions instead of the defaults.
+ *
+ * sp_autotune_spmv: for each of the ncand (1..16) candidate option sets,
+ * creates a plan on the CSR (row_ptr, col_idx, val: device), binds it to `work`
+ * (at least sp_autotune_workspace_size() bytes), runs one warm-up spmv and
+ * times `reps` spmv calls y = A x between two events on `stream`; writes the
+ * mean milliseconds per call to ms[i], the fastest index to *best (ties: the
+ * lower index) and stores that candidate under the key of A (N = 1, the given
+ * version).  Overwrites y.  Synchronises; allocates no device memory (the
+ * plans are created and destroyed on the host).  Errors: those of
+ * sp_plan_create / sp_plan_bind / spmv, SP_ERR_SIZE (ncand or reps out of
+ * range), SP_ERR_WORKSPACE.
+ */
+typedef struct sp_dispatch_key {
+    int32_t format, dtype, index_bits, transposed;
+    int64_t rows, cols, nnz;
+    int32_t N, arch;
+    int32_t avg_len_q, p95_len_q, max_len_q, cv_q;
+    uint64_t version;
+} sp_dispatch_key;
+
+int sp_plan_dispatch_key(const sp_plan* plan, int32_t transposed, int32_t N, uint64_t version,
+                         sp_dispatch_key* key);
+int sp_tune_cache_store(const sp_dispatch_key* key, const sp_plan_options* opt);  /* SP_ERR_UNSUPPORTED: bad options */
+int sp_tune_cache_lookup(const sp_dispatch_key* key, sp_plan_options* opt, int32_t* found);
+int sp_tune_cache_clear(void);
+int sp_tune_cache_size(int64_t* entries);
+int sp_autotune_workspace_size(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                               const float* val, const sp_plan_options* candidates, int32_t ncand,
+                               size_t* bytes, void* stream);
+int sp_autotune_spmv(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                     const float* val, const sp_plan_options* candidates, int32_t ncand, const float* x, float* y,
+                     int32_t reps, uint64_t version, void* work, size_t work_bytes, int32_t* best, float* ms,
+                     void* stream);
 
 /* --------------------------------------------------------- products
  * spmv:   y = alpha * A x + beta * y     x: n floats, y: m floats (device)

@@ -9,16 +9,19 @@ torch tensors into the C calls.  There is no CPU fallback:
 without the built library every call raises.
 """
 from ._binding import (  # noqa: F401
+    DEFAULT_CANDIDATES,
     EXPORTS,
     LIB_PATH,
     Plan,
     SparseError,
+    autotune_spmv,
     bsr_spmm,
     bsr_spmv,
     csr_build_from_coo,
     csr_to_bsr,
     csr_to_csc,
     lib,
+    options_dict,
     plan_options,
     sp_plan_create,
     sp_version,
@@ -26,4 +29,9 @@ from ._binding import (  # noqa: F401
     spmv,
     spmv_t,
     status_string,
+    tune_cache_clear,
+    tune_cache_lookup,
+    tune_cache_size,
+    tune_cache_store,
+    sp_dispatch_key,
 )

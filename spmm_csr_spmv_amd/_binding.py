@@ -22,7 +22,9 @@ STATUS = {0: "SP_OK", 1: "SP_ERR_NULL", 2: "SP_ERR_SIZE", 3: "SP_ERR_INDEX", 4: 
 EXPORTS = ("sp_status_string", "sp_version", "csr_build_from_coo_bufsize", "csr_build_from_coo",
            "csr_to_csc_bufsize", "csr_to_csc", "sp_plan_options_default", "sp_plan_create",
            "sp_plan_workspace_size", "sp_plan_bind", "sp_plan_profile", "sp_plan_destroy", "spmv", "spmv_t", "spmm",
-           "csr_to_bsr_bufsize", "csr_to_bsr_analyze", "csr_to_bsr_fill", "bsr_spmv", "bsr_spmm_bufsize", "bsr_spmm")
+           "csr_to_bsr_bufsize", "csr_to_bsr_analyze", "csr_to_bsr_fill", "bsr_spmv", "bsr_spmm_bufsize", "bsr_spmm",
+           "sp_plan_dispatch_key", "sp_tune_cache_store", "sp_tune_cache_lookup", "sp_tune_cache_clear",
+           "sp_tune_cache_size", "sp_autotune_workspace_size", "sp_autotune_spmv")
 
 
 class SparseError(RuntimeError):
@@ -49,6 +51,14 @@ class sp_profile(ctypes.Structure):
                 ("block_rows", ctypes.c_int64), ("block_nnz", ctypes.c_int64),
                 ("split_rows", ctypes.c_int64), ("split_segments", ctypes.c_int64), ("split_nnz", ctypes.c_int64),
                 ("sell_slots", ctypes.c_int64), ("col_panels", ctypes.c_int64)]
+
+
+class sp_dispatch_key(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("dtype", ctypes.c_int32), ("index_bits", ctypes.c_int32),
+                ("transposed", ctypes.c_int32), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("nnz", ctypes.c_int64), ("N", ctypes.c_int32), ("arch", ctypes.c_int32),
+                ("avg_len_q", ctypes.c_int32), ("p95_len_q", ctypes.c_int32), ("max_len_q", ctypes.c_int32),
+                ("cv_q", ctypes.c_int32), ("version", ctypes.c_uint64)]
 
 
 _lib = None
@@ -90,6 +100,16 @@ def lib():
         L.csr_to_bsr_fill.argtypes = [_i64, _i64, _i64, _p, _p, _p, _i32, _p, _i64, _p, _p, _i32, _p]
         L.bsr_spmv.argtypes = [_i64, _i64, _i32, _i64, _p, _p, _p, _f, _p, _f, _p, _p]
         L.bsr_spmm_bufsize.argtypes = [_i64, _i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
+        _key = ctypes.POINTER(sp_dispatch_key)
+        _opt = ctypes.POINTER(sp_plan_options)
+        L.sp_plan_dispatch_key.argtypes = [_p, _i32, _i32, ctypes.c_uint64, _key]
+        L.sp_tune_cache_store.argtypes = [_key, _opt]
+        L.sp_tune_cache_lookup.argtypes = [_key, _opt, ctypes.POINTER(_i32)]
+        L.sp_tune_cache_clear.argtypes = []
+        L.sp_tune_cache_size.argtypes = [ctypes.POINTER(_i64)]
+        L.sp_autotune_workspace_size.argtypes = [_i64, _i64, _i64, _p, _p, _p, _opt, _i32, ctypes.POINTER(_sz), _p]
+        L.sp_autotune_spmv.argtypes = [_i64, _i64, _i64, _p, _p, _p, _opt, _i32, _p, _p, _i32, ctypes.c_uint64, _p,
+                                       _sz, ctypes.POINTER(_i32), ctypes.POINTER(_f), _p]
         L.bsr_spmm.argtypes = [_i64, _i64, _i32, _i64, _p, _p, _p, _i32, _p, _i64, _f, _f, _p, _i64, _p, _sz, _p]
         for name in EXPORTS:
             if name not in ("sp_status_string", "sp_version"):
@@ -210,18 +230,23 @@ class Plan:
     """sp_plan of an m x n CSR matrix (and of its CSC when given), bound to a
     torch-allocated workspace.  Holds references to the arrays it points to."""
 
-    def __init__(self, m, n, row_ptr, col_idx, val, csc=None, max_N=1, stream=None, **options):
+    def __init__(self, m, n, row_ptr, col_idx, val, csc=None, max_N=1, stream=None, tuned=False, **options):
+        """tuned=True passes no options: the library uses the tuning cache's
+        options for this matrix's dispatch key if it holds any, else the defaults."""
         L = lib()
         self._arrays = (row_ptr, col_idx, val) + (tuple(csc) if csc is not None else ())
         _dev(row_ptr, torch.int32, "row_ptr"), _dev(col_idx, torch.int32, "col_idx"), _dev(val, torch.float32, "val")
         cp, ri, cv = csc if csc is not None else (None, None, None)
         self.m, self.n, self.nnz = m, n, col_idx.numel()
-        self.opt = plan_options(**options)
+        if tuned and options:
+            raise ValueError("tuned=True takes no explicit options")
+        self.opt = None if tuned else plan_options(**options)
         h = ctypes.c_void_p()
         _check("sp_plan_create",
                L.sp_plan_create(ctypes.byref(h), m, n, self.nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(val),
                                 _ptr(cp) if cp is not None else None, _ptr(ri) if ri is not None else None,
-                                _ptr(cv) if cv is not None else None, ctypes.byref(self.opt), _stream(stream)))
+                                _ptr(cv) if cv is not None else None,
+                                ctypes.byref(self.opt) if self.opt is not None else None, _stream(stream)))
         self.handle = h
         self.max_N = int(max_N)
         size = _sz()
@@ -229,6 +254,12 @@ class Plan:
         self.workspace_bytes = size.value
         self.work = _workspace(size.value, row_ptr.device)
         _check("sp_plan_bind", L.sp_plan_bind(h, _ptr(self.work), size.value, self.max_N, _stream(stream)))
+
+    def dispatch_key(self, transposed=False, N=1, version=0):
+        k = sp_dispatch_key()
+        _check("sp_plan_dispatch_key", lib().sp_plan_dispatch_key(self.handle, 1 if transposed else 0, int(N),
+                                                                  int(version), ctypes.byref(k)))
+        return k
 
     def profile(self, transposed=False):
         p = sp_profile()
@@ -249,6 +280,63 @@ class Plan:
 
 def sp_plan_create(m, n, row_ptr, col_idx, val, csc=None, max_N=1, **options):
     return Plan(m, n, row_ptr, col_idx, val, csc=csc, max_N=max_N, **options)
+
+
+# ---------------------------------------------------------------- tuning cache, autotune
+# The candidates timed by autotune_spmv when none are given: the plan's
+# automatic choice, the row bins alone, SELL-C-sigma, the 8-panel stream.
+DEFAULT_CANDIDATES = (dict(), dict(use_sell=0, col_panels=0), dict(use_sell=1, col_panels=0),
+                      dict(use_sell=0, col_panels=8))
+
+
+def options_dict(o):
+    return {k: getattr(o, k) for k, _ in sp_plan_options._fields_}
+
+
+def tune_cache_store(key, **options):
+    _check("sp_tune_cache_store", lib().sp_tune_cache_store(ctypes.byref(key), ctypes.byref(plan_options(**options))))
+
+
+def tune_cache_lookup(key):
+    """The cached options (dict) for key, or None."""
+    o, found = sp_plan_options(), _i32()
+    _check("sp_tune_cache_lookup", lib().sp_tune_cache_lookup(ctypes.byref(key), ctypes.byref(o), ctypes.byref(found)))
+    return options_dict(o) if found.value else None
+
+
+def tune_cache_clear():
+    _check("sp_tune_cache_clear", lib().sp_tune_cache_clear())
+
+
+def tune_cache_size():
+    n = _i64()
+    _check("sp_tune_cache_size", lib().sp_tune_cache_size(ctypes.byref(n)))
+    return n.value
+
+
+def autotune_spmv(m, n, row_ptr, col_idx, val, x, candidates=None, reps=20, version=0, stream=None):
+    """Times spmv under each candidate option set (dicts of plan options), caches
+    the fastest under the matrix's dispatch key; returns (best index, ms per call
+    for each candidate, best options as a dict)."""
+    L = lib()
+    _dev(row_ptr, torch.int32, "row_ptr"), _dev(col_idx, torch.int32, "col_idx"), _dev(val, torch.float32, "val")
+    _dev(x, torch.float32, "x")
+    cands = list(candidates) if candidates is not None else list(DEFAULT_CANDIDATES)
+    arr = (sp_plan_options * len(cands))(*[plan_options(**c) for c in cands])
+    nnz = col_idx.numel()
+    size = _sz()
+    _check("sp_autotune_workspace_size",
+           L.sp_autotune_workspace_size(m, n, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(val), arr, len(cands),
+                                        ctypes.byref(size), _stream(stream)))
+    work = _workspace(size.value, row_ptr.device)
+    y = torch.empty(m, dtype=torch.float32, device=row_ptr.device)
+    best = _i32()
+    ms = (_f * len(cands))()
+    _check("sp_autotune_spmv",
+           L.sp_autotune_spmv(m, n, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(val), arr, len(cands), _ptr(x), _ptr(y),
+                              int(reps), int(version), _ptr(work), size.value, ctypes.byref(best), ms,
+                              _stream(stream)))
+    return best.value, list(ms), options_dict(arr[best.value])
 
 
 # ---------------------------------------------------------------- products

@@ -24,6 +24,14 @@ hipError_t launch_check_indices(const int32_t* idx, int64_t nnz, int32_t n, int3
 using spx::DirDevice;
 
 namespace {
+int check_options_impl(const sp_plan_options& o);
+}
+
+namespace spx {
+int check_plan_options(const sp_plan_options& o) { return check_options_impl(o); }
+}
+
+namespace {
 
 constexpr int64_t kI32Max = 2147483647;
 
@@ -272,7 +280,7 @@ size_t plan_layout(const sp_plan* p, int32_t max_N) {
     return off < 256 ? 256 : off;
 }
 
-int check_options(const sp_plan_options& o) {
+int check_options_impl(const sp_plan_options& o) {
     if (o.group_nnz < 64 || o.group_nnz > spx::kGroupMaxNnz) return SP_ERR_UNSUPPORTED;
     if (o.wave_min < 0 || o.wave_min > o.group_nnz) return SP_ERR_UNSUPPORTED;
     if (o.block_min < o.wave_min || o.split_min < o.block_min) return SP_ERR_UNSUPPORTED;
@@ -635,7 +643,7 @@ int sp_plan_create(sp_plan** plan, int64_t m, int64_t n, int64_t nnz, const int3
     } else {
         sp_plan_options_default(&o);
     }
-    rc = check_options(o);
+    rc = check_options_impl(o);
     if (rc) return rc;
     // the kernels stream indices and values with 16-byte loads
     auto misaligned = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) != 0; };
@@ -649,6 +657,20 @@ int sp_plan_create(sp_plan** plan, int64_t m, int64_t n, int64_t nnz, const int3
     p->opt = o;
     hipStream_t s = (hipStream_t)stream;
     rc = setup_dir(p->fwd, m, n, nnz, row_ptr, col_idx, val, o, s);
+    if (rc == SP_OK && !opt) {
+        // no options given: a tuned winner cached for this matrix's dispatch key
+        // (SpMV, version 0) replaces the defaults
+        sp_dispatch_key key;
+        spx::make_dispatch_key(p->fwd.prof, 0, 1, 0, &key);
+        sp_plan_options tuned;
+        if (spx::tune_cache_find(key, &tuned) && check_options_impl(tuned) == SP_OK &&
+            std::memcmp(&tuned, &o, sizeof o) != 0) {
+            o = tuned;
+            p->opt = o;
+            p->fwd = Dir{};
+            rc = setup_dir(p->fwd, m, n, nnz, row_ptr, col_idx, val, o, s);
+        }
+    }
     if (rc == SP_OK && has_t) rc = setup_dir(p->tr, n, m, nnz, col_ptr, row_idx, cval, o, s);
     if (rc != SP_OK) {
         delete p;

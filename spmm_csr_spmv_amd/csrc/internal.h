@@ -99,6 +99,11 @@ int csr_to_bsr_fill_device(int64_t m, int64_t n, const int32_t* row_ptr, const i
 int bsr_spmv_device(int64_t m, int64_t n, int32_t bs, int64_t nnzb, const int32_t* brow_ptr, const int32_t* bcol,
                     const float* bval, float alpha, const float* x, float beta, float* y, hipStream_t s);
 
+// Plan option validation (api.cpp); dispatch key and tuning cache (tune.cpp).
+int check_plan_options(const sp_plan_options& o);
+void make_dispatch_key(const sp_profile& p, int32_t transposed, int32_t N, uint64_t version, sp_dispatch_key* key);
+bool tune_cache_find(const sp_dispatch_key& key, sp_plan_options* out);
+
 // BSR SpMM (bsr.hip).
 size_t bsr_work_bytes(int64_t mb, int64_t kb, int32_t bs, int64_t nnzb, int32_t N);
 int bsr_spmm_device(int64_t mb, int64_t kb, int32_t bs, int64_t nnzb, const int32_t* brow_ptr,

@@ -162,3 +162,50 @@ def test_csr_to_bsr_and_bsr_spmv_argument_errors():
     assert L.bsr_spmv(10, 10, 4, 2, FAKE, FAKE, ctypes.c_void_p(0x1004), 1.0, FAKE, 0.0, FAKE, None) == 5
     assert L.bsr_spmv(10, 10, 4, 2, FAKE, FAKE, FAKE, 1.0, ctypes.c_void_p(0x1004), 0.0, FAKE, None) == 5
     assert L.bsr_spmv(2 ** 31, 10, 4, 2, FAKE, FAKE, FAKE, 1.0, FAKE, 0.0, FAKE, None) == 2
+
+
+def _key(**kw):
+    k = sp.sp_dispatch_key()
+    fields = dict(format=0, dtype=0, index_bits=32, transposed=0, rows=1000, cols=900, nnz=12345, N=1, arch=950,
+                  avg_len_q=14, p95_len_q=20, max_len_q=30, cv_q=6, version=0)
+    fields.update(kw)
+    for f, v in fields.items():
+        setattr(k, f, v)
+    return k
+
+
+def test_tune_cache_store_lookup_version_and_clear():
+    sp.tune_cache_clear()
+    assert sp.tune_cache_size() == 0
+    assert sp.tune_cache_lookup(_key()) is None
+    sp.tune_cache_store(_key(), use_sell=1, sell_sigma=64)
+    got = sp.tune_cache_lookup(_key())
+    assert got["use_sell"] == 1 and got["sell_sigma"] == 64 and got["group_nnz"] == 2048
+    # any differing field of the key misses: a new matrix version, another N, the transpose
+    assert sp.tune_cache_lookup(_key(version=1)) is None
+    assert sp.tune_cache_lookup(_key(N=8)) is None
+    assert sp.tune_cache_lookup(_key(transposed=1)) is None
+    sp.tune_cache_store(_key(version=1), col_panels=8, use_sell=0)
+    assert sp.tune_cache_size() == 2
+    assert sp.tune_cache_lookup(_key(version=1))["col_panels"] == 8
+    assert sp.tune_cache_lookup(_key())["use_sell"] == 1   # the other version is untouched
+    # invalid options are refused, nothing is stored
+    with pytest.raises(sp.SparseError):
+        sp.tune_cache_store(_key(version=2), col_panels=3)
+    assert sp.tune_cache_size() == 2
+    sp.tune_cache_clear()
+    assert sp.tune_cache_size() == 0 and sp.tune_cache_lookup(_key()) is None
+
+
+def test_autotune_argument_errors():
+    L = sp.lib()
+    o = sp.plan_options()
+    best, ms, b = ctypes.c_int32(), (ctypes.c_float * 4)(), SZ()
+    assert L.sp_autotune_spmv(10, 10, 5, FAKE, FAKE, FAKE, ctypes.byref(o), 0, FAKE, FAKE, 5, 0, FAKE, 1 << 20,
+                              ctypes.byref(best), ms, None) == 2       # no candidate
+    assert L.sp_autotune_spmv(10, 10, 5, FAKE, FAKE, FAKE, ctypes.byref(o), 1, FAKE, FAKE, 0, 0, FAKE, 1 << 20,
+                              ctypes.byref(best), ms, None) == 2       # no repetition
+    assert L.sp_autotune_spmv(10, 10, 5, FAKE, FAKE, FAKE, ctypes.byref(o), 1, FAKE, FAKE, 5, 0, FAKE, 1 << 20,
+                              None, ms, None) == 1
+    assert L.sp_autotune_workspace_size(10, 10, 5, FAKE, FAKE, FAKE, ctypes.byref(o), 17, ctypes.byref(b), None) == 2
+    assert L.sp_plan_dispatch_key(None, 0, 1, 0, None) == 1
