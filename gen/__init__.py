@@ -19,6 +19,7 @@ from .workloads import (  # noqa: F401
     lognormal_coo,
     block_sparse_bsr,
     block_sparse_coo,
+    clustered_coo,
     bf16_matrix,
     ragged_coo,
     dense_vector,

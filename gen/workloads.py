@@ -18,6 +18,10 @@ Each function documents the distribution it draws.  The five named workloads
                   positions (6554) drawn without replacement, every block dense
                   with N(0, 0.02) values rounded to bf16; B is 16384 x 512 bf16
                   drawn N(0, 1).
+  spmm_clustered  2^20 x 2^20, rows in windows of 64 that draw their columns
+                  from a per-window pool of 128 distinct uniform columns, row
+                  lengths floor(exp(2.5 + Z)) clipped to 128, values U[-1, 1]
+                  (the workload of the windowed SpMM); B as spmm_lognormal.
   bsr_spmv        the bsr_blocks block positions as an fp32 COO (every element
                   of every block, N(0, 0.02)), converted on the GPU to 64 x 64
                   BSR; x in U[-1, 1].
@@ -225,6 +229,32 @@ def block_sparse_coo(mb=256, kb=256, bs=64, density=0.1, std=0.02, seed=0):
     col = (bcol[:, None] * bs + c_in[None, :]).reshape(-1).astype(np.int32)
     val = _rng(seed, 52).normal(0.0, std, size=row.size).astype(np.float32)
     return Coo(mb * bs, kb * bs, row, col, val)
+
+
+def clustered_coo(m=1 << 20, n=1 << 20, H=64, pool=128, mu=2.5, sigma=1.0, seed=0, batch=1 << 14):
+    """Rows in windows of H; window w draws a pool of `pool` distinct columns
+    uniformly from [0, n); a row's length is floor(exp(mu + sigma Z)) clipped
+    to [0, pool] (the lognormal of spmm_lognormal) and its columns are that
+    many distinct members of its window's pool; values U[-1, 1]."""
+    rng = _rng(seed, 70)
+    nw = (m + H - 1) // H
+    lens = np.minimum(np.floor(np.exp(mu + sigma * rng.standard_normal(m))), pool).astype(np.int64)
+    rows, cols = [], []
+    for r0 in range(0, m, batch):
+        r1 = min(m, r0 + batch)
+        w0, w1 = r0 // H, (r1 + H - 1) // H
+        pools = np.sort(np.stack([rng.choice(n, size=pool, replace=False) for _ in range(w0, w1)]), axis=1)
+        keys = rng.random((r1 - r0, pool), dtype=np.float32)
+        pick = np.argsort(keys, axis=1)                       # a random order of the pool per row
+        take = np.arange(pool)[None, :] < lens[r0:r1, None]   # the first l of it
+        rr = np.broadcast_to(np.arange(r0, r1)[:, None], pick.shape)[take]
+        cc = pools[(rr // H) - w0, pick[take]]
+        rows.append(rr.astype(np.int32))
+        cols.append(cc.astype(np.int32))
+    row = np.concatenate(rows) if rows else np.zeros(0, np.int32)
+    col = np.concatenate(cols) if cols else np.zeros(0, np.int32)
+    val = _rng(seed, 71).uniform(-1.0, 1.0, size=row.size).astype(np.float32)
+    return Coo(m, n, row, col, val)
 
 
 def bf16_matrix(rows, cols, seed, stream=51, std=1.0):

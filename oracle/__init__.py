@@ -22,6 +22,8 @@ from .oracle import (  # noqa: F401
     csr_to_bsr,
     f32_to_bf16,
     bsr_spmv,
+    csr_to_wcsr,
+    wcsr_spmm,
     row_profile,
     sell_build,
     sell_spmv,

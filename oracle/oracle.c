@@ -25,6 +25,9 @@
  *   - BSR blocks are stored row-major inside each block.
  *   - CSR -> BSR: entries that share an element position are summed in CSR
  *     order in fp32; bf16 blocks are that sum rounded once to nearest-even.
+ *   - CSR -> WCSR: the same duplicate rule; a window's compressed columns are
+ *     ascending and padded with -1 to a multiple of `pad`; values are stored
+ *     column by column inside a window.
  *   - SELL-C-sigma: windows of sigma rows sorted by decreasing length (ties by
  *     row index), slices of C rows padded to the slice's longest row, slot k of
  *     lane j stored at slice_ptr[s] + k*C + j; padded slots hold column -1.
@@ -445,6 +448,111 @@ void oracle_bsr_spmv(int64_t m, int64_t n, int64_t bs, const int32_t* brow_ptr, 
         }
         y_out[i] = y;
         if (scale_out) scale_out[i] = sc;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* CSR -> WCSR ([ASYNC] §2.2.2: rows grouped into windows of fixed height; for */
+/* each window the union of the column indices of its rows, with the values   */
+/* of those columns stored densely; padding columns carry index -1).  Window  */
+/* w holds rows [w*H, w*H + H); its compressed columns are the distinct column */
+/* indices of those rows, ascending, followed by -1 up to a multiple of pad.  */
+/* window_ptr[w] is the first compressed column of window w.  Values are      */
+/* stored column by column: values[q*H + r] is the element (w*H + r,          */
+/* window_col[q]), the CSR entries at that position added in CSR order in    */
+/* fp32 starting from the first; 0 where there is none (padding included).   */
+/* ------------------------------------------------------------------------ */
+int64_t oracle_csr_to_wcsr_count(int64_t m, int64_t n, const int32_t* row_ptr, const int32_t* col, int64_t H,
+                                 int64_t pad, int32_t* window_ptr)
+{
+    int64_t nw = (m + H - 1) / H;
+    char* seen = (char*)calloc((size_t)(n > 0 ? n : 1), 1);
+    int64_t total = 0;
+    window_ptr[0] = 0;
+    for (int64_t w = 0; w < nw; ++w) {
+        int64_t i_end = (w + 1) * H < m ? (w + 1) * H : m;
+        int64_t count = 0;
+        for (int64_t i = w * H; i < i_end; ++i)
+            for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p)
+                if (!seen[col[p]]) {
+                    seen[col[p]] = 1;
+                    ++count;
+                }
+        for (int64_t i = w * H; i < i_end; ++i)
+            for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p) seen[col[p]] = 0;
+        total += (count + pad - 1) / pad * pad;
+        window_ptr[w + 1] = (int32_t)total;
+    }
+    free(seen);
+    return total;
+}
+
+void oracle_csr_to_wcsr_fill(int64_t m, const int32_t* row_ptr, const int32_t* col, const float* val, int64_t H,
+                             const int32_t* window_ptr, int32_t* window_col, float* values)
+{
+    int64_t nw = (m + H - 1) / H;
+    int64_t total = window_ptr[nw];
+    char* filled = (char*)calloc((size_t)(total * H > 0 ? total * H : 1), 1);
+    for (int64_t q = 0; q < total * H; ++q) values[q] = 0.0f;
+    for (int64_t w = 0; w < nw; ++w) {
+        int64_t i_end = (w + 1) * H < m ? (w + 1) * H : m;
+        int64_t ne = row_ptr[i_end] - row_ptr[w * H];
+        int32_t* cs = (int32_t*)malloc((size_t)(ne > 0 ? ne : 1) * sizeof(int32_t));
+        for (int64_t p = row_ptr[w * H]; p < row_ptr[i_end]; ++p) cs[p - row_ptr[w * H]] = col[p];
+        qsort(cs, (size_t)ne, sizeof(int32_t), cmp_i32);
+        int64_t q = window_ptr[w];
+        for (int64_t e = 0; e < ne; ++e)
+            if (e == 0 || cs[e] != cs[e - 1]) window_col[q++] = cs[e];
+        int64_t used = q;
+        while (q < window_ptr[w + 1]) window_col[q++] = -1;
+        free(cs);
+        for (int64_t i = w * H; i < i_end; ++i) {
+            for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p) {
+                int64_t lo = window_ptr[w], hi = used - 1;
+                while (lo < hi) {
+                    int64_t mid = (lo + hi) / 2;
+                    if (window_col[mid] < col[p]) lo = mid + 1; else hi = mid;
+                }
+                int64_t slot = lo * H + (i - w * H);
+                if (!filled[slot]) {
+                    values[slot] = val[p];
+                    filled[slot] = 1;
+                } else {
+                    values[slot] = values[slot] + val[p];
+                }
+            }
+        }
+    }
+    free(filled);
+}
+
+/* SpMM over the WCSR layout: C[i, c] = alpha * sum over the compressed columns
+ * q of window i / H with window_col[q] >= 0 of values[q*H + i % H] *
+ * B[window_col[q], c] + beta * C[i, c], for rows i < m; fp64 sums, scale as
+ * in oracle_spmm. */
+void oracle_wcsr_spmm(int64_t m, int64_t H, const int32_t* window_ptr, const int32_t* window_col,
+                      const float* values, int64_t N, const float* B, int64_t ldb, double alpha, double beta,
+                      const float* C_in, int64_t ldc, double* C_out, double* scale_out)
+{
+    for (int64_t i = 0; i < m; ++i) {
+        int64_t w = i / H, r = i % H;
+        for (int64_t c = 0; c < N; ++c) {
+            double s = 0.0, a = 0.0;
+            for (int64_t q = window_ptr[w]; q < window_ptr[w + 1]; ++q) {
+                if (window_col[q] < 0) continue;
+                double t = (double)values[q * H + r] * (double)B[(int64_t)window_col[q] * ldb + c];
+                s += t;
+                a += fabs(t);
+            }
+            double y = alpha * s, sc = fabs(alpha) * a;
+            if (beta != 0.0) {
+                double old = (double)C_in[i * ldc + c];
+                y += beta * old;
+                sc += fabs(beta) * fabs(old);
+            }
+            C_out[i * N + c] = y;
+            if (scale_out) scale_out[i * N + c] = sc;
+        }
     }
 }
 

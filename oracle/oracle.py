@@ -78,6 +78,12 @@ def _declare(lib):
     lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
     lib.oracle_bsr_spmv.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _d, _d, _p, _p, _p]
     lib.oracle_bsr_spmv.restype = None
+    lib.oracle_csr_to_wcsr_count.argtypes = [_i64, _i64, _p, _p, _i64, _i64, _p]
+    lib.oracle_csr_to_wcsr_count.restype = _i64
+    lib.oracle_csr_to_wcsr_fill.argtypes = [_i64, _p, _p, _p, _i64, _p, _p, _p]
+    lib.oracle_csr_to_wcsr_fill.restype = None
+    lib.oracle_wcsr_spmm.argtypes = [_i64, _i64, _p, _p, _p, _i64, _p, _i64, _d, _d, _p, _i64, _p, _p]
+    lib.oracle_wcsr_spmm.restype = None
     lib.oracle_row_profile.argtypes = [_i64, _p, _p]
     lib.oracle_row_profile.restype = None
     lib.oracle_sell_build.argtypes = [_i64, _p, _p, _p, _i64, _i64, _p, _p, _p, _p, _p]
@@ -269,6 +275,35 @@ def bsr_spmv(m, n, bs, brow_ptr, bcol, bval, x, alpha=1.0, beta=0.0, y=None):
     scale = np.empty(m, np.float64)
     lib.oracle_bsr_spmv(m, n, bs, _ptr(brow_ptr), _ptr(bcol), _ptr(bval), _ptr(x), float(alpha), float(beta),
                         _ptr(y_in), _ptr(out), _ptr(scale))
+    return out, scale
+
+
+def csr_to_wcsr(m, n, row_ptr, col, val, H, pad):
+    """CSR -> WCSR with windows of H rows: (window_ptr int32[nw+1], window_col int32[total]
+    (-1 = padding), values float32[total, H] (compressed column major))."""
+    lib = _load()
+    row_ptr, col, val = _c(row_ptr, np.int32), _c(col, np.int32), _c(val, np.float32)
+    nw = (m + H - 1) // H
+    window_ptr = np.empty(nw + 1, np.int32)
+    total = lib.oracle_csr_to_wcsr_count(m, n, _ptr(row_ptr), _ptr(col), H, pad, _ptr(window_ptr))
+    window_col = np.empty(total, np.int32)
+    values = np.empty((total, H), np.float32)
+    lib.oracle_csr_to_wcsr_fill(m, _ptr(row_ptr), _ptr(col), _ptr(val), H, _ptr(window_ptr), _ptr(window_col),
+                                _ptr(values))
+    return window_ptr, window_col, values
+
+
+def wcsr_spmm(m, H, window_ptr, window_col, values, B, alpha=1.0, beta=0.0, C=None):
+    """fp64 SpMM over the WCSR layout: (C, scale)."""
+    lib = _load()
+    window_ptr, window_col, values = _c(window_ptr, np.int32), _c(window_col, np.int32), _c(values, np.float32)
+    B = _c(B, np.float32)
+    N = B.shape[1]
+    C_in = _c(C, np.float32) if beta != 0.0 else None
+    out = np.empty((m, N), np.float64)
+    scale = np.empty((m, N), np.float64)
+    lib.oracle_wcsr_spmm(m, H, _ptr(window_ptr), _ptr(window_col), _ptr(values), N, _ptr(B), N, float(alpha),
+                         float(beta), _ptr(C_in), N, _ptr(out), _ptr(scale))
     return out, scale
 
 

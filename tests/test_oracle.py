@@ -482,3 +482,62 @@ def test_oracle_bf16_rounding_matches_generator_and_pins():
     assert h.tolist() == [0x3F80, 0x3F82, 0x7F80, 0xFF80, 0x7F80]
     nan = oracle.f32_to_bf16(np.array([np.nan], np.float32))[0]
     assert (nan & 0x7F80) == 0x7F80 and (nan & 0x7F) != 0
+
+
+# --------------------------------------------------------------------------
+# CSR -> WCSR and SpMM over it
+# --------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def five_wcsr2(golden_dir):
+    with open(os.path.join(golden_dir, "five_by_five_wcsr2.json")) as f:
+        return json.load(f)
+
+
+def test_five_csr_to_wcsr2_matches_hand_derivation(five, five_wcsr2):
+    g = five_wcsr2
+    v = five["value_of"]
+    wp, wc, vals = oracle.csr_to_wcsr(5, 5, five["csr_row_ptr"], five["csr_col"], five["csr_valf"], g["H"], g["pad"])
+    assert wp.tolist() == g["window_ptr"]
+    assert wc.tolist() == g["window_col"]
+    exp = np.array([[v[e] if isinstance(e, str) else e for e in col] for col in g["values_by_column"]], np.float32)
+    np.testing.assert_array_equal(vals, exp)
+    C, _ = oracle.wcsr_spmm(5, 2, wp, wc, vals, np.arange(1, 6, dtype=np.float32).reshape(5, 1))
+    assert C[:, 0].tolist() == [7, 6, 54, 21, 40]
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(small_coo(), st.sampled_from([1, 2, 3, 4, 8]), st.sampled_from([1, 2, 4, 8]), st.integers(0, 2 ** 31 - 1))
+def test_csr_to_wcsr_brute_force(case, H, pad, seed):
+    m, n, row, col, val = case
+    rp, c, v = oracle.coo_to_csr(m, n, row, col, val)
+    wp, wc, vals = oracle.csr_to_wcsr(m, n, rp, c, v, H, pad)
+    nw = (m + H - 1) // H
+    assert wp.size == nw + 1
+    for w in range(nw):
+        cols = sorted(set(col[(row // H) == w].tolist()))
+        seg = wc[wp[w]:wp[w + 1]].tolist()
+        # the distinct columns ascending, then -1 up to a multiple of pad
+        assert seg[:len(cols)] == cols and all(s == -1 for s in seg[len(cols):])
+        assert len(seg) % pad == 0 and len(seg) - len(cols) < pad
+    # expanding the windows gives the dense matrix (duplicates summed in fp32 in CSR order)
+    d32 = np.zeros((m, n), np.float32)
+    for i in range(m):
+        for p in range(rp[i], rp[i + 1]):
+            d32[i, c[p]] = d32[i, c[p]] + v[p]
+    e = np.zeros((nw * H, n), np.float32)
+    for w in range(nw):
+        for q in range(wp[w], wp[w + 1]):
+            if wc[q] >= 0:
+                e[w * H:(w + 1) * H, wc[q]] = vals[q]
+            else:
+                assert not vals[q].any()
+    np.testing.assert_array_equal(e[:m], d32)
+    assert not e[m:].any()
+    rng = np.random.default_rng(seed)
+    N = int(rng.integers(1, 5))
+    B = rng.integers(-4, 5, size=(n, N)).astype(np.float32)
+    C0 = rng.integers(-4, 5, size=(m, N)).astype(np.float32)
+    alpha, beta = float(rng.integers(-3, 4)), float(rng.integers(-3, 4))
+    C, sc = oracle.wcsr_spmm(m, H, wp, wc, vals, B, alpha, beta, C0)
+    np.testing.assert_array_equal(C, alpha * (d32.astype(np.float64) @ B) + beta * C0)
+    np.testing.assert_array_equal(sc, abs(alpha) * (np.abs(d32).astype(np.float64) @ np.abs(B)) + abs(beta) * np.abs(C0))
