@@ -31,6 +31,7 @@ KERNEL_SOURCES = {
     "spmm": [_CSRC + f for f in ("spmm.hip", "device_common.h", "internal.h", "api.cpp")],
     "bsr": [_CSRC + f for f in ("bsr.hip", "device_common.h", "internal.h")],
     "bsr_spmv": [_CSRC + f for f in ("bsr_convert.hip", "device_common.h", "internal.h")],
+    "wcsr": [_CSRC + f for f in ("wcsr.hip", "device_common.h", "internal.h")],
 }
 
 
@@ -88,6 +89,8 @@ def block_index_bytes_per_value(bs, idx_bytes=4):
 def kernel_family(workload):
     if workload == "bsr_spmv":
         return "bsr_spmv"
+    if workload.startswith("spmm_clustered"):
+        return "wcsr"
     return "bsr" if workload.startswith("bsr") else ("spmm" if workload.startswith("spmm") else "spmv")
 
 
@@ -123,7 +126,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="spmv_powerlaw",
-                    choices=["spmv_uniform", "spmv_powerlaw", "stencil27", "spmm_lognormal", "bsr_blocks", "bsr_spmv"])
+                    choices=["spmv_uniform", "spmv_powerlaw", "stencil27", "spmm_lognormal", "bsr_blocks", "bsr_spmv",
+                             "spmm_clustered"])
     ap.add_argument("--N", type=int, default=32, help="right-hand-side columns for spmm_lognormal")
     ap.add_argument("--graph-batch", type=int, default=-1,
                     help="steps per replay of a captured HIP graph in the timed region (0: one plain launch per "
@@ -232,6 +236,52 @@ def main():
 
         cpu_leg = (cpu_call, flops, "full passes of y = A x over the same 64 x 64-block BSR (fp32 blocks, fp64 "
                                     "accumulation, single-threaded C loop)")
+    elif cfg == "spmm_clustered":
+        coo = gen.clustered_coo(seed=0)
+        setup["generate_s"] = time.time() - t0
+        m, n, nnz = coo.m, coo.n, coo.nnz
+        N = args.N
+        d_row, d_col, d_val = (torch.from_numpy(a).cuda() for a in (coo.row, coo.col, coo.val))
+        torch.cuda.synchronize()
+        t1 = time.time()
+        rp, ci, vv = sp.csr_build_from_coo(m, n, d_row, d_col, d_val)
+        torch.cuda.synchronize()
+        setup["csr_build_from_coo_ms"] = (time.time() - t1) * 1e3
+        del d_row, d_col, d_val
+        t1 = time.time()
+        wp, wc, wv, fill = sp.csr_to_wcsr(m, n, rp, ci, vv, pad=8)
+        torch.cuda.synchronize()
+        setup["csr_to_wcsr_ms"] = (time.time() - t1) * 1e3
+        total_cols = wc.numel()
+        B = torch.from_numpy(gen.dense_matrix(n, N, 0)).cuda()
+        C = torch.empty(m, N, device="cuda")
+
+        def step():
+            sp.wcsr_spmm(m, n, wp, wc, wv, 1.0, B, 0.0, C)
+
+        out_tensor = C
+        flops = 2 * nnz * N
+        nbytes = spmm_bytes(m, n, nnz, N)
+        launches = 1
+        dtype = "f32"
+        config = dict(workload=cfg, M=m, K=n, nnz=nnz, N=N, window=64, compressed_columns=total_cols,
+                      window_fill=round(fill, 4),
+                      mfma_flops=2 * total_cols * 64 * N,
+                      wcsr_bytes=4 * total_cols * 64 + 4 * total_cols + 4 * total_cols * N + 4 * m * N)
+        bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
+        # the CSR SpMM on the same matrix, for comparison
+        plan_c = sp.Plan(m, n, rp, ci, vv, max_N=N)
+        for _ in range(3):
+            sp.spmm(plan_c, 1.0, B, 0.0, C)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            sp.spmm(plan_c, 1.0, B, 0.0, C)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        config["csr_spmm_ms_same_matrix"] = round(e0.elapsed_time(e1) / 10, 5)
+        del plan_c
+        cpu_leg = None
     else:
         coo = {"spmv_uniform": lambda: gen.uniform_rows_coo(seed=0),
                "spmv_powerlaw": lambda: gen.powerlaw_coo(seed=0),
@@ -396,7 +446,7 @@ def main():
         achieved = per_launch_bytes / (launch_ms * 1e-3) / 1e9
     else:
         achieved = per_launch_flops / (launch_ms * 1e-3) / 1e12
-    traffic = load_traffic(cfg + ("_N%d" % N if cfg == "spmm_lognormal" else ""), per_launch_bytes)
+    traffic = load_traffic(cfg + ("_N%d" % N if cfg in ("spmm_lognormal", "spmm_clustered") else ""), per_launch_bytes)
     result["roofline"] = dict(bound=bound, achieved=round(achieved, 2), peak=peak, unit=unit,
                               frac=round(achieved / peak, 4), traffic=traffic,
                               kernel_ms=round(launch_ms, 5), algorithmic_bytes_per_launch=int(per_launch_bytes),

@@ -318,6 +318,44 @@ int csr_to_bsr_fill(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, c
 int bsr_spmv(int64_t m, int64_t n, int32_t bs, int64_t nnzb, const int32_t* brow_ptr, const int32_t* bcol,
              const float* bval, float alpha, const float* x, float beta, float* y, void* stream);
 
+/* --------------------------------------------------------- windowed rows (WCSR), windowed SpMM
+ * [ASYNC] §2.2.2: rows are grouped into windows of a fixed height; per window
+ * the union of its rows' column indices is kept (padding columns carry -1)
+ * and the values of those columns are stored densely, so that a row of B is
+ * fetched once per window; [ASYNC] §4: the window's B rows are gathered into
+ * on-chip memory and its dense tile is multiplied on the matrix units.
+ *
+ * Layout (windows of 64 rows, nw = ceil(m / 64)): window_ptr[nw+1] (first
+ * compressed column of each window), window_col[total_cols] (the window's
+ * distinct columns, ascending, then -1 up to a multiple of pad), values
+ * [total_cols][64] fp32: values[q*64 + r] is row 64w + r of the window at
+ * compressed column q (entries at one position added in CSR order in fp32,
+ * starting from the first; 0 where there is none, padding included).
+ * pad in {1, 2, 4, 8, 16, 32}.  Input: a CSR with rows sorted by column.
+ *
+ * csr_to_wcsr_analyze: writes window_ptr (device), returns total_cols and the
+ * fill nnz / (total_cols * 64) (host; 1.0 when total_cols == 0); synchronises
+ * once; work >= csr_to_wcsr_bufsize() bytes.  Errors as csr_to_bsr_analyze
+ * (SP_ERR_INDEX, SP_ERR_UNSUPPORTED for unsorted rows or a bad pad, ...).
+ * csr_to_wcsr_fill: writes window_col and values (device, caller-allocated:
+ * total_cols ints and total_cols * 64 floats); never synchronises, never
+ * writes outside the ranges window_ptr gives.
+ * wcsr_spmm: C = alpha * A B + beta * C with B n x N and C m x N row-major
+ * (fp32, device); N % 4 == 0, ldb % 4 == 0, B and values 16-byte aligned;
+ * window_col and values may be NULL when total_cols == 0.  Deterministic;
+ * never allocates, never synchronises.
+ */
+int csr_to_wcsr_bufsize(int64_t m, int64_t n, int64_t nnz, size_t* bytes);
+int csr_to_wcsr_analyze(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                        int32_t pad, int32_t* window_ptr, int64_t* total_cols, double* fill,
+                        void* work, size_t work_bytes, void* stream);
+int csr_to_wcsr_fill(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                     const float* val, const int32_t* window_ptr, int64_t total_cols, int32_t* window_col,
+                     float* values, void* stream);
+int wcsr_spmm(int64_t m, int64_t n, const int32_t* window_ptr, const int32_t* window_col, const float* values,
+              int32_t N, float alpha, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
+              void* stream);
+
 /* --------------------------------------------------------- BSR SpMM
  * [BCSR] §1 and [ASYNC] §2.2.1: block row pointer brow_ptr[mb+1], block column
  * index bcol[nnzb] (increasing within a block row), and the nnzb dense

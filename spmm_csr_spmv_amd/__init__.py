@@ -3,7 +3,8 @@
 Python binding of libspmm_csr_spmv.so (C ABI in include/spmm_csr_spmv.h):
 CSR SpMV y = alpha A x + beta y, its transpose through a one-time CSC,
 CSR SpMM C = alpha A B + beta C, BSR SpMM on MFMA (bf16 in, fp32
-accumulate), CSR -> BSR with a fill-ratio gate and BSR SpMV.  All
+accumulate), CSR -> BSR with a fill-ratio gate, BSR SpMV, windowed rows
+(WCSR) with a windowed SpMM on MFMA, and a tuning cache.  All
 arithmetic runs in the library's HIP kernels; this package only marshals
 torch tensors into the C calls.  There is no CPU fallback:
 without the built library every call raises.
@@ -20,6 +21,8 @@ from ._binding import (  # noqa: F401
     csr_build_from_coo,
     csr_to_bsr,
     csr_to_csc,
+    csr_to_wcsr,
+    wcsr_spmm,
     lib,
     options_dict,
     plan_options,

@@ -24,7 +24,8 @@ EXPORTS = ("sp_status_string", "sp_version", "csr_build_from_coo_bufsize", "csr_
            "sp_plan_workspace_size", "sp_plan_bind", "sp_plan_profile", "sp_plan_destroy", "spmv", "spmv_t", "spmm",
            "csr_to_bsr_bufsize", "csr_to_bsr_analyze", "csr_to_bsr_fill", "bsr_spmv", "bsr_spmm_bufsize", "bsr_spmm",
            "sp_plan_dispatch_key", "sp_tune_cache_store", "sp_tune_cache_lookup", "sp_tune_cache_clear",
-           "sp_tune_cache_size", "sp_autotune_workspace_size", "sp_autotune_spmv")
+           "sp_tune_cache_size", "sp_autotune_workspace_size", "sp_autotune_spmv", "csr_to_wcsr_bufsize",
+           "csr_to_wcsr_analyze", "csr_to_wcsr_fill", "wcsr_spmm")
 
 
 class SparseError(RuntimeError):
@@ -100,6 +101,11 @@ def lib():
         L.csr_to_bsr_fill.argtypes = [_i64, _i64, _i64, _p, _p, _p, _i32, _p, _i64, _p, _p, _i32, _p]
         L.bsr_spmv.argtypes = [_i64, _i64, _i32, _i64, _p, _p, _p, _f, _p, _f, _p, _p]
         L.bsr_spmm_bufsize.argtypes = [_i64, _i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
+        L.csr_to_wcsr_bufsize.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
+        L.csr_to_wcsr_analyze.argtypes = [_i64, _i64, _i64, _p, _p, _i32, _p, ctypes.POINTER(_i64),
+                                          ctypes.POINTER(ctypes.c_double), _p, _sz, _p]
+        L.csr_to_wcsr_fill.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _i64, _p, _p, _p]
+        L.wcsr_spmm.argtypes = [_i64, _i64, _p, _p, _p, _i32, _f, _p, _i64, _f, _p, _i64, _p]
         _key = ctypes.POINTER(sp_dispatch_key)
         _opt = ctypes.POINTER(sp_plan_options)
         L.sp_plan_dispatch_key.argtypes = [_p, _i32, _i32, ctypes.c_uint64, _key]
@@ -213,6 +219,41 @@ def csr_to_bsr(m, n, row_ptr, col_idx, val, bs, min_fill=0.0, out="f32", stream=
            L.csr_to_bsr_fill(m, n, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(val), bs, _ptr(brow_ptr), nnzb.value,
                              _ptr(bcol), _ptr(bval), 1 if out == "bf16" else 0, _stream(stream)))
     return brow_ptr, bcol, bval, fill.value
+
+
+def csr_to_wcsr(m, n, row_ptr, col_idx, val, pad=8, stream=None):
+    """CSR (rows sorted by column) -> windowed rows of 64: (window_ptr, window_col,
+    values float32 [total_cols, 64], fill)."""
+    L = lib()
+    _dev(row_ptr, torch.int32, "row_ptr"), _dev(col_idx, torch.int32, "col_idx"), _dev(val, torch.float32, "val")
+    nnz = col_idx.numel()
+    dev = row_ptr.device
+    size = _sz()
+    _check("csr_to_wcsr_bufsize", L.csr_to_wcsr_bufsize(m, n, nnz, ctypes.byref(size)))
+    work = _workspace(size.value, dev)
+    window_ptr = torch.empty((m + 63) // 64 + 1, dtype=torch.int32, device=dev)
+    total, fill = _i64(), ctypes.c_double()
+    _check("csr_to_wcsr_analyze",
+           L.csr_to_wcsr_analyze(m, n, nnz, _ptr(row_ptr), _ptr(col_idx), int(pad), _ptr(window_ptr),
+                                 ctypes.byref(total), ctypes.byref(fill), _ptr(work), size.value, _stream(stream)))
+    window_col = torch.empty(total.value, dtype=torch.int32, device=dev)
+    values = torch.empty((total.value, 64), dtype=torch.float32, device=dev)
+    _check("csr_to_wcsr_fill",
+           L.csr_to_wcsr_fill(m, n, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(val), _ptr(window_ptr), total.value,
+                              _ptr(window_col), _ptr(values), _stream(stream)))
+    return window_ptr, window_col, values, fill.value
+
+
+def wcsr_spmm(m, n, window_ptr, window_col, values, alpha, B, beta, C, stream=None):
+    """C = alpha * A B + beta * C (in place on C) with A in windowed rows; B n x N, C m x N."""
+    _dev(window_ptr, torch.int32, "window_ptr"), _dev(window_col, torch.int32, "window_col")
+    _dev(values, torch.float32, "values"), _dev(B, torch.float32, "B"), _dev(C, torch.float32, "C")
+    N = B.shape[1]
+    if B.shape[0] != n or C.shape[0] != m or C.shape[1] != N:
+        raise ValueError("shape mismatch")
+    _check("wcsr_spmm", lib().wcsr_spmm(m, n, _ptr(window_ptr), _ptr(window_col), _ptr(values), N, float(alpha),
+                                        _ptr(B), N, float(beta), _ptr(C), N, _stream(stream)))
+    return C
 
 
 # ---------------------------------------------------------------- plan

@@ -831,6 +831,69 @@ int bsr_spmv(int64_t m, int64_t n, int32_t bs, int64_t nnzb, const int32_t* brow
     return spx::bsr_spmv_device(m, n, bs, nnzb, brow_ptr, bcol, bval, alpha, x, beta, y, (hipStream_t)stream);
 }
 
+// ------------------------------------------------------------------ CSR -> WCSR, windowed SpMM
+static bool wcsr_pad_ok(int32_t pad) { return pad == 1 || pad == 2 || pad == 4 || pad == 8 || pad == 16 || pad == 32; }
+
+int csr_to_wcsr_bufsize(int64_t m, int64_t n, int64_t nnz, size_t* bytes) {
+    if (!bytes) return SP_ERR_NULL;
+    const int rc = check_dims(m, n, nnz);
+    if (rc) return rc;
+    *bytes = spx::wcsr_convert_work_bytes(m);
+    return SP_OK;
+}
+
+int csr_to_wcsr_analyze(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx, int32_t pad,
+                        int32_t* window_ptr, int64_t* total_cols, double* fill, void* work, size_t work_bytes,
+                        void* stream) {
+    int rc = check_dims(m, n, nnz);
+    if (rc) return rc;
+    if (!wcsr_pad_ok(pad)) return SP_ERR_UNSUPPORTED;
+    if (!row_ptr || !window_ptr || !total_cols || !fill || (nnz > 0 && !col_idx)) return SP_ERR_NULL;
+    if (!work || work_bytes < spx::wcsr_convert_work_bytes(m)) return SP_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    int32_t flags = 0;
+    rc = spx::csr_to_wcsr_analyze_device(m, n, row_ptr, col_idx, pad, window_ptr, work, s, &flags);
+    if (rc != SP_OK) return rc;
+    const int64_t nw = (m + 63) / 64;
+    int32_t tail[2] = {0, 0};
+    if (hipMemcpyAsync(&tail[0], window_ptr + nw, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipMemcpyAsync(&tail[1], row_ptr + m, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return SP_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return SP_ERR_HIP;
+    if (flags & 1) return SP_ERR_INDEX;
+    if (flags & 2) return SP_ERR_UNSUPPORTED;
+    if ((int64_t)tail[1] != nnz) return SP_ERR_SIZE;
+    *total_cols = tail[0];
+    *fill = tail[0] > 0 ? (double)nnz / ((double)tail[0] * 64.0) : 1.0;
+    return SP_OK;
+}
+
+int csr_to_wcsr_fill(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                     const float* val, const int32_t* window_ptr, int64_t total_cols, int32_t* window_col,
+                     float* values, void* stream) {
+    int rc = check_dims(m, n, nnz);
+    if (rc) return rc;
+    if (total_cols < 0 || total_cols > kI32Max) return SP_ERR_SIZE;
+    if (!row_ptr || !window_ptr || (nnz > 0 && (!col_idx || !val)) || (total_cols > 0 && (!window_col || !values)))
+        return SP_ERR_NULL;
+    return spx::csr_to_wcsr_fill_device(m, n, row_ptr, col_idx, val, window_ptr, window_col, values,
+                                        (hipStream_t)stream);
+}
+
+int wcsr_spmm(int64_t m, int64_t n, const int32_t* window_ptr, const int32_t* window_col, const float* values,
+              int32_t N, float alpha, const float* B, int64_t ldb, float beta, float* C, int64_t ldc, void* stream) {
+    int rc = check_dims(m, n, 0);
+    if (rc) return rc;
+    if (N < 0 || ldb < N || ldc < N) return SP_ERR_SIZE;
+    if (m == 0 || N == 0) return SP_OK;
+    // window_col / values may be NULL when every window is empty (they are then never read)
+    if (!window_ptr || !C || (n > 0 && !B)) return SP_ERR_NULL;
+    if (N % 4 != 0 || ldb % 4 != 0) return SP_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(B) & 15) || (reinterpret_cast<uintptr_t>(values) & 15)) return SP_ERR_UNSUPPORTED;
+    return spx::wcsr_spmm_device(m, window_ptr, window_col, values, N, B, ldb, alpha, beta, C, ldc,
+                                 (hipStream_t)stream);
+}
+
 // ------------------------------------------------------------------ BSR
 int bsr_spmm_bufsize(int64_t mb, int64_t kb, int32_t bs, int64_t nnzb, int32_t N, size_t* bytes) {
     if (!bytes) return SP_ERR_NULL;

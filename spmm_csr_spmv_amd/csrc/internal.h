@@ -99,6 +99,16 @@ int csr_to_bsr_fill_device(int64_t m, int64_t n, const int32_t* row_ptr, const i
 int bsr_spmv_device(int64_t m, int64_t n, int32_t bs, int64_t nnzb, const int32_t* brow_ptr, const int32_t* bcol,
                     const float* bval, float alpha, const float* x, float beta, float* y, hipStream_t s);
 
+// CSR -> WCSR and the windowed SpMM (wcsr.hip); windows of 64 rows.
+size_t wcsr_convert_work_bytes(int64_t m);
+int csr_to_wcsr_analyze_device(int64_t m, int64_t n, const int32_t* row_ptr, const int32_t* col_idx, int32_t pad,
+                               int32_t* window_ptr, void* work, hipStream_t s, int32_t* flags_host);
+int csr_to_wcsr_fill_device(int64_t m, int64_t n, const int32_t* row_ptr, const int32_t* col_idx, const float* val,
+                            const int32_t* window_ptr, int32_t* window_col, float* values, hipStream_t s);
+int wcsr_spmm_device(int64_t m, const int32_t* window_ptr, const int32_t* window_col, const float* values,
+                     int32_t N, const float* B, int64_t ldb, float alpha, float beta, float* C, int64_t ldc,
+                     hipStream_t s);
+
 // Plan option validation (api.cpp); dispatch key and tuning cache (tune.cpp).
 int check_plan_options(const sp_plan_options& o);
 void make_dispatch_key(const sp_profile& p, int32_t transposed, int32_t N, uint64_t version, sp_dispatch_key* key);

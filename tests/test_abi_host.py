@@ -209,3 +209,23 @@ def test_autotune_argument_errors():
                               None, ms, None) == 1
     assert L.sp_autotune_workspace_size(10, 10, 5, FAKE, FAKE, FAKE, ctypes.byref(o), 17, ctypes.byref(b), None) == 2
     assert L.sp_plan_dispatch_key(None, 0, 1, 0, None) == 1
+
+
+def test_wcsr_argument_errors():
+    L = sp.lib()
+    b = SZ()
+    assert L.csr_to_wcsr_bufsize(100, 100, 50, ctypes.byref(b)) == 0 and b.value > 0
+    assert L.csr_to_wcsr_bufsize(-1, 100, 50, ctypes.byref(b)) == 2
+    tot, fill = ctypes.c_int64(), ctypes.c_double()
+    assert L.csr_to_wcsr_analyze(10, 10, 5, FAKE, FAKE, 3, FAKE, ctypes.byref(tot), ctypes.byref(fill), FAKE,
+                                 1 << 20, None) == 5                 # pad not supported
+    assert L.csr_to_wcsr_analyze(10, 10, 5, FAKE, FAKE, 8, None, ctypes.byref(tot), ctypes.byref(fill), FAKE,
+                                 1 << 20, None) == 1
+    assert L.csr_to_wcsr_analyze(10, 10, 5, FAKE, FAKE, 8, FAKE, ctypes.byref(tot), ctypes.byref(fill), None, 0,
+                                 None) == 4
+    assert L.csr_to_wcsr_fill(10, 10, 5, FAKE, FAKE, FAKE, FAKE, 8, None, FAKE, None) == 1
+    assert L.wcsr_spmm(0, 10, None, None, None, 4, 1.0, None, 4, 0.0, None, 4, None) == 0   # no rows: no-op
+    assert L.wcsr_spmm(10, 10, FAKE, FAKE, FAKE, 6, 1.0, FAKE, 6, 0.0, FAKE, 6, None) == 5  # N % 4 != 0
+    assert L.wcsr_spmm(10, 10, FAKE, FAKE, FAKE, 8, 1.0, FAKE, 4, 0.0, FAKE, 8, None) == 2  # ldb < N
+    assert L.wcsr_spmm(10, 10, FAKE, FAKE, FAKE, 8, 1.0, ctypes.c_void_p(0x1004), 8, 0.0, FAKE, 8, None) == 5
+    assert L.wcsr_spmm(10, 10, None, FAKE, FAKE, 8, 1.0, FAKE, 8, 0.0, FAKE, 8, None) == 1

@@ -82,3 +82,17 @@ def test_bsr_spmv_and_bsr_spmm_graph_replays():
         sp.bsr_spmm(6, 5, 64, brp, bcol, bval16, B, 1.0, 0.0, C)
 
     _replays_match(run, [y, C])
+
+
+def test_wcsr_spmm_graph_replays():
+    say("graph replays, WCSR")
+    coo = gen.clustered_coo(m=2000, n=30000, seed=8)
+    rp, c, v = sp.csr_build_from_coo(coo.m, coo.n, dev(coo.row), dev(coo.col), dev(coo.val))
+    wp, wc, vals, _ = sp.csr_to_wcsr(coo.m, coo.n, rp, c, v)
+    B = dev(gen.dense_matrix(coo.n, 32, 6))
+    C = torch.empty(coo.m, 32, device="cuda")
+
+    def run():
+        sp.wcsr_spmm(coo.m, coo.n, wp, wc, vals, 1.0, B, 0.0, C)
+
+    _replays_match(run, [C])
