@@ -62,13 +62,14 @@ struct Dir {
     int64_t ps_total = 0;              // stream entries, padding included
     std::vector<int4> ps_split_tasks;  // {partial index, 0, nz_begin, nz_end}
     std::vector<int4> ps_split_rows;   // {row, partial_base, nseg, 0}
+    std::vector<uint32_t> ps_skip;     // bit r of word r / 32: row r is a split row
     sp_profile prof{};
     DirDevice dev{};
     // workspace offsets (byte offsets into the bound workspace)
     mutable size_t off_tasks = 0, off_split_rows = 0, off_partials = 0, off_counters = 0;
     mutable size_t off_sell_ptr = 0, off_sell_perm = 0, off_sell_len = 0, off_sell_col = 0, off_sell_val = 0;
     mutable size_t off_ps_chunks = 0, off_ps_pk = 0, off_ps_pv = 0, off_ps_ypart = 0, off_ps_split_tasks = 0;
-    mutable size_t off_ps_split_rows = 0, off_ps_partials = 0;
+    mutable size_t off_ps_split_rows = 0, off_ps_partials = 0, off_ps_skip = 0;
 };
 
 }  // namespace
@@ -254,6 +255,8 @@ size_t dir_layout(const Dir& d, const sp_plan_options& o, int32_t max_N, size_t 
         off = align256(off + d.ps_split_rows.size() * sizeof(int4));
         d.off_ps_partials = off;
         off = align256(off + d.ps_split_tasks.size() * sizeof(float));
+        d.off_ps_skip = off;
+        off = align256(off + d.ps_skip.size() * sizeof(uint32_t));
     }
     if (d.use_sell) {
         d.off_sell_ptr = off;
@@ -340,6 +343,7 @@ int build_pstream(const std::vector<int32_t>& hptr, const sp_plan_options& o, in
     d.ps_start.clear();
     d.ps_split_tasks.clear();
     d.ps_split_rows.clear();
+    d.ps_skip.clear();
     const int64_t rows = d.rows;
     int64_t w = std::max<int64_t>(32, ((int64_t)d.cols + P - 1) / P);
     int cb = 0;
@@ -408,6 +412,8 @@ int build_pstream(const std::vector<int32_t>& hptr, const sp_plan_options& o, in
         if (pos > kI32Max) return SP_OK;
     }
     for (int32_t p = P; p <= spx::kXcds; ++p) d.ps_coff[p] = (int32_t)d.ps_chunks.size();
+    d.ps_skip.assign((size_t)((rows + 31) / 32), 0u);
+    for (const int4& sr : d.ps_split_rows) d.ps_skip[(size_t)sr.x / 32] |= 1u << (sr.x % 32);
     d.ps_total = pos;
     d.ps_P = P;
     d.ps_cb = cb;
@@ -510,6 +516,7 @@ int upload_dir(Dir& d, char* ws, const sp_plan_options& o, hipStream_t s) {
         v.ps_n_split_rows = (int32_t)d.ps_split_rows.size();
         v.ps_split_rows = reinterpret_cast<const int4*>(ws + d.off_ps_split_rows);
         v.ps_partials = reinterpret_cast<float*>(ws + d.off_ps_partials);
+        v.ps_skip = reinterpret_cast<const uint32_t*>(ws + d.off_ps_skip);
         auto up = [&](size_t off, const void* src, size_t bytes) {
             return bytes == 0 || hipMemcpyAsync(ws + off, src, bytes, hipMemcpyHostToDevice, s) == hipSuccess;
         };
@@ -517,6 +524,7 @@ int upload_dir(Dir& d, char* ws, const sp_plan_options& o, hipStream_t s) {
         if (!up(d.off_ps_chunks, d.ps_chunks.data(), d.ps_chunks.size() * sizeof(int4)) ||
             !up(d.off_ps_split_tasks, d.ps_split_tasks.data(), d.ps_split_tasks.size() * sizeof(int4)) ||
             !up(d.off_ps_split_rows, d.ps_split_rows.data(), d.ps_split_rows.size() * sizeof(int4)) ||
+            !up(d.off_ps_skip, d.ps_skip.data(), d.ps_skip.size() * sizeof(uint32_t)) ||
             !up(d.off_ps_ypart, d.ps_start.data(), d.ps_start.size() * sizeof(int32_t)))
             return SP_ERR_HIP;
         if (spx::launch_pstream_build(v, reinterpret_cast<const int32_t*>(ws + d.off_ps_ypart), s) != hipSuccess)

@@ -51,6 +51,7 @@ struct DirDevice {
     int32_t ps_n_split_rows;
     const int4* ps_split_rows;       // {row, partial_base, nseg, 0}
     float* ps_partials;
+    const uint32_t* ps_skip;         // [ceil(rows / 32)] bit r: row r is a long (split) row
     // optional SELL-C-sigma copy of the group rows
     int32_t use_sell;
     int32_t sell_slices;

@@ -33,7 +33,8 @@
 // panel, straight to y with the axpby epilogue.
 //
 // spmv_pstream_reduce_kernel: y = alpha * (ypart[0] + ... + ypart[P-1]) +
-// beta * y for the stream rows (panel order fixed), and
+// beta * y for the stream rows (panel order fixed; 16-byte loads, the long
+// rows skipped through a bitmask built at bind), and
 // y = alpha * (sum of segment partials in segment order) + beta * y for the
 // split rows.
 #include <algorithm>
@@ -278,28 +279,48 @@ __global__ __launch_bounds__(kBlock) void spmv_pstream_kernel(const PsArgs a, co
     }
 }
 
-// Rows of panel 0's chunks (which cover every stream row), then the split
-// rows, one thread each.
+// Four consecutive rows per thread: the P panel sums are read with 16-byte
+// loads and added in panel order; rows marked in `skip` (the long rows, whose
+// panel sums are never written) are left to the split part: one thread per
+// long row adds its segment partials in segment order.
 __global__ __launch_bounds__(kBlock) void spmv_pstream_reduce_kernel(
-    const int4* __restrict__ chunks0, int n_chunks0, int P, const float* __restrict__ ypart, int64_t ystride,
-    int n_split_rows, const int4* __restrict__ split_rows, const float* __restrict__ partials, float alpha,
-    float beta, float* __restrict__ y) {
+    int64_t rows, int n_row_blocks, int P, const float* __restrict__ ypart, int64_t ystride,
+    const uint32_t* __restrict__ skip, int n_split_rows, const int4* __restrict__ split_rows,
+    const float* __restrict__ partials, float alpha, float beta, float* __restrict__ y) {
     const int b = blockIdx.x;
-    if (b < n_chunks0) {
-        const int4 c = chunks0[b];
-        for (int r = c.z + (int)threadIdx.x; r < c.w; r += kBlock) {
-            float s = ypart[r];
-            for (int p = 1; p < P; ++p) s += ypart[(int64_t)p * ystride + r];
-            store_axpby(y, r, s, alpha, beta);
+    if (b < n_row_blocks) {
+        const int64_t r0 = ((int64_t)b * kBlock + threadIdx.x) * 4;
+        if (r0 >= rows) return;
+        const uint32_t bits = (skip[r0 >> 5] >> (r0 & 31)) & 15u;
+        if (r0 + 4 <= rows) {
+            float4 s = *reinterpret_cast<const float4*>(ypart + r0);
+            for (int p = 1; p < P; ++p) {
+                const float4 t = *reinterpret_cast<const float4*>(ypart + (int64_t)p * ystride + r0);
+                s.x += t.x;
+                s.y += t.y;
+                s.z += t.z;
+                s.w += t.w;
+            }
+            const float v[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (!((bits >> j) & 1u)) store_axpby(y, (int)(r0 + j), v[j], alpha, beta);
+        } else {
+            for (int64_t r = r0; r < rows; ++r) {
+                if ((bits >> (r - r0)) & 1u) continue;
+                float t = ypart[r];
+                for (int p = 1; p < P; ++p) t += ypart[(int64_t)p * ystride + r];
+                store_axpby(y, (int)r, t, alpha, beta);
+            }
         }
         return;
     }
-    const int j = (b - n_chunks0) * kBlock + (int)threadIdx.x;
+    const int j = (b - n_row_blocks) * kBlock + (int)threadIdx.x;
     if (j >= n_split_rows) return;
     const int4 sr = split_rows[j];  // {row, partial_base, nseg, 0}
-    float s = 0.0f;
-    for (int k = 0; k < sr.z; ++k) s += partials[sr.y + k];
-    store_axpby(y, sr.x, s, alpha, beta);
+    float t = 0.0f;
+    for (int k = 0; k < sr.z; ++k) t += partials[sr.y + k];
+    store_axpby(y, sr.x, t, alpha, beta);
 }
 
 // Bind time: one workgroup per chunk writes the chunk's entries (row by row,
@@ -375,12 +396,12 @@ hipError_t launch_spmv_pstream(const DirDevice& d, float alpha, const float* x, 
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    const int n_chunks0 = d.ps_P > 1 ? d.ps_coff[1] : 0;
-    const int64_t rgrid = n_chunks0 + (d.ps_n_split_rows + kBlock - 1) / kBlock;
+    const int64_t n_row_blocks = d.ps_P > 1 ? ((int64_t)d.rows + 4 * kBlock - 1) / (4 * kBlock) : 0;
+    const int64_t rgrid = n_row_blocks + (d.ps_n_split_rows + kBlock - 1) / kBlock;
     if (rgrid > 0) {
-        hipLaunchKernelGGL(spmv_pstream_reduce_kernel, dim3((unsigned)rgrid), dim3(kBlock), 0, s, d.ps_chunks,
-                           n_chunks0, d.ps_P, d.ps_ypart, d.ps_ystride, d.ps_n_split_rows, d.ps_split_rows,
-                           d.ps_partials, alpha, beta, y);
+        hipLaunchKernelGGL(spmv_pstream_reduce_kernel, dim3((unsigned)rgrid), dim3(kBlock), 0, s, (int64_t)d.rows,
+                           (int)n_row_blocks, d.ps_P, d.ps_ypart, d.ps_ystride, d.ps_skip, d.ps_n_split_rows,
+                           d.ps_split_rows, d.ps_partials, alpha, beta, y);
         return hipGetLastError();
     }
     return hipSuccess;
