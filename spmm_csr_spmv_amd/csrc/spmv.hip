@@ -168,8 +168,11 @@ __global__ __launch_bounds__(kBlock) void spmv_bins_kernel(
 __global__ __launch_bounds__(kBlock) void spmv_sell_kernel(
     int rows, int slices, const int64_t* __restrict__ slice_ptr, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ len, const int32_t* __restrict__ col, const float* __restrict__ val,
-    const float* __restrict__ x, float alpha, float beta, float* __restrict__ y) {
-    const int slice = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const float* __restrict__ x, float alpha, float beta, float* __restrict__ y, int xcd_remap) {
+    // with xcd_remap each XCD takes one contiguous run of slices, so the x
+    // lines that neighbouring rows share stay in that XCD's L2
+    const int wg = xcd_remap ? xcd_contiguous(blockIdx.x, 0, gridDim.x) : blockIdx.x;
+    const int slice = wg * 4 + (threadIdx.x >> 6);
     if (slice >= slices) return;
     const int lane = threadIdx.x & 63;
     const int k = slice * 64 + lane;
@@ -242,7 +245,7 @@ hipError_t launch_spmv(const DirDevice& d, float alpha, const float* x, float be
     if (d.use_sell && d.sell_slices > 0) {
         hipLaunchKernelGGL(spmv_sell_kernel, dim3((unsigned)((d.sell_slices + 3) / 4)), dim3(kBlock), 0, s, d.rows,
                            d.sell_slices, d.sell_slice_ptr, d.sell_perm, d.sell_len, d.sell_col, d.sell_val, x,
-                           alpha, beta, y);
+                           alpha, beta, y, d.xcd_remap);
         return hipGetLastError();
     }
     return hipSuccess;
