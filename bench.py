@@ -27,7 +27,8 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 # traffic summary is used only while these are unchanged).
 _CSRC = "spmm_csr_spmv_amd/csrc/"
 KERNEL_SOURCES = {
-    "spmv": [_CSRC + f for f in ("spmv.hip", "pstream.hip", "device_common.h", "internal.h", "api.cpp")],
+    "spmv": [_CSRC + f for f in ("spmv.hip", "pstream.hip", "xwin.hip", "seg_rows.h", "device_common.h", "internal.h",
+                                 "api.cpp")],
     "spmm": [_CSRC + f for f in ("spmm.hip", "device_common.h", "internal.h", "api.cpp")],
     "bsr": [_CSRC + f for f in ("bsr.hip", "device_common.h", "internal.h")],
     "bsr_spmv": [_CSRC + f for f in ("bsr_convert.hip", "device_common.h", "internal.h")],
@@ -326,7 +327,10 @@ def main():
                       p99=prof["p99"], max_row=prof["max_len"],
                       bins=dict(group_tasks=prof["group_tasks"], wave_rows=prof["wave_rows"],
                                 block_rows=prof["block_rows"], split_rows=prof["split_rows"],
-                                split_segments=prof["split_segments"]))
+                                split_segments=prof["split_segments"]),
+                      path="x-window stream" if prof["x_window_bits"] else
+                      ("column-panel stream" if prof["col_panels"] else
+                       ("SELL-C-sigma" if prof["sell_slots"] else "row bins")))
         if opts:
             config["plan_options"] = opts
         if tune is not None:

@@ -136,6 +136,25 @@ int csr_to_csc(int64_t m, int64_t n, int64_t nnz,
  * none; SELL and panels exclude each other.  The copy costs 8 bytes per
  * entry plus 4 bytes per row and panel of workspace, and sp_plan_create
  * reads the column indices back to the host once to cut the chunks.
+ *
+ * x-window stream ([GEN] §2.5 as above; §2.1: stage through on-chip memory;
+ * §2.4: long rows in pieces reduced in a fixed order): with x_window_bits =
+ * b in 5..15, spmv and spmv_t instead cut x into windows of 2^b columns (at
+ * most 256 windows).  A first kernel holds one window of x in LDS and forms
+ * the product of every entry of that window from a window-major copy of the
+ * matrix (column within the window as uint16, value); a second kernel reads
+ * the products of a row chunk (at most 15360 entries and 1536 rows, in order)
+ * back into LDS in CSR order and forms the row sums; rows longer than a
+ * chunk are summed in chunk-sized segments added in segment order.  No
+ * gather of x leaves LDS.  The default (-1) uses 2^15-column windows where
+ * the column-panel rule above would pick 8 panels and x has at most 2^23
+ * columns; explicit col_panels > 0 turns the automatic choice off; an
+ * explicit b wins over col_panels; SELL excludes both.  The copy costs 14
+ * bytes per entry (the products are rewritten by every call) plus small
+ * tables; sp_plan_create reads the column indices back to the host once, and
+ * returns SP_ERR_UNSUPPORTED for an explicit b that needs more than 256
+ * windows.  Column indices outside [0, n) make sp_plan_create return
+ * SP_ERR_INDEX whenever either stream is built.
  */
 typedef struct sp_plan sp_plan;
 
@@ -149,6 +168,7 @@ typedef struct sp_plan_options {
     int32_t sell_sigma;  /* sorting window in rows for SELL, >= 1 (default 1024) */
     int32_t xcd_remap;   /* 1 (default): consecutive groups go to one XCD     */
     int32_t col_panels;  /* -1 auto (default), 0 off, or 1, 2, 4, 8 panels    */
+    int32_t x_window_bits; /* -1 auto (default), 0 off, or 5..15: x windows of 2^bits columns */
 } sp_plan_options;
 
 /* Row-length profile and bin sizes of one direction of a plan. */
@@ -163,6 +183,7 @@ typedef struct sp_profile {
     int64_t split_rows, split_segments, split_nnz;
     int64_t sell_slots;          /* padded SELL slots (0 without SELL)         */
     int64_t col_panels;          /* panels of the column-panel stream (0: off)  */
+    int64_t x_window_bits;       /* window bits of the x-window stream (0: off) */
 } sp_profile;
 
 /* Fills *opt with the defaults listed above. */
@@ -176,7 +197,9 @@ int sp_plan_options_default(sp_plan_options* opt);
  * CSR products); otherwise spmv_t returns SP_ERR_UNSUPPORTED.  opt may be NULL
  * (defaults).  Copies row_ptr (and col_ptr) to the host once: synchronises
  * `stream`.  The arrays must stay alive and unchanged until sp_plan_destroy.
- * Errors: SP_ERR_NULL, SP_ERR_SIZE, SP_ERR_UNSUPPORTED (bad option), SP_ERR_HIP. */
+ * Errors: SP_ERR_NULL, SP_ERR_SIZE, SP_ERR_UNSUPPORTED (bad option or an
+ * explicit x window width that does not fit), SP_ERR_INDEX (a column index
+ * outside [0, n) seen while building a stream), SP_ERR_HIP. */
 int sp_plan_create(sp_plan** plan, int64_t m, int64_t n, int64_t nnz,
                    const int32_t* row_ptr, const int32_t* col_idx, const float* val,
                    const int32_t* col_ptr, const int32_t* row_idx, const float* cval,

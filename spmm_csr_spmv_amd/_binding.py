@@ -39,7 +39,8 @@ class SparseError(RuntimeError):
 class sp_plan_options(ctypes.Structure):
     _fields_ = [("group_nnz", ctypes.c_int32), ("wave_min", ctypes.c_int32), ("block_min", ctypes.c_int32),
                 ("split_min", ctypes.c_int32), ("split_seg", ctypes.c_int32), ("use_sell", ctypes.c_int32),
-                ("sell_sigma", ctypes.c_int32), ("xcd_remap", ctypes.c_int32), ("col_panels", ctypes.c_int32)]
+                ("sell_sigma", ctypes.c_int32), ("xcd_remap", ctypes.c_int32), ("col_panels", ctypes.c_int32),
+                ("x_window_bits", ctypes.c_int32)]
 
 
 class sp_profile(ctypes.Structure):
@@ -51,7 +52,7 @@ class sp_profile(ctypes.Structure):
                 ("wave_rows", ctypes.c_int64), ("wave_nnz", ctypes.c_int64),
                 ("block_rows", ctypes.c_int64), ("block_nnz", ctypes.c_int64),
                 ("split_rows", ctypes.c_int64), ("split_segments", ctypes.c_int64), ("split_nnz", ctypes.c_int64),
-                ("sell_slots", ctypes.c_int64), ("col_panels", ctypes.c_int64)]
+                ("sell_slots", ctypes.c_int64), ("col_panels", ctypes.c_int64), ("x_window_bits", ctypes.c_int64)]
 
 
 class sp_dispatch_key(ctypes.Structure):
@@ -324,10 +325,10 @@ def sp_plan_create(m, n, row_ptr, col_idx, val, csc=None, max_N=1, **options):
 
 
 # ---------------------------------------------------------------- tuning cache, autotune
-# The candidates timed by autotune_spmv when none are given: the plan's
-# automatic choice, the row bins alone, SELL-C-sigma, the 8-panel stream.
-DEFAULT_CANDIDATES = (dict(), dict(use_sell=0, col_panels=0), dict(use_sell=1, col_panels=0),
-                      dict(use_sell=0, col_panels=8))
+# The candidates timed by autotune_spmv when none are given: the row bins
+# alone, SELL-C-sigma, the 8-panel stream, the x-window stream (2^15 columns).
+DEFAULT_CANDIDATES = (dict(use_sell=0, col_panels=0, x_window_bits=0), dict(use_sell=1, col_panels=0, x_window_bits=0),
+                      dict(use_sell=0, col_panels=8, x_window_bits=0), dict(use_sell=0, col_panels=0, x_window_bits=15))
 
 
 def options_dict(o):

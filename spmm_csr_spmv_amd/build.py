@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libspmm_csr_spmv.so")
 
-SOURCES = ["api.cpp", "tune.cpp", "convert.hip", "spmv.hip", "pstream.hip", "spmm.hip", "bsr.hip", "bsr_convert.hip", "wcsr.hip"]
+SOURCES = ["api.cpp", "tune.cpp", "convert.hip", "spmv.hip", "pstream.hip", "spmm.hip", "bsr.hip", "bsr_convert.hip", "wcsr.hip", "xwin.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -63,6 +63,16 @@ struct Dir {
     std::vector<int4> ps_split_tasks;  // {partial index, 0, nz_begin, nz_end}
     std::vector<int4> ps_split_rows;   // {row, partial_base, nseg, 0}
     std::vector<uint32_t> ps_skip;     // bit r of word r / 32: row r is a split row
+    // x-window stream (host side; see xwin.hip)
+    int32_t xw_bits = 0, xw_nw = 0;
+    std::vector<int4> xw_chunks;       // {stream_begin, stream_end, row_begin, row_end or -(partial + 1)}
+    std::vector<int2> xw_chunk_q;      // {first CSR entry, entries}
+    std::vector<int32_t> xw_runs;      // [n_chunks][nw + 1] chunk-major run starts
+    std::vector<int32_t> xw_wm_runs;   // [n_chunks][nw] window-major run starts
+    std::vector<int4> xw_pieces;       // product workgroup slots {window | runs << 8, chunk, start, groups}
+    std::vector<int4> xw_split_rows;   // {row, partial_base, nseg, 0}
+    std::vector<int32_t> xw_pos;       // [nnz] stream position of each CSR entry
+    int64_t xw_total = 0, xw_n_partials = 0;
     sp_profile prof{};
     DirDevice dev{};
     // workspace offsets (byte offsets into the bound workspace)
@@ -70,6 +80,9 @@ struct Dir {
     mutable size_t off_sell_ptr = 0, off_sell_perm = 0, off_sell_len = 0, off_sell_col = 0, off_sell_val = 0;
     mutable size_t off_ps_chunks = 0, off_ps_pk = 0, off_ps_pv = 0, off_ps_ypart = 0, off_ps_split_tasks = 0;
     mutable size_t off_ps_split_rows = 0, off_ps_partials = 0, off_ps_skip = 0;
+    mutable size_t off_xw_pieces = 0, off_xw_wcol = 0, off_xw_wval = 0, off_xw_off = 0, off_xw_prod = 0;
+    mutable size_t off_xw_chunks = 0, off_xw_chunk_q = 0, off_xw_runs = 0, off_xw_split_rows = 0, off_xw_partials = 0;
+    mutable size_t off_xw_wm_runs = 0;
 };
 
 }  // namespace
@@ -258,6 +271,31 @@ size_t dir_layout(const Dir& d, const sp_plan_options& o, int32_t max_N, size_t 
         d.off_ps_skip = off;
         off = align256(off + d.ps_skip.size() * sizeof(uint32_t));
     }
+    if (d.xw_bits > 0) {
+        d.off_xw_pieces = off;
+        off = align256(off + d.xw_pieces.size() * sizeof(int4));
+        d.off_xw_wcol = off;
+        off = align256(off + (size_t)d.xw_total * sizeof(uint16_t));
+        d.off_xw_wval = off;
+        off = align256(off + (size_t)d.xw_total * sizeof(float));
+        d.off_xw_off = off;
+        off = align256(off + (size_t)d.xw_total * sizeof(uint16_t));
+        // products; at bind it first holds the stream position of every entry
+        d.off_xw_prod = off;
+        off = align256(off + (size_t)std::max<int64_t>(d.xw_total, d.nnz) * sizeof(float));
+        d.off_xw_chunks = off;
+        off = align256(off + d.xw_chunks.size() * sizeof(int4));
+        d.off_xw_chunk_q = off;
+        off = align256(off + d.xw_chunk_q.size() * sizeof(int2));
+        d.off_xw_runs = off;
+        off = align256(off + d.xw_runs.size() * sizeof(int32_t));
+        d.off_xw_wm_runs = off;
+        off = align256(off + d.xw_wm_runs.size() * sizeof(int32_t));
+        d.off_xw_split_rows = off;
+        off = align256(off + d.xw_split_rows.size() * sizeof(int4));
+        d.off_xw_partials = off;
+        off = align256(off + (size_t)d.xw_n_partials * sizeof(float));
+    }
     if (d.use_sell) {
         d.off_sell_ptr = off;
         off = align256(off + d.sell_slice_ptr.size() * sizeof(int64_t));
@@ -294,6 +332,9 @@ int check_options_impl(const sp_plan_options& o) {
         o.col_panels != 8)
         return SP_ERR_UNSUPPORTED;
     if (o.xcd_remap != 0 && o.xcd_remap != 1) return SP_ERR_UNSUPPORTED;
+    if (o.x_window_bits != -1 && o.x_window_bits != 0 &&
+        (o.x_window_bits < spx::kXwMinBits || o.x_window_bits > spx::kXwMaxBits))
+        return SP_ERR_UNSUPPORTED;
     return SP_OK;
 }
 
@@ -337,6 +378,19 @@ int scattered_columns(const Dir& d, hipStream_t s, int32_t* P) {
 // Needs the column indices on the host: copies them once (synchronises).
 // Leaves d.ps_P = 0 (no stream) when the panel width would exceed 2^22
 // columns or the stream would not fit int32 positions.
+// Copies the column indices of d to the host (synchronises) and checks that
+// each lies in [0, cols).
+int fetch_columns(const Dir& d, hipStream_t s, std::vector<int32_t>& hidx) {
+    hidx.resize((size_t)d.nnz);
+    if (d.nnz == 0) return SP_OK;
+    if (hipMemcpyAsync(hidx.data(), d.idx, (size_t)d.nnz * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return SP_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return SP_ERR_HIP;
+    for (const int32_t c : hidx)
+        if (c < 0 || c >= d.cols) return SP_ERR_INDEX;
+    return SP_OK;
+}
+
 int build_pstream(const std::vector<int32_t>& hptr, const sp_plan_options& o, int32_t P, Dir& d, hipStream_t s) {
     d.ps_P = 0;
     d.ps_chunks.clear();
@@ -351,13 +405,9 @@ int build_pstream(const std::vector<int32_t>& hptr, const sp_plan_options& o, in
     if (cb > 22) return SP_OK;
     const int64_t rmax = std::min<int64_t>(spx::kPsMaxRows, (int64_t)1 << (32 - cb));
     const int64_t S = std::min<int64_t>(o.split_min, spx::kPsEntries - 64);
-    std::vector<int32_t> hidx((size_t)d.nnz);
-    if (d.nnz > 0) {
-        if (hipMemcpyAsync(hidx.data(), d.idx, (size_t)d.nnz * sizeof(int32_t), hipMemcpyDeviceToHost, s) !=
-            hipSuccess)
-            return SP_ERR_HIP;
-        if (hipStreamSynchronize(s) != hipSuccess) return SP_ERR_HIP;
-    }
+    std::vector<int32_t> hidx;
+    const int rc = fetch_columns(d, s, hidx);
+    if (rc != SP_OK) return rc;
     // entries of each stream row in each panel (a stream row has at most S <= 4032 entries)
     std::vector<uint16_t> cnt((size_t)P * (size_t)rows, 0);
     std::vector<char> longrow((size_t)rows, 0);
@@ -420,6 +470,140 @@ int build_pstream(const std::vector<int32_t>& hptr, const sp_plan_options& o, in
     return SP_OK;
 }
 
+// x-window stream (xwin.hip): windows of 2^bits columns; rows cut greedily
+// into chunks of at most kXwChunk entries and kXwMaxRows rows, a row longer
+// than kXwChunk entries forming segments of its own; the stream holds the
+// chunks in order, each chunk's entries window by window (CSR order inside a
+// window) with every window's run padded to a multiple of 8 slots; a product
+// workgroup takes the runs of one window over at most kXwPieceRuns chunks
+// and kXwPiece slots, window w on XCD w mod 8.  Needs the column indices on
+// the host: copies them once (synchronises).  Returns SP_ERR_UNSUPPORTED,
+// leaving the stream off, when x needs more than kXwMaxWindows windows,
+// positions would not fit int32 or the run table would exceed 2^26 entries.
+int build_xwin(const std::vector<int32_t>& hptr, int32_t bits, Dir& d, hipStream_t s) {
+    d.xw_bits = 0;
+    d.xw_chunks.clear();
+    d.xw_chunk_q.clear();
+    d.xw_runs.clear();
+    d.xw_wm_runs.clear();
+    d.xw_pieces.clear();
+    d.xw_split_rows.clear();
+    d.xw_pos.clear();
+    d.xw_total = 0;
+    d.xw_n_partials = 0;
+    const int64_t rows = d.rows, nnz = d.nnz;
+    const int64_t nw = std::max<int64_t>(1, ((int64_t)d.cols + ((int64_t)1 << bits) - 1) >> bits);
+    if (nw > spx::kXwMaxWindows) return SP_ERR_UNSUPPORTED;
+    // row chunks, in CSR order: {q_begin, q_end, row_begin, row_end or -(partial + 1)}
+    std::vector<int4> chunks;
+    std::vector<int4> split_rows;
+    int64_t n_partials = 0;
+    {
+        int64_t rb = -1, n = 0;
+        auto close = [&](int64_t re) {
+            if (rb >= 0)
+                chunks.push_back(make_int4(hptr[(size_t)rb], hptr[(size_t)re], (int32_t)rb, (int32_t)re));
+            rb = -1;
+            n = 0;
+        };
+        for (int64_t r = 0; r < rows; ++r) {
+            const int64_t b = hptr[(size_t)r], e = hptr[(size_t)r + 1], len = e - b;
+            if (len > spx::kXwChunk) {
+                close(r);
+                const int64_t nseg = (len + spx::kXwChunk - 1) / spx::kXwChunk;
+                split_rows.push_back(make_int4((int32_t)r, (int32_t)n_partials, (int32_t)nseg, 0));
+                for (int64_t k = 0; k < nseg; ++k) {
+                    const int64_t sb = b + k * spx::kXwChunk, se = std::min<int64_t>(e, sb + spx::kXwChunk);
+                    chunks.push_back(make_int4((int32_t)sb, (int32_t)se, (int32_t)r, (int32_t)(-(n_partials + k) - 1)));
+                }
+                n_partials += nseg;
+                continue;
+            }
+            if (rb >= 0 && (n + len > spx::kXwChunk || r - rb + 1 > spx::kXwMaxRows)) close(r);
+            if (rb < 0) rb = r;
+            n += len;
+        }
+        close(rows);
+    }
+    const int64_t n_chunks = (int64_t)chunks.size();
+    if (n_chunks * (nw + 1) > ((int64_t)1 << 26)) return SP_ERR_UNSUPPORTED;
+    std::vector<int32_t> hidx;
+    const int rc = fetch_columns(d, s, hidx);
+    if (rc != SP_OK) return rc;
+    // runs (padded to multiples of 8) and the stream position of every entry
+    std::vector<int32_t> runs((size_t)(n_chunks * (nw + 1)));
+    std::vector<int32_t> pos((size_t)nnz);
+    std::vector<int32_t> cnt((size_t)nw), cur((size_t)nw);
+    std::vector<int2> chunk_q((size_t)n_chunks);
+    int64_t total = 0;
+    for (int64_t c = 0; c < n_chunks; ++c) {
+        const int4 ch = chunks[(size_t)c];
+        std::fill(cnt.begin(), cnt.end(), 0);
+        for (int32_t q = ch.x; q < ch.y; ++q) cnt[(size_t)(hidx[(size_t)q] >> bits)] += 1;
+        int32_t* row = runs.data() + (size_t)(c * (nw + 1));
+        const int64_t begin = total;
+        for (int64_t w = 0; w < nw; ++w) {
+            row[w] = (int32_t)total;
+            cur[(size_t)w] = (int32_t)total;
+            total += (cnt[(size_t)w] + 7) & ~7;
+        }
+        if (total > kI32Max) return SP_ERR_UNSUPPORTED;
+        row[nw] = (int32_t)total;
+        for (int32_t q = ch.x; q < ch.y; ++q) pos[(size_t)q] = cur[(size_t)(hidx[(size_t)q] >> bits)]++;
+        chunk_q[(size_t)c] = make_int2(ch.x, ch.y - ch.x);
+        chunks[(size_t)c].x = (int32_t)begin;
+        chunks[(size_t)c].y = (int32_t)total;
+    }
+    // window-major run starts: window after window, runs in chunk order
+    std::vector<int32_t> wm_runs((size_t)(n_chunks * nw));
+    {
+        int64_t at = 0;
+        for (int64_t w = 0; w < nw; ++w)
+            for (int64_t c = 0; c < n_chunks; ++c) {
+                wm_runs[(size_t)(c * nw + w)] = (int32_t)at;
+                at += runs[(size_t)(c * (nw + 1) + w + 1)] - runs[(size_t)(c * (nw + 1) + w)];
+            }
+    }
+    // product workgroup slots: slot 8 i + x holds the i-th piece of XCD x; a
+    // piece is the runs of one window over at most kXwPieceRuns chunks and
+    // kXwPiece slots: {window | runs << 8, first chunk, window-major start, groups of 8}
+    std::vector<std::vector<int4>> per_xcd(spx::kXcds);
+    for (int64_t w = 0; w < nw; ++w) {
+        int64_t ca = 0, acc = 0;
+        auto emit = [&](int64_t cb) {
+            if (acc > 0)
+                per_xcd[(size_t)(w % spx::kXcds)].push_back(make_int4((int32_t)(w | ((cb - ca) << 8)), (int32_t)ca,
+                                                                      wm_runs[(size_t)(ca * nw + w)], (int32_t)(acc / 8)));
+        };
+        for (int64_t c = 0; c < n_chunks; ++c) {
+            const int64_t len = runs[(size_t)(c * (nw + 1) + w + 1)] - runs[(size_t)(c * (nw + 1) + w)];
+            if (c - ca == spx::kXwPieceRuns || (acc > 0 && acc + len > spx::kXwPiece)) {
+                emit(c);
+                ca = c;
+                acc = 0;
+            }
+            acc += len;
+        }
+        emit(n_chunks);
+    }
+    size_t most = 0;
+    for (const auto& v : per_xcd) most = std::max(most, v.size());
+    d.xw_pieces.assign(most * spx::kXcds, make_int4(-1, 0, 0, 0));
+    for (size_t x = 0; x < per_xcd.size(); ++x)
+        for (size_t i = 0; i < per_xcd[x].size(); ++i) d.xw_pieces[i * spx::kXcds + x] = per_xcd[x][i];
+    d.xw_chunks = std::move(chunks);
+    d.xw_chunk_q = std::move(chunk_q);
+    d.xw_runs = std::move(runs);
+    d.xw_wm_runs = std::move(wm_runs);
+    d.xw_split_rows = std::move(split_rows);
+    d.xw_pos = std::move(pos);
+    d.xw_total = total;
+    d.xw_n_partials = n_partials;
+    d.xw_nw = (int32_t)nw;
+    d.xw_bits = bits;
+    return SP_OK;
+}
+
 int setup_dir(Dir& d, int64_t rows, int64_t cols, int64_t nnz, const int32_t* ptr, const int32_t* idx, const float* val,
               const sp_plan_options& o, hipStream_t s) {
     d.present = true;
@@ -460,11 +644,26 @@ int setup_dir(Dir& d, int64_t rows, int64_t cols, int64_t nnz, const int32_t* pt
         d.prof.sell_slots = 0;
     }
     d.ps_P = 0;
-    if (!d.use_sell && o.col_panels != 0 && d.rows > 0) {
-        int32_t P = o.col_panels;
-        if (P < 0) {
-            const int rc = scattered_columns(d, s, &P);
+    d.xw_bits = 0;
+    if (!d.use_sell && d.rows > 0) {
+        // x windows (explicit or auto) take precedence over column panels;
+        // explicit panels rule out automatic windows
+        int32_t bits = o.x_window_bits, P = o.col_panels;
+        if (bits < 0 && P > 0) bits = 0;
+        if (bits < 0 || P < 0) {
+            int32_t scattered = 0;
+            const int rc = scattered_columns(d, s, &scattered);
             if (rc != SP_OK) return rc;
+            if (bits < 0) bits = scattered > 0 ? spx::kXwMaxBits : 0;
+            if (P < 0) P = scattered;
+        }
+        if (bits > 0) {
+            const int rc = build_xwin(hptr, bits, d, s);
+            if (rc == SP_OK) {
+                P = 0;
+            } else if (!(rc == SP_ERR_UNSUPPORTED && o.x_window_bits < 0)) {
+                return rc;  // an explicit request that cannot be met, or a failure
+            }
         }
         if (P > 0) {
             const int rc = build_pstream(hptr, o, P, d, s);
@@ -472,6 +671,7 @@ int setup_dir(Dir& d, int64_t rows, int64_t cols, int64_t nnz, const int32_t* pt
         }
     }
     d.prof.col_panels = d.ps_P;
+    d.prof.x_window_bits = d.xw_bits;
     return SP_OK;
 }
 
@@ -528,6 +728,41 @@ int upload_dir(Dir& d, char* ws, const sp_plan_options& o, hipStream_t s) {
             !up(d.off_ps_ypart, d.ps_start.data(), d.ps_start.size() * sizeof(int32_t)))
             return SP_ERR_HIP;
         if (spx::launch_pstream_build(v, reinterpret_cast<const int32_t*>(ws + d.off_ps_ypart), s) != hipSuccess)
+            return SP_ERR_HIP;
+    }
+    v.xw_bits = d.xw_bits;
+    if (d.xw_bits > 0) {
+        v.xw_nw = d.xw_nw;
+        v.xw_n_pieces = (int32_t)d.xw_pieces.size();
+        v.xw_pieces = reinterpret_cast<const int4*>(ws + d.off_xw_pieces);
+        v.xw_wcol = reinterpret_cast<uint16_t*>(ws + d.off_xw_wcol);
+        v.xw_wval = reinterpret_cast<float*>(ws + d.off_xw_wval);
+        v.xw_off = reinterpret_cast<uint16_t*>(ws + d.off_xw_off);
+        v.xw_prod = reinterpret_cast<float*>(ws + d.off_xw_prod);
+        v.xw_total = d.xw_total;
+        v.xw_n_chunks = (int32_t)d.xw_chunks.size();
+        v.xw_chunks = reinterpret_cast<const int4*>(ws + d.off_xw_chunks);
+        v.xw_chunk_q = reinterpret_cast<const int2*>(ws + d.off_xw_chunk_q);
+        v.xw_runs = reinterpret_cast<const int32_t*>(ws + d.off_xw_runs);
+        v.xw_wm_runs = reinterpret_cast<const int32_t*>(ws + d.off_xw_wm_runs);
+        // the row kernel keeps two workgroups per CU, each taking every grid-th chunk
+        v.xw_row_grid = (int32_t)std::min<int64_t>((int64_t)d.xw_chunks.size(), 2 * 256);
+        v.xw_n_split_rows = (int32_t)d.xw_split_rows.size();
+        v.xw_split_rows = reinterpret_cast<const int4*>(ws + d.off_xw_split_rows);
+        v.xw_partials = reinterpret_cast<float*>(ws + d.off_xw_partials);
+        auto up = [&](size_t off, const void* src, size_t bytes) {
+            return bytes == 0 || hipMemcpyAsync(ws + off, src, bytes, hipMemcpyHostToDevice, s) == hipSuccess;
+        };
+        // the entry positions go to the product area, which the build kernel reads before any product runs
+        if (!up(d.off_xw_pieces, d.xw_pieces.data(), d.xw_pieces.size() * sizeof(int4)) ||
+            !up(d.off_xw_chunks, d.xw_chunks.data(), d.xw_chunks.size() * sizeof(int4)) ||
+            !up(d.off_xw_chunk_q, d.xw_chunk_q.data(), d.xw_chunk_q.size() * sizeof(int2)) ||
+            !up(d.off_xw_runs, d.xw_runs.data(), d.xw_runs.size() * sizeof(int32_t)) ||
+            !up(d.off_xw_wm_runs, d.xw_wm_runs.data(), d.xw_wm_runs.size() * sizeof(int32_t)) ||
+            !up(d.off_xw_split_rows, d.xw_split_rows.data(), d.xw_split_rows.size() * sizeof(int4)) ||
+            !up(d.off_xw_prod, d.xw_pos.data(), d.xw_pos.size() * sizeof(int32_t)))
+            return SP_ERR_HIP;
+        if (spx::launch_xwin_build(v, reinterpret_cast<const int32_t*>(ws + d.off_xw_prod), s) != hipSuccess)
             return SP_ERR_HIP;
     }
     if (d.use_sell) {
@@ -630,6 +865,7 @@ int sp_plan_options_default(sp_plan_options* o) {
     o->split_seg = 8192;
     o->use_sell = -1;
     o->col_panels = -1;
+    o->x_window_bits = -1;
     o->sell_sigma = 1024;
     o->xcd_remap = 1;
     return SP_OK;

@@ -16,6 +16,13 @@ constexpr int kGroupMaxRows = 1024;  // rows per group task
 constexpr int kXcds = 8;             // MI355X: workgroups go round-robin to 8 XCDs
 constexpr int kPsEntries = 4096;     // column-panel stream: entries per chunk (16 per thread)
 constexpr int kPsMaxRows = 2048;     // column-panel stream: rows per chunk (LDS row sums)
+constexpr int kXwChunk = 15360;      // x-window stream: entries per row chunk (LDS products)
+constexpr int kXwMaxRows = 1536;     // x-window stream: rows per row chunk
+constexpr int kXwMaxWindows = 256;   // x-window stream: windows of x
+constexpr int kXwMinBits = 5;        // x-window stream: narrowest window, 2^5 columns
+constexpr int kXwMaxBits = 15;       // x-window stream: widest window, 2^15 columns = 128 KB of LDS
+constexpr int kXwPiece = 32768;      // x-window stream: window entries per product workgroup
+constexpr int kXwPieceRuns = 1024;   // x-window stream: chunks per product workgroup
 
 // Task tables of one direction (A or A^T), laid out in device memory as one
 // int4 array: [split tasks | block tasks | wave tasks | group tasks].
@@ -52,6 +59,25 @@ struct DirDevice {
     const int4* ps_split_rows;       // {row, partial_base, nseg, 0}
     float* ps_partials;
     const uint32_t* ps_skip;         // [ceil(rows / 32)] bit r: row r is a long (split) row
+    // optional x-window stream (xwin.hip)
+    int32_t xw_bits;                 // 0 = off; windows of 1 << xw_bits columns
+    int32_t xw_nw;                   // windows
+    int32_t xw_n_pieces;             // product workgroups, idle slots included
+    const int4* xw_pieces;           // {window | chunks << 8, chunk_begin, window-major start, groups of 8}; -1: idle
+    uint16_t* xw_wcol;               // window-major stream: column within the window (0 in padding)
+    float* xw_wval;                  // window-major stream: value (0 in padding)
+    uint16_t* xw_off;                // chunk-major stream: position in the chunk's CSR order (0xffff: padding)
+    float* xw_prod;                  // chunk-major stream: product (written by every call)
+    const int32_t* xw_wm_runs;       // [n_chunks][nw] window-major start of chunk c's run in window w (bind only)
+    int32_t xw_row_grid;             // workgroups of the row kernel (each takes every grid-th chunk)
+    int64_t xw_total;                // stream slots
+    int32_t xw_n_chunks;
+    const int4* xw_chunks;           // {stream_begin, stream_end, row_begin, row_end or -(partial + 1)}
+    const int2* xw_chunk_q;          // {first CSR entry, entries}
+    const int32_t* xw_runs;          // [n_chunks][nw + 1] chunk-major start of chunk c's run in window w
+    int32_t xw_n_split_rows;
+    const int4* xw_split_rows;       // {row, partial_base, nseg, 0}
+    float* xw_partials;
     // optional SELL-C-sigma copy of the group rows
     int32_t use_sell;
     int32_t sell_slices;
@@ -74,6 +100,10 @@ hipError_t launch_spmv_pstream(const DirDevice& d, float alpha, const float* x, 
 // Writes the panel stream of d from start[p * rows + r] (position of row r's
 // first panel-p entry), which the caller uploaded to device memory.
 hipError_t launch_pstream_build(const DirDevice& d, const int32_t* start, hipStream_t s);
+hipError_t launch_spmv_xwin(const DirDevice& d, float alpha, const float* x, float beta, float* y, hipStream_t s);
+// Writes the stream copies of d from pos[q] (chunk-major stream position of
+// CSR entry q), which the caller uploaded.
+hipError_t launch_xwin_build(const DirDevice& d, const int32_t* pos, hipStream_t s);
 
 // Conversions: workspace sizes and the two builders (host driver in convert.hip).
 size_t coo_build_bytes(int64_t m, int64_t n, int64_t nnz);

@@ -39,13 +39,13 @@
 // split rows.
 #include <algorithm>
 
-#include "device_common.h"
+#include "seg_rows.h"
 
 namespace spx {
 
 namespace {
 
-constexpr int kRuns = kPsEntries / 4;  // 1024 runs of 4 entries per chunk
+static_assert(kPsEntries == 4 * kPassRuns, "one pass of row sums per chunk");
 
 struct PanelOffsets {
     int v[kXcds + 1];  // first chunk of each panel, v[P] = number of chunks
@@ -83,64 +83,14 @@ __device__ float segment_sum(const int32_t* __restrict__ idx, const float* __res
     return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// One run of four consecutive stream entries: rows ro[j] are non-decreasing
-// over the valid prefix j < nv.
-struct Run {
-    int fr, lr;     // first and last row offset (-1: no valid entry)
-    float hsum;     // sum of the entries of row fr
-    float tsum;     // sum of the entries of row lr
-};
-
-__device__ __forceinline__ Run make_run(const int (&ro)[4], const float (&pr)[4], int nv) {
-    Run r;
-    r.fr = nv > 0 ? ro[0] : -1;
-    r.lr = nv > 0 ? ro[nv - 1] : -1;
-    float h = 0.0f, t = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (j < nv && ro[j] == r.fr) h += pr[j];
-        if (j < nv && ro[j] == r.lr) t += pr[j];
-    }
-    r.hsum = h;
-    r.tsum = t;
-    return r;
-}
-
-// Rows strictly between fr and lr start and end inside the run: write them.
-__device__ __forceinline__ void write_middle(const int (&ro)[4], const float (&pr)[4], int nv, const Run& r,
-                                             float* ysh) {
-    if (nv < 3 || r.fr == r.lr) return;
-    // candidates: entries 1 and 2 (entry 0 has row fr, entry nv-1 row lr)
-    int cur = -1;
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 1; j < 3; ++j) {
-        const bool mid = j < nv - 1 && ro[j] != r.fr && ro[j] != r.lr;
-        if (mid) {
-            if (ro[j] != cur) {
-                if (cur >= 0) ysh[cur] = s;
-                cur = ro[j];
-                s = 0.0f;
-            }
-            s += pr[j];
-        }
-    }
-    if (cur >= 0) ysh[cur] = s;
-}
-
 __global__ __launch_bounds__(kBlock) void spmv_pstream_kernel(const PsArgs a, const float* __restrict__ x) {
     __shared__ float ysh[kPsMaxRows];
-    __shared__ int16_t frs[kRuns + 1];
-    __shared__ int16_t lrs[kRuns];
-    __shared__ float agg_h[16];
-    __shared__ int agg_m[16];
-    __shared__ float cf[17];
+    __shared__ PassScratch sc;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
     int b = blockIdx.x;
     if (b < a.n_split) {
         const int4 t = a.split_tasks[b];
-        const float s = segment_sum(a.idx, a.val, x, t.z, t.w, agg_h);
+        const float s = segment_sum(a.idx, a.val, x, t.z, t.w, sc.agg_h);
         if (tid == 0) a.partials[t.x] = s;
         return;
     }
@@ -179,7 +129,6 @@ __global__ __launch_bounds__(kBlock) void spmv_pstream_kernel(const PsArgs a, co
     }
     // rows without entries in this chunk keep the zero written here
     for (int k = tid; k < R; k += kBlock) ysh[k] = 0.0f;
-    if (tid == 0) frs[kRuns] = -1;
     __syncthreads();
     // ---- gathers of x (all issued before any product)
     float xv[4][4];
@@ -189,85 +138,14 @@ __global__ __launch_bounds__(kBlock) void spmv_pstream_kernel(const PsArgs a, co
         for (int j = 0; j < 4; ++j) xv[u][j] = j < nv[u] ? xp[pk[u][j] & cmask] : 0.0f;
     int ro[4][4];
     float pr[4][4];
-    Run run[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             ro[u][j] = (int)(pk[u][j] >> a.cb);
             pr[u][j] = pv[u][j] * xv[u][j];
         }
-        run[u] = make_run(ro[u], pr[u], nv[u]);
-        write_middle(ro[u], pr[u], nv[u], run[u], ysh);
-        frs[256 * u + tid] = (int16_t)run[u].fr;
-        lrs[256 * u + tid] = (int16_t)run[u].lr;
-    }
-    __syncthreads();  // run rows published
-
-    // ---- segmented suffix scan: C_v = hsum_v + m_v * C_{v+1}, where
-    // m_v = (run v is one row) and (run v+1 starts with that row).
-    float H[4];
-    int M[4];
-    bool link[4], cont[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int v = 256 * u + tid;
-        link[u] = run[u].lr >= 0 && frs[v + 1] == run[u].lr;
-        cont[u] = v > 0 && run[u].fr >= 0 && lrs[v - 1] == run[u].fr;
-        H[u] = run[u].hsum;
-        M[u] = (run[u].fr == run[u].lr && link[u]) ? 1 : 0;
-    }
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float h2 = __shfl_down(H[u], k, 64);
-            const int m2 = __shfl_down(M[u], k, 64);
-            if (lane + k < 64 && M[u]) {
-                H[u] += h2;
-                M[u] = m2;
-            }
-        }
-    }
-    // block B = 4u + w holds runs [64B, 64B + 64); lane 0 has its aggregate
-    if (lane == 0) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            agg_h[4 * u + w] = H[u];
-            agg_m[4 * u + w] = M[u];
-        }
-    }
-    __syncthreads();
-    if (w == 0) {
-        // the same suffix scan over the 16 block aggregates, in lanes 0..15
-        float h = lane < 16 ? agg_h[lane] : 0.0f;
-        int m = lane < 16 ? agg_m[lane] : 0;
-#pragma unroll
-        for (int k = 1; k < 16; k <<= 1) {
-            const float h2 = __shfl_down(h, k, 64);
-            const int m2 = __shfl_down(m, k, 64);
-            if (lane + k < 16 && m) {
-                h += h2;
-                m = m2;
-            }
-        }
-        if (lane < 16) cf[lane] = h;
-        if (lane == 16) cf[16] = 0.0f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int B = 4 * u + w;
-        const float after = cf[B + 1];
-        const float C = M[u] ? H[u] + after : H[u];  // C_v
-        float Cn = __shfl_down(C, 1, 64);             // C_{v+1}
-        if (lane == 63) Cn = after;
-        const Run& r = run[u];
-        if (r.fr >= 0) {
-            if (!cont[u]) ysh[r.fr] = C;                               // head row starts here
-            if (r.lr != r.fr) ysh[r.lr] = link[u] ? r.tsum + Cn : r.tsum;  // tail row starts here
-        }
-    }
+    pass_row_sums(ro, pr, nv, ysh, sc);
     __syncthreads();
     // ---- rows of the chunk: panel partials, or y itself with one panel
     const int rb = c.z;

@@ -229,6 +229,7 @@ __global__ __launch_bounds__(kBlock) void sell_fill_kernel(
 }  // namespace
 
 hipError_t launch_spmv(const DirDevice& d, float alpha, const float* x, float beta, float* y, hipStream_t s) {
+    if (d.xw_bits > 0) return launch_spmv_xwin(d, alpha, x, beta, y, s);
     if (d.ps_P > 0) return launch_spmv_pstream(d, alpha, x, beta, y, s);
     const int n_wave_wg = (d.n_wave + 3) / 4;
     const int n_group = d.use_sell ? 0 : d.n_group;

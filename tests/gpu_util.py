@@ -28,6 +28,9 @@ BINS = {
     "ps2_split": dict(use_sell=0, col_panels=2, wave_min=8, block_min=40, split_min=100, split_seg=32),
     "ps4": dict(use_sell=0, col_panels=4),
     "ps8_split": dict(use_sell=0, col_panels=8, wave_min=8, block_min=20, split_min=40, split_seg=16),
+    # x-window stream (products with x windows in LDS, then row sums in CSR order)
+    "xw8": dict(use_sell=0, x_window_bits=8),
+    "xw15": dict(use_sell=0, x_window_bits=15),
 }
 
 

@@ -43,7 +43,7 @@ def test_status_strings_and_version():
 def test_option_defaults():
     o = sp.plan_options()
     assert (o.group_nnz, o.wave_min, o.block_min, o.split_min, o.split_seg) == (2048, 256, 4096, 32768, 8192)
-    assert (o.use_sell, o.sell_sigma, o.xcd_remap, o.col_panels) == (-1, 1024, 1, -1)
+    assert (o.use_sell, o.sell_sigma, o.xcd_remap, o.col_panels, o.x_window_bits) == (-1, 1024, 1, -1, -1)
 
 
 SZ = ctypes.c_size_t
@@ -83,7 +83,8 @@ def test_conversion_argument_errors():
 @pytest.mark.parametrize("field,value", [("group_nnz", 32), ("group_nnz", 8192), ("wave_min", 5000),
                                          ("block_min", 10), ("split_min", 100), ("split_seg", 8),
                                          ("use_sell", 2), ("use_sell", -2), ("sell_sigma", 0), ("xcd_remap", 3),
-                                         ("col_panels", 3), ("col_panels", 16), ("col_panels", -2)])
+                                         ("col_panels", 3), ("col_panels", 16), ("col_panels", -2),
+                                         ("x_window_bits", 4), ("x_window_bits", 16), ("x_window_bits", -2)])
 def test_plan_rejects_bad_options(field, value):
     L = sp.lib()
     o = sp.plan_options()

@@ -40,6 +40,7 @@ def _replays_match(run, outs, replays=3):
 
 @pytest.mark.parametrize("bins", [dict(), dict(use_sell=0, col_panels=4, wave_min=8, block_min=20, split_min=40,
                                                split_seg=16), dict(use_sell=1, sell_sigma=64),
+                                  dict(use_sell=0, x_window_bits=6),
                                   dict(wave_min=0, block_min=0, split_min=0, split_seg=16)])
 def test_spmv_spmv_t_spmm_graph_replays(bins):
     say("graph replays", bins)

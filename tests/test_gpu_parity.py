@@ -140,7 +140,7 @@ def test_spmv_and_transpose(name, bins):
         assert_close(host(z), ref_t, scale_t, what="spmv_t %s %s a=%g b=%g" % (name, bins, alpha, beta))
 
 
-@pytest.mark.parametrize("bins", ["default", "all_split", "mixed_small", "sell", "ps4", "ps8_split"])
+@pytest.mark.parametrize("bins", ["default", "all_split", "mixed_small", "sell", "ps4", "ps8_split", "xw8"])
 def test_spmv_bitwise_deterministic(bins):
     say("determinism", bins)
     coo, _, _ = case("ragged_long")
@@ -171,11 +171,12 @@ def test_profile_matches_oracle(name):
         assert got["group_nnz"] + got["wave_nnz"] + got["block_nnz"] + got["split_nnz"] == ptr[-1]
 
 
-def test_panels_with_concentrated_columns():
-    """Forced panels on a matrix whose columns all sit in the first panel (the
-    other panels hold no entries, only zero row sums), then on spread columns:
-    both stay exact."""
-    say("panels, concentrated and spread columns")
+@pytest.mark.parametrize("opts", [dict(use_sell=0, col_panels=4), dict(use_sell=0, x_window_bits=10)])
+def test_panels_with_concentrated_columns(opts):
+    """Forced panels (or x windows) on a matrix whose columns all sit in the
+    first panel (the others hold no entries, only zero row sums), then on
+    spread columns: both stay exact."""
+    say("panels / windows, concentrated and spread columns", opts)
     rng = np.random.default_rng(3)
     m, n = 20000, 100000
     row = np.repeat(np.arange(m, dtype=np.int32), 20)
@@ -184,12 +185,26 @@ def test_panels_with_concentrated_columns():
     for hi in (1000, n):
         col = rng.integers(0, hi, size=row.size).astype(np.int32)
         rp, c, v = oracle.coo_to_csr(m, n, row, col, val)
-        plan = sp.Plan(m, n, dev(rp), dev(c), dev(v), use_sell=0, col_panels=4)
-        assert plan.profile()["col_panels"] == 4
+        plan = sp.Plan(m, n, dev(rp), dev(c), dev(v), **opts)
+        prof = plan.profile()
+        assert (prof["col_panels"], prof["x_window_bits"]) == (opts.get("col_panels", 0), opts.get("x_window_bits", 0))
         y = torch.zeros(m, device="cuda")
         sp.spmv(plan, 1.0, dev(x), 0.0, y)
         ref, scale = oracle.spmv(rp, c, v, x)
         assert_close(host(y), ref, scale, what="panels, columns below %d" % hi)
+
+
+def test_x_windows_profile_and_limits():
+    """The x-window stream reports its width; an explicit width that needs
+    more than 256 windows is refused, the automatic choice never is."""
+    say("x windows: profile and window limit")
+    coo, (rp, c, v), _ = case("wide_m_ne_n")  # 20000 columns
+    g = (dev(rp), dev(c), dev(v))
+    assert sp.Plan(coo.m, coo.n, *g, use_sell=0, x_window_bits=7).profile()["x_window_bits"] == 7
+    with pytest.raises(sp.SparseError) as e:
+        sp.Plan(coo.m, coo.n, *g, use_sell=0, x_window_bits=6)  # 313 windows
+    assert e.value.code == 5
+    assert sp.Plan(coo.m, coo.n, *g).profile()["x_window_bits"] == 0  # x of 80 KB: no stream
 
 
 # ------------------------------------------------------------------ SpMM
