@@ -69,7 +69,8 @@ struct Dir {
     std::vector<int2> xw_chunk_q;      // {first CSR entry, entries}
     std::vector<int32_t> xw_runs;      // [n_chunks][nw + 1] chunk-major run starts
     std::vector<int32_t> xw_wm_runs;   // [n_chunks][nw] window-major run starts
-    std::vector<int4> xw_pieces;       // product workgroup slots {window | runs << 8, chunk, start, groups}
+    std::vector<int4> xw_pieces;       // {window | runs << 8, chunk, start, groups}, by XCD, window order
+    std::vector<int2> xw_prod_ranges;  // [kXwProdGrid] pieces of each product workgroup
     std::vector<int4> xw_split_rows;   // {row, partial_base, nseg, 0}
     std::vector<int32_t> xw_pos;       // [nnz] stream position of each CSR entry
     int64_t xw_total = 0, xw_n_partials = 0;
@@ -82,7 +83,7 @@ struct Dir {
     mutable size_t off_ps_split_rows = 0, off_ps_partials = 0, off_ps_skip = 0;
     mutable size_t off_xw_pieces = 0, off_xw_wcol = 0, off_xw_wval = 0, off_xw_off = 0, off_xw_prod = 0;
     mutable size_t off_xw_chunks = 0, off_xw_chunk_q = 0, off_xw_runs = 0, off_xw_split_rows = 0, off_xw_partials = 0;
-    mutable size_t off_xw_wm_runs = 0;
+    mutable size_t off_xw_wm_runs = 0, off_xw_prod_ranges = 0;
 };
 
 }  // namespace
@@ -274,6 +275,8 @@ size_t dir_layout(const Dir& d, const sp_plan_options& o, int32_t max_N, size_t 
     if (d.xw_bits > 0) {
         d.off_xw_pieces = off;
         off = align256(off + d.xw_pieces.size() * sizeof(int4));
+        d.off_xw_prod_ranges = off;
+        off = align256(off + d.xw_prod_ranges.size() * sizeof(int2));
         d.off_xw_wcol = off;
         off = align256(off + (size_t)d.xw_total * sizeof(uint16_t));
         d.off_xw_wval = off;
@@ -487,6 +490,7 @@ int build_xwin(const std::vector<int32_t>& hptr, int32_t bits, Dir& d, hipStream
     d.xw_runs.clear();
     d.xw_wm_runs.clear();
     d.xw_pieces.clear();
+    d.xw_prod_ranges.clear();
     d.xw_split_rows.clear();
     d.xw_pos.clear();
     d.xw_total = 0;
@@ -564,33 +568,53 @@ int build_xwin(const std::vector<int32_t>& hptr, int32_t bits, Dir& d, hipStream
                 at += runs[(size_t)(c * (nw + 1) + w + 1)] - runs[(size_t)(c * (nw + 1) + w)];
             }
     }
-    // product workgroup slots: slot 8 i + x holds the i-th piece of XCD x; a
-    // piece is the runs of one window over at most kXwPieceRuns chunks and
-    // kXwPiece slots: {window | runs << 8, first chunk, window-major start, groups of 8}
-    std::vector<std::vector<int4>> per_xcd(spx::kXcds);
-    for (int64_t w = 0; w < nw; ++w) {
-        int64_t ca = 0, acc = 0;
-        auto emit = [&](int64_t cb) {
-            if (acc > 0)
-                per_xcd[(size_t)(w % spx::kXcds)].push_back(make_int4((int32_t)(w | ((cb - ca) << 8)), (int32_t)ca,
-                                                                      wm_runs[(size_t)(ca * nw + w)], (int32_t)(acc / 8)));
-        };
-        for (int64_t c = 0; c < n_chunks; ++c) {
-            const int64_t len = runs[(size_t)(c * (nw + 1) + w + 1)] - runs[(size_t)(c * (nw + 1) + w)];
-            if (c - ca == spx::kXwPieceRuns || (acc > 0 && acc + len > spx::kXwPiece)) {
-                emit(c);
-                ca = c;
-                acc = 0;
+    // pieces: the runs of one window over at most kXwPieceRuns chunks and
+    // kXwPiece slots, {window | runs << 8, first chunk, window-major start,
+    // groups of 8}; listed XCD by XCD (window w on XCD w mod 8), windows in
+    // order; each XCD's list is cut into kXwProdGrid / 8 contiguous shares of
+    // about equal slot counts, one per product workgroup (workgroup b on XCD
+    // b mod 8)
+    constexpr int64_t kPerXcd = spx::kXwProdGrid / spx::kXcds;
+    std::vector<int4> pieces;
+    std::vector<int2> ranges((size_t)spx::kXwProdGrid, make_int2(0, 0));
+    for (int64_t xcd = 0; xcd < spx::kXcds; ++xcd) {
+        const size_t first = pieces.size();
+        int64_t slots = 0;
+        for (int64_t w = xcd; w < nw; w += spx::kXcds) {
+            int64_t ca = 0, acc = 0;
+            auto emit = [&](int64_t cb) {
+                if (acc > 0) {
+                    pieces.push_back(make_int4((int32_t)(w | ((cb - ca) << 8)), (int32_t)ca,
+                                               wm_runs[(size_t)(ca * nw + w)], (int32_t)(acc / 8)));
+                    slots += acc;
+                }
+            };
+            for (int64_t c = 0; c < n_chunks; ++c) {
+                const int64_t len = runs[(size_t)(c * (nw + 1) + w + 1)] - runs[(size_t)(c * (nw + 1) + w)];
+                if (c - ca == spx::kXwPieceRuns || (acc > 0 && acc + len > spx::kXwPiece)) {
+                    emit(c);
+                    ca = c;
+                    acc = 0;
+                }
+                acc += len;
             }
-            acc += len;
+            emit(n_chunks);
         }
-        emit(n_chunks);
+        // share i ends where the running slot count first reaches (i + 1) / kPerXcd of the XCD's slots
+        size_t at = first;
+        int64_t run = 0;
+        for (int64_t i = 0; i < kPerXcd; ++i) {
+            const size_t b0 = at;
+            const int64_t target = slots * (i + 1) / kPerXcd;
+            while (at < pieces.size() && (run < target || i == kPerXcd - 1)) {
+                run += (int64_t)pieces[at].w * 8;
+                ++at;
+            }
+            ranges[(size_t)(i * spx::kXcds + xcd)] = make_int2((int32_t)b0, (int32_t)at);
+        }
     }
-    size_t most = 0;
-    for (const auto& v : per_xcd) most = std::max(most, v.size());
-    d.xw_pieces.assign(most * spx::kXcds, make_int4(-1, 0, 0, 0));
-    for (size_t x = 0; x < per_xcd.size(); ++x)
-        for (size_t i = 0; i < per_xcd[x].size(); ++i) d.xw_pieces[i * spx::kXcds + x] = per_xcd[x][i];
+    d.xw_pieces = std::move(pieces);
+    d.xw_prod_ranges = std::move(ranges);
     d.xw_chunks = std::move(chunks);
     d.xw_chunk_q = std::move(chunk_q);
     d.xw_runs = std::move(runs);
@@ -734,6 +758,7 @@ int upload_dir(Dir& d, char* ws, const sp_plan_options& o, hipStream_t s) {
     if (d.xw_bits > 0) {
         v.xw_nw = d.xw_nw;
         v.xw_n_pieces = (int32_t)d.xw_pieces.size();
+        v.xw_prod_ranges = reinterpret_cast<const int2*>(ws + d.off_xw_prod_ranges);
         v.xw_pieces = reinterpret_cast<const int4*>(ws + d.off_xw_pieces);
         v.xw_wcol = reinterpret_cast<uint16_t*>(ws + d.off_xw_wcol);
         v.xw_wval = reinterpret_cast<float*>(ws + d.off_xw_wval);
@@ -755,6 +780,7 @@ int upload_dir(Dir& d, char* ws, const sp_plan_options& o, hipStream_t s) {
         };
         // the entry positions go to the product area, which the build kernel reads before any product runs
         if (!up(d.off_xw_pieces, d.xw_pieces.data(), d.xw_pieces.size() * sizeof(int4)) ||
+            !up(d.off_xw_prod_ranges, d.xw_prod_ranges.data(), d.xw_prod_ranges.size() * sizeof(int2)) ||
             !up(d.off_xw_chunks, d.xw_chunks.data(), d.xw_chunks.size() * sizeof(int4)) ||
             !up(d.off_xw_chunk_q, d.xw_chunk_q.data(), d.xw_chunk_q.size() * sizeof(int2)) ||
             !up(d.off_xw_runs, d.xw_runs.data(), d.xw_runs.size() * sizeof(int32_t)) ||

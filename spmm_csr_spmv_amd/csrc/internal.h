@@ -23,6 +23,7 @@ constexpr int kXwMinBits = 5;        // x-window stream: narrowest window, 2^5 c
 constexpr int kXwMaxBits = 15;       // x-window stream: widest window, 2^15 columns = 128 KB of LDS
 constexpr int kXwPiece = 32768;      // x-window stream: window entries per product workgroup
 constexpr int kXwPieceRuns = 1024;   // x-window stream: chunks per product workgroup
+constexpr int kXwProdGrid = 256;     // x-window stream: product workgroups (one per CU, 32 per XCD)
 
 // Task tables of one direction (A or A^T), laid out in device memory as one
 // int4 array: [split tasks | block tasks | wave tasks | group tasks].
@@ -62,8 +63,9 @@ struct DirDevice {
     // optional x-window stream (xwin.hip)
     int32_t xw_bits;                 // 0 = off; windows of 1 << xw_bits columns
     int32_t xw_nw;                   // windows
-    int32_t xw_n_pieces;             // product workgroups, idle slots included
-    const int4* xw_pieces;           // {window | chunks << 8, chunk_begin, window-major start, groups of 8}; -1: idle
+    const int4* xw_pieces;           // {window | chunks << 8, chunk_begin, window-major start, groups of 8}
+    const int2* xw_prod_ranges;      // [kXwProdGrid] pieces of each product workgroup (by XCD, window order)
+    int32_t xw_n_pieces;
     uint16_t* xw_wcol;               // window-major stream: column within the window (0 in padding)
     float* xw_wval;                  // window-major stream: value (0 in padding)
     uint16_t* xw_off;                // chunk-major stream: position in the chunk's CSR order (0xffff: padding)

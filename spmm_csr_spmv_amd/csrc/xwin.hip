@@ -26,18 +26,21 @@
 //   * window-major stream (column within the window as uint16, value):
 //     window after window, the window's runs in chunk order.
 //
-// xw_products_kernel (1024 threads, one window of x in LDS): a piece is the
-//   runs of one window over at most kXwPieceRuns consecutive chunks and
-//   kXwPiece slots, one contiguous stretch of the window-major stream.  Each
-//   thread loads its 4 groups of 8 slots (16-byte loads) before waiting for
-//   anything, forms value * x[window + column], finds the group's run by a
-//   branchless binary search over the piece's run table in LDS, and stores
-//   the 8 products at their chunk-major place.  Every piece of window w runs
-//   on XCD w mod 8, so the window's x is read from HBM once and from that
-//   XCD's L2 afterwards.
+// xw_products_kernel (1024 threads, one window of x in LDS, one workgroup
+//   per CU): a piece is the runs of one window over at most kXwPieceRuns
+//   consecutive chunks and kXwPiece slots, one contiguous stretch of the
+//   window-major stream.  The pieces of window w run on XCD w mod 8 (the
+//   window's x is read from HBM once, then from that XCD's L2); each
+//   workgroup takes a contiguous share of its XCD's pieces, in window order,
+//   and refills x only when the window changes.  Each thread holds 4 groups
+//   of 8 slots of a piece in registers (16-byte loads, issued while the
+//   previous piece is processed), forms value * x[window + column], finds
+//   the group's run by a branchless binary search over the piece's run table
+//   in LDS, and stores the 8 products at their chunk-major place.
 // xw_rows_kernel (256 threads, two workgroups per CU, each taking every
 //   grid-th chunk): the chunk's stream slice and row starts are loaded into
-//   registers while the previous chunk is being summed; each product is
+//   registers while the previous chunk is being scattered and summed (each
+//   register is refilled as soon as its value is consumed); each product is
 //   stored in LDS at its CSR position; then thread t adds the products of
 //   its slice of about n/256 consecutive entries in order (rows found
 //   through a bitmap of row starts and its per-word prefix counts), writes
@@ -64,9 +67,11 @@ static_assert(kXwPieceRuns <= kXwProdThreads, "one thread per run in the piece t
 static_assert(kXwMaxWindows <= 256 && kXwPieceRuns < (1 << 23), "piece descriptor packs window and run count");
 constexpr int kXwProdGroups = kXwPiece / 8 / kXwProdThreads;  // groups of 8 slots per thread and piece
 static_assert(kXwProdGroups * 8 * kXwProdThreads == kXwPiece, "a piece is whole groups per thread");
-// registers per thread for one chunk of the row kernel
-constexpr int kXwSpanLoads = (kXwChunk + 7 * kXwMaxWindows + 4 * kBlock - 1) / (4 * kBlock);
-constexpr int kXwRowLoads = (kXwMaxRows + 1 + kBlock - 1) / kBlock;
+// row kernel: threads per workgroup, and registers per thread for one chunk
+constexpr int kXwRowThreads = 256;
+constexpr int kXwSpanLoads = (kXwChunk + 7 * kXwMaxWindows + 4 * kXwRowThreads - 1) / (4 * kXwRowThreads);
+constexpr int kXwRowLoads = (kXwMaxRows + 1 + kXwRowThreads - 1) / kXwRowThreads;
+constexpr int kXwWordsPerThread = (kXwWords + kXwRowThreads - 1) / kXwRowThreads;  // prefix count
 
 // Exclusive sum over the workgroup (NT threads) of one value per thread; `tot`
 // receives the wave totals.  Contains one barrier.
@@ -94,21 +99,27 @@ __device__ __forceinline__ int row_rank(const uint32_t* rbits, const int16_t* wp
     return (int)wpre[e >> 5] + __popc(rbits[e >> 5] & m) - 1;
 }
 
+template <int NT>
 struct ChunkScratch {
-    int16_t frs[kBlock + 1];  // first row (rank) of each slice, -1 if empty; [kBlock] = -1
-    int16_t lrs[kBlock];      // last row of each slice
-    float agg_h[4];
-    int agg_m[4];
-    float cf[5];
+    int16_t frs[NT + 1];  // first row (rank) of each slice, -1 if empty; [NT] = -1
+    int16_t lrs[NT];      // last row of each slice
+    float agg_h[NT / 64];
+    int agg_m[NT / 64];
+    float cf[NT / 64 + 1];
 };
 
 // Row sums of the n <= kXwChunk products in ps (CSR order), written to
-// ysh[rank] for every non-empty row of the chunk.  Thread t owns entries
-// [t E, t E + E), E = ceil(n / 256) rounded up to a multiple of 4.
+// ysh[rank] for every non-empty row of the chunk, by a workgroup of NT
+// threads.  Thread t owns entries [t E, t E + E), E = ceil(n / NT) rounded up
+// to a multiple of 4.  ysh holds kXwMaxRows rows and then one slot per lane:
+// every entry stores to the completed row or, when no row completes there,
+// to the lane's own slot, so the loop has no branches.
+template <int NT>
 __device__ __forceinline__ void chunk_row_sums(const float* ps, int n, const uint32_t* rbits, const int16_t* wpre,
-                                               float* ysh, ChunkScratch& s) {
+                                               float* ysh, ChunkScratch<NT>& s) {
+    constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int E = (((n + kBlock - 1) / kBlock) + 3) & ~3;
+    const int E = (((n + NT - 1) / NT) + 3) & ~3;
     const int e0 = min(n, tid * E), e1 = min(n, e0 + E);
     int fr = -1, lr = -1;
     float hsum = 0.0f, tsum = 0.0f;
@@ -117,25 +128,32 @@ __device__ __forceinline__ void chunk_row_sums(const float* ps, int n, const uin
         fr = r;
         bool head = true;
         float acc = 0.0f;
-        for (int e = e0; e < e1; e += 4) {
-            // e is a multiple of 4 below n <= kXwChunk: the 16-byte read stays in ps
-            const float4 v = *reinterpret_cast<const float4*>(ps + e);
-            const uint32_t bw = rbits[e >> 5] >> (e & 31);
-            const float vv[4] = {v.x, v.y, v.z, v.w};
+        const int sink = kXwMaxRows + lane;
+        for (int eb = e0; eb < e1; eb += 16) {
+            // four 16-byte reads in flight; each e is a multiple of 4 below
+            // kXwChunk, so the reads stay in ps (values past e1 are not used)
+            float4 v[4];
+            uint32_t bw[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (e + j < e1) {
-                    if (((bw >> j) & 1u) && e + j > e0) {  // a row starts: the current one is complete here
-                        if (head) {
-                            hsum = acc;
-                            head = false;
-                        } else {
-                            ysh[r] = acc;  // starts and ends inside the slice
-                        }
-                        ++r;
-                        acc = 0.0f;
-                    }
-                    acc += vv[j];
+            for (int i = 0; i < 4; ++i) {
+                const int e = min(eb + 4 * i, kXwChunk - 4);
+                v[i] = *reinterpret_cast<const float4*>(ps + e);
+                bw[i] = rbits[e >> 5] >> (e & 31);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float vv[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int e = eb + 4 * i + j;
+                    const bool valid = e < e1;
+                    // a row starts at e: the current one is complete (the head row is kept for the scan)
+                    const bool st = valid && ((bw[i] >> j) & 1u) && e > e0;
+                    ysh[st && !head ? r : sink] = acc;
+                    hsum = st && head ? acc : hsum;
+                    head = head && !st;
+                    r += st ? 1 : 0;
+                    acc = st ? vv[j] : (valid ? acc + vv[j] : acc);
                 }
             }
         }
@@ -145,7 +163,7 @@ __device__ __forceinline__ void chunk_row_sums(const float* ps, int n, const uin
     }
     s.frs[tid] = (int16_t)fr;
     s.lrs[tid] = (int16_t)lr;
-    if (tid == 0) s.frs[kBlock] = -1;
+    if (tid == 0) s.frs[NT] = -1;
     __syncthreads();
     // segmented suffix scan over slices: C_t = hsum_t + m_t C_{t+1}, where
     // m_t = (slice t is one row) and (slice t + 1 starts inside that row)
@@ -169,8 +187,8 @@ __device__ __forceinline__ void chunk_row_sums(const float* ps, int n, const uin
     __syncthreads();
     if (tid == 0) {
         float c = 0.0f;
-        s.cf[4] = 0.0f;
-        for (int b = 3; b >= 0; --b) {
+        s.cf[NW] = 0.0f;
+        for (int b = NW - 1; b >= 0; --b) {
             c = s.agg_m[b] ? s.agg_h[b] + c : s.agg_h[b];
             s.cf[b] = c;
         }
@@ -186,78 +204,115 @@ __device__ __forceinline__ void chunk_row_sums(const float* ps, int n, const uin
     }
 }
 
+// Loads of one piece for one thread: its groups of 8 window-major slots
+// (16-byte loads) and its entry of the piece's run table.
+struct PieceRegs {
+    v4u32 k[kXwProdGroups];
+    v4f32 a0[kXwProdGroups], a1[kXwProdGroups];
+    int run_start, run_groups;
+};
+
+__device__ __forceinline__ void group_fetch(const int4& pc, int u, const uint16_t* __restrict__ wcol,
+                                            const float* __restrict__ wval, PieceRegs& r) {
+    const int g = threadIdx.x + kXwProdThreads * u;
+    if (g < pc.w) {
+        const int p = pc.z + 8 * g;
+        r.k[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(wcol + p));
+        r.a0[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f32*>(wval + p));
+        r.a1[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f32*>(wval + p + 4));
+    } else {
+        r.k[u] = v4u32{0u, 0u, 0u, 0u};
+        r.a0[u] = v4f32{0.0f, 0.0f, 0.0f, 0.0f};
+        r.a1[u] = r.a0[u];
+    }
+}
+
+__device__ __forceinline__ void runs_fetch(const int4& pc, const int32_t* __restrict__ runs, int nw, PieceRegs& r) {
+    const int tid = threadIdx.x;
+    const int w = pc.x & 255, nr = pc.x >> 8, ca = pc.y;
+    r.run_start = 0;
+    r.run_groups = 0;
+    if (tid < nr) {
+        const int32_t* q = runs + (int64_t)(ca + tid) * (nw + 1) + w;
+        r.run_start = q[0];
+        r.run_groups = (q[1] - r.run_start) >> 3;  // runs are whole groups of 8
+    }
+}
+
+// One workgroup per CU (grid 8 x 32): workgroup b takes the pieces
+// [ranges[b].x, ranges[b].y), all of XCD b mod 8 and in window order, so x is
+// refilled only when the window changes; the next piece's loads are issued
+// before the current piece's products are formed.
 __global__ __launch_bounds__(kXwProdThreads) void xw_products_kernel(
-    const int4* __restrict__ pieces, const int32_t* __restrict__ runs, int nw, int bits, int64_t cols,
-    const float* __restrict__ x, const uint16_t* __restrict__ wcol, const float* __restrict__ wval,
-    float* __restrict__ prod) {
+    const int4* __restrict__ pieces, const int2* __restrict__ ranges, const int32_t* __restrict__ runs, int nw,
+    int bits, int64_t cols, const float* __restrict__ x, const uint16_t* __restrict__ wcol,
+    const float* __restrict__ wval, float* __restrict__ prod) {
     __shared__ __attribute__((aligned(16))) float xs[1 << kXwMaxBits];
     __shared__ int rs[kXwPieceRuns];      // chunk-major start of each run of the piece
     __shared__ int gp[kXwPieceRuns + 1];  // groups of 8 slots before each run
     __shared__ int tot[kXwProdThreads / 64];
-    const int4 pc = pieces[blockIdx.x];   // {window | runs << 8, first chunk, window-major start, groups}
-    if (pc.x < 0) return;                 // idle slot
+    const int2 rg = ranges[blockIdx.x];
+    if (rg.x >= rg.y) return;
     const int tid = threadIdx.x;
-    const int w = pc.x & 255, nr = pc.x >> 8, ca = pc.y, src0 = pc.z, G = pc.w;  // 1 <= nr <= kXwPieceRuns
-    // the piece's slots: group g = tid + 1024 u holds window-major slots src0 + 8g .. src0 + 8g + 7
-    v4u32 k[kXwProdGroups];
-    v4f32 a0[kXwProdGroups], a1[kXwProdGroups];
-#pragma unroll
-    for (int u = 0; u < kXwProdGroups; ++u) {
-        const int g = tid + kXwProdThreads * u;
-        if (g < G) {
-            const int p = src0 + 8 * g;
-            k[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(wcol + p));
-            a0[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f32*>(wval + p));
-            a1[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f32*>(wval + p + 4));
-        } else {
-            k[u] = v4u32{0u, 0u, 0u, 0u};
-            a0[u] = v4f32{0.0f, 0.0f, 0.0f, 0.0f};
-            a1[u] = a0[u];
-        }
-    }
-    int groups = 0;
-    if (tid < nr) {
-        const int32_t* r = runs + (int64_t)(ca + tid) * (nw + 1) + w;
-        const int s = r[0];
-        rs[tid] = s;
-        groups = (r[1] - s) >> 3;  // runs are whole groups of 8
-    }
     const int W = 1 << bits;
-    const int64_t c0 = (int64_t)w << bits;
-    const int nx = (int)min((int64_t)W, cols - c0);
-    const float* __restrict__ xw = x + c0;
-    if (nx == W && (reinterpret_cast<uintptr_t>(xw) & 15) == 0) {
-        for (int j = tid; j < W / 4; j += kXwProdThreads)
-            reinterpret_cast<float4*>(xs)[j] = reinterpret_cast<const float4*>(xw)[j];
-    } else {
-        for (int j = tid; j < nx; j += kXwProdThreads) xs[j] = xw[j];
+    PieceRegs cur;
+    {
+        const int4 p0 = pieces[rg.x];
+#pragma unroll
+        for (int u = 0; u < kXwProdGroups; ++u) group_fetch(p0, u, wcol, wval, cur);
+        runs_fetch(p0, runs, nw, cur);
     }
-    const int ex = block_exclusive_sum<kXwProdThreads>(groups, tot);
-    if (tid < nr) gp[tid] = ex;
-    if (tid == nr - 1) gp[nr] = ex + groups;  // == G
-    __syncthreads();  // x window and run table in LDS
-    // group g lies in the last run c with gp[c] <= g (empty runs share their
-    // successor's gp); every column read is below nx (padding has column 0)
+    int loaded = -1;  // window held in xs
+    for (int pi = rg.x; pi < rg.y; ++pi) {
+        const int4 pc = pieces[pi];  // {window | runs << 8, first chunk, window-major start, groups}
+        const int w = pc.x & 255, nr = pc.x >> 8, G = pc.w;  // 1 <= nr <= kXwPieceRuns
+        __syncthreads();  // the previous piece is done with xs, rs and gp
+        if (w != loaded) {
+            const int64_t c0 = (int64_t)w << bits;
+            const int nx = (int)min((int64_t)W, cols - c0);
+            const float* __restrict__ xw = x + c0;
+            if (nx == W && (reinterpret_cast<uintptr_t>(xw) & 15) == 0) {
+                for (int j = tid; j < W / 4; j += kXwProdThreads)
+                    reinterpret_cast<float4*>(xs)[j] = reinterpret_cast<const float4*>(xw)[j];
+            } else {
+                for (int j = tid; j < nx; j += kXwProdThreads) xs[j] = xw[j];
+            }
+            loaded = w;
+        }
+        if (tid < nr) rs[tid] = cur.run_start;
+        const int ex = block_exclusive_sum<kXwProdThreads>(cur.run_groups, tot);
+        if (tid < nr) gp[tid] = ex;
+        if (tid == nr - 1) gp[nr] = ex + cur.run_groups;  // == G
+        __syncthreads();  // x window and run table in LDS
+        // the next piece's loads go into the registers as they are consumed
+        const bool more = pi + 1 < rg.y;
+        const int4 pn = more ? pieces[pi + 1] : make_int4(0, 0, 0, 0);
+        if (more) runs_fetch(pn, runs, nw, cur);
+        // group g lies in the last run c with gp[c] <= g (empty runs share
+        // their successor's gp); every column read is below the window's
+        // width (padding has column 0)
 #pragma unroll
-    for (int u = 0; u < kXwProdGroups; ++u) {
-        const int g = tid + kXwProdThreads * u;
-        int lo = 0;
+        for (int u = 0; u < kXwProdGroups; ++u) {
+            const int g = tid + kXwProdThreads * u;
+            int lo = 0;
 #pragma unroll
-        for (int step = kXwPieceRuns / 2; step > 0; step >>= 1)
-            if (lo + step < nr && gp[lo + step] <= g) lo += step;
-        v4f32 q0, q1;
-        q0.x = a0[u].x * xs[k[u].x & 0xffffu];
-        q0.y = a0[u].y * xs[k[u].x >> 16];
-        q0.z = a0[u].z * xs[k[u].y & 0xffffu];
-        q0.w = a0[u].w * xs[k[u].y >> 16];
-        q1.x = a1[u].x * xs[k[u].z & 0xffffu];
-        q1.y = a1[u].y * xs[k[u].z >> 16];
-        q1.z = a1[u].z * xs[k[u].w & 0xffffu];
-        q1.w = a1[u].w * xs[k[u].w >> 16];
-        if (g < G) {
-            const int d = rs[lo] + 8 * (g - gp[lo]);
-            *reinterpret_cast<v4f32*>(prod + d) = q0;
-            *reinterpret_cast<v4f32*>(prod + d + 4) = q1;
+            for (int step = kXwPieceRuns / 2; step > 0; step >>= 1)
+                if (lo + step < nr && gp[lo + step] <= g) lo += step;
+            v4f32 q0, q1;
+            q0.x = cur.a0[u].x * xs[cur.k[u].x & 0xffffu];
+            q0.y = cur.a0[u].y * xs[cur.k[u].x >> 16];
+            q0.z = cur.a0[u].z * xs[cur.k[u].y & 0xffffu];
+            q0.w = cur.a0[u].w * xs[cur.k[u].y >> 16];
+            q1.x = cur.a1[u].x * xs[cur.k[u].z & 0xffffu];
+            q1.y = cur.a1[u].y * xs[cur.k[u].z >> 16];
+            q1.z = cur.a1[u].z * xs[cur.k[u].w & 0xffffu];
+            q1.w = cur.a1[u].w * xs[cur.k[u].w >> 16];
+            if (more) group_fetch(pn, u, wcol, wval, cur);
+            if (g < G) {
+                const int d = rs[lo] + 8 * (g - gp[lo]);
+                *reinterpret_cast<v4f32*>(prod + d) = q0;
+                *reinterpret_cast<v4f32*>(prod + d + 4) = q1;
+            }
         }
     }
 }
@@ -274,46 +329,53 @@ struct XwRowArgs {
     float alpha, beta;
 };
 
-__global__ __launch_bounds__(kBlock) void xw_rows_kernel(const XwRowArgs a) {
-    __shared__ __attribute__((aligned(16))) float ps[kXwChunk];  // the chunk's products in CSR order
-    __shared__ float ysh[kXwMaxRows];                            // row sums by rank of non-empty row
+__global__ __launch_bounds__(kXwRowThreads) void xw_rows_kernel(const XwRowArgs a) {
+    // the chunk's products in CSR order, then one slot per lane that takes the padding
+    __shared__ __attribute__((aligned(16))) float ps[kXwChunk + 64];
+    __shared__ float ysh[kXwMaxRows + 64];                       // row sums by rank of non-empty row, lane slots
     __shared__ int16_t rp[kXwMaxRows + 1];                       // local row starts
-    __shared__ uint32_t rbits[kXwWords];                         // bit e: entry e starts a row
+    __shared__ uint32_t rbits[kXwWords + 64];                    // bit e: entry e starts a row; lane words
     __shared__ int16_t wpre[kXwWords];                           // row starts before each word
-    __shared__ int tot[4];
-    __shared__ ChunkScratch sc;
+    __shared__ int tot[kXwRowThreads / 64];
+    __shared__ ChunkScratch<kXwRowThreads> sc;
     const int tid = threadIdx.x;
 
     // one chunk's stream slice (4 slots per load) and row starts, in registers
     v4f32 pv[kXwSpanLoads];
     uint2 po[kXwSpanLoads];
     int rpv[kXwRowLoads];
-    auto fetch = [&](int ci) {
-        const int4 c = a.chunks[ci];
-        const int span = c.y - c.x;  // a multiple of 8
-#pragma unroll
-        for (int j = 0; j < kXwSpanLoads; ++j) {
-            const int f = 4 * tid + 4 * kBlock * j;
-            if (f < span) {
-                pv[j] = __builtin_nontemporal_load(reinterpret_cast<const v4f32*>(a.prod + c.x + f));
-                po[j] = *reinterpret_cast<const uint2*>(a.off + c.x + f);
-            } else {
-                po[j] = make_uint2(0xffffffffu, 0xffffffffu);
-            }
+    // slot j of chunk c: stream slots 4 tid + 4 NT j .. + 3; row start k = tid + NT j
+    auto fetch_slot = [&](const int4& c, int j) {
+        const int f = 4 * tid + 4 * kXwRowThreads * j;
+        if (f < c.y - c.x) {  // the span is a multiple of 8
+            pv[j] = __builtin_nontemporal_load(reinterpret_cast<const v4f32*>(a.prod + c.x + f));
+            po[j] = *reinterpret_cast<const uint2*>(a.off + c.x + f);
+        } else {
+            po[j] = make_uint2(0xffffffffu, 0xffffffffu);
         }
+    };
+    auto fetch_rows = [&](const int4& c) {
         const int R = c.w < 0 ? 0 : c.w - c.z;  // segments need no row starts
 #pragma unroll
         for (int j = 0; j < kXwRowLoads; ++j) {
-            const int k = tid + kBlock * j;
+            const int k = tid + kXwRowThreads * j;
             rpv[j] = k <= R && c.w >= 0 ? a.ptr[c.z + k] : 0;
         }
     };
 
     int ci = blockIdx.x;
-    if (ci < a.n_chunks) fetch(ci);
+    if (ci < a.n_chunks) {
+        const int4 c0 = a.chunks[ci];
+#pragma unroll
+        for (int j = 0; j < kXwSpanLoads; ++j) fetch_slot(c0, j);
+        fetch_rows(c0);
+    }
     for (; ci < a.n_chunks; ci += gridDim.x) {
         const int4 c = a.chunks[ci];  // {stream_begin, stream_end, row_begin, row_end or -(partial + 1)}
         const int2 qn = a.chunk_q[ci];
+        // the next chunk's loads go into the registers as soon as they are consumed
+        const bool more = ci + (int)gridDim.x < a.n_chunks;
+        const int4 cn = more ? a.chunks[ci + gridDim.x] : make_int4(0, 0, 0, -1);
         const int rb = c.z, q0 = qn.x, n = qn.y;
         const bool seg = c.w < 0;  // a segment of one long row
         const int R = seg ? 1 : c.w - rb;
@@ -322,51 +384,78 @@ __global__ __launch_bounds__(kBlock) void xw_rows_kernel(const XwRowArgs a) {
         // ---- local row starts and the bitmap of row starts
 #pragma unroll
         for (int j = 0; j < kXwRowLoads; ++j) {
-            const int k = tid + kBlock * j;
+            const int k = tid + kXwRowThreads * j;
             if (k <= R) rp[k] = (int16_t)(seg ? (k == 0 ? 0 : n) : rpv[j] - q0);
         }
-        for (int k = tid; k < nwords; k += kBlock) rbits[k] = 0u;
+        if (more) fetch_rows(cn);
+        for (int k = tid; k < nwords; k += kXwRowThreads) rbits[k] = 0u;
         __syncthreads();
-        for (int k = tid; k < R; k += kBlock) {
-            const int b0 = rp[k];
-            if (rp[k + 1] > b0) atomicOr(&rbits[b0 >> 5], 1u << (b0 & 31));
+        {  // mark the first entry of every non-empty row (reads first, then the atomics)
+            int b0[kXwRowLoads], b1[kXwRowLoads];
+#pragma unroll
+            for (int j = 0; j < kXwRowLoads; ++j) {
+                const int k = tid + kXwRowThreads * j;
+                b0[j] = k < R ? rp[k] : 0;
+                b1[j] = k < R ? rp[k + 1] : 0;
+            }
+#pragma unroll
+            for (int j = 0; j < kXwRowLoads; ++j)
+                atomicOr(&rbits[b1[j] > b0[j] ? b0[j] >> 5 : kXwWords + (tid & 63)], 1u << (b0[j] & 31));
         }
         // ---- the chunk's products into CSR order; the positions are a
-        // permutation of 0..n-1 plus padding, so no two stores meet
+        // permutation of 0..n-1 plus padding, which goes to the lane's own
+        // slot past the chunk, so no two stores of a wave meet
+        const uint32_t sink = kXwChunk + (tid & 63);
 #pragma unroll
         for (int j = 0; j < kXwSpanLoads; ++j) {
             const uint32_t o0 = po[j].x & 0xffffu, o1 = po[j].x >> 16, o2 = po[j].y & 0xffffu, o3 = po[j].y >> 16;
-            if (o0 != kXwPad) ps[o0] = pv[j].x;
-            if (o1 != kXwPad) ps[o1] = pv[j].y;
-            if (o2 != kXwPad) ps[o2] = pv[j].z;
-            if (o3 != kXwPad) ps[o3] = pv[j].w;
+            ps[o0 != kXwPad ? o0 : sink] = pv[j].x;
+            ps[o1 != kXwPad ? o1 : sink] = pv[j].y;
+            ps[o2 != kXwPad ? o2 : sink] = pv[j].z;
+            ps[o3 != kXwPad ? o3 : sink] = pv[j].w;
+            if (more) fetch_slot(cn, j);
         }
         __syncthreads();
-        {  // prefix counts of row starts per bitmap word, two words per thread
-            const int k0 = 2 * tid, k1 = 2 * tid + 1;
-            const int t0 = k0 < nwords ? __popc(rbits[k0]) : 0;
-            const int t1 = k1 < nwords ? __popc(rbits[k1]) : 0;
-            const int e0 = block_exclusive_sum<kBlock>(t0 + t1, tot);
-            if (k0 < nwords) wpre[k0] = (int16_t)e0;
-            if (k1 < nwords) wpre[k1] = (int16_t)(e0 + t0);
+        {  // prefix counts of row starts per bitmap word, consecutive words per thread
+            int cnt[kXwWordsPerThread], sum = 0;
+#pragma unroll
+            for (int j = 0; j < kXwWordsPerThread; ++j) {
+                const int k = kXwWordsPerThread * tid + j;
+                cnt[j] = k < nwords ? __popc(rbits[k]) : 0;
+                sum += cnt[j];
+            }
+            int e = block_exclusive_sum<kXwRowThreads>(sum, tot);
+#pragma unroll
+            for (int j = 0; j < kXwWordsPerThread; ++j) {
+                const int k = kXwWordsPerThread * tid + j;
+                if (k < nwords) wpre[k] = (int16_t)e;
+                e += cnt[j];
+            }
         }
         __syncthreads();
-        // ---- the next chunk's loads stay in flight through the row sums
-        if (ci + (int)gridDim.x < a.n_chunks) fetch(ci + gridDim.x);
         chunk_row_sums(ps, n, rbits, wpre, ysh, sc);
         __syncthreads();
         // ---- outputs
         if (seg) {
             if (tid == 0) a.partials[-c.w - 1] = ysh[0];
         } else {
-            for (int k = tid; k < R; k += kBlock) {
-                const int b0 = rp[k];
-                const float v = rp[k + 1] > b0 ? ysh[row_rank(rbits, wpre, b0)] : 0.0f;
-                store_axpby(a.y, rb + k, v, a.alpha, a.beta);
+            float v[kXwRowLoads];
+#pragma unroll
+            for (int j = 0; j < kXwRowLoads; ++j) {
+                const int k = tid + kXwRowThreads * j;
+                const int b0 = k < R ? rp[k] : 0;
+                const bool ne = k < R && rp[k + 1] > b0;
+                v[j] = ne ? ysh[row_rank(rbits, wpre, b0)] : 0.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < kXwRowLoads; ++j) {
+                const int k = tid + kXwRowThreads * j;
+                if (k < R) store_axpby(a.y, rb + k, v[j], a.alpha, a.beta);
             }
         }
         __syncthreads();  // LDS is reused by the next chunk
     }
+
 }
 
 // One thread per long row: its segment partials added in segment order.
@@ -433,9 +522,9 @@ hipError_t launch_xwin_build(const DirDevice& d, const int32_t* pos, hipStream_t
 
 hipError_t launch_spmv_xwin(const DirDevice& d, float alpha, const float* x, float beta, float* y, hipStream_t s) {
     if (d.xw_n_pieces > 0) {
-        hipLaunchKernelGGL(xw_products_kernel, dim3((unsigned)d.xw_n_pieces), dim3(kXwProdThreads), 0, s,
-                           d.xw_pieces, d.xw_runs, d.xw_nw, d.xw_bits, (int64_t)d.cols, x, d.xw_wcol, d.xw_wval,
-                           d.xw_prod);
+        hipLaunchKernelGGL(xw_products_kernel, dim3((unsigned)kXwProdGrid), dim3(kXwProdThreads), 0, s,
+                           d.xw_pieces, d.xw_prod_ranges, d.xw_runs, d.xw_nw, d.xw_bits, (int64_t)d.cols, x, d.xw_wcol,
+                           d.xw_wval, d.xw_prod);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -451,7 +540,7 @@ hipError_t launch_spmv_xwin(const DirDevice& d, float alpha, const float* x, flo
         a.y = y;
         a.alpha = alpha;
         a.beta = beta;
-        hipLaunchKernelGGL(xw_rows_kernel, dim3((unsigned)d.xw_row_grid), dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL(xw_rows_kernel, dim3((unsigned)d.xw_row_grid), dim3(kXwRowThreads), 0, s, a);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
