@@ -112,8 +112,11 @@ struct ChunkScratch {
 // ysh[rank] for every non-empty row of the chunk, by a workgroup of NT
 // threads.  Thread t owns entries [t E, t E + E), E = ceil(n / NT) rounded up
 // to a multiple of 4.  ysh holds kXwMaxRows rows and then one slot per lane:
-// every entry stores to the completed row or, when no row completes there,
-// to the lane's own slot, so the loop has no branches.
+// every entry stores the running sum to the row that ends before it or, when
+// no row ends there, to the lane's own slot, so the loop has no branches.
+// The first and last rows of a slice may continue in the neighbouring
+// slices; their parts are combined by a segmented suffix scan over slices
+// and written after it, over anything the loop stored for them.
 template <int NT>
 __device__ __forceinline__ void chunk_row_sums(const float* ps, int n, const uint32_t* rbits, const int16_t* wpre,
                                                float* ysh, ChunkScratch<NT>& s) {
@@ -124,41 +127,41 @@ __device__ __forceinline__ void chunk_row_sums(const float* ps, int n, const uin
     int fr = -1, lr = -1;
     float hsum = 0.0f, tsum = 0.0f;
     if (e0 < e1) {
-        int r = row_rank(rbits, wpre, e0);
-        fr = r;
-        bool head = true;
+        const int r0 = row_rank(rbits, wpre, e0);
+        int r = r0;
         float acc = 0.0f;
         const int sink = kXwMaxRows + lane;
         for (int eb = e0; eb < e1; eb += 16) {
             // four 16-byte reads in flight; each e is a multiple of 4 below
-            // kXwChunk, so the reads stay in ps (values past e1 are not used)
+            // kXwChunk, so the reads stay in ps (values past e1 are zeroed)
             float4 v[4];
-            uint32_t bw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const float4*>(ps + min(eb + 4 * i, kXwChunk - 4));
+            // row starts at eb..eb+15 (bit j), without entry e0 and past e1
+            const int wd = eb >> 5, sh = eb & 31;
+            const uint32_t lo = rbits[wd], hi = rbits[min(wd + 1, kXwWords - 1)];
+            uint32_t m = (lo >> sh) | (sh ? hi << (32 - sh) : 0u);
+            const int nv = min(e1 - eb, 16);
+            m &= (nv >= 16 ? 0xffffu : ((1u << nv) - 1u)) & (eb == e0 ? ~1u : ~0u);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int e = min(eb + 4 * i, kXwChunk - 4);
-                v[i] = *reinterpret_cast<const float4*>(ps + e);
-                bw[i] = rbits[e >> 5] >> (e & 31);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float vv[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+                const float vv[4] = {4 * i + 0 < nv ? v[i].x : 0.0f, 4 * i + 1 < nv ? v[i].y : 0.0f,
+                                     4 * i + 2 < nv ? v[i].z : 0.0f, 4 * i + 3 < nv ? v[i].w : 0.0f};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int e = eb + 4 * i + j;
-                    const bool valid = e < e1;
-                    // a row starts at e: the current one is complete (the head row is kept for the scan)
-                    const bool st = valid && ((bw[i] >> j) & 1u) && e > e0;
-                    ysh[st && !head ? r : sink] = acc;
-                    hsum = st && head ? acc : hsum;
-                    head = head && !st;
+                    // a row starts here: the current one is complete (kept in LDS)
+                    const bool st = (m >> (4 * i + j)) & 1u;
+                    ysh[st ? r : sink] = acc;
                     r += st ? 1 : 0;
-                    acc = st ? vv[j] : (valid ? acc + vv[j] : acc);
+                    acc = st ? vv[j] : acc + vv[j];
                 }
             }
         }
+        fr = r0;
         lr = r;
-        if (head) hsum = acc;
+        // the first row's part in this slice: stored in the loop if that row
+        // ended inside the slice (its final value is written after the scan)
+        hsum = r > r0 ? ysh[r0] : acc;
         tsum = acc;
     }
     s.frs[tid] = (int16_t)fr;
