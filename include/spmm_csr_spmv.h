@@ -119,7 +119,10 @@ int csr_to_csc(int64_t m, int64_t n, int64_t nnz,
  * use_sell = -1 (the default) picks SELL when every row has at most 64
  * entries, rows average at least 4 entries and the padded slots exceed the
  * entries by at most 20 % ([GEN] §4 rule table: short regular rows, padding
- * checked first); use_sell = 0 never uses it.
+ * checked first); use_sell = 0 never uses it.  sp_plan_bind stores the SELL
+ * columns as int16 offsets from the row when every SELL entry lies within
+ * 32767 of its row (banded matrices: 6 instead of 8 bytes per slot), else
+ * as int32 columns.
  *
  * Column-panel stream ([GEN] §2.5: random x gathers are the real cost once
  * x is much larger than the cache; §2.4: split long rows, reduce the pieces in

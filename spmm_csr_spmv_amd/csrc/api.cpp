@@ -808,6 +808,15 @@ int upload_dir(Dir& d, char* ws, const sp_plan_options& o, hipStream_t s) {
              hipMemcpyAsync(ws + d.off_sell_len, d.sell_len.data(), d.sell_len.size() * sizeof(int32_t),
                             hipMemcpyHostToDevice, s) != hipSuccess))
             return SP_ERR_HIP;
+        // int16 column offsets when every SELL column lies within 32767 of its row
+        // (the slot area is sized for int32 columns either way)
+        int32_t* most = reinterpret_cast<int32_t*>(ws + 64);
+        int32_t hmost = 0;
+        if (spx::launch_fill_i32(most, 1, 0, s) != hipSuccess || spx::launch_sell_offset(v, most, s) != hipSuccess ||
+            hipMemcpyAsync(&hmost, most, sizeof hmost, hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+            return SP_ERR_HIP;
+        v.sell_narrow = hmost <= 32767 ? 1 : 0;
         if (spx::launch_sell_fill(v, d.sell_slots, reinterpret_cast<int32_t*>(ws + d.off_sell_col),
                                   reinterpret_cast<float*>(ws + d.off_sell_val), s) != hipSuccess)
             return SP_ERR_HIP;

@@ -86,7 +86,8 @@ struct DirDevice {
     const int64_t* sell_slice_ptr;   // [slices + 1]
     const int32_t* sell_perm;        // [rows]  sorted position -> row
     const int32_t* sell_len;         // [rows]  length at sorted position, -1 = row served elsewhere
-    const int32_t* sell_col;         // [slots]
+    const int32_t* sell_col;         // [slots] columns, or int16 column - row when sell_narrow
+    int32_t sell_narrow;             // 1: every SELL column lies within 32767 of its row
     const float* sell_val;           // [slots]
 };
 
@@ -97,6 +98,8 @@ hipError_t launch_spmm(const DirDevice& d, int32_t N, float alpha, const float* 
                        float beta, float* C, int64_t ldc, hipStream_t s);
 hipError_t launch_sell_fill(const DirDevice& d, int64_t slots, int32_t* sell_col, float* sell_val,
                             hipStream_t s);
+// Largest |column - row| over the SELL rows, atomically maxed into *out (set to 0 first).
+hipError_t launch_sell_offset(const DirDevice& d, int32_t* out, hipStream_t s);
 hipError_t launch_spmv_pstream(const DirDevice& d, float alpha, const float* x, float beta, float* y,
                                hipStream_t s);
 // Writes the panel stream of d from start[p * rows + r] (position of row r's

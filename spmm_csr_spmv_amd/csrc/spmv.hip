@@ -11,6 +11,8 @@
 // Every bin streams values and column indices with 16-byte loads, gathers x,
 // and fuses the axpby epilogue y = alpha*acc + beta*y into its single store
 // (「CUDA LSMR 专栏（二）」 §5.2); beta == 0 never reads y.
+#include <algorithm>
+
 #include "device_common.h"
 
 namespace spx {
@@ -164,10 +166,13 @@ __global__ __launch_bounds__(kBlock) void spmv_bins_kernel(
 // (「通用稀疏矩阵乘法CUDA算子实现」 §1.4; the slot layout of
 // 「稀疏矩阵存储格式…」 §4 with slot t of all lanes adjacent.)  Lanes whose
 // row is served by another bin (length -1) do nothing; padding is skipped by
-// the length test, never multiplied.
+// the length test, never multiplied.  Col is the column itself (int32) or,
+// when every stored column lies within 32767 of its row (banded matrices),
+// the offset column - row (int16), which cuts 2 of the 8 bytes per slot.
+template <typename Col>
 __global__ __launch_bounds__(kBlock) void spmv_sell_kernel(
     int rows, int slices, const int64_t* __restrict__ slice_ptr, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ len, const int32_t* __restrict__ col, const float* __restrict__ val,
+    const int32_t* __restrict__ len, const Col* __restrict__ col, const float* __restrict__ val,
     const float* __restrict__ x, float alpha, float beta, float* __restrict__ y, int xcd_remap) {
     // with xcd_remap each XCD takes one contiguous run of slices, so the x
     // lines that neighbouring rows share stay in that XCD's L2
@@ -179,7 +184,9 @@ __global__ __launch_bounds__(kBlock) void spmv_sell_kernel(
     if (k >= rows) return;
     const int L = len[k];
     if (L < 0) return;
-    const int32_t* cp = col + slice_ptr[slice] + lane;
+    const int row = perm[k];
+    const int base = sizeof(Col) == 2 ? row : 0;  // columns are stored relative to the row
+    const Col* cp = col + slice_ptr[slice] + lane;
     const float* vp = val + slice_ptr[slice] + lane;
     float s = 0.0f;
     int t = 0;
@@ -189,7 +196,7 @@ __global__ __launch_bounds__(kBlock) void spmv_sell_kernel(
         float a[8], xv[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            c[u] = __builtin_nontemporal_load(cp + (int64_t)(t + u) * 64);
+            c[u] = base + (int)__builtin_nontemporal_load(cp + (int64_t)(t + u) * 64);
             a[u] = __builtin_nontemporal_load(vp + (int64_t)(t + u) * 64);
         }
 #pragma unroll
@@ -197,15 +204,37 @@ __global__ __launch_bounds__(kBlock) void spmv_sell_kernel(
 #pragma unroll
         for (int u = 0; u < 8; ++u) s += a[u] * xv[u];
     }
-    for (; t < L; ++t) s += __builtin_nontemporal_load(vp + (int64_t)t * 64) * x[__builtin_nontemporal_load(cp + (int64_t)t * 64)];
-    store_axpby(y, perm[k], s, alpha, beta);
+    for (; t < L; ++t)
+        s += __builtin_nontemporal_load(vp + (int64_t)t * 64) *
+             x[base + (int)__builtin_nontemporal_load(cp + (int64_t)t * 64)];
+    store_axpby(y, row, s, alpha, beta);
 }
 
-// Fill the SELL slot arrays from the CSR (padding: column -1, value 0).
+// Largest |column - row| over the entries of the SELL rows (atomic max into *out).
+__global__ __launch_bounds__(kBlock) void sell_offset_kernel(int rows, int slices, const int32_t* __restrict__ perm,
+                                                             const int32_t* __restrict__ len,
+                                                             const int32_t* __restrict__ ptr,
+                                                             const int32_t* __restrict__ idx, int32_t* out) {
+    const int k = blockIdx.x * kBlock + threadIdx.x;
+    int m = 0;
+    if (k < rows && k < slices * 64) {
+        const int L = len[k];
+        if (L > 0) {
+            const int row = perm[k];
+            const int p0 = ptr[row];
+            for (int t = 0; t < L; ++t) m = max(m, abs(idx[p0 + t] - row));
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
+    if ((threadIdx.x & 63) == 0 && m > 0) atomicMax(out, m);
+}
+
+// Fill the SELL slot arrays from the CSR (padding: column -1 or offset 0, value 0).
+template <typename Col>
 __global__ __launch_bounds__(kBlock) void sell_fill_kernel(
     int rows, int slices, const int64_t* __restrict__ slice_ptr, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ len, const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
-    const float* __restrict__ val, int32_t* __restrict__ scol, float* __restrict__ sval) {
+    const float* __restrict__ val, Col* __restrict__ scol, float* __restrict__ sval) {
     const int slice = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (slice >= slices) return;
     const int lane = threadIdx.x & 63;
@@ -213,14 +242,16 @@ __global__ __launch_bounds__(kBlock) void sell_fill_kernel(
     const int64_t base = slice_ptr[slice];
     const int width = (int)((slice_ptr[slice + 1] - base) / 64);
     const int L = k < rows ? len[k] : -1;
-    const int p0 = (k < rows && L > 0) ? ptr[perm[k]] : 0;
+    const int row = (k < rows && L > 0) ? perm[k] : 0;
+    const int p0 = (k < rows && L > 0) ? ptr[row] : 0;
+    const int rel = sizeof(Col) == 2 ? row : 0;
     for (int t = 0; t < width; ++t) {
         const int64_t q = base + (int64_t)t * 64 + lane;
         if (t < L) {
-            scol[q] = idx[p0 + t];
+            scol[q] = (Col)(idx[p0 + t] - rel);
             sval[q] = val[p0 + t];
         } else {
-            scol[q] = -1;
+            scol[q] = (Col)(sizeof(Col) == 2 ? 0 : -1);
             sval[q] = 0.0f;
         }
     }
@@ -244,20 +275,39 @@ hipError_t launch_spmv(const DirDevice& d, float alpha, const float* x, float be
         if (err != hipSuccess) return err;
     }
     if (d.use_sell && d.sell_slices > 0) {
-        hipLaunchKernelGGL(spmv_sell_kernel, dim3((unsigned)((d.sell_slices + 3) / 4)), dim3(kBlock), 0, s, d.rows,
-                           d.sell_slices, d.sell_slice_ptr, d.sell_perm, d.sell_len, d.sell_col, d.sell_val, x,
-                           alpha, beta, y, d.xcd_remap);
+        const dim3 grid((unsigned)((d.sell_slices + 3) / 4));
+        if (d.sell_narrow)
+            hipLaunchKernelGGL(spmv_sell_kernel<int16_t>, grid, dim3(kBlock), 0, s, d.rows, d.sell_slices,
+                               d.sell_slice_ptr, d.sell_perm, d.sell_len, reinterpret_cast<const int16_t*>(d.sell_col),
+                               d.sell_val, x, alpha, beta, y, d.xcd_remap);
+        else
+            hipLaunchKernelGGL(spmv_sell_kernel<int32_t>, grid, dim3(kBlock), 0, s, d.rows, d.sell_slices,
+                               d.sell_slice_ptr, d.sell_perm, d.sell_len, d.sell_col, d.sell_val, x, alpha, beta, y,
+                               d.xcd_remap);
         return hipGetLastError();
     }
     return hipSuccess;
 }
 
+hipError_t launch_sell_offset(const DirDevice& d, int32_t* out, hipStream_t s) {
+    if (d.sell_slices <= 0) return hipSuccess;
+    const int64_t n = std::min<int64_t>((int64_t)d.rows, (int64_t)d.sell_slices * 64);
+    hipLaunchKernelGGL(sell_offset_kernel, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, d.rows,
+                       d.sell_slices, d.sell_perm, d.sell_len, d.ptr, d.idx, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_sell_fill(const DirDevice& d, int64_t slots, int32_t* sell_col, float* sell_val, hipStream_t s) {
     (void)slots;
     if (d.sell_slices <= 0) return hipSuccess;
-    hipLaunchKernelGGL(sell_fill_kernel, dim3((unsigned)((d.sell_slices + 3) / 4)), dim3(kBlock), 0, s, d.rows,
-                       d.sell_slices, d.sell_slice_ptr, d.sell_perm, d.sell_len, d.ptr, d.idx, d.val, sell_col,
-                       sell_val);
+    const dim3 grid((unsigned)((d.sell_slices + 3) / 4));
+    if (d.sell_narrow)
+        hipLaunchKernelGGL(sell_fill_kernel<int16_t>, grid, dim3(kBlock), 0, s, d.rows, d.sell_slices, d.sell_slice_ptr,
+                           d.sell_perm, d.sell_len, d.ptr, d.idx, d.val, reinterpret_cast<int16_t*>(sell_col),
+                           sell_val);
+    else
+        hipLaunchKernelGGL(sell_fill_kernel<int32_t>, grid, dim3(kBlock), 0, s, d.rows, d.sell_slices, d.sell_slice_ptr,
+                           d.sell_perm, d.sell_len, d.ptr, d.idx, d.val, sell_col, sell_val);
     return hipGetLastError();
 }
 

@@ -194,6 +194,32 @@ def test_panels_with_concentrated_columns(opts):
         assert_close(host(y), ref, scale, what="panels, columns below %d" % hi)
 
 
+def test_sell_with_wide_column_offsets():
+    """SELL stores int16 column offsets from the row when every column lies
+    within 32767 of its row (all the small cases above) and int32 columns
+    otherwise: a matrix whose columns reach 120000 away takes the second
+    form, and both directions stay exact."""
+    say("sell, wide column offsets")
+    coo = gen.ragged_coo(3000, 120000, seed=9, max_len=40, empty_frac=0.1)
+    rp, c, v = oracle.coo_to_csr(coo.m, coo.n, coo.row, coo.col, coo.val)
+    assert np.abs(c.astype(np.int64) - np.repeat(np.arange(coo.m), np.diff(rp))).max() > 32767
+    cp, ri, cv = oracle.csr_to_csc(coo.m, coo.n, rp, c, v)
+    plan = sp.Plan(coo.m, coo.n, dev(rp), dev(c), dev(v), csc=(dev(cp), dev(ri), dev(cv)), use_sell=1, col_panels=0,
+                   x_window_bits=0)
+    assert plan.profile()["sell_slots"] > 0
+    x = gen.dense_vector(coo.n, 3)
+    u = gen.dense_vector(coo.m, 4)
+    y0 = gen.dense_vector(coo.m, 5)
+    y = dev(y0)
+    sp.spmv(plan, 1.5, dev(x), -0.5, y)
+    ref, scale = oracle.spmv(rp, c, v, x, 1.5, -0.5, y0)
+    assert_close(host(y), ref, scale, what="sell wide spmv")
+    z = torch.zeros(coo.n, device="cuda")
+    sp.spmv_t(plan, 1.0, dev(u), 0.0, z)
+    ref_t, scale_t = oracle.spmv(cp, ri, cv, u)
+    assert_close(host(z), ref_t, scale_t, what="sell wide spmv_t")
+
+
 def test_x_windows_profile_and_limits():
     """The x-window stream reports its width; an explicit width that needs
     more than 256 windows is refused, the automatic choice never is."""
