@@ -153,8 +153,9 @@ def main():
         print(json.dumps(dict(copy_bytes_read=4 * n, copy_bytes_written=4 * n, launches=5)))
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: the sparse products here are single-GPU kernels "
-              "(see the sharding paragraph of DESIGN.md); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        print("bench.py runs on one GPU only: the sparse products here are single-GPU kernels (rows would be "
+              "sharded across GPUs with x all-gathered first, which is not built); --gpus %d is not supported"
+              % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
