@@ -175,16 +175,23 @@ __device__ __forceinline__ float dot4(float acc, const float4 a, const float4 xv
     return acc;
 }
 
-// bs in {16, 32, 64}: one workgroup (W waves) per block row.
-template <int BS, int W>
+// bs in {16, 32, 64}: SPLIT workgroups of W waves per block row, workgroup
+// (I, part) owning rows [part BS/SPLIT, (part + 1) BS/SPLIT) of block row I,
+// i.e. one contiguous slice of every block of the row.  The outputs of the
+// workgroups are disjoint, so the sums need no second stage; splitting a long
+// block row over several workgroups balances the rows' unequal block counts.
+template <int BS, int W, int SPLIT>
 __global__ __launch_bounds__(64 * W) void bsr_spmv_big(int64_t m, int64_t n, int32_t kb, int64_t nnzb,
                                                        const int32_t* __restrict__ brow_ptr,
                                                        const int32_t* __restrict__ bcol, const float* __restrict__ bval,
                                                        float alpha, const float* __restrict__ x, float beta,
                                                        float* __restrict__ y) {
-    constexpr int E = BS * BS, P = E / 256, Q = BS / 4;  // steps per block, lanes per row slice
-    __shared__ float red[W][BS];
-    const int I = blockIdx.x, tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    constexpr int RS = BS / SPLIT;                        // rows of the slice
+    constexpr int E = RS * BS, P = E / 256, Q = BS / 4;  // slice elements, steps per slice, lanes per row slice
+    static_assert(E % 256 == 0, "a slice is whole 256-element steps");
+    __shared__ float red[W][RS];
+    const int I = blockIdx.x / SPLIT, part = blockIdx.x % SPLIT;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int c = (4 * l) % BS, rloc = (4 * l) / BS;
     const int kb0 = (int)min<int64_t>(max(brow_ptr[I], 0), nnzb), kb1 = (int)min<int64_t>(max(brow_ptr[I + 1], 0), nnzb);
     float acc[P];
@@ -195,7 +202,7 @@ __global__ __launch_bounds__(64 * W) void bsr_spmv_big(int64_t m, int64_t n, int
         if (J < 0 || J >= kb) continue;
         const int64_t j = (int64_t)J * BS + c;
         const float4 xv = load_x4(x, j, n);
-        const float* blk = bval + (int64_t)b * E + 4 * l;
+        const float* blk = bval + (int64_t)b * BS * BS + (int64_t)part * E + 4 * l;
         float4 a[P];
 #pragma unroll
         for (int ph = 0; ph < P; ++ph) a[ph] = ldg4_nt(blk + 256 * ph);
@@ -209,8 +216,8 @@ __global__ __launch_bounds__(64 * W) void bsr_spmv_big(int64_t m, int64_t n, int
         if (l % Q == 0) red[w][ph * (256 / BS) + rloc] = v;
     }
     __syncthreads();
-    if (tid < BS) {
-        const int64_t row = (int64_t)I * BS + tid;
+    if (tid < RS) {
+        const int64_t row = (int64_t)I * BS + part * RS + tid;
         if (row < m) {
             float s = red[0][tid];
 #pragma unroll
@@ -323,8 +330,11 @@ int spmv_bs(int64_t m, int64_t n, int64_t nnzb, const int32_t* brow_ptr, const i
     const int64_t mb = (m + BS - 1) / BS, kb = (n + BS - 1) / BS;
     if (mb == 0) return SP_OK;
     if constexpr (BS >= 16) {
-        hipLaunchKernelGGL((bsr_spmv_big<BS, 16>), dim3((unsigned)mb), dim3(1024), 0, s, m, n, (int32_t)kb, nnzb,
-                           brow_ptr, bcol, bval, alpha, x, beta, y);
+        // 64 x 64 blocks: four 16-row slices per block row; smaller blocks: the
+        // whole block row in one workgroup; 16 waves per workgroup
+        constexpr int SPLIT = BS == 64 ? 4 : 1, W = 16;
+        hipLaunchKernelGGL((bsr_spmv_big<BS, W, SPLIT>), dim3((unsigned)(mb * SPLIT)), dim3(64 * W), 0, s, m, n,
+                           (int32_t)kb, nnzb, brow_ptr, bcol, bval, alpha, x, beta, y);
     } else {
         hipLaunchKernelGGL(bsr_spmv_small<BS>, dim3((unsigned)((mb + 3) / 4)), dim3(kBlock), 0, s, m, n,
                            (int32_t)mb, (int32_t)kb, nnzb, brow_ptr, bcol, bval, alpha, x, beta, y);
