@@ -134,6 +134,9 @@ def main():
                     help="steps per replay of a captured HIP graph in the timed region (0: one plain launch per "
                          "step; -1: up to 20 for workloads whose step is a single short kernel, else 0)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", type=int, default=0, metavar="R",
+                    help="after the timed region, also time R single steps each preceded by writing a 512 MiB "
+                         "buffer (evicts the L2s and the 256 MB MALL): cold-cache numbers, reported under 'cold'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--options", default="", help="plan options, e.g. group_nnz=1024,wave_min=128")
     ap.add_argument("--autotune", action="store_true",
@@ -458,7 +461,37 @@ def main():
                               flops_per_launch=int(per_launch_flops), event_ms_median=round(float(np.median(ev_ms)), 5))
     if bound == "mfma":
         result["roofline"]["hbm_gbs"] = round(per_launch_bytes / (launch_ms * 1e-3) / 1e9, 1)
+    result["roofline"]["event_ms_min"] = round(float(np.min(ev_ms)), 5)
     result["gflops_event"] = round(per_launch_flops / (launch_ms * 1e-3) / 1e9, 2)
+
+    # ---------------- cold-cache steps (outside the timed region, on request)
+    if args.cold > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.cold)]
+        if restore_fn:
+            restore_fn()
+        # each rep: flush, one timed step (cold), then one more timed step the
+        # same way (warm: what the flushed step left in the caches), so that
+        # the difference is the caches' and not the single launch's
+        for i in range(args.cold):
+            flush.fill_(i & 255)
+            for j in (0, 2):
+                ev[i][j].record(stream)
+                step()
+                ev[i][j + 1].record(stream)
+        torch.cuda.synchronize()
+        del flush
+        cold_ms = [e[0].elapsed_time(e[1]) / launches for e in ev]
+        single_ms = [e[2].elapsed_time(e[3]) / launches for e in ev]
+        med = float(np.median(cold_ms))
+        if bound == "hbm":
+            cold_achieved = per_launch_bytes / (med * 1e-3) / 1e9
+        else:
+            cold_achieved = per_launch_flops / (med * 1e-3) / 1e12
+        result["cold"] = dict(reps=args.cold, flush_bytes=512 << 20, kernel_ms_median=round(med, 5),
+                              kernel_ms_min=round(float(np.min(cold_ms)), 5), achieved=round(cold_achieved, 2),
+                              unit=unit, frac=round(cold_achieved / peak, 4),
+                              warm_single_ms_median=round(float(np.median(single_ms)), 5))
     result["setup"] = {k: round(v, 2) for k, v in setup.items()}
 
     # ---------------- CPU baseline: the oracle on the host cores
