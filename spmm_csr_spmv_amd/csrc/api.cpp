@@ -82,7 +82,8 @@ struct Dir {
     mutable size_t off_ps_chunks = 0, off_ps_pk = 0, off_ps_pv = 0, off_ps_ypart = 0, off_ps_split_tasks = 0;
     mutable size_t off_ps_split_rows = 0, off_ps_partials = 0, off_ps_skip = 0;
     mutable size_t off_xw_pieces = 0, off_xw_wcol = 0, off_xw_wval = 0, off_xw_off = 0, off_xw_prod = 0;
-    mutable size_t off_xw_chunks = 0, off_xw_chunk_q = 0, off_xw_runs = 0, off_xw_split_rows = 0, off_xw_partials = 0;
+    mutable size_t off_xw_chunks = 0, off_xw_chunk_q = 0, off_xw_runs = 0, off_xw_split_rows = 0, off_xw_partials = 0,
+                   off_xw_counters = 0;
     mutable size_t off_xw_wm_runs = 0, off_xw_prod_ranges = 0;
 };
 
@@ -298,6 +299,8 @@ size_t dir_layout(const Dir& d, const sp_plan_options& o, int32_t max_N, size_t 
         off = align256(off + d.xw_split_rows.size() * sizeof(int4));
         d.off_xw_partials = off;
         off = align256(off + (size_t)d.xw_n_partials * sizeof(float));
+        d.off_xw_counters = off;
+        off = align256(off + d.xw_split_rows.size() * sizeof(int32_t));
     }
     if (d.use_sell) {
         d.off_sell_ptr = off;
@@ -498,7 +501,7 @@ int build_xwin(const std::vector<int32_t>& hptr, int32_t bits, Dir& d, hipStream
     const int64_t rows = d.rows, nnz = d.nnz;
     const int64_t nw = std::max<int64_t>(1, ((int64_t)d.cols + ((int64_t)1 << bits) - 1) >> bits);
     if (nw > spx::kXwMaxWindows) return SP_ERR_UNSUPPORTED;
-    // row chunks, in CSR order: {q_begin, q_end, row_begin, row_end or -(partial + 1)}
+    // row chunks, in CSR order: {q_begin, q_end, row_begin or long row, row_end or -(partial + 1)}
     std::vector<int4> chunks;
     std::vector<int4> split_rows;
     int64_t n_partials = 0;
@@ -515,10 +518,11 @@ int build_xwin(const std::vector<int32_t>& hptr, int32_t bits, Dir& d, hipStream
             if (len > spx::kXwChunk) {
                 close(r);
                 const int64_t nseg = (len + spx::kXwChunk - 1) / spx::kXwChunk;
+                const int32_t j = (int32_t)split_rows.size();
                 split_rows.push_back(make_int4((int32_t)r, (int32_t)n_partials, (int32_t)nseg, 0));
                 for (int64_t k = 0; k < nseg; ++k) {
                     const int64_t sb = b + k * spx::kXwChunk, se = std::min<int64_t>(e, sb + spx::kXwChunk);
-                    chunks.push_back(make_int4((int32_t)sb, (int32_t)se, (int32_t)r, (int32_t)(-(n_partials + k) - 1)));
+                    chunks.push_back(make_int4((int32_t)sb, (int32_t)se, j, (int32_t)(-(n_partials + k) - 1)));
                 }
                 n_partials += nseg;
                 continue;
@@ -775,6 +779,7 @@ int upload_dir(Dir& d, char* ws, const sp_plan_options& o, hipStream_t s) {
         v.xw_n_split_rows = (int32_t)d.xw_split_rows.size();
         v.xw_split_rows = reinterpret_cast<const int4*>(ws + d.off_xw_split_rows);
         v.xw_partials = reinterpret_cast<float*>(ws + d.off_xw_partials);
+        v.xw_counters = reinterpret_cast<int32_t*>(ws + d.off_xw_counters);
         auto up = [&](size_t off, const void* src, size_t bytes) {
             return bytes == 0 || hipMemcpyAsync(ws + off, src, bytes, hipMemcpyHostToDevice, s) == hipSuccess;
         };
@@ -789,6 +794,10 @@ int upload_dir(Dir& d, char* ws, const sp_plan_options& o, hipStream_t s) {
             !up(d.off_xw_prod, d.xw_pos.data(), d.xw_pos.size() * sizeof(int32_t)))
             return SP_ERR_HIP;
         if (spx::launch_xwin_build(v, reinterpret_cast<const int32_t*>(ws + d.off_xw_prod), s) != hipSuccess)
+            return SP_ERR_HIP;
+        // the long rows' arrival counters start at zero; the row kernel puts them back to zero
+        if (!d.xw_split_rows.empty() &&
+            spx::launch_fill_i32(v.xw_counters, (int64_t)d.xw_split_rows.size(), 0, s) != hipSuccess)
             return SP_ERR_HIP;
     }
     if (d.use_sell) {

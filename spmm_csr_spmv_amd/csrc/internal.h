@@ -74,12 +74,13 @@ struct DirDevice {
     int32_t xw_row_grid;             // workgroups of the row kernel (each takes every grid-th chunk)
     int64_t xw_total;                // stream slots
     int32_t xw_n_chunks;
-    const int4* xw_chunks;           // {stream_begin, stream_end, row_begin, row_end or -(partial + 1)}
+    const int4* xw_chunks;           // {stream_begin, stream_end, row_begin or long row, row_end or -(partial + 1)}
     const int2* xw_chunk_q;          // {first CSR entry, entries}
     const int32_t* xw_runs;          // [n_chunks][nw + 1] chunk-major start of chunk c's run in window w
     int32_t xw_n_split_rows;
     const int4* xw_split_rows;       // {row, partial_base, nseg, 0}
     float* xw_partials;
+    int32_t* xw_counters;            // [n_split_rows] arrival counters (self-resetting)
     // optional SELL-C-sigma copy of the group rows
     int32_t use_sell;
     int32_t sell_slices;

@@ -47,9 +47,11 @@
 //   the rows that start and end inside the slice, and one segmented suffix
 //   scan over the 256 slices completes the rows that cross slice boundaries.
 //   The order of every sum is fixed by the chunk alone, so results are
-//   bitwise reproducible.
-// xw_split_kernel: y = alpha * (segment partials in order) + beta * y for the
-//   rows longer than a chunk.
+//   bitwise reproducible.  A chunk that is a segment of a row longer than a
+//   chunk stores its sum as that row's partial; the workgroup that stores
+//   the row's last partial (an integer arrival counter) adds the partials in
+//   segment order, writes y and puts the counter back to zero, so the sum
+//   does not depend on which workgroup arrives last.
 #include <algorithm>
 
 #include "device_common.h"
@@ -327,7 +329,9 @@ struct XwRowArgs {
     const float* prod;
     const uint16_t* off;
     const int32_t* ptr;
+    const int4* split_rows;  // {row, partial_base, nseg, 0} of each row longer than a chunk
     float* partials;
+    int32_t* counters;       // arrival counter of each such row (zero between calls)
     float* y;
     float alpha, beta;
 };
@@ -374,7 +378,8 @@ __global__ __launch_bounds__(kXwRowThreads) void xw_rows_kernel(const XwRowArgs 
         fetch_rows(c0);
     }
     for (; ci < a.n_chunks; ci += gridDim.x) {
-        const int4 c = a.chunks[ci];  // {stream_begin, stream_end, row_begin, row_end or -(partial + 1)}
+        // {stream_begin, stream_end, row_begin or long row, row_end or -(partial + 1)}
+        const int4 c = a.chunks[ci];
         const int2 qn = a.chunk_q[ci];
         // the next chunk's loads go into the registers as soon as they are consumed
         const bool more = ci + (int)gridDim.x < a.n_chunks;
@@ -440,7 +445,18 @@ __global__ __launch_bounds__(kXwRowThreads) void xw_rows_kernel(const XwRowArgs 
         __syncthreads();
         // ---- outputs
         if (seg) {
-            if (tid == 0) a.partials[-c.w - 1] = ysh[0];
+            if (tid == 0) {
+                const int4 sr = a.split_rows[c.z];
+                atomic_store_f(a.partials + (-c.w - 1), ysh[0]);
+                const int arrived =
+                    __hip_atomic_fetch_add(a.counters + c.z, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                if (arrived == sr.z - 1) {
+                    float t = 0.0f;
+                    for (int k = 0; k < sr.z; ++k) t += atomic_load_f(a.partials + sr.y + k);
+                    store_axpby(a.y, sr.x, t, a.alpha, a.beta);
+                    __hip_atomic_store(a.counters + c.z, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
         } else {
             float v[kXwRowLoads];
 #pragma unroll
@@ -459,18 +475,6 @@ __global__ __launch_bounds__(kXwRowThreads) void xw_rows_kernel(const XwRowArgs 
         __syncthreads();  // LDS is reused by the next chunk
     }
 
-}
-
-// One thread per long row: its segment partials added in segment order.
-__global__ __launch_bounds__(kBlock) void xw_split_kernel(int n_split_rows, const int4* __restrict__ split_rows,
-                                                          const float* __restrict__ partials, float alpha, float beta,
-                                                          float* __restrict__ y) {
-    const int j = blockIdx.x * kBlock + (int)threadIdx.x;
-    if (j >= n_split_rows) return;
-    const int4 sr = split_rows[j];  // {row, partial_base, nseg, 0}
-    float t = 0.0f;
-    for (int k = 0; k < sr.z; ++k) t += partials[sr.y + k];
-    store_axpby(y, sr.x, t, alpha, beta);
 }
 
 // Bind time: every stream slot starts as padding...
@@ -539,18 +543,15 @@ hipError_t launch_spmv_xwin(const DirDevice& d, float alpha, const float* x, flo
         a.prod = d.xw_prod;
         a.off = d.xw_off;
         a.ptr = d.ptr;
+        a.split_rows = d.xw_split_rows;
         a.partials = d.xw_partials;
+        a.counters = d.xw_counters;
         a.y = y;
         a.alpha = alpha;
         a.beta = beta;
         hipLaunchKernelGGL(xw_rows_kernel, dim3((unsigned)d.xw_row_grid), dim3(kXwRowThreads), 0, s, a);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
-    }
-    if (d.xw_n_split_rows > 0) {
-        hipLaunchKernelGGL(xw_split_kernel, dim3((unsigned)((d.xw_n_split_rows + kBlock - 1) / kBlock)), dim3(kBlock),
-                           0, s, d.xw_n_split_rows, d.xw_split_rows, d.xw_partials, alpha, beta, y);
-        return hipGetLastError();
     }
     return hipSuccess;
 }

@@ -67,6 +67,29 @@ def test_spmv_spmv_t_spmm_graph_replays(bins):
     assert np.all(np.abs(y.cpu().numpy() - ref) <= 1e-5 * scale + 1e-30)
 
 
+def test_x_window_long_rows_graph_replays():
+    """Rows longer than a row chunk are finished by the workgroup that stores
+    their last segment sum, through an arrival counter the kernel puts back
+    to zero: every replay and every eager call gives the same result, and it
+    is the oracle's."""
+    say("graph replays, x windows with long rows")
+    coo = gen.ragged_coo(3000, 100000, seed=21, max_len=20, long_rows=(40000, 30721, 15361))
+    rp, c, v = sp.csr_build_from_coo(coo.m, coo.n, dev(coo.row), dev(coo.col), dev(coo.val))
+    plan = sp.Plan(coo.m, coo.n, rp, c, v, use_sell=0, x_window_bits=12)
+    assert plan.profile()["x_window_bits"] == 12
+    x = dev(gen.dense_vector(coo.n, 1))
+    y = torch.empty(coo.m, device="cuda")
+
+    def run():
+        sp.spmv(plan, 1.0, x, 0.0, y)
+
+    _replays_match(run, [y], replays=4)
+    hrp, hc, hv = oracle.coo_to_csr(coo.m, coo.n, coo.row, coo.col, coo.val)
+    assert np.diff(hrp).max() == 40000
+    ref, scale = oracle.spmv(hrp, hc, hv, x.cpu().numpy())
+    assert np.all(np.abs(y.cpu().numpy() - ref) <= 1e-5 * scale + 1e-30)
+
+
 def test_bsr_spmv_and_bsr_spmm_graph_replays():
     say("graph replays, BSR")
     coo = gen.block_sparse_coo(mb=6, kb=5, bs=64, density=0.4, std=1.0, seed=7)

@@ -79,8 +79,11 @@ def test_x_window_chunk_edges(bits):
     plan = sp.Plan(coo.m, coo.n, dev(rp), dev(c), dev(v), csc=(dev(cp), dev(ri), dev(cv)), use_sell=0,
                    x_window_bits=bits)
     assert plan.profile()["x_window_bits"] == bits
-    _check_spmv(plan, coo.m, coo.n, rp, c, v, 30, "chunk edges, bits %d" % bits)
-    _check_spmv_t(plan, coo.m, coo.n, cp, ri, cv, 32, "chunk edges transposed, bits %d" % bits)
+    # repeated calls: the long rows' arrival counters are back at zero after each
+    for k, (alpha, beta) in enumerate(((1.25, -0.5), (1.0, 0.0), (-2.0, 1.5))):
+        _check_spmv(plan, coo.m, coo.n, rp, c, v, 30 + 2 * k, "chunk edges, bits %d, call %d" % (bits, k),
+                    alpha, beta)
+    _check_spmv_t(plan, coo.m, coo.n, cp, ri, cv, 38, "chunk edges transposed, bits %d" % bits)
 
 
 @pytest.mark.parametrize("opts", [dict(use_sell=0, x_window_bits=15), dict(use_sell=0, x_window_bits=0, col_panels=0)])
