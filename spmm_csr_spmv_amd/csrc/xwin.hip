@@ -35,8 +35,10 @@
 //   and refills x only when the window changes.  Each thread holds 4 groups
 //   of 8 slots of a piece in registers (16-byte loads, issued while the
 //   previous piece is processed), forms value * x[window + column], finds
-//   the group's run by a branchless binary search over the piece's run table
-//   in LDS, and stores the 8 products at their chunk-major place.
+//   the group's run in the piece's run map in LDS (the first group of each
+//   run holds the run's destination; a wave ballot finds the last run start
+//   at or before the group), and stores the 8 products at their chunk-major
+//   place.
 // xw_rows_kernel (256 threads, two workgroups per CU, each taking every
 //   grid-th chunk): the chunk's stream slice and row starts are loaded into
 //   registers while the previous chunk is being scattered and summed (each
@@ -63,6 +65,7 @@ namespace {
 constexpr int kXwProdThreads = 1024;
 constexpr int kXwWords = kXwChunk / 32;  // row-start bitmap words of a chunk
 constexpr uint32_t kXwPad = 0xffffu;     // position of a padding slot
+constexpr int kNoRun = -2147483647 - 1;  // run map entry of a group that starts no run
 static_assert(kXwChunk % 32 == 0, "chunk bitmap in whole words");
 static_assert(kXwChunk < (int)kXwPad && kXwMaxRows <= 32767, "local positions and ranks fit 16 bits");
 static_assert(kXwPieceRuns <= kXwProdThreads, "one thread per run in the piece table");
@@ -214,7 +217,7 @@ __device__ __forceinline__ void chunk_row_sums(const float* ps, int n, const uin
 struct PieceRegs {
     v4u32 k[kXwProdGroups];
     v4f32 a0[kXwProdGroups], a1[kXwProdGroups];
-    int run_start, run_groups;
+    int run_start, run_groups, run_first;  // chunk-major start, groups, groups of the piece before it
 };
 
 __device__ __forceinline__ void group_fetch(const int4& pc, int u, const uint16_t* __restrict__ wcol,
@@ -232,15 +235,20 @@ __device__ __forceinline__ void group_fetch(const int4& pc, int u, const uint16_
     }
 }
 
-__device__ __forceinline__ void runs_fetch(const int4& pc, const int32_t* __restrict__ runs, int nw, PieceRegs& r) {
+__device__ __forceinline__ void runs_fetch(const int4& pc, const int32_t* __restrict__ runs,
+                                           const int32_t* __restrict__ wm_runs, int nw, PieceRegs& r) {
     const int tid = threadIdx.x;
     const int w = pc.x & 255, nr = pc.x >> 8, ca = pc.y;
     r.run_start = 0;
     r.run_groups = 0;
+    r.run_first = 0;
     if (tid < nr) {
         const int32_t* q = runs + (int64_t)(ca + tid) * (nw + 1) + w;
         r.run_start = q[0];
         r.run_groups = (q[1] - r.run_start) >> 3;  // runs are whole groups of 8
+        // the piece is one stretch of the window-major stream, which holds
+        // the window's runs in chunk order
+        r.run_first = (wm_runs[(int64_t)(ca + tid) * nw + w] - pc.z) >> 3;
     }
 }
 
@@ -249,13 +257,17 @@ __device__ __forceinline__ void runs_fetch(const int4& pc, const int32_t* __rest
 // refilled only when the window changes; the next piece's loads are issued
 // before the current piece's products are formed.
 __global__ __launch_bounds__(kXwProdThreads) void xw_products_kernel(
-    const int4* __restrict__ pieces, const int2* __restrict__ ranges, const int32_t* __restrict__ runs, int nw,
-    int bits, int64_t cols, const float* __restrict__ x, const uint16_t* __restrict__ wcol,
-    const float* __restrict__ wval, float* __restrict__ prod) {
+    const int4* __restrict__ pieces, const int2* __restrict__ ranges, const int32_t* __restrict__ runs,
+    const int32_t* __restrict__ wm_runs, int nw, int bits, int64_t cols, const float* __restrict__ x,
+    const uint16_t* __restrict__ wcol, const float* __restrict__ wval, float* __restrict__ prod) {
+    constexpr int kGroups = kXwProdGroups * kXwProdThreads;  // groups of 8 slots per piece
     __shared__ __attribute__((aligned(16))) float xs[1 << kXwMaxBits];
-    __shared__ int rs[kXwPieceRuns];      // chunk-major start of each run of the piece
-    __shared__ int gp[kXwPieceRuns + 1];  // groups of 8 slots before each run
-    __shared__ int tot[kXwProdThreads / 64];
+    // run map of the piece: for the first group g of each non-empty run,
+    // base[g] = (chunk-major start of the run) - 8 g, so that group g' of that
+    // run goes to base[g] + 8 g'; kNoRun elsewhere.  carry[b] = the base of
+    // the run that holds group 64 b.
+    __shared__ int base[kGroups];
+    __shared__ int carry[kGroups / 64];
     const int2 rg = ranges[blockIdx.x];
     if (rg.x >= rg.y) return;
     const int tid = threadIdx.x;
@@ -265,13 +277,16 @@ __global__ __launch_bounds__(kXwProdThreads) void xw_products_kernel(
         const int4 p0 = pieces[rg.x];
 #pragma unroll
         for (int u = 0; u < kXwProdGroups; ++u) group_fetch(p0, u, wcol, wval, cur);
-        runs_fetch(p0, runs, nw, cur);
+        runs_fetch(p0, runs, wm_runs, nw, cur);
     }
+#pragma unroll
+    for (int u = 0; u < kXwProdGroups; ++u) base[tid + kXwProdThreads * u] = kNoRun;  // each thread reads and
+                                                                                       // clears its own entries
     int loaded = -1;  // window held in xs
     for (int pi = rg.x; pi < rg.y; ++pi) {
         const int4 pc = pieces[pi];  // {window | runs << 8, first chunk, window-major start, groups}
         const int w = pc.x & 255, nr = pc.x >> 8, G = pc.w;  // 1 <= nr <= kXwPieceRuns
-        __syncthreads();  // the previous piece is done with xs, rs and gp
+        __syncthreads();  // the previous piece is done with xs, base and carry
         if (w != loaded) {
             const int64_t c0 = (int64_t)w << bits;
             const int nx = (int)min((int64_t)W, cols - c0);
@@ -284,25 +299,32 @@ __global__ __launch_bounds__(kXwProdThreads) void xw_products_kernel(
             }
             loaded = w;
         }
-        if (tid < nr) rs[tid] = cur.run_start;
-        const int ex = block_exclusive_sum<kXwProdThreads>(cur.run_groups, tot);
-        if (tid < nr) gp[tid] = ex;
-        if (tid == nr - 1) gp[nr] = ex + cur.run_groups;  // == G
-        __syncthreads();  // x window and run table in LDS
+        if (tid < nr && cur.run_groups > 0) {
+            const int ex = cur.run_first;
+            const int b0 = cur.run_start - 8 * ex;
+            base[ex] = b0;
+            for (int b = (ex + 63) >> 6; 64 * b < ex + cur.run_groups; ++b) carry[b] = b0;
+        }
+        __syncthreads();  // x window and run map in LDS
         // the next piece's loads go into the registers as they are consumed
         const bool more = pi + 1 < rg.y;
         const int4 pn = more ? pieces[pi + 1] : make_int4(0, 0, 0, 0);
-        if (more) runs_fetch(pn, runs, nw, cur);
-        // group g lies in the last run c with gp[c] <= g (empty runs share
-        // their successor's gp); every column read is below the window's
-        // width (padding has column 0)
+        if (more) runs_fetch(pn, runs, wm_runs, nw, cur);
+        // group g lies in the last run that starts at or before it: the
+        // wave's 64 lanes hold one 64-group block, so that run is the last
+        // marked lane up to this one, else the run that crosses into the
+        // block; every column read is below the window's width (padding has
+        // column 0)
+        const uint64_t upto = (2ull << (tid & 63)) - 1ull;  // lanes 0 .. this lane
 #pragma unroll
         for (int u = 0; u < kXwProdGroups; ++u) {
             const int g = tid + kXwProdThreads * u;
-            int lo = 0;
-#pragma unroll
-            for (int step = kXwPieceRuns / 2; step > 0; step >>= 1)
-                if (lo + step < nr && gp[lo + step] <= g) lo += step;
+            const int mk = base[g];
+            base[g] = kNoRun;  // clear for the next piece (read by no other thread)
+            const uint64_t starts = __ballot(mk != kNoRun) & upto;
+            const int src = starts ? 63 - __clzll(starts) : 0;
+            const int from_lane = __shfl(mk, src, 64);
+            const int b0 = starts ? from_lane : carry[g >> 6];
             v4f32 q0, q1;
             q0.x = cur.a0[u].x * xs[cur.k[u].x & 0xffffu];
             q0.y = cur.a0[u].y * xs[cur.k[u].x >> 16];
@@ -314,7 +336,7 @@ __global__ __launch_bounds__(kXwProdThreads) void xw_products_kernel(
             q1.w = cur.a1[u].w * xs[cur.k[u].w >> 16];
             if (more) group_fetch(pn, u, wcol, wval, cur);
             if (g < G) {
-                const int d = rs[lo] + 8 * (g - gp[lo]);
+                const int d = b0 + 8 * g;
                 *reinterpret_cast<v4f32*>(prod + d) = q0;
                 *reinterpret_cast<v4f32*>(prod + d + 4) = q1;
             }
@@ -530,8 +552,8 @@ hipError_t launch_xwin_build(const DirDevice& d, const int32_t* pos, hipStream_t
 hipError_t launch_spmv_xwin(const DirDevice& d, float alpha, const float* x, float beta, float* y, hipStream_t s) {
     if (d.xw_n_pieces > 0) {
         hipLaunchKernelGGL(xw_products_kernel, dim3((unsigned)kXwProdGrid), dim3(kXwProdThreads), 0, s,
-                           d.xw_pieces, d.xw_prod_ranges, d.xw_runs, d.xw_nw, d.xw_bits, (int64_t)d.cols, x, d.xw_wcol,
-                           d.xw_wval, d.xw_prod);
+                           d.xw_pieces, d.xw_prod_ranges, d.xw_runs, d.xw_wm_runs, d.xw_nw, d.xw_bits, (int64_t)d.cols,
+                           x, d.xw_wcol, d.xw_wval, d.xw_prod);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
