@@ -69,6 +69,7 @@ struct Dir {
     std::vector<int2> xw_chunk_q;      // {first CSR entry, entries}
     std::vector<int32_t> xw_runs;      // [n_chunks][nw + 1] chunk-major run starts
     std::vector<int32_t> xw_wm_runs;   // [n_chunks][nw] window-major run starts
+    std::vector<int2> xw_wm_tab;       // [nw][n_chunks] + 1: {chunk-major, window-major start}, window-major order
     std::vector<int4> xw_pieces;       // {window | runs << 8, chunk, start, groups}, by XCD, window order
     std::vector<int2> xw_prod_ranges;  // [kXwProdGrid] pieces of each product workgroup
     std::vector<int4> xw_split_rows;   // {row, partial_base, nseg, 0}
@@ -84,7 +85,7 @@ struct Dir {
     mutable size_t off_xw_pieces = 0, off_xw_wcol = 0, off_xw_wval = 0, off_xw_off = 0, off_xw_prod = 0;
     mutable size_t off_xw_chunks = 0, off_xw_chunk_q = 0, off_xw_runs = 0, off_xw_split_rows = 0, off_xw_partials = 0,
                    off_xw_counters = 0;
-    mutable size_t off_xw_wm_runs = 0, off_xw_prod_ranges = 0;
+    mutable size_t off_xw_wm_runs = 0, off_xw_wm_tab = 0, off_xw_prod_ranges = 0;
 };
 
 }  // namespace
@@ -295,6 +296,8 @@ size_t dir_layout(const Dir& d, const sp_plan_options& o, int32_t max_N, size_t 
         off = align256(off + d.xw_runs.size() * sizeof(int32_t));
         d.off_xw_wm_runs = off;
         off = align256(off + d.xw_wm_runs.size() * sizeof(int32_t));
+        d.off_xw_wm_tab = off;
+        off = align256(off + d.xw_wm_tab.size() * sizeof(int2));
         d.off_xw_split_rows = off;
         off = align256(off + d.xw_split_rows.size() * sizeof(int4));
         d.off_xw_partials = off;
@@ -492,6 +495,7 @@ int build_xwin(const std::vector<int32_t>& hptr, int32_t bits, Dir& d, hipStream
     d.xw_chunk_q.clear();
     d.xw_runs.clear();
     d.xw_wm_runs.clear();
+    d.xw_wm_tab.clear();
     d.xw_pieces.clear();
     d.xw_prod_ranges.clear();
     d.xw_split_rows.clear();
@@ -572,6 +576,14 @@ int build_xwin(const std::vector<int32_t>& hptr, int32_t bits, Dir& d, hipStream
                 at += runs[(size_t)(c * (nw + 1) + w + 1)] - runs[(size_t)(c * (nw + 1) + w)];
             }
     }
+    // the same run starts in window-major order, for the product kernel: the
+    // runs of a piece are consecutive entries; a last entry closes the stream
+    std::vector<int2> wm_tab((size_t)(n_chunks * nw + 1));
+    for (int64_t w = 0; w < nw; ++w)
+        for (int64_t c = 0; c < n_chunks; ++c)
+            wm_tab[(size_t)(w * n_chunks + c)] =
+                make_int2(runs[(size_t)(c * (nw + 1) + w)], wm_runs[(size_t)(c * nw + w)]);
+    wm_tab[(size_t)(n_chunks * nw)] = make_int2(0, (int32_t)total);
     // pieces: the runs of one window over at most kXwPieceRuns chunks and
     // kXwPiece slots, {window | runs << 8, first chunk, window-major start,
     // groups of 8}; listed XCD by XCD (window w on XCD w mod 8), windows in
@@ -623,6 +635,7 @@ int build_xwin(const std::vector<int32_t>& hptr, int32_t bits, Dir& d, hipStream
     d.xw_chunk_q = std::move(chunk_q);
     d.xw_runs = std::move(runs);
     d.xw_wm_runs = std::move(wm_runs);
+    d.xw_wm_tab = std::move(wm_tab);
     d.xw_split_rows = std::move(split_rows);
     d.xw_pos = std::move(pos);
     d.xw_total = total;
@@ -774,6 +787,7 @@ int upload_dir(Dir& d, char* ws, const sp_plan_options& o, hipStream_t s) {
         v.xw_chunk_q = reinterpret_cast<const int2*>(ws + d.off_xw_chunk_q);
         v.xw_runs = reinterpret_cast<const int32_t*>(ws + d.off_xw_runs);
         v.xw_wm_runs = reinterpret_cast<const int32_t*>(ws + d.off_xw_wm_runs);
+        v.xw_wm_tab = reinterpret_cast<const int2*>(ws + d.off_xw_wm_tab);
         // the row kernel keeps two workgroups per CU, each taking every grid-th chunk
         v.xw_row_grid = (int32_t)std::min<int64_t>((int64_t)d.xw_chunks.size(), 2 * 256);
         v.xw_n_split_rows = (int32_t)d.xw_split_rows.size();
@@ -790,6 +804,7 @@ int upload_dir(Dir& d, char* ws, const sp_plan_options& o, hipStream_t s) {
             !up(d.off_xw_chunk_q, d.xw_chunk_q.data(), d.xw_chunk_q.size() * sizeof(int2)) ||
             !up(d.off_xw_runs, d.xw_runs.data(), d.xw_runs.size() * sizeof(int32_t)) ||
             !up(d.off_xw_wm_runs, d.xw_wm_runs.data(), d.xw_wm_runs.size() * sizeof(int32_t)) ||
+            !up(d.off_xw_wm_tab, d.xw_wm_tab.data(), d.xw_wm_tab.size() * sizeof(int2)) ||
             !up(d.off_xw_split_rows, d.xw_split_rows.data(), d.xw_split_rows.size() * sizeof(int4)) ||
             !up(d.off_xw_prod, d.xw_pos.data(), d.xw_pos.size() * sizeof(int32_t)))
             return SP_ERR_HIP;

@@ -70,7 +70,8 @@ struct DirDevice {
     float* xw_wval;                  // window-major stream: value (0 in padding)
     uint16_t* xw_off;                // chunk-major stream: position in the chunk's CSR order (0xffff: padding)
     float* xw_prod;                  // chunk-major stream: product (written by every call)
-    const int32_t* xw_wm_runs;       // [n_chunks][nw] window-major start of chunk c's run in window w
+    const int32_t* xw_wm_runs;       // [n_chunks][nw] window-major start of chunk c's run in window w (bind only)
+    const int2* xw_wm_tab;           // [nw][n_chunks] + 1 {chunk-major, window-major start} of run (c, w)
     int32_t xw_row_grid;             // workgroups of the row kernel (each takes every grid-th chunk)
     int64_t xw_total;                // stream slots
     int32_t xw_n_chunks;

@@ -25,6 +25,8 @@
 //     runs[c][nw] the chunk's end.
 //   * window-major stream (column within the window as uint16, value):
 //     window after window, the window's runs in chunk order.
+//   * the run starts in both streams, listed in window-major order, so that
+//     the runs of a piece are consecutive entries.
 //
 // xw_products_kernel (1024 threads, one window of x in LDS, one workgroup
 //   per CU): a piece is the runs of one window over at most kXwPieceRuns
@@ -235,20 +237,22 @@ __device__ __forceinline__ void group_fetch(const int4& pc, int u, const uint16_
     }
 }
 
-__device__ __forceinline__ void runs_fetch(const int4& pc, const int32_t* __restrict__ runs,
-                                           const int32_t* __restrict__ wm_runs, int nw, PieceRegs& r) {
+__device__ __forceinline__ void runs_fetch(const int4& pc, const int2* __restrict__ wm_tab, int n_chunks,
+                                           PieceRegs& r) {
     const int tid = threadIdx.x;
     const int w = pc.x & 255, nr = pc.x >> 8, ca = pc.y;
     r.run_start = 0;
     r.run_groups = 0;
     r.run_first = 0;
     if (tid < nr) {
-        const int32_t* q = runs + (int64_t)(ca + tid) * (nw + 1) + w;
-        r.run_start = q[0];
-        r.run_groups = (q[1] - r.run_start) >> 3;  // runs are whole groups of 8
-        // the piece is one stretch of the window-major stream, which holds
-        // the window's runs in chunk order
-        r.run_first = (wm_runs[(int64_t)(ca + tid) * nw + w] - pc.z) >> 3;
+        // the piece's runs are consecutive in the window-major table, and so
+        // are their stretches of the window-major stream (runs are whole
+        // groups of 8)
+        const int64_t i = (int64_t)w * n_chunks + ca + tid;
+        const int2 t = wm_tab[i];
+        r.run_start = t.x;
+        r.run_groups = (wm_tab[i + 1].y - t.y) >> 3;
+        r.run_first = (t.y - pc.z) >> 3;
     }
 }
 
@@ -257,9 +261,9 @@ __device__ __forceinline__ void runs_fetch(const int4& pc, const int32_t* __rest
 // refilled only when the window changes; the next piece's loads are issued
 // before the current piece's products are formed.
 __global__ __launch_bounds__(kXwProdThreads) void xw_products_kernel(
-    const int4* __restrict__ pieces, const int2* __restrict__ ranges, const int32_t* __restrict__ runs,
-    const int32_t* __restrict__ wm_runs, int nw, int bits, int64_t cols, const float* __restrict__ x,
-    const uint16_t* __restrict__ wcol, const float* __restrict__ wval, float* __restrict__ prod) {
+    const int4* __restrict__ pieces, const int2* __restrict__ ranges, const int2* __restrict__ wm_tab,
+    int n_chunks, int bits, int64_t cols, const float* __restrict__ x, const uint16_t* __restrict__ wcol,
+    const float* __restrict__ wval, float* __restrict__ prod) {
     constexpr int kGroups = kXwProdGroups * kXwProdThreads;  // groups of 8 slots per piece
     __shared__ __attribute__((aligned(16))) float xs[1 << kXwMaxBits];
     // run map of the piece: for the first group g of each non-empty run,
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(kXwProdThreads) void xw_products_kernel(
         const int4 p0 = pieces[rg.x];
 #pragma unroll
         for (int u = 0; u < kXwProdGroups; ++u) group_fetch(p0, u, wcol, wval, cur);
-        runs_fetch(p0, runs, wm_runs, nw, cur);
+        runs_fetch(p0, wm_tab, n_chunks, cur);
     }
 #pragma unroll
     for (int u = 0; u < kXwProdGroups; ++u) base[tid + kXwProdThreads * u] = kNoRun;  // each thread reads and
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(kXwProdThreads) void xw_products_kernel(
         // the next piece's loads go into the registers as they are consumed
         const bool more = pi + 1 < rg.y;
         const int4 pn = more ? pieces[pi + 1] : make_int4(0, 0, 0, 0);
-        if (more) runs_fetch(pn, runs, wm_runs, nw, cur);
+        if (more) runs_fetch(pn, wm_tab, n_chunks, cur);
         // group g lies in the last run that starts at or before it: the
         // wave's 64 lanes hold one 64-group block, so that run is the last
         // marked lane up to this one, else the run that crosses into the
@@ -552,8 +556,8 @@ hipError_t launch_xwin_build(const DirDevice& d, const int32_t* pos, hipStream_t
 hipError_t launch_spmv_xwin(const DirDevice& d, float alpha, const float* x, float beta, float* y, hipStream_t s) {
     if (d.xw_n_pieces > 0) {
         hipLaunchKernelGGL(xw_products_kernel, dim3((unsigned)kXwProdGrid), dim3(kXwProdThreads), 0, s,
-                           d.xw_pieces, d.xw_prod_ranges, d.xw_runs, d.xw_wm_runs, d.xw_nw, d.xw_bits, (int64_t)d.cols,
-                           x, d.xw_wcol, d.xw_wval, d.xw_prod);
+                           d.xw_pieces, d.xw_prod_ranges, d.xw_wm_tab, d.xw_n_chunks, d.xw_bits, (int64_t)d.cols, x,
+                           d.xw_wcol, d.xw_wval, d.xw_prod);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
