@@ -364,6 +364,14 @@ def main():
             nbytes = 2 * spmv_bytes(m, n, nnz, True)  # per step (two launches)
             launches = 2
             config["step"] = "u <- A v - alpha u ; v <- A^T u - beta v"
+            # the iterates grow by about |A| per step and pass the fp32 range
+            # after some 20 steps: put u, v back every 8 steps (inside the
+            # wall-clock region, outside the per-step events)
+            restore_every = 8
+            config["restore_every"] = restore_every
+
+            def iterates_finite():
+                return bool(torch.isfinite(u).all().item() and torch.isfinite(v).all().item())
         elif cfg == "spmm_lognormal":
             B = torch.from_numpy(gen.dense_matrix(n, N, 0)).cuda()
             C = torch.empty(m, N, device="cuda")
@@ -398,6 +406,7 @@ def main():
                                                      "accumulation, single-threaded C loop)" % cfg)
 
     restore_fn = locals().get("restore")
+    restore_every = locals().get("restore_every", 0)
     # ---------------- warmup + timed region
     for _ in range(args.warmup):
         step()
@@ -423,6 +432,8 @@ def main():
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(nrec):
+        if restore_every and i > 0 and i % restore_every == 0:
+            restore_fn()
         starts[i].record(stream)
         if G > 0:
             graph.replay()
@@ -431,6 +442,9 @@ def main():
         ends[i].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
+    finite = locals().get("iterates_finite")
+    if finite is not None:
+        result["iterates_finite"] = finite()
     ev_ms = [s.elapsed_time(e) / (G if G > 0 else 1) for s, e in zip(starts, ends)]
     if G > 0:
         # the graph's result equals an eager step's, bit for bit (deterministic kernels)
@@ -468,12 +482,12 @@ def main():
     if args.cold > 0:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.cold)]
-        if restore_fn:
-            restore_fn()
         # each rep: flush, one timed step (cold), then one more timed step the
         # same way (warm: what the flushed step left in the caches), so that
         # the difference is the caches' and not the single launch's
         for i in range(args.cold):
+            if restore_fn:
+                restore_fn()  # before the flush, so the copy leaves nothing in the caches
             flush.fill_(i & 255)
             for j in (0, 2):
                 ev[i][j].record(stream)
