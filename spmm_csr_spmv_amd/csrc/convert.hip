@@ -11,12 +11,19 @@
 // format requires; each segment is then sorted by key:
 //   COO -> CSR : key = (col << 32) | input position   (by column, ties by input order)
 //   CSR -> CSC : key = (row << 32) | CSR position      (by row, ties by CSR order)
-// Segments of length 2..64 are sorted by one wave (rank by comparison),
-// longer ones by one workgroup (bitonic sort of 4096-key chunks in LDS, then
-// merge passes in global memory where each key finds its place by binary
-// search in the partner run).
+// Segments of length 2..256 are sorted by rank counting (16, 32 or 64 lanes
+// per segment up to 64 keys, one wave with 4 keys per lane up to 256),
+// 257..4096 by one workgroup (bitonic sort in LDS); longer ones by the whole
+// GPU: one workgroup per 4096-key chunk sorts it in LDS, then each merge
+// level is one launch over all their keys, each key finding its place by
+// binary search in the partner run.
+//
+// Counts and scatters work on runs: lanes of a wave that hold consecutive
+// entries of one segment (sorted input has long runs) take one atomic for
+// the whole run, the run's first lane adding its length.
 #include "device_common.h"
 
+#include <algorithm>
 #include <vector>
 
 namespace spx {
@@ -25,37 +32,79 @@ namespace {
 
 constexpr int kScanTile = 2048;  // elements scanned per workgroup (8 per thread)
 constexpr int kChunk = 4096;     // keys sorted in LDS at once
+constexpr int kTinySeg = 16;     // segments up to this length: 16 lanes each
+constexpr int kHalfSeg = 32;     // up to this length: 32 lanes each
 constexpr int kSmallSeg = 64;    // segments up to this length are sorted by one wave
+constexpr int kMidSeg = 256;     // up to this length: one wave, 4 keys per lane
+constexpr int kClassifyThreads = 1024;
+constexpr int32_t kI32MaxLen = 2147483647;
 
-enum Misc { kErr = 0, kCntSmall = 1, kCntLarge = 2, kMaxLen = 3, kMiscWords = 16 };
+// Segment classes by length: tiny 2..16, half 17..32, small 33..64, mid
+// 65..256, large 257..4096, huge longer (segments of 0 or 1 keys need no
+// sort).
+enum SegClass { kTiny = 0, kHalf = 1, kSmall = 2, kMid = 3, kLarge = 4, kHuge = 5, kClasses = 6 };
+enum Misc { kErr = 0, kCnt = 1 /* kCnt + class: listed segments */, kMaxLen = kCnt + kClasses, kMiscWords = 16 };
+
+struct SegLists {
+    int32_t* l[kClasses];
+};
+
+// Runs of equal segment ids in consecutive lanes of a wave.  `ok` marks the
+// lanes that hold an entry; a run is a maximal stretch of ok lanes with the
+// same id.  Returns the lane's run head (its first lane); *len receives, in
+// a head lane, the run's length.
+__device__ __forceinline__ int lane_run(bool ok, int32_t id, int* len) {
+    const int lane = threadIdx.x & 63;
+    const int32_t prev = __shfl_up(id, 1, 64);
+    const bool prev_ok = __shfl_up(ok ? 1 : 0, 1, 64) != 0;
+    const bool head = ok && (lane == 0 || !prev_ok || prev != id);
+    const uint64_t heads = __ballot(head);
+    const uint64_t stops = heads | __ballot(!ok);  // a run ends before the next head or empty lane
+    const uint64_t after = stops & ~((2ull << lane) - 1ull);  // stops above this lane (none for lane 63)
+    *len = (after ? __ffsll((unsigned long long)after) - 1 : 64) - lane;
+    const uint64_t upto = heads & ((2ull << lane) - 1ull);
+    return upto ? 63 - __clzll(upto) : lane;
+}
 
 __global__ __launch_bounds__(kBlock) void fill_i32(int32_t* p, int64_t n, int32_t v) {
     for (int64_t i = blockIdx.x * (int64_t)kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock) p[i] = v;
 }
 
+// Grid-stride loops over whole waves, so that every lane of a wave takes
+// part in the run ballots: entry i = i0 + lane, present when i < nnz.
+#define SPX_WAVE_LOOP(i0, nnz)                                                                        \
+    for (int64_t i0 = blockIdx.x * (int64_t)kBlock + (threadIdx.x & ~63); i0 < (nnz); \
+         i0 += (int64_t)gridDim.x * kBlock)
+
 // counts[r + 1] += 1 for every valid (r, c); flags invalid entries.
 __global__ __launch_bounds__(kBlock) void coo_count(int64_t nnz, const int32_t* __restrict__ row,
                                                     const int32_t* __restrict__ col, int32_t m, int32_t n,
                                                     int32_t* __restrict__ counts1, int32_t* __restrict__ misc) {
-    for (int64_t i = blockIdx.x * (int64_t)kBlock + threadIdx.x; i < nnz; i += (int64_t)gridDim.x * kBlock) {
-        const int32_t r = row[i], c = col[i];
-        if (r < 0 || r >= m || c < 0 || c >= n) {
-            atomicOr(misc + kErr, 1);
-        } else {
-            atomicAdd(counts1 + r, 1);
-        }
+    const int lane = threadIdx.x & 63;
+    SPX_WAVE_LOOP(i0, nnz) {
+        const int64_t i = i0 + lane;
+        const bool in = i < nnz;
+        const int32_t r = in ? row[i] : 0, c = in ? col[i] : 0;
+        const bool bad = in && (r < 0 || r >= m || c < 0 || c >= n);
+        if (bad) atomicOr(misc + kErr, 1);
+        int len;
+        const int head = lane_run(in && !bad, r, &len);
+        if (in && !bad && head == lane) atomicAdd(counts1 + r, len);
     }
 }
 
 __global__ __launch_bounds__(kBlock) void col_count(int64_t nnz, const int32_t* __restrict__ col, int32_t n,
                                                     int32_t* __restrict__ counts1, int32_t* __restrict__ misc) {
-    for (int64_t i = blockIdx.x * (int64_t)kBlock + threadIdx.x; i < nnz; i += (int64_t)gridDim.x * kBlock) {
-        const int32_t c = col[i];
-        if (c < 0 || c >= n) {
-            atomicOr(misc + kErr, 1);
-        } else {
-            atomicAdd(counts1 + c, 1);
-        }
+    const int lane = threadIdx.x & 63;
+    SPX_WAVE_LOOP(i0, nnz) {
+        const int64_t i = i0 + lane;
+        const bool in = i < nnz;
+        const int32_t c = in ? col[i] : 0;
+        const bool bad = in && (c < 0 || c >= n);
+        if (bad) atomicOr(misc + kErr, 1);
+        int len;
+        const int head = lane_run(in && !bad, c, &len);
+        if (in && !bad && head == lane) atomicAdd(counts1 + c, len);
     }
 }
 
@@ -119,44 +168,76 @@ __global__ __launch_bounds__(kBlock) void scan_add(int32_t* __restrict__ a, int6
 }
 
 // ---- segment classification -------------------------------------------------
-// cursor[s] = ptr[s]; segments of length 2..64 go to `small`, longer ones to
-// `large`; tracks the longest segment.
-__global__ __launch_bounds__(kBlock) void classify(int32_t nseg, const int32_t* __restrict__ ptr,
-                                                   int32_t* __restrict__ cursor, int32_t* __restrict__ small,
-                                                   int32_t* __restrict__ large, int32_t* __restrict__ misc) {
-    // One atomic per wave and list: the wave's lanes take consecutive slots
-    // (list order does not matter, every listed segment is sorted on its own).
-    const int lane = threadIdx.x & 63;
+// cursor[s] = ptr[s]; every segment of 2 or more keys goes to the list of its
+// class; tracks the longest segment.  One atomic per list and workgroup
+// pass: the workgroup's segments of a class take consecutive slots (list
+// order does not matter, every listed segment is sorted on its own).
+__global__ __launch_bounds__(kClassifyThreads) void classify(int32_t nseg, const int32_t* __restrict__ ptr,
+                                                            int32_t* __restrict__ cursor, SegLists lists,
+                                                            int32_t* __restrict__ misc) {
+    constexpr int NW = kClassifyThreads / 64;
+    __shared__ int cnt[NW][kClasses];  // per wave, then the waves before it
+    __shared__ int base[kClasses];
+    __shared__ int wmax[NW];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const uint64_t below = (1ull << lane) - 1;
-    for (int32_t s0 = blockIdx.x * kBlock; s0 < nseg; s0 += gridDim.x * kBlock) {
-        const int32_t s = s0 + threadIdx.x;
+    for (int64_t s0 = (int64_t)blockIdx.x * kClassifyThreads; s0 < nseg; s0 += (int64_t)gridDim.x * kClassifyThreads) {
+        const int64_t s = s0 + tid;
         const bool in = s < nseg;
         const int32_t b = in ? ptr[s] : 0, len = in ? ptr[s + 1] - b : 0;
         if (in) cursor[s] = b;
-        const bool is_small = len >= 2 && len <= kSmallSeg, is_large = len > kSmallSeg;
-        const uint64_t ms = __ballot(is_small), ml = __ballot(is_large);
-        int32_t base_s = 0, base_l = 0;
-        if (lane == 0) {
-            if (ms) base_s = atomicAdd(misc + kCntSmall, (int)__popcll(ms));
-            if (ml) base_l = atomicAdd(misc + kCntLarge, (int)__popcll(ml));
+        const int cls = len < 2 ? -1
+                        : len <= kTinySeg  ? kTiny
+                        : len <= kHalfSeg  ? kHalf
+                        : len <= kSmallSeg ? kSmall
+                        : len <= kMidSeg   ? kMid
+                        : len <= kChunk    ? kLarge
+                                           : kHuge;
+        uint64_t mine = 0;
+#pragma unroll
+        for (int c = 0; c < kClasses; ++c) {
+            const uint64_t m = __ballot(cls == c);
+            if (lane == 0) cnt[w][c] = (int)__popcll(m);
+            if (cls == c) mine = m;
         }
-        base_s = __shfl(base_s, 0, 64);
-        base_l = __shfl(base_l, 0, 64);
-        if (is_small) small[base_s + __popcll(ms & below)] = s;
-        if (is_large) large[base_l + __popcll(ml & below)] = s;
         int32_t mx = len;
         for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
-        if (lane == 0 && mx > 0) atomicMax(misc + kMaxLen, mx);
+        if (lane == 0) wmax[w] = mx;
+        __syncthreads();
+        if (tid < kClasses) {
+            int tot = 0;
+            for (int k = 0; k < NW; ++k) {
+                const int t = cnt[k][tid];
+                cnt[k][tid] = tot;
+                tot += t;
+            }
+            base[tid] = tot > 0 ? atomicAdd(misc + kCnt + tid, tot) : 0;
+        } else if (tid == kClasses) {
+            int mm = 0;
+            for (int k = 0; k < NW; ++k) mm = max(mm, wmax[k]);
+            if (mm > 0) atomicMax(misc + kMaxLen, mm);
+        }
+        __syncthreads();
+        if (cls >= 0) lists.l[cls][base[cls] + cnt[w][cls] + __popcll(mine & below)] = (int32_t)s;
+        __syncthreads();  // cnt and base are rewritten by the next pass
     }
 }
 
 // ---- keyed scatters ---------------------------------------------------------
+// (All indices were checked by the count kernel before the scatters run.)
 __global__ __launch_bounds__(kBlock) void coo_scatter(int64_t nnz, const int32_t* __restrict__ row,
                                                       const int32_t* __restrict__ col, int32_t* __restrict__ cursor,
                                                       uint64_t* __restrict__ keys) {
-    for (int64_t i = blockIdx.x * (int64_t)kBlock + threadIdx.x; i < nnz; i += (int64_t)gridDim.x * kBlock) {
-        const int32_t p = atomicAdd(cursor + row[i], 1);
-        keys[p] = ((uint64_t)(uint32_t)col[i] << 32) | (uint64_t)i;
+    const int lane = threadIdx.x & 63;
+    SPX_WAVE_LOOP(i0, nnz) {
+        const int64_t i = i0 + lane;
+        const bool in = i < nnz;
+        const int32_t r = in ? row[i] : 0;
+        int len;
+        const int head = lane_run(in, r, &len);
+        const int32_t base = in && head == lane ? atomicAdd(cursor + r, len) : 0;
+        const int32_t p = __shfl(base, head, 64) + (lane - head);
+        if (in) keys[p] = ((uint64_t)(uint32_t)col[i] << 32) | (uint64_t)i;
     }
 }
 
@@ -173,10 +254,16 @@ __device__ __forceinline__ int32_t row_of(const int32_t* __restrict__ row_ptr, i
 __global__ __launch_bounds__(kBlock) void csr_scatter(int64_t nnz, const int32_t* __restrict__ row_ptr, int32_t m,
                                                       const int32_t* __restrict__ col, int32_t* __restrict__ cursor,
                                                       uint64_t* __restrict__ keys) {
-    for (int64_t p = blockIdx.x * (int64_t)kBlock + threadIdx.x; p < nnz; p += (int64_t)gridDim.x * kBlock) {
-        const int32_t r = row_of(row_ptr, m, (int32_t)p);
-        const int32_t q = atomicAdd(cursor + col[p], 1);
-        keys[q] = ((uint64_t)(uint32_t)r << 32) | (uint64_t)p;
+    const int lane = threadIdx.x & 63;
+    SPX_WAVE_LOOP(p0, nnz) {
+        const int64_t p = p0 + lane;
+        const bool in = p < nnz;
+        const int32_t c = in ? col[p] : 0;
+        int len;
+        const int head = lane_run(in, c, &len);
+        const int32_t base = in && head == lane ? atomicAdd(cursor + c, len) : 0;
+        const int32_t q = __shfl(base, head, 64) + (lane - head);
+        if (in) keys[q] = ((uint64_t)(uint32_t)row_of(row_ptr, m, (int32_t)p) << 32) | (uint64_t)p;
     }
 }
 
@@ -187,19 +274,26 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
     return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-// One wave per segment of 2..64 keys: rank = number of smaller keys (keys are unique).
-__global__ __launch_bounds__(kBlock) void sort_small(const int32_t* __restrict__ list, const int32_t* __restrict__ misc,
+// G lanes per segment of 2..G keys (64 / G segments per wave): rank = the
+// number of smaller keys in the segment (keys are unique, and below ~0).
+template <int G>
+__global__ __launch_bounds__(kBlock) void sort_small(const int32_t* __restrict__ list, int32_t count,
                                                      const int32_t* __restrict__ ptr, uint64_t* __restrict__ keys) {
-    const int32_t count = misc[kCntSmall];
-    const int32_t wv = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
-    if (wv >= count) return;
-    const int lane = threadIdx.x & 63;
-    const int32_t s = list[wv];
-    const int32_t b = ptr[s], len = ptr[s + 1] - b;
-    const uint64_t key = lane < len ? keys[b + lane] : ~0ull;
+    const int lane = threadIdx.x & 63, g0 = lane & ~(G - 1), gl = lane & (G - 1);
+    const int64_t k = ((int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6)) * (64 / G) + lane / G;
+    if (k - lane / G >= count) return;  // the whole wave is past the list
+    int32_t b = 0, len = 0;
+    if (k < count) {
+        const int32_t s = list[k];
+        b = ptr[s];
+        len = ptr[s + 1] - b;
+    }
+    const uint64_t key = gl < len ? keys[b + gl] : ~0ull;
+    int longest = len;
+    for (int off = 32; off > 0; off >>= 1) longest = max(longest, __shfl_xor(longest, off, 64));
     int rank = 0;
-    for (int i = 0; i < len; ++i) rank += shfl_u64(key, i) < key ? 1 : 0;
-    if (lane < len) keys[b + rank] = key;
+    for (int i = 0; i < longest; ++i) rank += shfl_u64(key, g0 + i) < key ? 1 : 0;
+    if (gl < len) keys[b + rank] = key;
 }
 
 // Bitonic sort of sh[0..P) (P a power of two, <= kChunk), ascending.
@@ -232,48 +326,116 @@ __device__ __forceinline__ int32_t lower_bound_u64(const uint64_t* __restrict__ 
     return lo;
 }
 
-// One workgroup per segment longer than 64 keys.
+// Sorts seg[0..n) (n <= kChunk) in LDS; the whole workgroup takes part.
+__device__ void sort_chunk(uint64_t* __restrict__ seg, int32_t n, uint64_t* sh) {
+    int P = 2;
+    while (P < n) P <<= 1;
+    for (int i = threadIdx.x; i < P; i += kBlock) sh[i] = i < n ? seg[i] : ~0ull;
+    __syncthreads();
+    bitonic_lds(sh, P);
+    for (int i = threadIdx.x; i < n; i += kBlock) seg[i] = sh[i];
+    __syncthreads();
+}
+
+// One wave per segment of 65..256 keys, 4 keys per lane: rank = the number of
+// smaller keys, read back one by one from the segment's copy in LDS.
+__global__ __launch_bounds__(kBlock) void sort_mid(const int32_t* __restrict__ list, int32_t count,
+                                                   const int32_t* __restrict__ ptr, uint64_t* __restrict__ keys) {
+    constexpr int KPL = kMidSeg / 64;  // keys per lane
+    __shared__ uint64_t sh[kBlock / 64][kMidSeg];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t k = (int64_t)blockIdx.x * (kBlock / 64) + w;
+    int32_t b = 0, len = 0;
+    if (k < count) {
+        const int32_t s = list[k];
+        b = ptr[s];
+        len = ptr[s + 1] - b;
+    }
+    uint64_t key[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+        const int i = lane + 64 * j;
+        key[j] = i < len ? keys[b + i] : ~0ull;
+        sh[w][i] = key[j];
+    }
+    __syncthreads();
+    int rank[KPL] = {};
+    for (int i = 0; i < len; ++i) {
+        const uint64_t o = sh[w][i];
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) rank[j] += o < key[j] ? 1 : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < KPL; ++j)
+        if (lane + 64 * j < len) keys[b + rank[j]] = key[j];
+}
+
+// One workgroup per segment of 257..kChunk keys.
 __global__ __launch_bounds__(kBlock) void sort_large(const int32_t* __restrict__ list, const int32_t* __restrict__ ptr,
-                                                     uint64_t* __restrict__ keys, uint64_t* __restrict__ tmp) {
+                                                     uint64_t* __restrict__ keys) {
     __shared__ uint64_t sh[kChunk];
     const int32_t s = list[blockIdx.x];
-    const int32_t b = ptr[s], len = ptr[s + 1] - b;
-    uint64_t* seg = keys + b;
-    // 1. sort every chunk of kChunk keys in LDS
-    for (int32_t c0 = 0; c0 < len; c0 += kChunk) {
-        const int32_t n = len - c0 < kChunk ? len - c0 : kChunk;
-        int P = 2;
-        while (P < n) P <<= 1;
-        for (int i = threadIdx.x; i < P; i += kBlock) sh[i] = i < n ? seg[c0 + i] : ~0ull;
-        __syncthreads();
-        bitonic_lds(sh, P);
-        for (int i = threadIdx.x; i < n; i += kBlock) seg[c0 + i] = sh[i];
-        __syncthreads();
+    const int32_t b = ptr[s];
+    sort_chunk(keys + b, ptr[s + 1] - b, sh);
+}
+
+// ---- segments longer than kChunk: the whole GPU sorts them together.
+// tab[k] = {begin, length, keys before segment k, chunks before segment k}
+// over the huge segments, and tab[n] = {0, 0, all keys, all chunks}.
+__global__ __launch_bounds__(kBlock) void huge_info(const int32_t* __restrict__ list, int32_t n,
+                                                    const int32_t* __restrict__ ptr, int2* __restrict__ out) {
+    const int32_t k = blockIdx.x * kBlock + threadIdx.x;
+    if (k < n) {
+        const int32_t s = list[k];
+        out[k] = make_int2(ptr[s], ptr[s + 1] - ptr[s]);
     }
-    // 2. merge runs of width w, 2w, ... until one run covers the segment
-    uint64_t* src = seg;
-    uint64_t* dst = tmp + b;
-    for (int32_t w = kChunk; w < len; w <<= 1) {
-        for (int32_t e = threadIdx.x; e < len; e += kBlock) {
-            const int32_t run = e / w;
-            const int32_t pair0 = (run & ~1) * w;           // start of the left run of the pair
-            const int32_t own0 = run * w;
-            const bool left = (run & 1) == 0;
-            const int32_t p0 = left ? own0 + w : pair0;     // partner run start
-            int32_t pn = left ? (len - p0 < w ? len - p0 : w) : w;
-            if (pn < 0) pn = 0;
-            const uint64_t key = src[e];
-            const int32_t rank = pn > 0 ? lower_bound_u64(src + p0, pn, key) : 0;
-            dst[pair0 + (e - own0) + rank] = key;
-        }
-        __syncthreads();
-        uint64_t* t = src;
-        src = dst;
-        dst = t;
+}
+
+// The last k in [0, n) with field(tab[k]) <= f (field: .z keys or .w chunks).
+template <bool kByChunk>
+__device__ __forceinline__ int32_t huge_of(const int4* __restrict__ tab, int32_t n, int64_t f) {
+    int32_t lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int32_t mid = lo + (hi - lo + 1) / 2;
+        const int32_t v = kByChunk ? tab[mid].w : tab[mid].z;
+        if (v <= f) lo = mid; else hi = mid - 1;
     }
-    if (src != seg) {
-        for (int32_t e = threadIdx.x; e < len; e += kBlock) seg[e] = src[e];
-    }
+    return lo;
+}
+
+// Workgroup c sorts chunk c of the huge segments in LDS.
+__global__ __launch_bounds__(kBlock) void huge_chunks(const int4* __restrict__ tab, int32_t n,
+                                                      uint64_t* __restrict__ keys) {
+    __shared__ uint64_t sh[kChunk];
+    const int32_t c = blockIdx.x;
+    const int4 t = tab[huge_of<true>(tab, n, c)];
+    const int32_t j = c - t.w;  // chunk within the segment
+    const int32_t n_keys = min(kChunk, t.y - j * kChunk);
+    sort_chunk(keys + t.x + (int64_t)j * kChunk, n_keys, sh);
+}
+
+// One merge level over all huge segments: within each segment, sorted runs
+// of width w are merged in pairs from src to dst; key e of run r goes to the
+// start of its pair plus its place in its own run plus the number of smaller
+// keys in the partner run.  A segment no longer than w is copied.
+__global__ __launch_bounds__(kBlock) void huge_merge(const int4* __restrict__ tab, int32_t n, int32_t w,
+                                                     const uint64_t* __restrict__ src, uint64_t* __restrict__ dst) {
+    const int64_t f = blockIdx.x * (int64_t)kBlock + threadIdx.x;
+    if (f >= tab[n].z) return;
+    const int4 t = tab[huge_of<false>(tab, n, f)];
+    const int32_t e = (int32_t)(f - t.z), len = t.y;
+    const uint64_t* sseg = src + t.x;
+    uint64_t* dseg = dst + t.x;
+    const int64_t run = e / w;
+    const int64_t pair0 = (run & ~1ll) * w;  // start of the left run of the pair
+    const int64_t own0 = run * w;
+    const bool left = (run & 1) == 0;
+    const int64_t p0 = left ? own0 + w : pair0;  // partner run start
+    int64_t pn = left ? min((int64_t)len - p0, (int64_t)w) : (int64_t)w;
+    if (pn < 0) pn = 0;
+    const uint64_t key = sseg[e];
+    const int32_t rank = pn > 0 ? lower_bound_u64(sseg + p0, (int32_t)pn, key) : 0;
+    dseg[pair0 + (e - own0) + rank] = key;
 }
 
 // ---- gathers -------------------------------------------------------------------
@@ -298,8 +460,11 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout shared by both builders (nseg = number of segments).
 struct Layout {
-    size_t keys, tmp, cursor, small, large, sums, misc, total;
+    size_t keys, tmp, cursor, tiny, half, small, mid, large, huge, hinfo, htab, sums, misc, total;
 };
+
+// Segments longer than kChunk: at most this many.
+int64_t max_huge(int64_t nnz) { return nnz / (kChunk + 1) + 1; }
 
 Layout layout(int64_t nseg, int64_t nnz) {
     Layout L;
@@ -307,8 +472,14 @@ Layout layout(int64_t nseg, int64_t nnz) {
     L.keys = off; off = align256(off + (size_t)nnz * 8);
     L.tmp = off; off = align256(off + (size_t)nnz * 8);
     L.cursor = off; off = align256(off + (size_t)(nseg + 1) * 4);
+    L.tiny = off; off = align256(off + (size_t)(nseg + 1) * 4);
+    L.half = off; off = align256(off + (size_t)(nseg + 1) * 4);
     L.small = off; off = align256(off + (size_t)(nseg + 1) * 4);
+    L.mid = off; off = align256(off + (size_t)(nseg + 1) * 4);
     L.large = off; off = align256(off + (size_t)(nseg + 1) * 4);
+    L.huge = off; off = align256(off + (size_t)max_huge(nnz) * 4);
+    L.hinfo = off; off = align256(off + (size_t)max_huge(nnz) * 8);
+    L.htab = off; off = align256(off + (size_t)(max_huge(nnz) + 1) * 16);
     const int64_t ntiles = (nseg + 1 + kScanTile - 1) / kScanTile;
     L.sums = off; off = align256(off + (size_t)(ntiles + 1) * 4);
     L.misc = off; off = align256(off + kMiscWords * 4);
@@ -341,9 +512,16 @@ int scan_inplace(int32_t* a, int64_t n, int32_t* sums, hipStream_t s) {
 // misc in *h (error flag, counts, max length) after the sync.
 int classify_and_sync(int32_t nseg, const int32_t* ptr, char* ws, const Layout& L, int32_t* h, hipStream_t s) {
     int32_t* misc = reinterpret_cast<int32_t*>(ws + L.misc);
-    hipLaunchKernelGGL(classify, dim3(grid_for(nseg)), dim3(kBlock), 0, s, nseg, ptr,
-                       reinterpret_cast<int32_t*>(ws + L.cursor), reinterpret_cast<int32_t*>(ws + L.small),
-                       reinterpret_cast<int32_t*>(ws + L.large), misc);
+    SegLists lists;
+    lists.l[kTiny] = reinterpret_cast<int32_t*>(ws + L.tiny);
+    lists.l[kHalf] = reinterpret_cast<int32_t*>(ws + L.half);
+    lists.l[kSmall] = reinterpret_cast<int32_t*>(ws + L.small);
+    lists.l[kMid] = reinterpret_cast<int32_t*>(ws + L.mid);
+    lists.l[kLarge] = reinterpret_cast<int32_t*>(ws + L.large);
+    lists.l[kHuge] = reinterpret_cast<int32_t*>(ws + L.huge);
+    const int64_t passes = std::max<int64_t>(1, std::min<int64_t>((nseg + kClassifyThreads - 1) / kClassifyThreads, 4096));
+    hipLaunchKernelGGL(classify, dim3((unsigned)passes), dim3(kClassifyThreads), 0, s, nseg, ptr,
+                       reinterpret_cast<int32_t*>(ws + L.cursor), lists, misc);
     SPX_LAUNCH();
     SPX_HIP(hipMemcpyAsync(h, misc, kMiscWords * 4, hipMemcpyDeviceToHost, s));
     SPX_HIP(hipStreamSynchronize(s));
@@ -352,18 +530,76 @@ int classify_and_sync(int32_t nseg, const int32_t* ptr, char* ws, const Layout& 
 
 int sort_segments(const int32_t* ptr, char* ws, const Layout& L, const int32_t* h, hipStream_t s) {
     uint64_t* keys = reinterpret_cast<uint64_t*>(ws + L.keys);
-    const int32_t n_small = h[kCntSmall], n_large = h[kCntLarge];
+    const int32_t n_tiny = h[kCnt + kTiny], n_half = h[kCnt + kHalf], n_small = h[kCnt + kSmall];
+    const int32_t n_mid = h[kCnt + kMid], n_large = h[kCnt + kLarge];
+    constexpr int kWaves = kBlock / 64;
+    if (n_tiny > 0) {  // 4 segments per wave
+        const int64_t waves = (n_tiny + 3) / 4;
+        hipLaunchKernelGGL(sort_small<kTinySeg>, dim3((unsigned)((waves + kWaves - 1) / kWaves)), dim3(kBlock), 0, s,
+                           reinterpret_cast<const int32_t*>(ws + L.tiny), n_tiny, ptr, keys);
+        SPX_LAUNCH();
+    }
+    if (n_half > 0) {  // 2 segments per wave
+        const int64_t waves = (n_half + 1) / 2;
+        hipLaunchKernelGGL(sort_small<kHalfSeg>, dim3((unsigned)((waves + kWaves - 1) / kWaves)), dim3(kBlock), 0, s,
+                           reinterpret_cast<const int32_t*>(ws + L.half), n_half, ptr, keys);
+        SPX_LAUNCH();
+    }
     if (n_small > 0) {
-        hipLaunchKernelGGL(sort_small, dim3((unsigned)((n_small + 3) / 4)), dim3(kBlock), 0, s,
-                           reinterpret_cast<const int32_t*>(ws + L.small),
-                           reinterpret_cast<const int32_t*>(ws + L.misc), ptr, keys);
+        hipLaunchKernelGGL(sort_small<kSmallSeg>, dim3((unsigned)((n_small + kWaves - 1) / kWaves)), dim3(kBlock), 0,
+                           s, reinterpret_cast<const int32_t*>(ws + L.small), n_small, ptr, keys);
+        SPX_LAUNCH();
+    }
+    if (n_mid > 0) {
+        hipLaunchKernelGGL(sort_mid, dim3((unsigned)((n_mid + kWaves - 1) / kWaves)), dim3(kBlock), 0, s,
+                           reinterpret_cast<const int32_t*>(ws + L.mid), n_mid, ptr, keys);
         SPX_LAUNCH();
     }
     if (n_large > 0) {
         hipLaunchKernelGGL(sort_large, dim3((unsigned)n_large), dim3(kBlock), 0, s,
-                           reinterpret_cast<const int32_t*>(ws + L.large), ptr, keys,
-                           reinterpret_cast<uint64_t*>(ws + L.tmp));
+                           reinterpret_cast<const int32_t*>(ws + L.large), ptr, keys);
         SPX_LAUNCH();
+    }
+    const int32_t n_huge = h[kCnt + kHuge];
+    if (n_huge > 0) {
+        // lengths to the host, the segment table back (both small), then
+        // chunk sorts and merge levels over all huge keys at once
+        int2* hinfo = reinterpret_cast<int2*>(ws + L.hinfo);
+        int4* htab = reinterpret_cast<int4*>(ws + L.htab);
+        hipLaunchKernelGGL(huge_info, dim3((unsigned)((n_huge + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
+                           reinterpret_cast<const int32_t*>(ws + L.huge), n_huge, ptr, hinfo);
+        SPX_LAUNCH();
+        std::vector<int2> info((size_t)n_huge);
+        SPX_HIP(hipMemcpyAsync(info.data(), hinfo, (size_t)n_huge * sizeof(int2), hipMemcpyDeviceToHost, s));
+        SPX_HIP(hipStreamSynchronize(s));
+        std::vector<int4> tab((size_t)n_huge + 1);
+        int64_t keys_before = 0, chunks_before = 0, longest = 0;
+        for (int32_t k = 0; k < n_huge; ++k) {
+            const int64_t len = info[(size_t)k].y;
+            tab[(size_t)k] = make_int4(info[(size_t)k].x, (int32_t)len, (int32_t)keys_before, (int32_t)chunks_before);
+            keys_before += len;
+            chunks_before += (len + kChunk - 1) / kChunk;
+            longest = std::max(longest, len);
+        }
+        tab[(size_t)n_huge] = make_int4(0, 0, (int32_t)keys_before, (int32_t)chunks_before);
+        SPX_HIP(hipMemcpyAsync(htab, tab.data(), tab.size() * sizeof(int4), hipMemcpyHostToDevice, s));
+        hipLaunchKernelGGL(huge_chunks, dim3((unsigned)chunks_before), dim3(kBlock), 0, s, htab, n_huge, keys);
+        SPX_LAUNCH();
+        uint64_t* src = keys;
+        uint64_t* dst = reinterpret_cast<uint64_t*>(ws + L.tmp);
+        const unsigned grid = (unsigned)((keys_before + kBlock - 1) / kBlock);
+        int levels = 0;
+        for (int64_t w = kChunk; w < longest; w <<= 1, ++levels) {
+            hipLaunchKernelGGL(huge_merge, dim3(grid), dim3(kBlock), 0, s, htab, n_huge, (int32_t)w, src, dst);
+            SPX_LAUNCH();
+            std::swap(src, dst);
+        }
+        if (levels & 1) {  // the result is in tmp: a width past every segment copies it back
+            hipLaunchKernelGGL(huge_merge, dim3(grid), dim3(kBlock), 0, s, htab, n_huge, (int32_t)kI32MaxLen, src,
+                               dst);
+            SPX_LAUNCH();
+        }
+        SPX_HIP(hipStreamSynchronize(s));  // the host table is freed on return
     }
     return SP_OK;
 }

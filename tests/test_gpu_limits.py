@@ -126,3 +126,47 @@ def test_sell_offsets_at_the_int16_limit(reach):
     assert plan.profile()["sell_slots"] > 0
     _check_spmv(plan, m, n, rp, c, v, 50, "sell reach %d" % reach)
     _check_spmv_t(plan, m, n, cp, ri, cv, 52, "sell reach %d transposed" % reach)
+
+
+@pytest.mark.parametrize("order", ["shuffled", "row_major"])
+def test_conversions_with_long_segments(order):
+    """COO -> CSR and CSR -> CSC bit for bit where rows and columns are longer
+    than one 4096-key sort chunk (one key past it, a power of two and one
+    past it, 18 chunks), plus random entries with duplicates, in shuffled and
+    in row-major input order (row-major input gives long runs of one row
+    inside a wave)."""
+    say("conversions with long segments", order)
+    m, n = 30000, 90000
+    rng = np.random.default_rng(15)
+    rows, cols = [], []
+    # long rows 11..14 take columns >= 100, long columns 5..7 rows >= 100, the
+    # random entries both, so the long segments have exactly these lengths
+    for r, L in ((11, 4097), (12, 8192), (13, 8193), (14, 70000)):
+        rows.append(np.full(L, r))
+        cols.append(100 + rng.choice(n - 100, L, replace=False))
+    for c, L in ((5, 4097), (6, 16384), (7, 29899)):
+        rows.append(100 + rng.choice(m - 100, L, replace=False))
+        cols.append(np.full(L, c))
+    r_rand = rng.integers(100, m, 200000)
+    c_rand = rng.integers(100, n, 200000)
+    dup = rng.random(r_rand.size) < 0.05
+    rows += [r_rand, r_rand[dup]]
+    cols += [c_rand, c_rand[dup]]
+    row = np.concatenate(rows).astype(np.int32)
+    col = np.concatenate(cols).astype(np.int32)
+    val = rng.uniform(-1, 1, row.size).astype(np.float32)
+    p = rng.permutation(row.size) if order == "shuffled" else np.lexsort((col, row))
+    row, col, val = row[p], col[p], val[p]
+    rp, c, v = oracle.coo_to_csr(m, n, row, col, val)
+    cp, ri, cv = oracle.csr_to_csc(m, n, rp, c, v)
+    lens, clens = np.diff(rp), np.diff(cp)
+    assert [lens[r] for r in (11, 12, 13, 14)] == [4097, 8192, 8193, 70000]
+    assert [clens[c] for c in (5, 6, 7)] == [4097, 16384, 29899]
+    g_rp, g_c, g_v = sp.csr_build_from_coo(m, n, dev(row), dev(col), dev(val))
+    np.testing.assert_array_equal(host(g_rp), rp)
+    np.testing.assert_array_equal(host(g_c), c)
+    np.testing.assert_array_equal(host(g_v).view(np.uint32), v.view(np.uint32))
+    g_cp, g_ri, g_cv = sp.csr_to_csc(m, n, g_rp, g_c, g_v)
+    np.testing.assert_array_equal(host(g_cp), cp)
+    np.testing.assert_array_equal(host(g_ri), ri)
+    np.testing.assert_array_equal(host(g_cv).view(np.uint32), cv.view(np.uint32))
