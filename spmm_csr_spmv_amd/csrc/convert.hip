@@ -24,7 +24,6 @@
 #include "device_common.h"
 
 #include <algorithm>
-#include <vector>
 
 namespace spx {
 
@@ -382,13 +381,50 @@ __global__ __launch_bounds__(kBlock) void sort_large(const int32_t* __restrict__
 // ---- segments longer than kChunk: the whole GPU sorts them together.
 // tab[k] = {begin, length, keys before segment k, chunks before segment k}
 // over the huge segments, and tab[n] = {0, 0, all keys, all chunks}.
-__global__ __launch_bounds__(kBlock) void huge_info(const int32_t* __restrict__ list, int32_t n,
-                                                    const int32_t* __restrict__ ptr, int2* __restrict__ out) {
-    const int32_t k = blockIdx.x * kBlock + threadIdx.x;
-    if (k < n) {
-        const int32_t s = list[k];
-        out[k] = make_int2(ptr[s], ptr[s + 1] - ptr[s]);
+// One workgroup builds the table: prefix sums of the segments' key and chunk
+// counts, 1024 segments per pass.
+constexpr int kTableThreads = 1024;
+__global__ __launch_bounds__(kTableThreads) void huge_table(const int32_t* __restrict__ list, int32_t n,
+                                                           const int32_t* __restrict__ ptr, int4* __restrict__ tab) {
+    constexpr int NW = kTableThreads / 64;
+    __shared__ int wk[NW], wc[NW];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int carry_k = 0, carry_c = 0;  // keys and chunks of the passes before (every thread)
+    for (int32_t k0 = 0; k0 < n; k0 += kTableThreads) {
+        const int32_t k = k0 + tid;
+        int32_t b = 0, len = 0;
+        if (k < n) {
+            const int32_t s = list[k];
+            b = ptr[s];
+            len = ptr[s + 1] - b;
+        }
+        const int ch = (len + kChunk - 1) / kChunk;
+        int ik = len, ic = ch;  // inclusive sums over the wave
+        for (int off = 1; off < 64; off <<= 1) {
+            const int tk = __shfl_up(ik, off, 64), tc = __shfl_up(ic, off, 64);
+            if (lane >= off) {
+                ik += tk;
+                ic += tc;
+            }
+        }
+        if (lane == 63) {
+            wk[w] = ik;
+            wc[w] = ic;
+        }
+        __syncthreads();
+        int bk = carry_k, bc = carry_c;
+        for (int j = 0; j < w; ++j) {
+            bk += wk[j];
+            bc += wc[j];
+        }
+        if (k < n) tab[k] = make_int4(b, len, bk + ik - len, bc + ic - ch);
+        for (int j = 0; j < NW; ++j) {
+            carry_k += wk[j];
+            carry_c += wc[j];
+        }
+        __syncthreads();  // wk and wc are rewritten by the next pass
     }
+    if (tid == 0) tab[n] = make_int4(0, 0, carry_k, carry_c);
 }
 
 // The last k in [0, n) with field(tab[k]) <= f (field: .z keys or .w chunks).
@@ -408,6 +444,7 @@ __global__ __launch_bounds__(kBlock) void huge_chunks(const int4* __restrict__ t
                                                       uint64_t* __restrict__ keys) {
     __shared__ uint64_t sh[kChunk];
     const int32_t c = blockIdx.x;
+    if (c >= tab[n].w) return;  // the grid is an upper bound
     const int4 t = tab[huge_of<true>(tab, n, c)];
     const int32_t j = c - t.w;  // chunk within the segment
     const int32_t n_keys = min(kChunk, t.y - j * kChunk);
@@ -460,7 +497,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout shared by both builders (nseg = number of segments).
 struct Layout {
-    size_t keys, tmp, cursor, tiny, half, small, mid, large, huge, hinfo, htab, sums, misc, total;
+    size_t keys, tmp, cursor, tiny, half, small, mid, large, huge, htab, sums, misc, total;
 };
 
 // Segments longer than kChunk: at most this many.
@@ -478,7 +515,6 @@ Layout layout(int64_t nseg, int64_t nnz) {
     L.mid = off; off = align256(off + (size_t)(nseg + 1) * 4);
     L.large = off; off = align256(off + (size_t)(nseg + 1) * 4);
     L.huge = off; off = align256(off + (size_t)max_huge(nnz) * 4);
-    L.hinfo = off; off = align256(off + (size_t)max_huge(nnz) * 8);
     L.htab = off; off = align256(off + (size_t)(max_huge(nnz) + 1) * 16);
     const int64_t ntiles = (nseg + 1 + kScanTile - 1) / kScanTile;
     L.sums = off; off = align256(off + (size_t)(ntiles + 1) * 4);
@@ -528,7 +564,7 @@ int classify_and_sync(int32_t nseg, const int32_t* ptr, char* ws, const Layout& 
     return SP_OK;
 }
 
-int sort_segments(const int32_t* ptr, char* ws, const Layout& L, const int32_t* h, hipStream_t s) {
+int sort_segments(const int32_t* ptr, int64_t nnz, char* ws, const Layout& L, const int32_t* h, hipStream_t s) {
     uint64_t* keys = reinterpret_cast<uint64_t*>(ws + L.keys);
     const int32_t n_tiny = h[kCnt + kTiny], n_half = h[kCnt + kHalf], n_small = h[kCnt + kSmall];
     const int32_t n_mid = h[kCnt + kMid], n_large = h[kCnt + kLarge];
@@ -562,32 +598,21 @@ int sort_segments(const int32_t* ptr, char* ws, const Layout& L, const int32_t* 
     }
     const int32_t n_huge = h[kCnt + kHuge];
     if (n_huge > 0) {
-        // lengths to the host, the segment table back (both small), then
-        // chunk sorts and merge levels over all huge keys at once
-        int2* hinfo = reinterpret_cast<int2*>(ws + L.hinfo);
+        // the segment table is built on the device; the grids take upper
+        // bounds (every huge segment is at most the longest, all together
+        // at most nnz keys) and their kernels stop at the table's totals
         int4* htab = reinterpret_cast<int4*>(ws + L.htab);
-        hipLaunchKernelGGL(huge_info, dim3((unsigned)((n_huge + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
-                           reinterpret_cast<const int32_t*>(ws + L.huge), n_huge, ptr, hinfo);
+        hipLaunchKernelGGL(huge_table, dim3(1), dim3(kTableThreads), 0, s,
+                           reinterpret_cast<const int32_t*>(ws + L.huge), n_huge, ptr, htab);
         SPX_LAUNCH();
-        std::vector<int2> info((size_t)n_huge);
-        SPX_HIP(hipMemcpyAsync(info.data(), hinfo, (size_t)n_huge * sizeof(int2), hipMemcpyDeviceToHost, s));
-        SPX_HIP(hipStreamSynchronize(s));
-        std::vector<int4> tab((size_t)n_huge + 1);
-        int64_t keys_before = 0, chunks_before = 0, longest = 0;
-        for (int32_t k = 0; k < n_huge; ++k) {
-            const int64_t len = info[(size_t)k].y;
-            tab[(size_t)k] = make_int4(info[(size_t)k].x, (int32_t)len, (int32_t)keys_before, (int32_t)chunks_before);
-            keys_before += len;
-            chunks_before += (len + kChunk - 1) / kChunk;
-            longest = std::max(longest, len);
-        }
-        tab[(size_t)n_huge] = make_int4(0, 0, (int32_t)keys_before, (int32_t)chunks_before);
-        SPX_HIP(hipMemcpyAsync(htab, tab.data(), tab.size() * sizeof(int4), hipMemcpyHostToDevice, s));
-        hipLaunchKernelGGL(huge_chunks, dim3((unsigned)chunks_before), dim3(kBlock), 0, s, htab, n_huge, keys);
+        const int64_t longest = h[kMaxLen];
+        const int64_t max_keys = std::min<int64_t>(nnz, (int64_t)n_huge * longest);
+        const int64_t max_chunks = std::min<int64_t>(max_keys / kChunk + n_huge, (int64_t)n_huge * ((longest + kChunk - 1) / kChunk));
+        hipLaunchKernelGGL(huge_chunks, dim3((unsigned)max_chunks), dim3(kBlock), 0, s, htab, n_huge, keys);
         SPX_LAUNCH();
         uint64_t* src = keys;
         uint64_t* dst = reinterpret_cast<uint64_t*>(ws + L.tmp);
-        const unsigned grid = (unsigned)((keys_before + kBlock - 1) / kBlock);
+        const unsigned grid = (unsigned)((max_keys + kBlock - 1) / kBlock);
         int levels = 0;
         for (int64_t w = kChunk; w < longest; w <<= 1, ++levels) {
             hipLaunchKernelGGL(huge_merge, dim3(grid), dim3(kBlock), 0, s, htab, n_huge, (int32_t)w, src, dst);
@@ -599,7 +624,6 @@ int sort_segments(const int32_t* ptr, char* ws, const Layout& L, const int32_t* 
                                dst);
             SPX_LAUNCH();
         }
-        SPX_HIP(hipStreamSynchronize(s));  // the host table is freed on return
     }
     return SP_OK;
 }
@@ -663,7 +687,7 @@ int coo_to_csr_device(int64_t m, int64_t n, int64_t nnz, const int32_t* coo_row,
     hipLaunchKernelGGL(coo_scatter, dim3(grid_for(nnz)), dim3(kBlock), 0, s, nnz, coo_row, coo_col,
                        reinterpret_cast<int32_t*>(ws + L.cursor), keys);
     SPX_LAUNCH();
-    rc = sort_segments(row_ptr, ws, L, h, s);
+    rc = sort_segments(row_ptr, nnz, ws, L, h, s);
     if (rc != SP_OK) return rc;
     hipLaunchKernelGGL(gather_out, dim3(grid_for(nnz)), dim3(kBlock), 0, s, nnz, keys, coo_val, col_idx, val);
     SPX_LAUNCH();
@@ -702,7 +726,7 @@ int csr_to_csc_device(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr,
     hipLaunchKernelGGL(csr_scatter, dim3(grid_for(nnz)), dim3(kBlock), 0, s, nnz, row_ptr, (int32_t)m, col_idx,
                        reinterpret_cast<int32_t*>(ws + L.cursor), keys);
     SPX_LAUNCH();
-    rc = sort_segments(col_ptr, ws, L, h, s);
+    rc = sort_segments(col_ptr, nnz, ws, L, h, s);
     if (rc != SP_OK) return rc;
     hipLaunchKernelGGL(gather_out, dim3(grid_for(nnz)), dim3(kBlock), 0, s, nnz, keys, val, row_idx, cval);
     SPX_LAUNCH();

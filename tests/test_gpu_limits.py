@@ -170,3 +170,28 @@ def test_conversions_with_long_segments(order):
     np.testing.assert_array_equal(host(g_cp), cp)
     np.testing.assert_array_equal(host(g_ri), ri)
     np.testing.assert_array_equal(host(g_cv).view(np.uint32), cv.view(np.uint32))
+
+
+def test_conversions_with_many_long_segments():
+    """More than 1024 rows longer than one sort chunk, so the table of long
+    segments takes several passes of its one-workgroup prefix sum; then the
+    transpose, whose columns are all short."""
+    say("conversions with 1100 long rows")
+    m, n = 1100, 200000
+    rng = np.random.default_rng(16)
+    lens = rng.integers(4097, 4400, m)
+    row = np.repeat(np.arange(m), lens).astype(np.int32)
+    col = np.concatenate([rng.choice(n, L, replace=False) for L in lens]).astype(np.int32)
+    val = rng.uniform(-1, 1, row.size).astype(np.float32)
+    p = rng.permutation(row.size)
+    row, col, val = row[p], col[p], val[p]
+    rp, c, v = oracle.coo_to_csr(m, n, row, col, val)
+    cp, ri, cv = oracle.csr_to_csc(m, n, rp, c, v)
+    g_rp, g_c, g_v = sp.csr_build_from_coo(m, n, dev(row), dev(col), dev(val))
+    np.testing.assert_array_equal(host(g_rp), rp)
+    np.testing.assert_array_equal(host(g_c), c)
+    np.testing.assert_array_equal(host(g_v).view(np.uint32), v.view(np.uint32))
+    g_cp, g_ri, g_cv = sp.csr_to_csc(m, n, g_rp, g_c, g_v)
+    np.testing.assert_array_equal(host(g_cp), cp)
+    np.testing.assert_array_equal(host(g_ri), ri)
+    np.testing.assert_array_equal(host(g_cv).view(np.uint32), cv.view(np.uint32))
