@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstring>
 #include <new>
+#include <thread>
 #include <vector>
 
 #include "internal.h"
@@ -102,6 +103,27 @@ namespace {
 
 // Nearest-rank percentile of the sorted lengths: smallest L such that at least
 // q percent of the rows have length <= L.
+// Runs f(i) for every i in [0, n) on up to 16 host threads, each taking one
+// contiguous block of indices; f must not throw.  Results do not depend on
+// the thread count when every f(i) writes only what belongs to i.
+template <class F>
+void parallel_for(int64_t n, F f) {
+    const int64_t hw = (int64_t)std::thread::hardware_concurrency();
+    const int64_t T = std::max<int64_t>(1, std::min<int64_t>({hw, (int64_t)16, n / 64}));
+    if (T < 2) {
+        for (int64_t i = 0; i < n; ++i) f(i);
+        return;
+    }
+    const int64_t per = (n + T - 1) / T;
+    std::vector<std::thread> pool;
+    pool.reserve((size_t)T);
+    for (int64_t t = 0; t < T; ++t)
+        pool.emplace_back([&f, t, per, n] {
+            for (int64_t i = t * per; i < std::min(n, (t + 1) * per); ++i) f(i);
+        });
+    for (std::thread& th : pool) th.join();
+}
+
 int64_t nearest_rank(std::vector<int32_t>& len, int q) {
     const int64_t m = (int64_t)len.size();
     const int64_t k = (q * m + 99) / 100 - 1;
@@ -221,11 +243,12 @@ void build_sell(const std::vector<int32_t>& hptr, const sp_plan_options& o, Dir&
     }
     d.sell_perm.resize((size_t)m);
     for (int64_t i = 0; i < m; ++i) d.sell_perm[(size_t)i] = (int32_t)i;
-    for (int64_t w = 0; w < m; w += o.sell_sigma) {
-        const int64_t e = std::min<int64_t>(m, w + o.sell_sigma);
+    // each window of sigma rows sorted on its own (windows in parallel)
+    parallel_for((m + o.sell_sigma - 1) / o.sell_sigma, [&](int64_t i) {
+        const int64_t w = i * o.sell_sigma, e = std::min<int64_t>(m, w + o.sell_sigma);
         std::stable_sort(d.sell_perm.begin() + w, d.sell_perm.begin() + e,
                          [&](int32_t a, int32_t b) { return len[(size_t)a] > len[(size_t)b]; });
-    }
+    });
     d.sell_len.resize((size_t)m);
     for (int64_t k = 0; k < m; ++k) d.sell_len[(size_t)k] = len[(size_t)d.sell_perm[(size_t)k]];
     const int64_t slices = (m + 63) / 64;
@@ -395,8 +418,16 @@ int fetch_columns(const Dir& d, hipStream_t s, std::vector<int32_t>& hidx) {
     if (hipMemcpyAsync(hidx.data(), d.idx, (size_t)d.nnz * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
         return SP_ERR_HIP;
     if (hipStreamSynchronize(s) != hipSuccess) return SP_ERR_HIP;
-    for (const int32_t c : hidx)
-        if (c < 0 || c >= d.cols) return SP_ERR_INDEX;
+    constexpr int64_t kBlockEntries = 1 << 20;
+    const int64_t blocks = (d.nnz + kBlockEntries - 1) / kBlockEntries;
+    std::vector<char> bad((size_t)blocks, 0);
+    parallel_for(blocks, [&](int64_t b) {
+        const int64_t e = std::min<int64_t>(d.nnz, (b + 1) * kBlockEntries);
+        for (int64_t q = b * kBlockEntries; q < e; ++q)
+            if (hidx[(size_t)q] < 0 || hidx[(size_t)q] >= d.cols) bad[(size_t)b] = 1;
+    });
+    for (const char f : bad)
+        if (f) return SP_ERR_INDEX;
     return SP_OK;
 }
 
@@ -542,30 +573,46 @@ int build_xwin(const std::vector<int32_t>& hptr, int32_t bits, Dir& d, hipStream
     std::vector<int32_t> hidx;
     const int rc = fetch_columns(d, s, hidx);
     if (rc != SP_OK) return rc;
-    // runs (padded to multiples of 8) and the stream position of every entry
+    // runs (padded to multiples of 8) and the stream position of every entry;
+    // chunks are independent but for where each starts: their padded sizes
+    // in parallel, the starts in order, then runs and positions in parallel
     std::vector<int32_t> runs((size_t)(n_chunks * (nw + 1)));
     std::vector<int32_t> pos((size_t)nnz);
-    std::vector<int32_t> cnt((size_t)nw), cur((size_t)nw);
     std::vector<int2> chunk_q((size_t)n_chunks);
-    int64_t total = 0;
-    for (int64_t c = 0; c < n_chunks; ++c) {
+    std::vector<int64_t> first((size_t)n_chunks + 1);
+    parallel_for(n_chunks, [&](int64_t c) {
         const int4 ch = chunks[(size_t)c];
-        std::fill(cnt.begin(), cnt.end(), 0);
-        for (int32_t q = ch.x; q < ch.y; ++q) cnt[(size_t)(hidx[(size_t)q] >> bits)] += 1;
+        int32_t cnt[spx::kXwMaxWindows] = {};
+        for (int32_t q = ch.x; q < ch.y; ++q) cnt[hidx[(size_t)q] >> bits] += 1;
         int32_t* row = runs.data() + (size_t)(c * (nw + 1));
-        const int64_t begin = total;
+        int64_t span = 0;
         for (int64_t w = 0; w < nw; ++w) {
-            row[w] = (int32_t)total;
-            cur[(size_t)w] = (int32_t)total;
-            total += (cnt[(size_t)w] + 7) & ~7;
+            row[w] = (cnt[w] + 7) & ~7;  // padded length for now
+            span += row[w];
         }
-        if (total > kI32Max) return SP_ERR_UNSUPPORTED;
-        row[nw] = (int32_t)total;
-        for (int32_t q = ch.x; q < ch.y; ++q) pos[(size_t)q] = cur[(size_t)(hidx[(size_t)q] >> bits)]++;
+        first[(size_t)c + 1] = span;
+    });
+    first[0] = 0;
+    for (int64_t c = 0; c < n_chunks; ++c) first[(size_t)c + 1] += first[(size_t)c];
+    const int64_t total = first[(size_t)n_chunks];
+    if (total > kI32Max) return SP_ERR_UNSUPPORTED;
+    parallel_for(n_chunks, [&](int64_t c) {
+        const int4 ch = chunks[(size_t)c];
+        int32_t* row = runs.data() + (size_t)(c * (nw + 1));
+        int32_t cur[spx::kXwMaxWindows];
+        int64_t at = first[(size_t)c];
+        for (int64_t w = 0; w < nw; ++w) {
+            const int32_t len = row[w];
+            row[w] = (int32_t)at;
+            cur[w] = (int32_t)at;
+            at += len;
+        }
+        row[nw] = (int32_t)at;
+        for (int32_t q = ch.x; q < ch.y; ++q) pos[(size_t)q] = cur[hidx[(size_t)q] >> bits]++;
         chunk_q[(size_t)c] = make_int2(ch.x, ch.y - ch.x);
-        chunks[(size_t)c].x = (int32_t)begin;
-        chunks[(size_t)c].y = (int32_t)total;
-    }
+        chunks[(size_t)c].x = (int32_t)first[(size_t)c];
+        chunks[(size_t)c].y = (int32_t)at;
+    });
     // window-major run starts: window after window, runs in chunk order
     std::vector<int32_t> wm_runs((size_t)(n_chunks * nw));
     {
