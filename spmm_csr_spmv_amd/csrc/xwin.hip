@@ -19,9 +19,10 @@
 //     added in segment order at the end.  Chunks partition the CSR entries in
 //     order.  Run (c, w) = the entries of chunk c in window w, CSR order,
 //     padded to a multiple of 8 slots.
-//   * chunk-major stream (position in the chunk's CSR order as uint16,
-//     0xffff in padding; the products of a call): chunk after chunk, the
-//     chunk's runs in window order.  runs[c][w] is where run (c, w) starts,
+//   * chunk-major stream (the entry's place in the row kernel's LDS copy of
+//     the chunk, as a byte offset: 4 x its position in the chunk's CSR
+//     order, a padding slot pointing past the chunk; the products of a
+//     call): chunk after chunk, the chunk's runs in window order.  runs[c][w] is where run (c, w) starts,
 //     runs[c][nw] the chunk's end.
 //   * window-major stream (column within the window as uint16, value):
 //     window after window, the window's runs in chunk order.
@@ -57,6 +58,7 @@
 //   segment order, writes y and puts the counter back to zero, so the sum
 //   does not depend on which workgroup arrives last.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 
@@ -66,10 +68,10 @@ namespace {
 
 constexpr int kXwProdThreads = 1024;
 constexpr int kXwWords = kXwChunk / 32;  // row-start bitmap words of a chunk
-constexpr uint32_t kXwPad = 0xffffu;     // position of a padding slot
 constexpr int kNoRun = -2147483647 - 1;  // run map entry of a group that starts no run
+constexpr uint32_t kXwSpare = 4u * kXwChunk;  // byte offset of the first spare slot past a chunk
 static_assert(kXwChunk % 32 == 0, "chunk bitmap in whole words");
-static_assert(kXwChunk < (int)kXwPad && kXwMaxRows <= 32767, "local positions and ranks fit 16 bits");
+static_assert((kXwChunk + 64) * 4 <= 65536 && kXwMaxRows <= 32767, "LDS byte offsets and ranks fit 16 bits");
 static_assert(kXwPieceRuns <= kXwProdThreads, "one thread per run in the piece table");
 static_assert(kXwMaxWindows <= 256 && kXwPieceRuns < (1 << 23), "piece descriptor packs window and run count");
 constexpr int kXwProdGroups = kXwPiece / 8 / kXwProdThreads;  // groups of 8 slots per thread and piece
@@ -135,35 +137,42 @@ __device__ __forceinline__ void chunk_row_sums(const float* ps, int n, const uin
     float hsum = 0.0f, tsum = 0.0f;
     if (e0 < e1) {
         const int r0 = row_rank(rbits, wpre, e0);
-        int r = r0;
+        // the current row's and the lane's sink slot as byte offsets in ysh
+        uint32_t rb = 4u * r0;
+        const uint32_t sb = 4u * (kXwMaxRows + lane);
+        char* const yb = reinterpret_cast<char*>(ysh);
         float acc = 0.0f;
-        const int sink = kXwMaxRows + lane;
-        for (int eb = e0; eb < e1; eb += 16) {
-            // four 16-byte reads in flight; each e is a multiple of 4 below
-            // kXwChunk, so the reads stay in ps (values past e1 are zeroed)
+        // one block of nv <= 16 entries from eb: row starts at eb..eb+15
+        // (bit j), without entry e0 and past nv; kTail masks the values past
+        // nv (a full block reads only its own entries)
+        auto block = [&](int eb, int nv, auto tail) {
+            constexpr bool kTail = decltype(tail)::value;
             float4 v[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const float4*>(ps + min(eb + 4 * i, kXwChunk - 4));
-            // row starts at eb..eb+15 (bit j), without entry e0 and past e1
+            for (int i = 0; i < 4; ++i)
+                v[i] = *reinterpret_cast<const float4*>(ps + (kTail ? min(eb + 4 * i, kXwChunk - 4) : eb + 4 * i));
             const int wd = eb >> 5, sh = eb & 31;
             const uint32_t lo = rbits[wd], hi = rbits[min(wd + 1, kXwWords - 1)];
             uint32_t m = (lo >> sh) | (sh ? hi << (32 - sh) : 0u);
-            const int nv = min(e1 - eb, 16);
-            m &= (nv >= 16 ? 0xffffu : ((1u << nv) - 1u)) & (eb == e0 ? ~1u : ~0u);
+            m &= (kTail ? ((1u << nv) - 1u) : 0xffffu) & (eb == e0 ? ~1u : ~0u);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float vv[4] = {4 * i + 0 < nv ? v[i].x : 0.0f, 4 * i + 1 < nv ? v[i].y : 0.0f,
-                                     4 * i + 2 < nv ? v[i].z : 0.0f, 4 * i + 3 < nv ? v[i].w : 0.0f};
+                const float vv[4] = {!kTail || 4 * i + 0 < nv ? v[i].x : 0.0f, !kTail || 4 * i + 1 < nv ? v[i].y : 0.0f,
+                                     !kTail || 4 * i + 2 < nv ? v[i].z : 0.0f, !kTail || 4 * i + 3 < nv ? v[i].w : 0.0f};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     // a row starts here: the current one is complete (kept in LDS)
-                    const bool st = (m >> (4 * i + j)) & 1u;
-                    ysh[st ? r : sink] = acc;
-                    r += st ? 1 : 0;
+                    const bool st = (m & (1u << (4 * i + j))) != 0u;
+                    *reinterpret_cast<float*>(yb + (st ? rb : sb)) = acc;
+                    rb += st ? 4u : 0u;
                     acc = st ? vv[j] : acc + vv[j];
                 }
             }
-        }
+        };
+        int eb = e0;
+        for (; eb + 16 <= e1; eb += 16) block(eb, 16, std::false_type{});
+        if (eb < e1) block(eb, e1 - eb, std::true_type{});
+        const int r = (int)(rb >> 2);
         fr = r0;
         lr = r;
         // the first row's part in this slice: stored in the loop if that row
@@ -384,7 +393,7 @@ __global__ __launch_bounds__(kXwRowThreads) void xw_rows_kernel(const XwRowArgs 
             pv[j] = __builtin_nontemporal_load(reinterpret_cast<const v4f32*>(a.prod + c.x + f));
             po[j] = *reinterpret_cast<const uint2*>(a.off + c.x + f);
         } else {
-            po[j] = make_uint2(0xffffffffu, 0xffffffffu);
+            po[j] = make_uint2(kXwSpare | (kXwSpare << 16), kXwSpare | (kXwSpare << 16));  // past the chunk
         }
     };
     auto fetch_rows = [&](const int4& c) {
@@ -436,17 +445,16 @@ __global__ __launch_bounds__(kXwRowThreads) void xw_rows_kernel(const XwRowArgs 
             for (int j = 0; j < kXwRowLoads; ++j)
                 atomicOr(&rbits[b1[j] > b0[j] ? b0[j] >> 5 : kXwWords + (tid & 63)], 1u << (b0[j] & 31));
         }
-        // ---- the chunk's products into CSR order; the positions are a
-        // permutation of 0..n-1 plus padding, which goes to the lane's own
-        // slot past the chunk, so no two stores of a wave meet
-        const uint32_t sink = kXwChunk + (tid & 63);
+        // ---- the chunk's products into CSR order: the stream holds each
+        // slot's byte offset in ps, a permutation of the chunk's n places
+        // plus padding slots, which point to the 64 spare slots past them
+        char* const psb = reinterpret_cast<char*>(ps);
 #pragma unroll
         for (int j = 0; j < kXwSpanLoads; ++j) {
-            const uint32_t o0 = po[j].x & 0xffffu, o1 = po[j].x >> 16, o2 = po[j].y & 0xffffu, o3 = po[j].y >> 16;
-            ps[o0 != kXwPad ? o0 : sink] = pv[j].x;
-            ps[o1 != kXwPad ? o1 : sink] = pv[j].y;
-            ps[o2 != kXwPad ? o2 : sink] = pv[j].z;
-            ps[o3 != kXwPad ? o3 : sink] = pv[j].w;
+            *reinterpret_cast<float*>(psb + (po[j].x & 0xffffu)) = pv[j].x;
+            *reinterpret_cast<float*>(psb + (po[j].x >> 16)) = pv[j].y;
+            *reinterpret_cast<float*>(psb + (po[j].y & 0xffffu)) = pv[j].z;
+            *reinterpret_cast<float*>(psb + (po[j].y >> 16)) = pv[j].w;
             if (more) fetch_slot(cn, j);
         }
         __syncthreads();
@@ -509,7 +517,7 @@ __global__ __launch_bounds__(kBlock) void xw_pad_kernel(int64_t total, uint16_t*
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBlock) {
         wcol[i] = 0;
         wval[i] = 0.0f;
-        off[i] = (uint16_t)kXwPad;
+        off[i] = (uint16_t)(4 * (kXwChunk + (int)(i & 63)));  // one of the 64 spare slots
     }
 }
 
@@ -533,7 +541,7 @@ __global__ __launch_bounds__(kBlock) void xw_build_kernel(
         const int pw = p + delta[col >> bits];
         wcol[pw] = (uint16_t)((uint32_t)col & mask);
         wval[pw] = val[q];
-        off[p] = (uint16_t)k;
+        off[p] = (uint16_t)(4 * k);
     }
 }
 
