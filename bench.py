@@ -476,6 +476,26 @@ def main():
     if bound == "mfma":
         result["roofline"]["hbm_gbs"] = round(per_launch_bytes / (launch_ms * 1e-3) / 1e9, 1)
     result["roofline"]["event_ms_min"] = round(float(np.min(ev_ms)), 5)
+    # the copy rate this GPU measures now (outside the timed region): a plain
+    # 256 MiB device copy, read + write bytes over its time, as a reference
+    # beside the 8 TB/s spec (algorithmic bytes can exceed what a kernel
+    # moves, so the fraction can pass 1)
+    if bound == "hbm":
+        ref = torch.ones(64 << 20, device="cuda")
+        dst = torch.empty_like(ref)
+        dst.copy_(ref)
+        t = []
+        for _ in range(5):
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            dst.copy_(ref)
+            a1.record(stream)
+            torch.cuda.synchronize()
+            t.append(a0.elapsed_time(a1))
+        del ref, dst
+        copy_gbs = 2 * (64 << 20) * 4 / (float(np.median(t)) * 1e-3) / 1e9
+        result["roofline"]["measured_copy_gbs"] = round(copy_gbs, 1)
+        result["roofline"]["frac_of_copy"] = round(achieved / copy_gbs, 4)
     result["gflops_event"] = round(per_launch_flops / (launch_ms * 1e-3) / 1e9, 2)
 
     # ---------------- cold-cache steps (outside the timed region, on request)
