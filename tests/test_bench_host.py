@@ -1,0 +1,60 @@
+"""bench.py on the host: it refuses more than one GPU, its algorithmic byte
+and flop models give the figures of the measurement plan (8 bytes per entry,
+the LSMR page's section 1 bound, plus the vectors once), and a committed HBM
+traffic summary counts only while the kernels it was taken on are
+unchanged."""
+import json
+import os
+import shutil
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_byte_and_flop_models():
+    # SpMV: values and column indices, row pointer, x and y once (y twice with beta)
+    assert bench.spmv_bytes(4, 5, 7) == 8 * 7 + 4 * 5 + 4 * 5 + 4 * 4
+    assert bench.spmv_bytes(4, 5, 7, True) - bench.spmv_bytes(4, 5, 7) == 4 * 4
+    assert bench.spmv_flops(4, 7) == 14 and bench.spmv_flops(4, 7, True) == 22
+    # the workloads' figures: power-law SpMV, one stencil direction (beta != 0)
+    assert bench.spmv_bytes(1 << 22, 1 << 22, 46823854) == 424922484
+    assert bench.spmv_bytes(4096000, 4096000, 109215352, True) == 939258820
+    # SpMM reads B and writes C once
+    assert bench.spmm_bytes(3, 4, 5, 8) == 8 * 5 + 4 * 4 + 4 * 4 * 8 + 4 * 3 * 8
+    # BSR SpMM: 6554 bf16 64 x 64 blocks, B 16384 x 512 bf16, C fp32: about 104.0 MB, 27.49 GFLOP
+    b = bench.bsr_bytes(256, 256, 64, 6554, 512)
+    assert b == 2 * 6554 * 4096 + 4 * (6554 + 256 + 1) + 2 * 16384 * 512 + 4 * 16384 * 512
+    assert abs(b / 1e6 - 104.0) < 0.1
+    assert bench.bsr_flops(6554, 64, 512) == 2 * 6554 * 64 * 64 * 512  # 27.49 GFLOP
+    # BSR SpMV with fp32 blocks
+    assert bench.bsr_spmv_bytes(16384, 16384, 64, 6554) == 4 * 6554 * 4096 + 4 * (6554 + 256 + 1) + 8 * 16384
+
+
+def test_traffic_counts_only_for_unchanged_kernels(tmp_path, monkeypatch):
+    wl = "spmv_powerlaw"
+    for f in bench.KERNEL_SOURCES["spmv"]:
+        os.makedirs(tmp_path / os.path.dirname(f), exist_ok=True)
+        shutil.copy(os.path.join(ROOT, f), tmp_path / f)
+    monkeypatch.setattr(bench, "HERE", str(tmp_path))
+    assert bench.load_traffic(wl, 1) is None  # no summary
+    os.makedirs(tmp_path / "profiles")
+    with open(tmp_path / "profiles" / ("traffic_%s.json" % wl), "w") as fh:
+        json.dump(dict(kernel_fingerprint=bench.kernel_fingerprint(wl), bytes_per_launch=123), fh)
+    assert bench.load_traffic(wl, 1) == 123
+    # any change to a source of that workload's kernels retires the summary
+    with open(tmp_path / bench.KERNEL_SOURCES["spmv"][0], "a") as fh:
+        fh.write("\n")
+    assert bench.load_traffic(wl, 1) is None
+    # the other families do not depend on it
+    assert bench.kernel_family("bsr_blocks") == "bsr" and bench.kernel_family("spmm_lognormal_N32") == "spmm"
+    assert bench.kernel_family("spmm_clustered_N32") == "wcsr" and bench.kernel_family("bsr_spmv") == "bsr_spmv"
