@@ -124,11 +124,20 @@ void parallel_for(int64_t n, F f) {
     for (std::thread& th : pool) th.join();
 }
 
-int64_t nearest_rank(std::vector<int32_t>& len, int q) {
+// Nearest-rank q-th percentile of the lengths: the (ceil(q m / 100))-th
+// smallest.  hist[l] counts the rows of length l for l < hist.size(); a rank
+// beyond the histogram is found by selection on a copy.
+int64_t nearest_rank(const std::vector<int32_t>& len, const std::vector<int64_t>& hist, int q) {
     const int64_t m = (int64_t)len.size();
     const int64_t k = (q * m + 99) / 100 - 1;
-    std::nth_element(len.begin(), len.begin() + k, len.end());
-    return len[(size_t)k];
+    int64_t below = 0;
+    for (size_t l = 0; l < hist.size(); ++l) {
+        below += hist[l];
+        if (below > k) return (int64_t)l;
+    }
+    std::vector<int32_t> c(len);
+    std::nth_element(c.begin(), c.begin() + k, c.end());
+    return c[(size_t)k];
 }
 
 void profile_rows(const std::vector<int32_t>& hptr, Dir& d) {
@@ -157,8 +166,11 @@ void profile_rows(const std::vector<int32_t>& hptr, Dir& d) {
     p.cv = mean > 0.0 ? std::sqrt(var) / mean : 0.0;
     p.max_len = mx;
     p.empty_rows = empty;
-    p.p95 = nearest_rank(len, 95);
-    p.p99 = nearest_rank(len, 99);
+    std::vector<int64_t> hist((size_t)std::min<int64_t>(mx + 1, (int64_t)1 << 20), 0);
+    for (const int32_t l : len)
+        if ((size_t)l < hist.size()) hist[(size_t)l] += 1;
+    p.p95 = nearest_rank(len, hist, 95);
+    p.p99 = nearest_rank(len, hist, 99);
 }
 
 // Row-to-bin assignment (see the sp_plan_options comment in the public header).
