@@ -67,6 +67,7 @@ namespace spx {
 namespace {
 
 constexpr int kXwProdThreads = 1024;
+typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));  // 4 stream positions
 constexpr int kXwWords = kXwChunk / 32;  // row-start bitmap words of a chunk
 constexpr int kNoRun = -2147483647 - 1;  // run map entry of a group that starts no run
 constexpr uint32_t kXwSpare = 4u * kXwChunk;  // byte offset of the first spare slot past a chunk
@@ -391,7 +392,8 @@ __global__ __launch_bounds__(kXwRowThreads) void xw_rows_kernel(const XwRowArgs 
         const int f = 4 * tid + 4 * kXwRowThreads * j;
         if (f < c.y - c.x) {  // the span is a multiple of 8
             pv[j] = __builtin_nontemporal_load(reinterpret_cast<const v4f32*>(a.prod + c.x + f));
-            po[j] = *reinterpret_cast<const uint2*>(a.off + c.x + f);
+            const v2u32 o = __builtin_nontemporal_load(reinterpret_cast<const v2u32*>(a.off + c.x + f));
+            po[j] = make_uint2(o.x, o.y);
         } else {
             po[j] = make_uint2(kXwSpare | (kXwSpare << 16), kXwSpare | (kXwSpare << 16));  // past the chunk
         }
