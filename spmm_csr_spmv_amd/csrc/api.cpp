@@ -646,47 +646,50 @@ int build_xwin(const std::vector<int32_t>& hptr, int32_t bits, Dir& d, hipStream
     // pieces: the runs of one window over at most kXwPieceRuns chunks and
     // kXwPiece slots, {window | runs << 8, first chunk, window-major start,
     // groups of 8}; listed XCD by XCD (window w on XCD w mod 8), windows in
-    // order; each XCD's list is cut into kXwProdGrid / 8 contiguous shares of
-    // about equal slot counts, one per product workgroup (workgroup b on XCD
-    // b mod 8)
+    // order.  Each XCD's run sequence is cut into kXwProdGrid / 8 contiguous
+    // shares, one per product workgroup (workgroup b on XCD b mod 8), at the
+    // run boundaries nearest to equal slot counts, so that shares differ by
+    // less than one run; no piece crosses a share boundary
     constexpr int64_t kPerXcd = spx::kXwProdGrid / spx::kXcds;
     std::vector<int4> pieces;
     std::vector<int2> ranges((size_t)spx::kXwProdGrid, make_int2(0, 0));
+    auto run_len = [&](int64_t c, int64_t w) {
+        return (int64_t)(runs[(size_t)(c * (nw + 1) + w + 1)] - runs[(size_t)(c * (nw + 1) + w)]);
+    };
     for (int64_t xcd = 0; xcd < spx::kXcds; ++xcd) {
-        const size_t first = pieces.size();
         int64_t slots = 0;
+        for (int64_t w = xcd; w < nw; w += spx::kXcds)
+            for (int64_t c = 0; c < n_chunks; ++c) slots += run_len(c, w);
+        int64_t share = 0, done = 0;  // current share, slots before the current run
+        size_t share_first = pieces.size();
+        auto close_share = [&]() {
+            ranges[(size_t)(share * spx::kXcds + xcd)] = make_int2((int32_t)share_first, (int32_t)pieces.size());
+            share_first = pieces.size();
+            share += 1;
+        };
         for (int64_t w = xcd; w < nw; w += spx::kXcds) {
             int64_t ca = 0, acc = 0;
             auto emit = [&](int64_t cb) {
-                if (acc > 0) {
+                if (acc > 0)
                     pieces.push_back(make_int4((int32_t)(w | ((cb - ca) << 8)), (int32_t)ca,
                                                wm_runs[(size_t)(ca * nw + w)], (int32_t)(acc / 8)));
-                    slots += acc;
-                }
+                ca = cb;
+                acc = 0;
             };
             for (int64_t c = 0; c < n_chunks; ++c) {
-                const int64_t len = runs[(size_t)(c * (nw + 1) + w + 1)] - runs[(size_t)(c * (nw + 1) + w)];
-                if (c - ca == spx::kXwPieceRuns || (acc > 0 && acc + len > spx::kXwPiece)) {
+                const int64_t len = run_len(c, w);
+                // share i ends at the run boundary nearest to (i + 1) / kPerXcd of the XCD's slots
+                while (share < kPerXcd - 1 && 2 * done + len > 2 * (slots * (share + 1) / kPerXcd)) {
                     emit(c);
-                    ca = c;
-                    acc = 0;
+                    close_share();
                 }
+                if (c - ca == spx::kXwPieceRuns || (acc > 0 && acc + len > spx::kXwPiece)) emit(c);
                 acc += len;
+                done += len;
             }
             emit(n_chunks);
         }
-        // share i ends where the running slot count first reaches (i + 1) / kPerXcd of the XCD's slots
-        size_t at = first;
-        int64_t run = 0;
-        for (int64_t i = 0; i < kPerXcd; ++i) {
-            const size_t b0 = at;
-            const int64_t target = slots * (i + 1) / kPerXcd;
-            while (at < pieces.size() && (run < target || i == kPerXcd - 1)) {
-                run += (int64_t)pieces[at].w * 8;
-                ++at;
-            }
-            ranges[(size_t)(i * spx::kXcds + xcd)] = make_int2((int32_t)b0, (int32_t)at);
-        }
+        while (share < kPerXcd) close_share();
     }
     d.xw_pieces = std::move(pieces);
     d.xw_prod_ranges = std::move(ranges);
