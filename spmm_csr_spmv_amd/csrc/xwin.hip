@@ -408,19 +408,25 @@ __global__ __launch_bounds__(kXwRowThreads) void xw_rows_kernel(const XwRowArgs 
     };
 
     int ci = blockIdx.x;
+    // chunk descriptors {stream_begin, stream_end, row_begin or long row,
+    // row_end or -(partial + 1)} and {first entry, entries}, read one chunk ahead
+    int4 c_next = make_int4(0, 0, 0, -1);
+    int2 q_next = make_int2(0, 0);
     if (ci < a.n_chunks) {
-        const int4 c0 = a.chunks[ci];
+        c_next = a.chunks[ci];
+        q_next = a.chunk_q[ci];
 #pragma unroll
-        for (int j = 0; j < kXwSpanLoads; ++j) fetch_slot(c0, j);
-        fetch_rows(c0);
+        for (int j = 0; j < kXwSpanLoads; ++j) fetch_slot(c_next, j);
+        fetch_rows(c_next);
     }
     for (; ci < a.n_chunks; ci += gridDim.x) {
-        // {stream_begin, stream_end, row_begin or long row, row_end or -(partial + 1)}
-        const int4 c = a.chunks[ci];
-        const int2 qn = a.chunk_q[ci];
+        const int4 c = c_next;
+        const int2 qn = q_next;
         // the next chunk's loads go into the registers as soon as they are consumed
         const bool more = ci + (int)gridDim.x < a.n_chunks;
         const int4 cn = more ? a.chunks[ci + gridDim.x] : make_int4(0, 0, 0, -1);
+        if (more) q_next = a.chunk_q[ci + gridDim.x];
+        c_next = cn;
         const int rb = c.z, q0 = qn.x, n = qn.y;
         const bool seg = c.w < 0;  // a segment of one long row
         const int R = seg ? 1 : c.w - rb;
