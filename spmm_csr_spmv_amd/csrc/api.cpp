@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -648,8 +649,9 @@ int build_xwin(const std::vector<int32_t>& hptr, int32_t bits, Dir& d, hipStream
     // groups of 8}; listed XCD by XCD (window w on XCD w mod 8), windows in
     // order.  Each XCD's run sequence is cut into kXwProdGrid / 8 contiguous
     // shares, one per product workgroup (workgroup b on XCD b mod 8), at the
-    // run boundaries nearest to equal slot counts, so that shares differ by
-    // less than one run; no piece crosses a share boundary
+    // run boundaries nearest to equal slot counts, or at a window boundary
+    // within 2 % of a share of that (one x window fewer to load); no piece
+    // crosses a share boundary
     constexpr int64_t kPerXcd = spx::kXwProdGrid / spx::kXcds;
     std::vector<int4> pieces;
     std::vector<int2> ranges((size_t)spx::kXwProdGrid, make_int2(0, 0));
@@ -667,7 +669,12 @@ int build_xwin(const std::vector<int32_t>& hptr, int32_t bits, Dir& d, hipStream
             share_first = pieces.size();
             share += 1;
         };
+        const int64_t snap = slots / kPerXcd / 50;  // a share may end at a window boundary this close to its target
+        auto target = [&](int64_t i) { return slots * (i + 1) / kPerXcd; };
         for (int64_t w = xcd; w < nw; w += spx::kXcds) {
+            int64_t w_end = done;
+            for (int64_t c = 0; c < n_chunks; ++c) w_end += run_len(c, w);
+            while (share < kPerXcd - 1 && std::llabs(target(share) - done) <= snap) close_share();
             int64_t ca = 0, acc = 0;
             auto emit = [&](int64_t cb) {
                 if (acc > 0)
@@ -679,7 +686,7 @@ int build_xwin(const std::vector<int32_t>& hptr, int32_t bits, Dir& d, hipStream
             for (int64_t c = 0; c < n_chunks; ++c) {
                 const int64_t len = run_len(c, w);
                 // share i ends at the run boundary nearest to (i + 1) / kPerXcd of the XCD's slots
-                while (share < kPerXcd - 1 && 2 * done + len > 2 * (slots * (share + 1) / kPerXcd)) {
+                while (share < kPerXcd - 1 && 2 * done + len > 2 * target(share) && w_end - target(share) > snap) {
                     emit(c);
                     close_share();
                 }
