@@ -34,8 +34,9 @@
 //   consecutive chunks and kXwPiece slots, one contiguous stretch of the
 //   window-major stream.  The pieces of window w run on XCD w mod 8 (the
 //   window's x is read from HBM once, then from that XCD's L2); each
-//   workgroup takes a contiguous share of its XCD's pieces, in window order,
-//   and refills x only when the window changes.  Each thread holds 4 groups
+//   workgroup takes a contiguous share of its XCD's pieces, in window order
+//   (equal slot counts to within one run, or ending at a nearby window
+//   boundary), and refills x only when the window changes.  Each thread holds 4 groups
 //   of 8 slots of a piece in registers (16-byte loads, issued while the
 //   previous piece is processed), forms value * x[window + column], finds
 //   the group's run in the piece's run map in LDS (the first group of each
@@ -457,6 +458,7 @@ __global__ __launch_bounds__(kXwRowThreads) void xw_rows_kernel(const XwRowArgs 
         // slot's byte offset in ps, a permutation of the chunk's n places
         // plus padding slots, which point to the 64 spare slots past them
         char* const psb = reinterpret_cast<char*>(ps);
+        __builtin_amdgcn_s_setprio(3);  // issue the next chunk's loads ahead of the other workgroup's sums
 #pragma unroll
         for (int j = 0; j < kXwSpanLoads; ++j) {
             *reinterpret_cast<float*>(psb + (po[j].x & 0xffffu)) = pv[j].x;
@@ -465,6 +467,7 @@ __global__ __launch_bounds__(kXwRowThreads) void xw_rows_kernel(const XwRowArgs 
             *reinterpret_cast<float*>(psb + (po[j].y >> 16)) = pv[j].w;
             if (more) fetch_slot(cn, j);
         }
+        __builtin_amdgcn_s_setprio(0);
         __syncthreads();
         {  // prefix counts of row starts per bitmap word, consecutive words per thread
             int cnt[kXwWordsPerThread], sum = 0;
