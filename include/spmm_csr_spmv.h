@@ -210,19 +210,44 @@ int sp_plan_create(sp_plan** plan, int64_t m, int64_t n, int64_t nnz,
 
 /* Bytes of device workspace the plan needs to serve spmv/spmv_t and spmm with
  * up to max_N right-hand-side columns ([LSMR] §5.1: one query covering both
- * directions). */
+ * directions).  For a view (below): the bytes of its per-call scratch only. */
 int sp_plan_workspace_size(const sp_plan* plan, int32_t max_N, size_t* bytes);
 
 /* Attaches a device workspace of at least the queried size and uploads the
  * plan's task tables into it (enqueued on `stream`).  The workspace must stay
- * alive until sp_plan_destroy or the next bind.  Calls that share a plan share
- * its workspace, so they must be ordered on one stream. */
+ * alive until sp_plan_destroy or the next bind.  Binding a view attaches its
+ * scratch instead (no upload, no synchronisation; SP_ERR_STATE when its base
+ * is not bound).  Errors: SP_ERR_NULL, SP_ERR_SIZE (max_N < 1),
+ * SP_ERR_WORKSPACE, SP_ERR_INDEX (a stored index outside its dimension),
+ * SP_ERR_STATE, SP_ERR_HIP.
+ *
+ * Concurrency ([LSMR] §5.1: the matrix is set up once, and each call only
+ * supplies its vectors).  After bind the task tables and matrix copies are
+ * read-only; what a product writes besides its output (split-row partials and
+ * arrival counters, panel row sums, x-window products) lives in the per-call
+ * scratch of the plan or view it is called on.  So calls on one plan or view
+ * must be ordered (one stream at a time), and calls on different views of a
+ * plan, or on the plan and its views, may run concurrently on different
+ * streams when their outputs are disjoint. */
 int sp_plan_bind(sp_plan* plan, void* work, size_t work_bytes, int32_t max_N, void* stream);
 
-/* Profile of A (transposed = 0) or of A^T (transposed = 1). */
+/* Creates a view of `base` (a plan, or a view: then of its plan): an sp_plan
+ * that every product entry point accepts, which reads the base's bound tables
+ * and owns only a per-call scratch, attached with sp_plan_bind after
+ * sp_plan_workspace_size (with its own max_N).  Host-only: allocates the small
+ * host struct, no device memory.  A view stops working (SP_ERR_STATE) when
+ * its base is bound again; bind the view again then.  Destroy the views of a
+ * plan before the plan (sp_plan_destroy of a plan with live views returns
+ * SP_ERR_STATE and frees nothing).  Errors: SP_ERR_NULL, SP_ERR_SIZE (out of
+ * host memory). */
+int sp_plan_view_create(const sp_plan* base, sp_plan** view);
+
+/* Profile of A (transposed = 0) or of A^T (transposed = 1); a view reports its
+ * base's. */
 int sp_plan_profile(const sp_plan* plan, int32_t transposed, sp_profile* out);
 
-/* Frees the host-side plan. */
+/* Frees the host-side plan or view (NULL is accepted).  SP_ERR_STATE, freeing
+ * nothing, for a plan whose views are not all destroyed. */
 int sp_plan_destroy(sp_plan* plan);
 
 /* --------------------------------------------------------- dispatch key, tuning cache, autotune
@@ -284,9 +309,11 @@ int sp_autotune_spmv(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, 
  * spmm:   C = alpha * A B + beta * C     B: n x N row-major with leading
  *         dimension ldb >= N, C: m x N row-major with ldc >= N (device)
  *         ([GEN] §3, C[i,n] sums A[i,k] B[k,n] over the row's entries)
+ * `plan` is a bound plan or a bound view (see sp_plan_view_create).
  * Never allocate, never synchronise.  x/u/B must not alias y/z/C.
  * Errors: SP_ERR_NULL, SP_ERR_SIZE (N < 1, ld < N, N above the bound max_N),
- * SP_ERR_STATE (not bound), SP_ERR_UNSUPPORTED (spmv_t without CSC), SP_ERR_HIP.
+ * SP_ERR_STATE (not bound, or a view whose base was bound again since),
+ * SP_ERR_UNSUPPORTED (spmv_t without CSC), SP_ERR_HIP.
  */
 int spmv(const sp_plan* plan, float alpha, const float* x, float beta, float* y, void* stream);
 int spmv_t(const sp_plan* plan, float alpha, const float* u, float beta, float* z, void* stream);

@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     Plan,
+    PlanView,
     SparseError,
     autotune_spmv,
     bsr_spmm,

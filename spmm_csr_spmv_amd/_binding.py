@@ -5,7 +5,13 @@ arithmetic of its own: it checks dtypes/devices, allocates outputs and
 workspaces with torch (PyTorch is the device-memory and stream provider),
 passes raw device pointers and the current torch HIP stream, and raises
 SparseError on a non-zero status.
+
+Streams: a call given `stream=` enqueues its kernels there and allocates its
+outputs and workspaces on that stream (torch's caching allocator then does not
+hand the memory to other streams' work before the call's kernels are done); a
+plan's workspace used on another stream is marked with record_stream.
 """
+import contextlib
 import ctypes
 import os
 
@@ -25,7 +31,7 @@ EXPORTS = ("sp_status_string", "sp_version", "csr_build_from_coo_bufsize", "csr_
            "csr_to_bsr_bufsize", "csr_to_bsr_analyze", "csr_to_bsr_fill", "bsr_spmv", "bsr_spmm_bufsize", "bsr_spmm",
            "sp_plan_dispatch_key", "sp_tune_cache_store", "sp_tune_cache_lookup", "sp_tune_cache_clear",
            "sp_tune_cache_size", "sp_autotune_workspace_size", "sp_autotune_spmv", "csr_to_wcsr_bufsize",
-           "csr_to_wcsr_analyze", "csr_to_wcsr_fill", "wcsr_spmm")
+           "csr_to_wcsr_analyze", "csr_to_wcsr_fill", "wcsr_spmm", "sp_plan_view_create")
 
 
 class SparseError(RuntimeError):
@@ -93,6 +99,7 @@ def lib():
         L.sp_plan_bind.argtypes = [_p, _p, _sz, _i32, _p]
         L.sp_plan_profile.argtypes = [_p, _i32, ctypes.POINTER(sp_profile)]
         L.sp_plan_destroy.argtypes = [_p]
+        L.sp_plan_view_create.argtypes = [_p, ctypes.POINTER(_p)]
         L.spmv.argtypes = [_p, _f, _p, _f, _p, _p]
         L.spmv_t.argtypes = [_p, _f, _p, _f, _p, _p]
         L.spmm.argtypes = [_p, _i32, _f, _p, _i64, _f, _p, _i64, _p]
@@ -157,8 +164,19 @@ def sp_version():
     return lib().sp_version()
 
 
+def _on(stream):
+    """Allocation context: torch allocations inside it belong to `stream`."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _workspace(nbytes, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _used_on(t, stream):
+    """Marks a tensor allocated on another stream as in use on `stream`."""
+    if stream is not None and t is not None:
+        t.record_stream(stream)
 
 
 # ---------------------------------------------------------------- conversions
@@ -170,10 +188,11 @@ def csr_build_from_coo(m, n, coo_row, coo_col, coo_val, stream=None):
     dev = coo_row.device
     size = _sz()
     _check("csr_build_from_coo_bufsize", L.csr_build_from_coo_bufsize(m, n, nnz, ctypes.byref(size)))
-    work = _workspace(size.value, dev)
-    row_ptr = torch.empty(m + 1, dtype=torch.int32, device=dev)
-    col_idx = torch.empty(nnz, dtype=torch.int32, device=dev)
-    val = torch.empty(nnz, dtype=torch.float32, device=dev)
+    with _on(stream):
+        work = _workspace(size.value, dev)
+        row_ptr = torch.empty(m + 1, dtype=torch.int32, device=dev)
+        col_idx = torch.empty(nnz, dtype=torch.int32, device=dev)
+        val = torch.empty(nnz, dtype=torch.float32, device=dev)
     _check("csr_build_from_coo",
            L.csr_build_from_coo(m, n, nnz, _ptr(coo_row), _ptr(coo_col), _ptr(coo_val), _ptr(row_ptr), _ptr(col_idx),
                                 _ptr(val), _ptr(work), size.value, _stream(stream)))
@@ -188,10 +207,11 @@ def csr_to_csc(m, n, row_ptr, col_idx, val, stream=None):
     dev = row_ptr.device
     size = _sz()
     _check("csr_to_csc_bufsize", L.csr_to_csc_bufsize(m, n, nnz, ctypes.byref(size)))
-    work = _workspace(size.value, dev)
-    col_ptr = torch.empty(n + 1, dtype=torch.int32, device=dev)
-    row_idx = torch.empty(nnz, dtype=torch.int32, device=dev)
-    cval = torch.empty(nnz, dtype=torch.float32, device=dev)
+    with _on(stream):
+        work = _workspace(size.value, dev)
+        col_ptr = torch.empty(n + 1, dtype=torch.int32, device=dev)
+        row_idx = torch.empty(nnz, dtype=torch.int32, device=dev)
+        cval = torch.empty(nnz, dtype=torch.float32, device=dev)
     _check("csr_to_csc", L.csr_to_csc(m, n, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(val), _ptr(col_ptr),
                                       _ptr(row_idx), _ptr(cval), _ptr(work), size.value, _stream(stream)))
     return col_ptr, row_idx, cval
@@ -207,15 +227,17 @@ def csr_to_bsr(m, n, row_ptr, col_idx, val, bs, min_fill=0.0, out="f32", stream=
     dev = row_ptr.device
     size = _sz()
     _check("csr_to_bsr_bufsize", L.csr_to_bsr_bufsize(m, n, nnz, bs, ctypes.byref(size)))
-    work = _workspace(size.value, dev)
     mb = (m + bs - 1) // bs
-    brow_ptr = torch.empty(mb + 1, dtype=torch.int32, device=dev)
+    with _on(stream):
+        work = _workspace(size.value, dev)
+        brow_ptr = torch.empty(mb + 1, dtype=torch.int32, device=dev)
     nnzb, fill = _i64(), ctypes.c_double()
     _check("csr_to_bsr_analyze",
            L.csr_to_bsr_analyze(m, n, nnz, _ptr(row_ptr), _ptr(col_idx), bs, float(min_fill), _ptr(brow_ptr),
                                 ctypes.byref(nnzb), ctypes.byref(fill), _ptr(work), size.value, _stream(stream)))
-    bcol = torch.empty(nnzb.value, dtype=torch.int32, device=dev)
-    bval = torch.empty((nnzb.value, bs, bs), dtype=torch.int16 if out == "bf16" else torch.float32, device=dev)
+    with _on(stream):
+        bcol = torch.empty(nnzb.value, dtype=torch.int32, device=dev)
+        bval = torch.empty((nnzb.value, bs, bs), dtype=torch.int16 if out == "bf16" else torch.float32, device=dev)
     _check("csr_to_bsr_fill",
            L.csr_to_bsr_fill(m, n, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(val), bs, _ptr(brow_ptr), nnzb.value,
                              _ptr(bcol), _ptr(bval), 1 if out == "bf16" else 0, _stream(stream)))
@@ -231,14 +253,16 @@ def csr_to_wcsr(m, n, row_ptr, col_idx, val, pad=8, stream=None):
     dev = row_ptr.device
     size = _sz()
     _check("csr_to_wcsr_bufsize", L.csr_to_wcsr_bufsize(m, n, nnz, ctypes.byref(size)))
-    work = _workspace(size.value, dev)
-    window_ptr = torch.empty((m + 63) // 64 + 1, dtype=torch.int32, device=dev)
+    with _on(stream):
+        work = _workspace(size.value, dev)
+        window_ptr = torch.empty((m + 63) // 64 + 1, dtype=torch.int32, device=dev)
     total, fill = _i64(), ctypes.c_double()
     _check("csr_to_wcsr_analyze",
            L.csr_to_wcsr_analyze(m, n, nnz, _ptr(row_ptr), _ptr(col_idx), int(pad), _ptr(window_ptr),
                                  ctypes.byref(total), ctypes.byref(fill), _ptr(work), size.value, _stream(stream)))
-    window_col = torch.empty(total.value, dtype=torch.int32, device=dev)
-    values = torch.empty((total.value, 64), dtype=torch.float32, device=dev)
+    with _on(stream):
+        window_col = torch.empty(total.value, dtype=torch.int32, device=dev)
+        values = torch.empty((total.value, 64), dtype=torch.float32, device=dev)
     _check("csr_to_wcsr_fill",
            L.csr_to_wcsr_fill(m, n, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(val), _ptr(window_ptr), total.value,
                               _ptr(window_col), _ptr(values), _stream(stream)))
@@ -294,8 +318,14 @@ class Plan:
         size = _sz()
         _check("sp_plan_workspace_size", L.sp_plan_workspace_size(h, self.max_N, ctypes.byref(size)))
         self.workspace_bytes = size.value
-        self.work = _workspace(size.value, row_ptr.device)
+        self.stream = stream
+        with _on(stream):
+            self.work = _workspace(size.value, row_ptr.device)
         _check("sp_plan_bind", L.sp_plan_bind(h, _ptr(self.work), size.value, self.max_N, _stream(stream)))
+
+    def view(self, max_N=None, stream=None):
+        """A PlanView of this plan (its own per-call scratch; see PlanView)."""
+        return PlanView(self, self.max_N if max_N is None else max_N, stream=stream)
 
     def dispatch_key(self, transposed=False, N=1, version=0):
         k = sp_dispatch_key()
@@ -309,6 +339,43 @@ class Plan:
         return {k: getattr(p, k) for k, _ in sp_profile._fields_}
 
     def destroy(self):
+        """Frees the plan; SparseError (SP_ERR_STATE) while views of it are alive."""
+        if self.handle is not None and self.handle.value:
+            _check("sp_plan_destroy", lib().sp_plan_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+class PlanView:
+    """sp_plan_view_create + sp_plan_bind: a handle that reads the bound tables of
+    `plan` and owns only a per-call scratch (allocated here on `stream`), so that
+    products on different views, or on the plan and its views, can run at the
+    same time on different streams.  Accepted wherever a Plan is."""
+
+    def __init__(self, plan, max_N=1, stream=None):
+        L = lib()
+        h = ctypes.c_void_p()
+        _check("sp_plan_view_create", L.sp_plan_view_create(plan.handle, ctypes.byref(h)))
+        self.handle = h
+        self.base = plan  # keeps the plan (and its arrays) alive while the view exists
+        self.m, self.n, self.nnz, self.max_N = plan.m, plan.n, plan.nnz, int(max_N)
+        size = _sz()
+        _check("sp_plan_workspace_size", L.sp_plan_workspace_size(h, self.max_N, ctypes.byref(size)))
+        self.workspace_bytes = size.value
+        self.stream = stream
+        with _on(stream):
+            self.work = _workspace(size.value, plan.work.device)
+        _check("sp_plan_bind", L.sp_plan_bind(h, _ptr(self.work), size.value, self.max_N, _stream(stream)))
+
+    def profile(self, transposed=False):
+        return Plan.profile(self, transposed)
+
+    def destroy(self):
         if self.handle is not None and self.handle.value:
             lib().sp_plan_destroy(self.handle)
             self.handle = None
@@ -318,6 +385,17 @@ class Plan:
             self.destroy()
         except Exception:
             pass
+
+
+def _plan_used_on(plan, stream):
+    """The plan's (or view's) workspace, and a view's base workspace, are in use on `stream`."""
+    if stream is None:
+        return
+    if plan.stream is not stream:
+        _used_on(plan.work, stream)
+    base = getattr(plan, "base", None)
+    if base is not None and base.stream is not stream:
+        _used_on(base.work, stream)
 
 
 def sp_plan_create(m, n, row_ptr, col_idx, val, csc=None, max_N=1, **options):
@@ -370,8 +448,9 @@ def autotune_spmv(m, n, row_ptr, col_idx, val, x, candidates=None, reps=20, vers
     _check("sp_autotune_workspace_size",
            L.sp_autotune_workspace_size(m, n, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(val), arr, len(cands),
                                         ctypes.byref(size), _stream(stream)))
-    work = _workspace(size.value, row_ptr.device)
-    y = torch.empty(m, dtype=torch.float32, device=row_ptr.device)
+    with _on(stream):
+        work = _workspace(size.value, row_ptr.device)
+        y = torch.empty(m, dtype=torch.float32, device=row_ptr.device)
     best = _i32()
     ms = (_f * len(cands))()
     _check("sp_autotune_spmv",
@@ -387,6 +466,7 @@ def spmv(plan, alpha, x, beta, y, stream=None):
     _dev(x, torch.float32, "x"), _dev(y, torch.float32, "y")
     if x.numel() != plan.n or y.numel() != plan.m:
         raise ValueError("x must have n entries and y m entries")
+    _plan_used_on(plan, stream)
     _check("spmv", lib().spmv(plan.handle, float(alpha), _ptr(x), float(beta), _ptr(y), _stream(stream)))
     return y
 
@@ -396,6 +476,7 @@ def spmv_t(plan, alpha, u, beta, z, stream=None):
     _dev(u, torch.float32, "u"), _dev(z, torch.float32, "z")
     if u.numel() != plan.m or z.numel() != plan.n:
         raise ValueError("u must have m entries and z n entries")
+    _plan_used_on(plan, stream)
     _check("spmv_t", lib().spmv_t(plan.handle, float(alpha), _ptr(u), float(beta), _ptr(z), _stream(stream)))
     return z
 
@@ -406,6 +487,7 @@ def spmm(plan, alpha, B, beta, C, stream=None):
     N = B.shape[1]
     if B.shape[0] != plan.n or C.shape[0] != plan.m or C.shape[1] != N:
         raise ValueError("shape mismatch")
+    _plan_used_on(plan, stream)
     _check("spmm", lib().spmm(plan.handle, N, float(alpha), _ptr(B), N, float(beta), _ptr(C), N, _stream(stream)))
     return C
 
@@ -437,7 +519,8 @@ def bsr_spmm(mb, kb, bs, brow_ptr, bcol, bval, B, alpha, beta, C, stream=None, w
     size = _sz()
     _check("bsr_spmm_bufsize", L.bsr_spmm_bufsize(mb, kb, bs, nnzb, N, ctypes.byref(size)))
     if size.value > 0 and work is None:
-        work = _workspace(size.value, C.device)
+        with _on(stream):
+            work = _workspace(size.value, C.device)
     wbytes = size.value if work is not None else 0
     _check("bsr_spmm", L.bsr_spmm(mb, kb, bs, nnzb, _ptr(brow_ptr), _ptr(bcol), _ptr(bval), N, _ptr(B), N,
                                   float(alpha), float(beta), _ptr(C), N, _ptr(work) if work is not None else None,

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <cmath>
 #include <cstring>
@@ -98,6 +99,14 @@ struct sp_plan {
     Dir fwd, tr;
     bool bound = false;
     int32_t bound_max_N = 0;
+    uint64_t bind_gen = 0;              // bumped by every bind of a plan (not of a view)
+    mutable std::atomic<int> views{0};  // views created on this plan and not yet destroyed
+    // A view (base != nullptr) reads the bound tables of its base plan and owns
+    // only the per-call scratch bound to it: its descriptors are the base's
+    // with the scratch pointers replaced.
+    const sp_plan* base = nullptr;
+    uint64_t base_gen = 0;  // the base's bind_gen when the view was bound
+    DirDevice vdev[2];
 };
 
 namespace {
@@ -364,6 +373,61 @@ size_t plan_layout(const sp_plan* p, int32_t max_N) {
     if (p->fwd.present) off = dir_layout(p->fwd, p->opt, max_N, off);
     if (p->tr.present) off = dir_layout(p->tr, p->opt, max_N, off);
     return off < 256 ? 256 : off;
+}
+
+// Per-call scratch of one direction, the part of the workspace every product
+// writes: split-row partials and their arrival counters (row bins), the panel
+// row sums and long-row partials (column-panel stream), the products and the
+// long-row partials and counters (x-window stream).  A view holds its own copy.
+struct ScratchOff {
+    size_t partials = 0, counters = 0, ps_ypart = 0, ps_partials = 0, xw_prod = 0, xw_partials = 0, xw_counters = 0;
+};
+
+size_t view_dir_layout(const Dir& d, int32_t max_N, size_t base, ScratchOff& so) {
+    size_t off = base;
+    so.partials = off;
+    off = align256(off + (size_t)d.n_partials * (size_t)std::max(1, max_N) * sizeof(float));
+    const int64_t max_tiles = std::max<int64_t>(1, (max_N + 63) / 64);
+    so.counters = off;
+    off = align256(off + d.split_rows.size() * (size_t)max_tiles * sizeof(int32_t));
+    if (d.ps_P > 0) {
+        so.ps_ypart = off;
+        off = align256(off + (size_t)d.ps_P * (size_t)ps_ystride(d.rows) * sizeof(float));
+        so.ps_partials = off;
+        off = align256(off + d.ps_split_tasks.size() * sizeof(float));
+    }
+    if (d.xw_bits > 0) {
+        so.xw_prod = off;
+        off = align256(off + (size_t)d.xw_total * sizeof(float));
+        so.xw_partials = off;
+        off = align256(off + (size_t)d.xw_n_partials * sizeof(float));
+        so.xw_counters = off;
+        off = align256(off + d.xw_split_rows.size() * sizeof(int32_t));
+    }
+    return off;
+}
+
+size_t view_layout(const sp_plan* base, int32_t max_N, ScratchOff so[2]) {
+    size_t off = 0;
+    if (base->fwd.present) off = view_dir_layout(base->fwd, max_N, off, so[0]);
+    if (base->tr.present) off = view_dir_layout(base->tr, max_N, off, so[1]);
+    return off < 256 ? 256 : off;
+}
+
+// The descriptors a product launches with: a plan's own, or a view's.
+const DirDevice& dir_dev(const sp_plan* p, int transposed) {
+    if (p->base) return p->vdev[transposed ? 1 : 0];
+    return transposed ? p->tr.dev : p->fwd.dev;
+}
+
+// The plan that holds the tables (the base of a view, else the plan itself).
+const sp_plan* tables_of(const sp_plan* p) { return p->base ? p->base : p; }
+
+// A view may run only while its base is still bound to the workspace it had
+// when the view was bound.
+bool usable(const sp_plan* p) {
+    if (!p->bound) return false;
+    return !p->base || (p->base->bound && p->base->bind_gen == p->base_gen);
 }
 
 int check_options_impl(const sp_plan_options& o) {
@@ -1055,18 +1119,82 @@ int sp_plan_create(sp_plan** plan, int64_t m, int64_t n, int64_t nnz, const int3
 int sp_plan_workspace_size(const sp_plan* plan, int32_t max_N, size_t* bytes) {
     if (!plan || !bytes) return SP_ERR_NULL;
     if (max_N < 1) return SP_ERR_SIZE;
-    *bytes = plan_layout(plan, max_N);
+    if (plan->base) {
+        ScratchOff so[2];
+        *bytes = view_layout(plan->base, max_N, so);
+    } else {
+        *bytes = plan_layout(plan, max_N);
+    }
+    return SP_OK;
+}
+
+int sp_plan_view_create(const sp_plan* base, sp_plan** view) {
+    if (!base || !view) return SP_ERR_NULL;
+    *view = nullptr;
+    if (base->base) base = base->base;  // a view of a view reads the same tables
+    sp_plan* v = new (std::nothrow) sp_plan;
+    if (!v) return SP_ERR_SIZE;
+    v->m = base->m;
+    v->n = base->n;
+    v->nnz = base->nnz;
+    v->opt = base->opt;
+    v->base = base;
+    base->views.fetch_add(1);
+    *view = v;
+    return SP_OK;
+}
+
+// Binds a view: its descriptors are the base's current ones with the scratch
+// pointers moved into `work`; the arrival counters there are set to zero.
+static int bind_view(sp_plan* view, void* work, size_t work_bytes, int32_t max_N, hipStream_t s) {
+    const sp_plan* base = view->base;
+    if (!base->bound) return SP_ERR_STATE;
+    ScratchOff so[2];
+    const size_t need = view_layout(base, max_N, so);
+    if (!work || work_bytes < need) return SP_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(work);
+    view->bound = false;
+    const Dir* dirs[2] = {&base->fwd, &base->tr};
+    for (int t = 0; t < 2; ++t) {
+        const Dir& d = *dirs[t];
+        DirDevice& v = view->vdev[t];
+        v = d.dev;
+        if (!d.present) continue;
+        v.partials = reinterpret_cast<float*>(ws + so[t].partials);
+        v.counters = reinterpret_cast<int32_t*>(ws + so[t].counters);
+        if (d.ps_P > 0) {
+            v.ps_ypart = reinterpret_cast<float*>(ws + so[t].ps_ypart);
+            v.ps_partials = reinterpret_cast<float*>(ws + so[t].ps_partials);
+        }
+        if (d.xw_bits > 0) {
+            v.xw_prod = reinterpret_cast<float*>(ws + so[t].xw_prod);
+            v.xw_partials = reinterpret_cast<float*>(ws + so[t].xw_partials);
+            v.xw_counters = reinterpret_cast<int32_t*>(ws + so[t].xw_counters);
+            if (!d.xw_split_rows.empty() &&
+                spx::launch_fill_i32(v.xw_counters, (int64_t)d.xw_split_rows.size(), 0, s) != hipSuccess)
+                return SP_ERR_HIP;
+        }
+        const int64_t max_tiles = std::max<int64_t>(1, (max_N + 63) / 64);
+        if (!d.split_rows.empty() &&
+            spx::launch_fill_i32(v.counters, (int64_t)d.split_rows.size() * max_tiles, 0, s) != hipSuccess)
+            return SP_ERR_HIP;
+    }
+    view->base_gen = base->bind_gen;
+    view->bound = true;
+    view->bound_max_N = max_N;
     return SP_OK;
 }
 
 int sp_plan_bind(sp_plan* plan, void* work, size_t work_bytes, int32_t max_N, void* stream) {
     if (!plan) return SP_ERR_NULL;
     if (max_N < 1) return SP_ERR_SIZE;
+    if (plan->base) return bind_view(plan, work, work_bytes, max_N, (hipStream_t)stream);
     const size_t need = plan_layout(plan, max_N);
     if (!work || work_bytes < need) return SP_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     char* ws = static_cast<char*>(work);
     plan->bound = false;
+    ++plan->bind_gen;  // views bound to the previous tables stop working
     // every stored index must lie inside its dimension before any product runs
     int32_t* flag = reinterpret_cast<int32_t*>(ws);
     if (spx::launch_fill_i32(flag, 4, 0, s) != hipSuccess) return SP_ERR_HIP;
@@ -1096,6 +1224,7 @@ int sp_plan_bind(sp_plan* plan, void* work, size_t work_bytes, int32_t max_N, vo
 
 int sp_plan_profile(const sp_plan* plan, int32_t transposed, sp_profile* out) {
     if (!plan || !out) return SP_ERR_NULL;
+    plan = tables_of(plan);
     const Dir& d = transposed ? plan->tr : plan->fwd;
     if (!d.present) return SP_ERR_UNSUPPORTED;
     *out = d.prof;
@@ -1103,6 +1232,9 @@ int sp_plan_profile(const sp_plan* plan, int32_t transposed, sp_profile* out) {
 }
 
 int sp_plan_destroy(sp_plan* plan) {
+    if (!plan) return SP_OK;
+    if (plan->views.load() != 0) return SP_ERR_STATE;  // its views still read its tables
+    if (plan->base) plan->base->views.fetch_sub(1);
     delete plan;
     return SP_OK;
 }
@@ -1110,30 +1242,32 @@ int sp_plan_destroy(sp_plan* plan) {
 // ------------------------------------------------------------------ products
 int spmv(const sp_plan* plan, float alpha, const float* x, float beta, float* y, void* stream) {
     if (!plan) return SP_ERR_NULL;
-    if (!plan->bound) return SP_ERR_STATE;
+    if (!usable(plan)) return SP_ERR_STATE;
     if ((plan->n > 0 && !x) || (plan->m > 0 && !y)) return SP_ERR_NULL;
     if (plan->m == 0) return SP_OK;
-    return spx::launch_spmv(plan->fwd.dev, alpha, x, beta, y, (hipStream_t)stream) == hipSuccess ? SP_OK : SP_ERR_HIP;
+    return spx::launch_spmv(dir_dev(plan, 0), alpha, x, beta, y, (hipStream_t)stream) == hipSuccess ? SP_OK
+                                                                                                    : SP_ERR_HIP;
 }
 
 int spmv_t(const sp_plan* plan, float alpha, const float* u, float beta, float* z, void* stream) {
     if (!plan) return SP_ERR_NULL;
-    if (!plan->tr.present) return SP_ERR_UNSUPPORTED;
-    if (!plan->bound) return SP_ERR_STATE;
+    if (!tables_of(plan)->tr.present) return SP_ERR_UNSUPPORTED;
+    if (!usable(plan)) return SP_ERR_STATE;
     if ((plan->m > 0 && !u) || (plan->n > 0 && !z)) return SP_ERR_NULL;
     if (plan->n == 0) return SP_OK;
-    return spx::launch_spmv(plan->tr.dev, alpha, u, beta, z, (hipStream_t)stream) == hipSuccess ? SP_OK : SP_ERR_HIP;
+    return spx::launch_spmv(dir_dev(plan, 1), alpha, u, beta, z, (hipStream_t)stream) == hipSuccess ? SP_OK
+                                                                                                    : SP_ERR_HIP;
 }
 
 int spmm(const sp_plan* plan, int32_t N, float alpha, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
          void* stream) {
     if (!plan) return SP_ERR_NULL;
-    if (!plan->bound) return SP_ERR_STATE;
+    if (!usable(plan)) return SP_ERR_STATE;
     if (N < 1 || ldb < N || ldc < N) return SP_ERR_SIZE;
-    if (!plan->fwd.split_rows.empty() && N > plan->bound_max_N) return SP_ERR_SIZE;
+    if (!tables_of(plan)->fwd.split_rows.empty() && N > plan->bound_max_N) return SP_ERR_SIZE;
     if ((plan->n > 0 && !B) || (plan->m > 0 && !C)) return SP_ERR_NULL;
     if (plan->m == 0) return SP_OK;
-    return spx::launch_spmm(plan->fwd.dev, N, alpha, B, ldb, beta, C, ldc, (hipStream_t)stream) == hipSuccess
+    return spx::launch_spmm(dir_dev(plan, 0), N, alpha, B, ldb, beta, C, ldc, (hipStream_t)stream) == hipSuccess
                ? SP_OK
                : SP_ERR_HIP;
 }

@@ -68,7 +68,8 @@ struct DirDevice {
     int32_t xw_n_pieces;
     uint16_t* xw_wcol;               // window-major stream: column within the window (0 in padding)
     float* xw_wval;                  // window-major stream: value (0 in padding)
-    uint16_t* xw_off;                // chunk-major stream: position in the chunk's CSR order (0xffff: padding)
+    uint16_t* xw_off;                // chunk-major stream: LDS byte offset of the entry's slot in its chunk's CSR
+                                     // order (4 * position); a padding slot points at one of 64 spare slots past the chunk
     float* xw_prod;                  // chunk-major stream: product (written by every call)
     const int32_t* xw_wm_runs;       // [n_chunks][nw] window-major start of chunk c's run in window w (bind only)
     const int2* xw_wm_tab;           // [nw][n_chunks] + 1 {chunk-major, window-major start} of run (c, w)

@@ -230,3 +230,11 @@ def test_wcsr_argument_errors():
     assert L.wcsr_spmm(10, 10, FAKE, FAKE, FAKE, 8, 1.0, FAKE, 4, 0.0, FAKE, 8, None) == 2  # ldb < N
     assert L.wcsr_spmm(10, 10, FAKE, FAKE, FAKE, 8, 1.0, ctypes.c_void_p(0x1004), 8, 0.0, FAKE, 8, None) == 5
     assert L.wcsr_spmm(10, 10, None, FAKE, FAKE, 8, 1.0, FAKE, 8, 0.0, FAKE, 8, None) == 1
+
+
+def test_view_argument_errors():
+    L = sp.lib()
+    v = ctypes.c_void_p()
+    assert L.sp_plan_view_create(None, ctypes.byref(v)) == 1
+    assert L.sp_plan_view_create(FAKE, None) == 1
+    assert L.sp_plan_destroy(None) == 0

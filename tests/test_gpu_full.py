@@ -121,25 +121,32 @@ def lognormal():
 
 
 @pytest.mark.parametrize("N", [8, 32, 128])
-def test_spmm_lognormal_sampled(lognormal, N):
+def test_spmm_lognormal_all_rows(lognormal, N):
     coo, (rp, c, v), (g_rp, g_c, g_v) = lognormal
     if N == 8:
         np.testing.assert_array_equal(host(g_rp), rp)
         np.testing.assert_array_equal(host(g_c), c)
     plan = sp.Plan(coo.m, coo.n, g_rp, g_c, g_v, max_N=N)
     B = gen.dense_matrix(coo.n, N, 0)
+    dB = dev(B)
     C = torch.full((coo.m, N), float("nan"), device="cuda")
     say("gpu spmm", N)
-    sp.spmm(plan, 1.0, dev(B), 0.0, C)
-    lens = np.diff(rp)
-    rows = np.unique(np.concatenate([np.random.default_rng(N).choice(coo.m, 20000, replace=False),
-                                     np.argsort(lens)[-64:]]))
-    got = host(C)[rows]
-    ref, scale = oracle.spmm(rp, c, v, B, rows=rows)
+    sp.spmm(plan, 1.0, dB, 0.0, C)
+    got = host(C)
+    say("oracle spmm", N)
+    ref, scale = oracle.spmm(rp, c, v, B)
     assert_close(got, ref, scale, what="spmm N=%d" % N)
+    del ref, scale, got
+    # beta != 0 over every row with the same plan
+    C0 = gen.dense_matrix(coo.m, N, 5)
+    C = dev(C0)
+    say("gpu spmm axpby", N)
+    sp.spmm(plan, -0.75, dB, 1.5, C)
+    ref, scale = oracle.spmm(rp, c, v, B, -0.75, 1.5, C0)
+    assert_close(host(C), ref, scale, what="spmm axpby N=%d" % N)
 
 
-def test_bsr_full_sampled():
+def test_bsr_full_heavy_rows():
     b = gen.block_sparse_bsr(seed=0)
     N = 512
     B = gen.bf16_matrix(b.kb * b.bs, N, seed=0)
@@ -148,10 +155,11 @@ def test_bsr_full_sampled():
     sp.bsr_spmm(b.mb, b.kb, b.bs, dev(b.brow_ptr), dev(b.bcol), dev(b.bval.view(np.int16)), dev(B.view(np.int16)),
                 1.0, 0.0, C)
     counts = np.diff(b.brow_ptr)
-    heavy = np.argsort(counts)[-4:]
+    # every row of the 8 heaviest block rows, plus 1024 sampled rows
+    heavy = np.argsort(counts, kind="stable")[-8:]
     rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([heavy[:, None] * 64 + rng.integers(0, 64, size=(4, 8)),
-                                     rng.choice(b.mb * b.bs, 96, replace=False)[:, None]], axis=None))
+    rows = np.unique(np.concatenate([(heavy[:, None] * 64 + np.arange(64)[None, :]).ravel(),
+                                     rng.choice(b.mb * b.bs, 1024, replace=False)]))
     rp, col, v64 = oracle.bsr_to_csr(b.mb, b.bs, b.brow_ptr, b.bcol, b.bval)
     ref, scale = oracle.spmm_bf16(rp, col, v64, B, rows=rows)
     got = host(C)[rows]
