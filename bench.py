@@ -1,15 +1,23 @@
 #!/usr/bin/env python3
 """Throughput of the sparse x dense products on one MI355X.
 
-Default workload: CSR SpMV y = A x on the power-law matrix (2^22 x 2^22,
+Headline workload: CSR SpMV y = A x on the power-law matrix (2^22 x 2^22,
 lognormal row lengths plus planted hub rows, ~46.8M entries, fp32).  One step
-is one `spmv` call: every row bin of the plan (group / wave / block / split
-rows and the split reduction, with the fused axpby store).  The one-time work
-(COO -> CSR build, plan) is timed separately and reported under "setup".
+is one `spmv` call over the whole matrix with the plan's default path.  The
+one-time work (COO -> CSR build, plan) is timed separately under "setup".
 
-Prints ONE JSON line.  Other workloads (--config) exist for profiling:
-  spmv_uniform, spmv_powerlaw, stencil27 (u <- A v - a u, v <- A^T u - b v per
-  step), spmm_lognormal (--N), bsr_blocks.
+Prints ONE JSON line: the headline's metric, value, timing, roofline and CPU
+baseline at the top level, and under "configs" the same record for every other
+workload, each timed in this run the same way:
+  spmv_uniform (4096^2, rows of 1..16 entries), stencil27 (u <- A v - a u,
+  v <- A^T u - b v per step through the CSR and the CSC), spmm_lognormal_N8 /
+  _N32 / _N128, bsr_blocks (bf16 64 x 64 blocks on MFMA), and the extra paths
+  bsr_spmv (fp32 64 x 64 blocks) and spmm_clustered_N32 (windowed rows).
+--config NAME runs only that workload (as the headline), for profiling.
+
+CPU baseline ("cpu_baseline" of each record): the oracle (plain C, fp64
+accumulation) on the host's cores, threads over row ranges of equal entry
+counts, and on one core; on a bounded row sample when a full pass is long.
 """
 import argparse
 import hashlib
@@ -17,12 +25,18 @@ import json
 import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "SpMV/SpMM GFLOP/s + achieved HBM GB/s vs MI355X peak (fp32), 1 GPU"
+HEADLINE = "spmv_powerlaw"
+# every workload of a default run, in order (the headline first)
+ALL_WORKLOADS = ["spmv_powerlaw", "spmv_uniform", "stencil27", "spmm_lognormal_N8", "spmm_lognormal_N32",
+                 "spmm_lognormal_N128", "bsr_blocks", "bsr_spmv", "spmm_clustered_N32"]
 # Sources whose code decides the kernels each workload runs (a committed
 # traffic summary is used only while these are unchanged).
 _CSRC = "spmm_csr_spmv_amd/csrc/"
@@ -54,6 +68,12 @@ def spmm_bytes(m, k, nnz, N, beta_nonzero=False):
     return 8 * nnz + 4 * (m + 1) + 4 * k * N + 4 * m * N + (4 * m * N if beta_nonzero else 0)
 
 
+def spmm_gather_bytes(m, nnz, N, line=128):
+    """What a row-by-row SpMM without B reuse must read: per entry its B row
+    segment, at least one 128-byte cache line, plus the matrix and C once."""
+    return 8 * nnz + 4 * (m + 1) + nnz * max(4 * N, line) + 4 * m * N
+
+
 def bsr_bytes(mb, kb, bs, nnzb, N, beta_nonzero=False):
     return 2 * nnzb * bs * bs + 4 * (nnzb + mb + 1) + 2 * kb * bs * N + 4 * mb * bs * N * (2 if beta_nonzero else 1)
 
@@ -69,8 +89,12 @@ def bsr_spmv_bytes(m, n, bs, nnzb, beta_nonzero=False):
     return 4 * nnzb * bs * bs + 4 * (nnzb + mb + 1) + 4 * n + 4 * m + (4 * m if beta_nonzero else 0)
 
 
+# Storage accounts of the format page (section 1: COO and CSR of a 10^6-row
+# matrix with 10^7 fp64 entries; section 5: block index cost per value) and of
+# the LSMR page (section 4: the CSR + CSC pair).
 def csr_storage_bytes(m, nnz, val_bytes=8, idx_bytes=4):
-    """Bytes of a CSR (values, column indices, row pointer of m+1 entries)."""
+    """Values and column indices per entry plus one row pointer per row (the
+    format page counts m pointers; the extra end pointer is kept here)."""
     return nnz * (val_bytes + idx_bytes) + (m + 1) * idx_bytes
 
 
@@ -78,9 +102,14 @@ def coo_storage_bytes(nnz, val_bytes=8, idx_bytes=4):
     return nnz * (val_bytes + 2 * idx_bytes)
 
 
+def dual_value_index_bytes(nnz, val_bytes=4, idx_bytes=4):
+    """Values and indices of both the CSR and the CSC (pointers not counted)."""
+    return 2 * nnz * (val_bytes + idx_bytes)
+
+
 def dual_storage_bytes(m, n, nnz):
-    """CSR + CSC of an fp32/int32 matrix (LSMR page, section 4)."""
-    return 2 * (8 * nnz + 4 * (m + n + 2))
+    """CSR + CSC of an fp32/int32 matrix, pointers included."""
+    return dual_value_index_bytes(nnz) + 4 * (m + 1) + 4 * (n + 1)
 
 
 def block_index_bytes_per_value(bs, idx_bytes=4):
@@ -103,9 +132,9 @@ def kernel_fingerprint(workload):
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload, launches_bytes):
-    """HBM traffic per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernels (same fingerprint); else None."""
+def load_traffic_record(workload):
+    """The committed rocprofv3 counter summary of a workload, if it was taken on
+    the current kernels (same fingerprint); else None."""
     path = os.path.join(HERE, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(path):
         return None
@@ -113,35 +142,613 @@ def load_traffic(workload, launches_bytes):
         t = json.load(f)
     if t.get("kernel_fingerprint") != kernel_fingerprint(workload):
         return None
-    return t.get("bytes_per_launch")
+    return t
+
+
+def load_traffic(workload, launches_bytes=None):
+    """HBM bytes per launch from the committed counter summary, or None."""
+    t = load_traffic_record(workload)
+    return None if t is None else t.get("bytes_per_launch")
+
+
+def parse_workload(name):
+    """'spmm_lognormal_N32' -> ('spmm_lognormal', 32); others -> (name, None)."""
+    for base in ("spmm_lognormal", "spmm_clustered"):
+        if name.startswith(base + "_N"):
+            return base, int(name[len(base) + 2:])
+    return name, None
 
 
 # --------------------------------------------------------------------------
+# host facts for the CPU baseline
+# --------------------------------------------------------------------------
+def cpu_threads():
+    """Threads the oracle baseline uses: the cores this process may run on,
+    at most 16 (the GPU machine's CPU share per GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------
+# CPU baseline: the oracle over row ranges
+# --------------------------------------------------------------------------
+class CpuLeg:
+    """One pass of the oracle over a workload: phases run in order, each over
+    the rows [0, rows_hi) of its own row pointer (a sample when rows_hi < m),
+    split among threads into ranges of equal entry counts.  flops and bytes are
+    those of the sampled rows on the GPU side's models."""
+
+    def __init__(self, phases, flops, nbytes, desc, max_threads=None):
+        self.phases = phases  # [(row_ptr, rows_hi, fn(lo, hi))]
+        self.flops = flops
+        self.nbytes = nbytes
+        self.desc = desc
+        self.max_threads = max_threads  # 1: the oracle call cannot be split by rows
+
+
+def _ranges(row_ptr, rows_hi, parts):
+    import numpy as np
+    hi_nz = int(row_ptr[rows_hi])
+    cuts = np.searchsorted(row_ptr[:rows_hi + 1], np.linspace(0, hi_nz, parts + 1)[1:-1])
+    b = [0] + [int(c) for c in cuts] + [rows_hi]
+    return [(b[i], b[i + 1]) for i in range(parts) if b[i + 1] > b[i]]
+
+
+def time_cpu_leg(leg, threads, seconds):
+    import numpy as np  # noqa: F401
+    plans = [(fn, _ranges(rp, hi, threads)) for rp, hi, fn in leg.phases]
+    reps, t = 0, 0.0
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        t0 = time.perf_counter()
+        while True:
+            for fn, rr in plans:
+                list(ex.map(lambda r, fn=fn: fn(r[0], r[1]), rr))
+            reps += 1
+            t = time.perf_counter() - t0
+            if t >= seconds or reps >= 1000:
+                break
+    return t / reps, reps, t
+
+
+def cpu_baseline(leg, seconds):
+    threads = cpu_threads() if leg.max_threads is None else min(cpu_threads(), leg.max_threads)
+    per_1, reps_1, t_1 = time_cpu_leg(leg, 1, seconds / 2)
+    if threads > 1:
+        per_all, reps_all, t_all = time_cpu_leg(leg, threads, seconds / 2)
+    else:
+        per_all, reps_all, t_all = per_1, reps_1, t_1
+    gf = lambda per: leg.flops / per / 1e9  # noqa: E731
+    gb = lambda per: leg.nbytes / per / 1e9  # noqa: E731
+    return dict(value=round(gf(per_all), 4), unit="GFLOP/s", cores=threads, kind="oracle",
+                gbs=round(gb(per_all), 3), value_1core=round(gf(per_1), 4), gbs_1core=round(gb(per_1), 3),
+                cores_all=threads, value_all=round(gf(per_all), 4), cpu_model=cpu_model(), nproc=os.cpu_count(),
+                sample="%s; %d passes on %d threads in %.1f s, %d passes on 1 thread in %.1f s"
+                       % (leg.desc, reps_all, threads, t_all, reps_1, t_1))
+
+
+def _sample_rows(row_ptr, per_entry_flops, budget_flops):
+    """Rows [0, hi) whose entries cost at most budget_flops (all rows if they fit)."""
+    import numpy as np
+    m = row_ptr.size - 1
+    if int(row_ptr[m]) * per_entry_flops <= budget_flops:
+        return m
+    return max(1, int(np.searchsorted(row_ptr, budget_flops / per_entry_flops)) - 1)
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+class Workload:
+    """What one workload's measurement needs (fields filled by prepare())."""
+
+    def __init__(self, name):
+        self.name = name
+        self.setup = {}
+        self.restore = None
+        self.restore_every = 0
+        self.iterates_finite = None
+        self.out_tensor = None
+        self.graph = 0        # steps per captured graph replay in the timed region
+        self.cpu = None       # CpuLeg or None
+        self.extra = {}       # roofline extras (e.g. a gather-aware bound)
+        self.keep = []        # device tensors to free afterwards
+
+
+def _to_dev(torch, a):
+    return torch.from_numpy(a).cuda()
+
+
+def _csr_from_coo(w, sp, torch, coo):
+    d_row, d_col, d_val = (_to_dev(torch, a) for a in (coo.row, coo.col, coo.val))
+    torch.cuda.synchronize()
+    t1 = time.time()
+    rp, ci, vv = sp.csr_build_from_coo(coo.m, coo.n, d_row, d_col, d_val)
+    torch.cuda.synchronize()
+    w.setup["csr_build_from_coo_ms"] = (time.time() - t1) * 1e3
+    return rp, ci, vv
+
+
+def prepare(name, args, opts):
+    import numpy as np
+    import torch
+
+    import gen
+    import spmm_csr_spmv_amd as sp
+
+    base, N = parse_workload(name)
+    w = Workload(name)
+    t0 = time.time()
+    if base == "bsr_blocks":
+        b = gen.block_sparse_bsr(seed=0)
+        N = 512
+        Bh = gen.bf16_matrix(b.kb * b.bs, N, seed=0)
+        d_brow, d_bcol = _to_dev(torch, b.brow_ptr), _to_dev(torch, b.bcol)
+        d_bval = _to_dev(torch, b.bval.view(np.int16))
+        d_B = _to_dev(torch, Bh.view(np.int16))
+        C = torch.empty(b.mb * b.bs, N, device="cuda")
+        w.setup["generate_s"] = time.time() - t0
+
+        def step():
+            sp.bsr_spmm(b.mb, b.kb, b.bs, d_brow, d_bcol, d_bval, d_B, 1.0, 0.0, C)
+
+        w.step, w.out_tensor, w.graph = step, C, 20
+        w.flops = bsr_flops(b.nnzb, b.bs, N)
+        w.nbytes = bsr_bytes(b.mb, b.kb, b.bs, b.nnzb, N)
+        w.launches = 1
+        w.dtype = "bf16 in / f32 acc"
+        w.config = dict(workload=name, M=b.mb * b.bs, K=b.kb * b.bs, block=b.bs, nnz_blocks=b.nnzb, N=N)
+        w.bound, w.peak, w.unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
+        if not args.no_cpu_baseline:
+            import oracle
+            rp, col, v64 = oracle.bsr_to_csr(b.mb, b.bs, b.brow_ptr, b.bcol, b.bval)
+            hi = _sample_rows(rp, 2 * N, args.cpu_sample_gflop * 1e9)
+            w.cpu = CpuLeg([(rp, hi, lambda lo, h: oracle.spmm_bf16(rp, col, v64, Bh, rows=np.arange(lo, h)))],
+                           2 * int(rp[hi]) * N, bsr_bytes(b.mb, b.kb, b.bs, b.nnzb, N) * int(rp[hi]) / max(1, int(rp[-1])),
+                           "rows [0, %d) of %d of C = A B over the expanded bf16 blocks (fp64 accumulation)"
+                           % (hi, rp.size - 1))
+        return w
+    if base == "bsr_spmv":
+        bs = 64
+        coo = gen.block_sparse_coo(seed=0)
+        w.setup["generate_s"] = time.time() - t0
+        m, n = coo.m, coo.n
+        rp, ci, vv = _csr_from_coo(w, sp, torch, coo)
+        t1 = time.time()
+        brp, bcol, bval, fill = sp.csr_to_bsr(m, n, rp, ci, vv, bs, min_fill=0.5)
+        torch.cuda.synchronize()
+        w.setup["csr_to_bsr_ms"] = (time.time() - t1) * 1e3
+        del rp, ci, vv
+        nnzb = bcol.numel()
+        x = _to_dev(torch, gen.dense_vector(n, 0, 1))
+        y = torch.zeros(m, device="cuda")
+
+        def step():
+            sp.bsr_spmv(m, n, bs, brp, bcol, bval, 1.0, x, 0.0, y)
+
+        w.step, w.out_tensor, w.graph = step, y, 20
+        w.flops = 2 * nnzb * bs * bs
+        w.nbytes = bsr_spmv_bytes(m, n, bs, nnzb)
+        w.launches = 1
+        w.dtype = "f32"
+        w.config = dict(workload=name, M=m, K=n, block=bs, nnz=coo.nnz, nnz_blocks=nnzb, fill_ratio=fill)
+        w.bound, w.peak, w.unit = "hbm", PEAK_HBM_GBS, "GB/s"
+        if not args.no_cpu_baseline:
+            import oracle
+            h_brp, h_bcol, h_bval, h_x = (t.cpu().numpy() for t in (brp, bcol, bval, x))
+            w.cpu = CpuLeg([(np.array([0, m], np.int64), 1,
+                             lambda lo, h: oracle.bsr_spmv(m, n, bs, h_brp, h_bcol, h_bval, h_x))],
+                           w.flops, w.nbytes, "full passes of y = A x over the 64 x 64-block BSR (fp64 accumulation, "
+                                              "one call per pass)", max_threads=1)
+        return w
+    if base == "spmm_clustered":
+        coo = gen.clustered_coo(seed=0)
+        w.setup["generate_s"] = time.time() - t0
+        m, n, nnz = coo.m, coo.n, coo.nnz
+        rp, ci, vv = _csr_from_coo(w, sp, torch, coo)
+        t1 = time.time()
+        wp, wc, wv, fill = sp.csr_to_wcsr(m, n, rp, ci, vv, pad=8)
+        torch.cuda.synchronize()
+        w.setup["csr_to_wcsr_ms"] = (time.time() - t1) * 1e3
+        total_cols = wc.numel()
+        B = _to_dev(torch, gen.dense_matrix(n, N, 0))
+        C = torch.empty(m, N, device="cuda")
+
+        def step():
+            sp.wcsr_spmm(m, n, wp, wc, wv, 1.0, B, 0.0, C)
+
+        w.step, w.out_tensor = step, C
+        w.flops = 2 * nnz * N
+        w.nbytes = spmm_bytes(m, n, nnz, N)
+        w.launches = 1
+        w.dtype = "f32"
+        w.config = dict(workload=name, M=m, K=n, nnz=nnz, N=N, window=64, compressed_columns=total_cols,
+                        window_fill=round(fill, 4), mfma_flops=2 * total_cols * 64 * N,
+                        wcsr_bytes=4 * total_cols * 64 + 4 * total_cols + 4 * total_cols * N + 4 * m * N)
+        w.bound, w.peak, w.unit = "hbm", PEAK_HBM_GBS, "GB/s"
+        # the CSR SpMM on the same matrix, for comparison
+        plan_c = sp.Plan(m, n, rp, ci, vv, max_N=N)
+        for _ in range(3):
+            sp.spmm(plan_c, 1.0, B, 0.0, C)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            sp.spmm(plan_c, 1.0, B, 0.0, C)
+        e1.record()
+        torch.cuda.synchronize()
+        w.config["csr_spmm_ms_same_matrix"] = round(e0.elapsed_time(e1) / 10, 5)
+        del plan_c
+        if not args.no_cpu_baseline:
+            import oracle
+            h_rp, h_ci, h_vv = (t.cpu().numpy() for t in (rp, ci, vv))
+            Bh = B.cpu().numpy()
+            hi = _sample_rows(h_rp, 2 * N, args.cpu_sample_gflop * 1e9)
+            w.cpu = CpuLeg([(h_rp, hi, lambda lo, h: oracle.spmm(h_rp, h_ci, h_vv, Bh, rows=np.arange(lo, h)))],
+                           2 * int(h_rp[hi]) * N, spmm_bytes(m, n, nnz, N) * int(h_rp[hi]) / max(1, nnz),
+                           "rows [0, %d) of %d of C = A B over the CSR (fp64 accumulation)" % (hi, m))
+        w.keep = [rp, ci, vv, wp, wc, wv]
+        return w
+
+    # CSR workloads through a plan
+    coo = {"spmv_uniform": lambda: gen.uniform_rows_coo(seed=0),
+           "spmv_powerlaw": lambda: gen.powerlaw_coo(seed=0),
+           "stencil27": lambda: gen.stencil27_coo(seed=0),
+           "spmm_lognormal": lambda: gen.lognormal_coo(seed=0)}[base]()
+    w.setup["generate_s"] = time.time() - t0
+    m, n, nnz = coo.m, coo.n, coo.nnz
+    rp, ci, vv = _csr_from_coo(w, sp, torch, coo)
+    del coo
+    csc = None
+    if base == "stencil27":
+        t1 = time.time()
+        csc = sp.csr_to_csc(m, n, rp, ci, vv)
+        torch.cuda.synchronize()
+        w.setup["csr_to_csc_ms"] = (time.time() - t1) * 1e3
+    N = N if base == "spmm_lognormal" else 1
+    tune = None
+    if args.autotune and base != "spmm_lognormal":
+        x_t = _to_dev(torch, gen.dense_vector(n, 0, 1))
+        t1 = time.time()
+        best, ms, best_opts = sp.autotune_spmv(m, n, rp, ci, vv, x_t, reps=10)
+        w.setup["autotune_ms"] = (time.time() - t1) * 1e3
+        tune = dict(candidates=[dict(c) for c in sp.DEFAULT_CANDIDATES], ms_per_call=[round(t, 5) for t in ms],
+                    best=best)
+        del x_t
+    t1 = time.time()
+    if tune is not None:
+        plan = sp.Plan(m, n, rp, ci, vv, csc=csc, max_N=N, tuned=True)
+    else:
+        plan = sp.Plan(m, n, rp, ci, vv, csc=csc, max_N=N, **opts)
+    torch.cuda.synchronize()
+    w.setup["plan_ms"] = (time.time() - t1) * 1e3
+    prof = plan.profile()
+    x = _to_dev(torch, gen.dense_vector(n, 0, 1))
+    y = torch.zeros(m, device="cuda")
+    w.config = dict(workload=name, M=m, K=n, nnz=nnz, row_len_mean=round(prof["mean"], 3), p95=prof["p95"],
+                    p99=prof["p99"], max_row=prof["max_len"],
+                    bins=dict(group_tasks=prof["group_tasks"], wave_rows=prof["wave_rows"],
+                              block_rows=prof["block_rows"], split_rows=prof["split_rows"],
+                              split_segments=prof["split_segments"]),
+                    path="x-window stream" if prof["x_window_bits"] else
+                    ("column-panel stream" if prof["col_panels"] else
+                     ("SELL-C-sigma" if prof["sell_slots"] else "row bins")))
+    if opts:
+        w.config["plan_options"] = opts
+    if tune is not None:
+        w.config["autotune"] = tune
+        w.config["col_panels"] = prof["col_panels"]
+    w.bound, w.peak, w.unit = "hbm", PEAK_HBM_GBS, "GB/s"
+    w.dtype = "f32"
+    want_cpu = not args.no_cpu_baseline
+    if want_cpu:
+        import oracle
+        h_rp, h_ci, h_vv = (t.cpu().numpy() for t in (rp, ci, vv))
+    if base == "stencil27":
+        u = _to_dev(torch, gen.dense_vector(m, 0, 2))
+        v = _to_dev(torch, gen.dense_vector(n, 0, 3))
+        u0, v0 = u.clone(), v.clone()
+        rng = np.random.default_rng(5)
+        ab = rng.uniform(0.5, 2.0, size=(1 << 16, 2)).astype(np.float32)
+        it = [0]
+
+        def step():
+            a, bt = ab[it[0] % ab.shape[0]]
+            it[0] += 1
+            sp.spmv(plan, 1.0, v, -float(a), u)
+            sp.spmv_t(plan, 1.0, u, -float(bt), v)
+
+        def restore():
+            u.copy_(u0)
+            v.copy_(v0)
+
+        w.step, w.restore = step, restore
+        w.flops = 2 * spmv_flops(m, nnz, True)
+        w.nbytes = 2 * spmv_bytes(m, n, nnz, True)  # per step (two launches)
+        w.launches = 2
+        w.config["step"] = "u <- A v - alpha u ; v <- A^T u - beta v"
+        # the LSMR page's section 4 account: values and indices of the CSR + CSC pair
+        w.config["dual_storage_bytes"] = dual_storage_bytes(m, n, nnz)
+        # the iterates grow by about |A| per step and pass the fp32 range
+        # after some 20 steps: put u, v back every 8 steps (inside the
+        # wall-clock region, outside the per-step events)
+        w.restore_every = 8
+        w.config["restore_every"] = 8
+        w.iterates_finite = lambda: bool(torch.isfinite(u).all().item() and torch.isfinite(v).all().item())
+        if want_cpu:
+            h_cp, h_ri, h_cv = (t.cpu().numpy() for t in csc)
+            hu, hv = u0.cpu().numpy(), v0.cpu().numpy()
+            w.cpu = CpuLeg([(h_rp, m, lambda lo, h: oracle.spmv(h_rp, h_ci, h_vv, hv, 1.0, -1.25, hu,
+                                                                rows=np.arange(lo, h))),
+                            (h_cp, n, lambda lo, h: oracle.spmv(h_cp, h_ri, h_cv, hu, 1.0, -0.75, hv,
+                                                                rows=np.arange(lo, h)))],
+                           w.flops, w.nbytes, "full operator pairs u <- A v - a u, v <- A^T u - b v over the CSR "
+                                              "and the CSC (fp64 accumulation)")
+    elif base == "spmm_lognormal":
+        Bh = gen.dense_matrix(n, N, 0)
+        B = _to_dev(torch, Bh)
+        C = torch.empty(m, N, device="cuda")
+
+        def step():
+            sp.spmm(plan, 1.0, B, 0.0, C)
+
+        w.step, w.out_tensor = step, C
+        w.flops = 2 * nnz * N
+        w.nbytes = spmm_bytes(m, n, nnz, N)
+        w.launches = 1
+        w.config["N"] = N
+        # a row-by-row SpMM reads every entry's B row segment (at least a line)
+        w.extra["gather_bound_bytes"] = spmm_gather_bytes(m, nnz, N)
+        if want_cpu:
+            hi = _sample_rows(h_rp, 2 * N, args.cpu_sample_gflop * 1e9)
+            w.cpu = CpuLeg([(h_rp, hi, lambda lo, h: oracle.spmm(h_rp, h_ci, h_vv, Bh, rows=np.arange(lo, h)))],
+                           2 * int(h_rp[hi]) * N, spmm_bytes(m, n, nnz, N) * int(h_rp[hi]) / max(1, nnz),
+                           "rows [0, %d) of %d of C = A B (fp64 accumulation)" % (hi, m))
+    else:
+        def step():
+            sp.spmv(plan, 1.0, x, 0.0, y)
+
+        w.step, w.out_tensor = step, y
+        w.flops = spmv_flops(m, nnz)
+        w.nbytes = spmv_bytes(m, n, nnz)
+        w.launches = 1
+        w.graph = 20 if base == "spmv_uniform" else 0
+        if want_cpu:
+            hx = x.cpu().numpy()
+            # the 4096-row matrix is too small to split among threads
+            w.cpu = CpuLeg([(h_rp, m, lambda lo, h: oracle.spmv(h_rp, h_ci, h_vv, hx, rows=np.arange(lo, h)))],
+                           w.flops, w.nbytes, "full passes of y = A x over the same %s matrix (fp64 accumulation)"
+                           % base, max_threads=1 if base == "spmv_uniform" else None)
+        if base == "spmv_powerlaw" and args.gather_probe:
+            w.probe = (ci, nnz, n)
+    w.keep = [plan, rp, ci, vv, csc]
+    return w
+
+
+# --------------------------------------------------------------------------
+# GPU measurement
+# --------------------------------------------------------------------------
+def copy_rate_gbs():
+    """A plain 256 MiB device copy, read + write bytes over its time."""
+    import numpy as np
+    import torch
+    ref = torch.ones(64 << 20, device="cuda")
+    dst = torch.empty_like(ref)
+    dst.copy_(ref)
+    t = []
+    for _ in range(5):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        dst.copy_(ref)
+        a1.record()
+        torch.cuda.synchronize()
+        t.append(a0.elapsed_time(a1))
+    del ref, dst
+    return 2 * (64 << 20) * 4 / (float(np.median(t)) * 1e-3) / 1e9
+
+
+def gather_probe(col, nnz, n):
+    """Stream rate and gather rate over the matrix's own column array (see
+    csrc/probe.hip): times of 3 runs each, medians."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    from spmm_csr_spmv_amd import build as b
+    if not os.path.exists(b.PROBE_LIB):
+        raise ImportError("%s is not built" % b.PROBE_LIB)
+    L = ctypes.CDLL(b.PROBE_LIB)
+    L.spx_probe_out_bytes.restype = ctypes.c_int64
+    L.spx_probe_entries.restype = ctypes.c_int64
+    L.spx_probe_entries.argtypes = [ctypes.c_int64]
+    L.spx_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                   ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    bits = max(1, (n - 1).bit_length())
+    x = torch.ones(1 << bits, device="cuda")
+    val = torch.ones(nnz, device="cuda")
+    out = torch.empty(L.spx_probe_out_bytes() // 4, device="cuda")
+    s = torch.cuda.current_stream()
+    cases = {"stream_only": (0xFFFFFFFF, 0), "gather_x": ((1 << bits) - 1, 1),
+             "gather_2MiB_slice": ((1 << 19) - 1, 1), "gather_16KiB": ((1 << 12) - 1, 1)}
+    res = {}
+    for key, (mask, mode) in cases.items():
+        ts = []
+        for _ in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            rc = L.spx_probe_gather(ctypes.c_void_p(col.data_ptr()), ctypes.c_void_p(val.data_ptr()), nnz,
+                                    ctypes.c_void_p(x.data_ptr()), mask & 0xFFFFFFFF, mode,
+                                    ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(s.cuda_stream))
+            e1.record(s)
+            if rc != 0:
+                raise RuntimeError("spx_probe_gather failed: %d" % rc)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        res[key + "_ms"] = round(float(np.median(ts[1:])), 5)
+    entries = int(L.spx_probe_entries(nnz))
+    res["entries"] = entries
+    res["stream_gbs"] = round(8 * entries / (res["stream_only_ms"] * 1e-3) / 1e9, 1)
+    for key in ("gather_x", "gather_2MiB_slice", "gather_16KiB"):
+        res[key + "_gps"] = round(entries / (res[key + "_ms"] * 1e-3) / 1e9, 1)  # G gathers / s
+    del x, val, out
+    return res
+
+
+def measure(w, args, stream):
+    """Warm-up, then exactly args.steps timed steps; returns the record."""
+    import numpy as np
+    import torch
+    for _ in range(args.warmup):
+        w.step()
+    if w.restore:
+        w.restore()
+    torch.cuda.synchronize()
+    # Short single-kernel steps are timed as replays of a captured HIP graph of
+    # G back-to-back steps, so that the events measure the kernels and not the
+    # host's launch rate; G divides the step count.
+    G = args.graph_batch if args.graph_batch >= 0 else w.graph
+    graph = None
+    if G > 0:
+        G = max(g for g in range(1, min(G, args.steps) + 1) if args.steps % g == 0)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(G):
+                w.step()
+        torch.cuda.synchronize()
+    nrec = args.steps // G if G > 0 else args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(nrec)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(nrec)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(nrec):
+        if w.restore_every and i > 0 and i % w.restore_every == 0:
+            w.restore()
+        starts[i].record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            w.step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    r = dict(metric=METRIC, unit="GFLOP/s")
+    if w.iterates_finite is not None:
+        r["iterates_finite"] = w.iterates_finite()
+    ev_ms = [s.elapsed_time(e) / (G if G > 0 else 1) for s, e in zip(starts, ends)]
+    if graph is not None:
+        # the graph's result equals an eager step's, bit for bit (deterministic kernels)
+        if w.out_tensor is not None:
+            got = w.out_tensor.clone()
+            w.step()
+            torch.cuda.synchronize()
+            r["graph_replay_matches_eager"] = bool(torch.equal(got, w.out_tensor))
+        r["graph_batch"] = G
+    ms_per_step = elapsed * 1e3 / args.steps
+    launch_ms = float(np.mean(ev_ms)) / w.launches
+    r["value"] = round(w.flops / (ms_per_step * 1e-3) / 1e9, 3)
+    r["ms_per_step"] = round(ms_per_step, 5)
+    r["dtype"] = w.dtype
+    r["config"] = w.config
+    per_launch_bytes = w.nbytes / w.launches
+    per_launch_flops = w.flops / w.launches
+    if w.bound == "hbm":
+        achieved = per_launch_bytes / (launch_ms * 1e-3) / 1e9
+    else:
+        achieved = per_launch_flops / (launch_ms * 1e-3) / 1e12
+    tr = load_traffic_record(w.name)
+    roof = dict(bound=w.bound, achieved=round(achieved, 2), peak=w.peak, unit=w.unit, frac=round(achieved / w.peak, 4),
+                traffic=None if tr is None else tr.get("bytes_per_launch"),
+                kernel_ms=round(launch_ms, 5), algorithmic_bytes_per_launch=int(per_launch_bytes),
+                flops_per_launch=int(per_launch_flops), event_ms_median=round(float(np.median(ev_ms)), 5),
+                event_ms_min=round(float(np.min(ev_ms)), 5))
+    if tr is not None:
+        for k in ("hbm_read_bytes_per_launch", "mall_read_bytes_per_launch", "write_bytes_per_launch", "method"):
+            if k in tr:
+                roof["traffic_" + k.replace("_per_launch", "")] = tr[k]
+    if w.bound == "mfma":
+        roof["hbm_gbs"] = round(per_launch_bytes / (launch_ms * 1e-3) / 1e9, 1)
+        roof["frac_of_hbm_peak"] = round(per_launch_bytes / (launch_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    if "gather_bound_bytes" in w.extra:
+        gb = w.extra["gather_bound_bytes"]
+        roof["gather_bound_bytes"] = int(gb)
+        roof["gather_bound_gbs"] = round(gb / (launch_ms * 1e-3) / 1e9, 1)
+        roof["gather_bound_frac"] = round(gb / (launch_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    r["roofline"] = roof
+    r["gflops_event"] = round(per_launch_flops / (launch_ms * 1e-3) / 1e9, 2)
+
+    if args.cold > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.cold)]
+        # each rep: flush, one timed step (cold), then one more timed step the
+        # same way (warm: what the flushed step left in the caches)
+        for i in range(args.cold):
+            if w.restore:
+                w.restore()  # before the flush, so the copy leaves nothing in the caches
+            flush.fill_(i & 255)
+            for j in (0, 2):
+                ev[i][j].record(stream)
+                w.step()
+                ev[i][j + 1].record(stream)
+        torch.cuda.synchronize()
+        del flush
+        cold_ms = [e[0].elapsed_time(e[1]) / w.launches for e in ev]
+        single_ms = [e[2].elapsed_time(e[3]) / w.launches for e in ev]
+        med = float(np.median(cold_ms))
+        if w.bound == "hbm":
+            cold_achieved = per_launch_bytes / (med * 1e-3) / 1e9
+        else:
+            cold_achieved = per_launch_flops / (med * 1e-3) / 1e12
+        r["cold"] = dict(reps=args.cold, flush_bytes=512 << 20, kernel_ms_median=round(med, 5),
+                         kernel_ms_min=round(float(np.min(cold_ms)), 5), achieved=round(cold_achieved, 2),
+                         unit=w.unit, frac=round(cold_achieved / w.peak, 4),
+                         warm_single_ms_median=round(float(np.median(single_ms)), 5))
+    r["setup"] = {k: round(v, 2) for k, v in w.setup.items()}
+    return r
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="spmv_powerlaw",
-                    choices=["spmv_uniform", "spmv_powerlaw", "stencil27", "spmm_lognormal", "bsr_blocks", "bsr_spmv",
-                             "spmm_clustered"])
-    ap.add_argument("--N", type=int, default=32, help="right-hand-side columns for spmm_lognormal")
+    ap.add_argument("--config", default=None, choices=ALL_WORKLOADS + ["spmm_lognormal", "spmm_clustered"],
+                    help="run only this workload (spmm_lognormal / spmm_clustered take --N)")
+    ap.add_argument("--N", type=int, default=32, help="right-hand-side columns for --config spmm_lognormal")
     ap.add_argument("--graph-batch", type=int, default=-1,
                     help="steps per replay of a captured HIP graph in the timed region (0: one plain launch per "
-                         "step; -1: up to 20 for workloads whose step is a single short kernel, else 0)")
+                         "step; -1: 20 for workloads whose step is a single short kernel, else 0)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", type=int, default=0, metavar="R",
                     help="after the timed region, also time R single steps each preceded by writing a 512 MiB "
                          "buffer (evicts the L2s and the 256 MB MALL): cold-cache numbers, reported under 'cold'")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="oracle time of the headline's CPU baseline (half on all threads, half on one)")
+    ap.add_argument("--cpu-seconds-other", type=float, default=2.0,
+                    help="oracle time of every other workload's CPU baseline")
+    ap.add_argument("--cpu-sample-gflop", type=float, default=1.0,
+                    help="flops of the row sample when a full oracle pass would be longer")
     ap.add_argument("--options", default="", help="plan options, e.g. group_nnz=1024,wave_min=128")
     ap.add_argument("--autotune", action="store_true",
                     help="SpMV workloads: time the default candidate plans (sp_autotune_spmv), then build the plan "
                          "from the tuning cache; the candidates' times are reported under 'autotune'")
+    ap.add_argument("--no-gather-probe", dest="gather_probe", action="store_false",
+                    help="skip the gather-rate probe over the power-law matrix's columns")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (5 launches) to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -161,11 +768,7 @@ def main():
               % args.gpus, file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
-
-    import gen
-    import spmm_csr_spmv_amd as sp
 
     opts = {}
     for kv in filter(None, args.options.split(",")):
@@ -173,375 +776,51 @@ def main():
         opts[k] = int(v)
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
-    setup = {}
-    cfg = args.config
-    result = dict(metric="SpMV/SpMM GFLOP/s + achieved HBM GB/s vs MI355X peak (fp32), 1 GPU", unit="GFLOP/s",
-                  n_gpus=1, steps=args.steps, warmup=args.warmup, higher_is_better=True, scaling="weak",
-                  vs_baseline=None, data="synthetic (seeded generators in gen/, seed 0)")
-
-    t0 = time.time()
-    if cfg == "bsr_blocks":
-        b = gen.block_sparse_bsr(seed=0)
-        N = 512
-        Bh = gen.bf16_matrix(b.kb * b.bs, N, seed=0)
-        d_brow, d_bcol = torch.from_numpy(b.brow_ptr).cuda(), torch.from_numpy(b.bcol).cuda()
-        d_bval = torch.from_numpy(b.bval.view(np.int16)).cuda()
-        d_B = torch.from_numpy(Bh.view(np.int16)).cuda()
-        C = torch.empty(b.mb * b.bs, N, device="cuda")
-        setup["generate_s"] = time.time() - t0
-
-        def step():
-            sp.bsr_spmm(b.mb, b.kb, b.bs, d_brow, d_bcol, d_bval, d_B, 1.0, 0.0, C)
-
-        out_tensor = C
-
-        flops = bsr_flops(b.nnzb, b.bs, N)
-        nbytes = bsr_bytes(b.mb, b.kb, b.bs, b.nnzb, N)
-        launches = 1
-        dtype = "bf16 in / f32 acc"
-        config = dict(workload=cfg, M=b.mb * b.bs, K=b.kb * b.bs, block=b.bs, nnz_blocks=b.nnzb, N=N)
-        bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
-        cpu_leg = None
-    elif cfg == "bsr_spmv":
-        bs = 64
-        coo = gen.block_sparse_coo(seed=0)
-        setup["generate_s"] = time.time() - t0
-        m, n = coo.m, coo.n
-        d_row, d_col, d_val = (torch.from_numpy(a).cuda() for a in (coo.row, coo.col, coo.val))
-        torch.cuda.synchronize()
-        t1 = time.time()
-        rp, ci, vv = sp.csr_build_from_coo(m, n, d_row, d_col, d_val)
-        torch.cuda.synchronize()
-        setup["csr_build_from_coo_ms"] = (time.time() - t1) * 1e3
-        del d_row, d_col, d_val
-        t1 = time.time()
-        brp, bcol, bval, fill = sp.csr_to_bsr(m, n, rp, ci, vv, bs, min_fill=0.5)
-        torch.cuda.synchronize()
-        setup["csr_to_bsr_ms"] = (time.time() - t1) * 1e3
-        nnzb = bcol.numel()
-        x = torch.from_numpy(gen.dense_vector(n, 0, 1)).cuda()
-        y = torch.zeros(m, device="cuda")
-
-        def step():
-            sp.bsr_spmv(m, n, bs, brp, bcol, bval, 1.0, x, 0.0, y)
-
-        out_tensor = y
-
-        flops = 2 * nnzb * bs * bs
-        nbytes = bsr_spmv_bytes(m, n, bs, nnzb)
-        launches = 1
-        dtype = "f32"
-        config = dict(workload=cfg, M=m, K=n, block=bs, nnz=coo.nnz, nnz_blocks=nnzb, fill_ratio=fill)
-        bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
-        h_brp, h_bcol, h_bval, h_x = (t.cpu().numpy() for t in (brp, bcol, bval, x))
-
-        def cpu_call():
-            import oracle
-            oracle.bsr_spmv(m, n, bs, h_brp, h_bcol, h_bval, h_x)
-
-        cpu_leg = (cpu_call, flops, "full passes of y = A x over the same 64 x 64-block BSR (fp32 blocks, fp64 "
-                                    "accumulation, single-threaded C loop)")
-    elif cfg == "spmm_clustered":
-        coo = gen.clustered_coo(seed=0)
-        setup["generate_s"] = time.time() - t0
-        m, n, nnz = coo.m, coo.n, coo.nnz
-        N = args.N
-        d_row, d_col, d_val = (torch.from_numpy(a).cuda() for a in (coo.row, coo.col, coo.val))
-        torch.cuda.synchronize()
-        t1 = time.time()
-        rp, ci, vv = sp.csr_build_from_coo(m, n, d_row, d_col, d_val)
-        torch.cuda.synchronize()
-        setup["csr_build_from_coo_ms"] = (time.time() - t1) * 1e3
-        del d_row, d_col, d_val
-        t1 = time.time()
-        wp, wc, wv, fill = sp.csr_to_wcsr(m, n, rp, ci, vv, pad=8)
-        torch.cuda.synchronize()
-        setup["csr_to_wcsr_ms"] = (time.time() - t1) * 1e3
-        total_cols = wc.numel()
-        B = torch.from_numpy(gen.dense_matrix(n, N, 0)).cuda()
-        C = torch.empty(m, N, device="cuda")
-
-        def step():
-            sp.wcsr_spmm(m, n, wp, wc, wv, 1.0, B, 0.0, C)
-
-        out_tensor = C
-        flops = 2 * nnz * N
-        nbytes = spmm_bytes(m, n, nnz, N)
-        launches = 1
-        dtype = "f32"
-        config = dict(workload=cfg, M=m, K=n, nnz=nnz, N=N, window=64, compressed_columns=total_cols,
-                      window_fill=round(fill, 4),
-                      mfma_flops=2 * total_cols * 64 * N,
-                      wcsr_bytes=4 * total_cols * 64 + 4 * total_cols + 4 * total_cols * N + 4 * m * N)
-        bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
-        # the CSR SpMM on the same matrix, for comparison
-        plan_c = sp.Plan(m, n, rp, ci, vv, max_N=N)
-        for _ in range(3):
-            sp.spmm(plan_c, 1.0, B, 0.0, C)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(10):
-            sp.spmm(plan_c, 1.0, B, 0.0, C)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        config["csr_spmm_ms_same_matrix"] = round(e0.elapsed_time(e1) / 10, 5)
-        del plan_c
-        cpu_leg = None
+    if args.config is None:
+        names = ALL_WORKLOADS
+    elif args.config in ("spmm_lognormal", "spmm_clustered"):
+        names = ["%s_N%d" % (args.config, args.N)]
     else:
-        coo = {"spmv_uniform": lambda: gen.uniform_rows_coo(seed=0),
-               "spmv_powerlaw": lambda: gen.powerlaw_coo(seed=0),
-               "stencil27": lambda: gen.stencil27_coo(seed=0),
-               "spmm_lognormal": lambda: gen.lognormal_coo(seed=0)}[cfg]()
-        setup["generate_s"] = time.time() - t0
-        m, n, nnz = coo.m, coo.n, coo.nnz
-        d_row, d_col, d_val = (torch.from_numpy(a).cuda() for a in (coo.row, coo.col, coo.val))
+        names = [args.config]
+    copy_gbs = copy_rate_gbs()
+    records = {}
+    for i, name in enumerate(names):
+        log("workload", name)
+        w = prepare(name, args, opts if i == 0 else {})
+        rec = measure(w, args, stream)
+        if w.bound == "hbm":
+            rec["roofline"]["measured_copy_gbs"] = round(copy_gbs, 1)
+            rec["roofline"]["frac_of_copy"] = round(rec["roofline"]["achieved"] / copy_gbs, 4)
+        probe = getattr(w, "probe", None)
+        if probe is not None:
+            p = gather_probe(*probe)
+            rec["gather_probe"] = p
+            # the one-pass floor: every entry's gather at the best measured rate
+            # (x cut into L2-sized slices, one per XCD), against this call's time
+            floor_ms = p["entries"] / (p["gather_2MiB_slice_gps"] * 1e9) * 1e3
+            rec["roofline"]["measured_gather_rate"] = p["gather_2MiB_slice_gps"]
+            rec["roofline"]["one_pass_gather_floor_ms"] = round(floor_ms, 5)
+            rec["roofline"]["frac_of_gather_floor"] = round(floor_ms / rec["roofline"]["kernel_ms"], 4)
+        if w.cpu is not None:
+            secs = args.cpu_seconds if i == 0 else args.cpu_seconds_other
+            rec["cpu_baseline"] = cpu_baseline(w.cpu, secs)
+        elif not args.no_cpu_baseline:
+            rec["cpu_baseline"] = None
+        records[name] = rec
+        del w
         torch.cuda.synchronize()
-        t1 = time.time()
-        rp, ci, vv = sp.csr_build_from_coo(m, n, d_row, d_col, d_val)
-        torch.cuda.synchronize()
-        setup["csr_build_from_coo_ms"] = (time.time() - t1) * 1e3
-        del d_row, d_col, d_val
-        csc = None
-        if cfg == "stencil27":
-            t1 = time.time()
-            csc = sp.csr_to_csc(m, n, rp, ci, vv)
-            torch.cuda.synchronize()
-            setup["csr_to_csc_ms"] = (time.time() - t1) * 1e3
-        N = args.N if cfg == "spmm_lognormal" else 1
-        tune = None
-        if args.autotune and cfg != "spmm_lognormal":
-            x_t = torch.from_numpy(gen.dense_vector(n, 0, 1)).cuda()
-            t1 = time.time()
-            best, ms, best_opts = sp.autotune_spmv(m, n, rp, ci, vv, x_t, reps=10)
-            setup["autotune_ms"] = (time.time() - t1) * 1e3
-            tune = dict(candidates=[dict(c) for c in sp.DEFAULT_CANDIDATES], ms_per_call=[round(t, 5) for t in ms],
-                        best=best)
-            del x_t
-        t1 = time.time()
-        if tune is not None:
-            plan = sp.Plan(m, n, rp, ci, vv, csc=csc, max_N=N, tuned=True)
-        else:
-            plan = sp.Plan(m, n, rp, ci, vv, csc=csc, max_N=N, **opts)
-        torch.cuda.synchronize()
-        setup["plan_ms"] = (time.time() - t1) * 1e3
-        prof = plan.profile()
-        x = torch.from_numpy(gen.dense_vector(n, 0, 1)).cuda()
-        y = torch.zeros(m, device="cuda")
-        config = dict(workload=cfg, M=m, K=n, nnz=nnz, row_len_mean=round(prof["mean"], 3), p95=prof["p95"],
-                      p99=prof["p99"], max_row=prof["max_len"],
-                      bins=dict(group_tasks=prof["group_tasks"], wave_rows=prof["wave_rows"],
-                                block_rows=prof["block_rows"], split_rows=prof["split_rows"],
-                                split_segments=prof["split_segments"]),
-                      path="x-window stream" if prof["x_window_bits"] else
-                      ("column-panel stream" if prof["col_panels"] else
-                       ("SELL-C-sigma" if prof["sell_slots"] else "row bins")))
-        if opts:
-            config["plan_options"] = opts
-        if tune is not None:
-            result["autotune"] = tune
-            config["col_panels"] = prof["col_panels"]
-        bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
-        dtype = "f32"
-        if cfg == "stencil27":
-            u = torch.from_numpy(gen.dense_vector(m, 0, 2)).cuda()
-            v = torch.from_numpy(gen.dense_vector(n, 0, 3)).cuda()
-            u0, v0 = u.clone(), v.clone()
-            rng = np.random.default_rng(5)
-            ab = rng.uniform(0.5, 2.0, size=(1 << 16, 2)).astype(np.float32)
-            it = [0]
-
-            def step():
-                a, bt = ab[it[0] % ab.shape[0]]
-                it[0] += 1
-                sp.spmv(plan, 1.0, v, -float(a), u)
-                sp.spmv_t(plan, 1.0, u, -float(bt), v)
-
-            def restore():
-                u.copy_(u0)
-                v.copy_(v0)
-
-            flops = 2 * spmv_flops(m, nnz, True)
-            nbytes = 2 * spmv_bytes(m, n, nnz, True)  # per step (two launches)
-            launches = 2
-            config["step"] = "u <- A v - alpha u ; v <- A^T u - beta v"
-            # the iterates grow by about |A| per step and pass the fp32 range
-            # after some 20 steps: put u, v back every 8 steps (inside the
-            # wall-clock region, outside the per-step events)
-            restore_every = 8
-            config["restore_every"] = restore_every
-
-            def iterates_finite():
-                return bool(torch.isfinite(u).all().item() and torch.isfinite(v).all().item())
-        elif cfg == "spmm_lognormal":
-            B = torch.from_numpy(gen.dense_matrix(n, N, 0)).cuda()
-            C = torch.empty(m, N, device="cuda")
-
-            def step():
-                sp.spmm(plan, 1.0, B, 0.0, C)
-
-            out_tensor = C
-
-            flops = 2 * nnz * N
-            nbytes = spmm_bytes(m, n, nnz, N)
-            launches = 1
-            config["N"] = N
-        else:
-            def step():
-                sp.spmv(plan, 1.0, x, 0.0, y)
-
-            out_tensor = y
-
-            flops = spmv_flops(m, nnz)
-            nbytes = spmv_bytes(m, n, nnz)
-            launches = 1
-        cpu_leg = None
-        if cfg in ("spmv_powerlaw", "spmv_uniform"):
-            h_rp, h_ci, h_vv, h_x = (t.cpu().numpy() for t in (rp, ci, vv, x))
-
-            def cpu_call():
-                import oracle
-                oracle.spmv(h_rp, h_ci, h_vv, h_x)
-
-            cpu_leg = (cpu_call, spmv_flops(m, nnz), "full passes of y = A x over the same %s matrix (fp64 "
-                                                     "accumulation, single-threaded C loop)" % cfg)
-
-    restore_fn = locals().get("restore")
-    restore_every = locals().get("restore_every", 0)
-    # ---------------- warmup + timed region
-    for _ in range(args.warmup):
-        step()
-    if restore_fn:
-        restore_fn()
-    torch.cuda.synchronize()
-    # Short single-kernel steps are timed as replays of a captured HIP graph of
-    # G back-to-back steps, so that the events measure the kernels and not the
-    # host's launch rate; G divides the step count.
-    G = args.graph_batch
-    if G < 0:
-        G = 20 if cfg in ("spmv_uniform", "bsr_spmv", "bsr_blocks") else 0
-    if G > 0:
-        G = max(g for g in range(1, min(G, args.steps) + 1) if args.steps % g == 0)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(G):
-                step()
-        torch.cuda.synchronize()
-    nrec = args.steps // G if G > 0 else args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(nrec)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(nrec)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(nrec):
-        if restore_every and i > 0 and i % restore_every == 0:
-            restore_fn()
-        starts[i].record(stream)
-        if G > 0:
-            graph.replay()
-        else:
-            step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    finite = locals().get("iterates_finite")
-    if finite is not None:
-        result["iterates_finite"] = finite()
-    ev_ms = [s.elapsed_time(e) / (G if G > 0 else 1) for s, e in zip(starts, ends)]
-    if G > 0:
-        # the graph's result equals an eager step's, bit for bit (deterministic kernels)
-        out = locals().get("out_tensor")
-        if out is not None:
-            got = out.clone()
-            step()
-            torch.cuda.synchronize()
-            result["graph_replay_matches_eager"] = bool(torch.equal(got, out))
-        result["graph_batch"] = G
-    ms_per_step = elapsed * 1e3 / args.steps
-    launch_ms = float(np.mean(ev_ms)) / launches
-    step_flops_s = flops / (ms_per_step * 1e-3)
-    result["value"] = round(step_flops_s / 1e9, 3)
-    result["ms_per_step"] = round(ms_per_step, 5)
-    result["dtype"] = dtype
-    result["config"] = config
-    per_launch_bytes = nbytes / launches
-    per_launch_flops = flops / launches
-    if bound == "hbm":
-        achieved = per_launch_bytes / (launch_ms * 1e-3) / 1e9
-    else:
-        achieved = per_launch_flops / (launch_ms * 1e-3) / 1e12
-    traffic = load_traffic(cfg + ("_N%d" % N if cfg in ("spmm_lognormal", "spmm_clustered") else ""), per_launch_bytes)
-    result["roofline"] = dict(bound=bound, achieved=round(achieved, 2), peak=peak, unit=unit,
-                              frac=round(achieved / peak, 4), traffic=traffic,
-                              kernel_ms=round(launch_ms, 5), algorithmic_bytes_per_launch=int(per_launch_bytes),
-                              flops_per_launch=int(per_launch_flops), event_ms_median=round(float(np.median(ev_ms)), 5))
-    if bound == "mfma":
-        result["roofline"]["hbm_gbs"] = round(per_launch_bytes / (launch_ms * 1e-3) / 1e9, 1)
-    result["roofline"]["event_ms_min"] = round(float(np.min(ev_ms)), 5)
-    # the copy rate this GPU measures now (outside the timed region): a plain
-    # 256 MiB device copy, read + write bytes over its time, as a reference
-    # beside the 8 TB/s spec (algorithmic bytes can exceed what a kernel
-    # moves, so the fraction can pass 1)
-    if bound == "hbm":
-        ref = torch.ones(64 << 20, device="cuda")
-        dst = torch.empty_like(ref)
-        dst.copy_(ref)
-        t = []
-        for _ in range(5):
-            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a0.record(stream)
-            dst.copy_(ref)
-            a1.record(stream)
-            torch.cuda.synchronize()
-            t.append(a0.elapsed_time(a1))
-        del ref, dst
-        copy_gbs = 2 * (64 << 20) * 4 / (float(np.median(t)) * 1e-3) / 1e9
-        result["roofline"]["measured_copy_gbs"] = round(copy_gbs, 1)
-        result["roofline"]["frac_of_copy"] = round(achieved / copy_gbs, 4)
-    result["gflops_event"] = round(per_launch_flops / (launch_ms * 1e-3) / 1e9, 2)
-
-    # ---------------- cold-cache steps (outside the timed region, on request)
-    if args.cold > 0:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.cold)]
-        # each rep: flush, one timed step (cold), then one more timed step the
-        # same way (warm: what the flushed step left in the caches), so that
-        # the difference is the caches' and not the single launch's
-        for i in range(args.cold):
-            if restore_fn:
-                restore_fn()  # before the flush, so the copy leaves nothing in the caches
-            flush.fill_(i & 255)
-            for j in (0, 2):
-                ev[i][j].record(stream)
-                step()
-                ev[i][j + 1].record(stream)
-        torch.cuda.synchronize()
-        del flush
-        cold_ms = [e[0].elapsed_time(e[1]) / launches for e in ev]
-        single_ms = [e[2].elapsed_time(e[3]) / launches for e in ev]
-        med = float(np.median(cold_ms))
-        if bound == "hbm":
-            cold_achieved = per_launch_bytes / (med * 1e-3) / 1e9
-        else:
-            cold_achieved = per_launch_flops / (med * 1e-3) / 1e12
-        result["cold"] = dict(reps=args.cold, flush_bytes=512 << 20, kernel_ms_median=round(med, 5),
-                              kernel_ms_min=round(float(np.min(cold_ms)), 5), achieved=round(cold_achieved, 2),
-                              unit=unit, frac=round(cold_achieved / peak, 4),
-                              warm_single_ms_median=round(float(np.median(single_ms)), 5))
-    result["setup"] = {k: round(v, 2) for k, v in setup.items()}
-
-    # ---------------- CPU baseline: the oracle on the host cores
-    if not args.no_cpu_baseline and cpu_leg is not None:
-        cpu_call, cpu_flops, cpu_desc = cpu_leg
-        reps, t_cpu = 0, 0.0
-        t0 = time.perf_counter()
-        while t_cpu < args.cpu_seconds and reps < 1000:
-            cpu_call()
-            reps += 1
-            t_cpu = time.perf_counter() - t0
-        per = t_cpu / reps
-        result["cpu_baseline"] = dict(value=round(cpu_flops / per / 1e9, 4), unit="GFLOP/s", cores=1, kind="oracle",
-                                      sample="%d %s, %.1f s" % (reps, cpu_desc, t_cpu))
-    elif not args.no_cpu_baseline:
-        result["cpu_baseline"] = None
+        torch.cuda.empty_cache()
+    head = records[names[0]]
+    result = dict(metric=METRIC, value=head["value"], unit="GFLOP/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+                  ms_per_step=head["ms_per_step"], higher_is_better=True, scaling="weak", vs_baseline=None,
+                  dtype=head["dtype"], data="synthetic (seeded generators in gen/, seed 0)", config=head["config"],
+                  roofline=head["roofline"])
+    for k, v in head.items():
+        if k not in result and k not in ("metric", "unit"):
+            result[k] = v
+    if len(names) > 1:
+        result["configs"] = {k: {kk: vv for kk, vv in v.items() if kk not in ("metric",)}
+                             for k, v in records.items() if k != names[0]}
     print(json.dumps(result), flush=True)
 
 

@@ -58,3 +58,46 @@ def test_traffic_counts_only_for_unchanged_kernels(tmp_path, monkeypatch):
     # the other families do not depend on it
     assert bench.kernel_family("bsr_blocks") == "bsr" and bench.kernel_family("spmm_lognormal_N32") == "spmm"
     assert bench.kernel_family("spmm_clustered_N32") == "wcsr" and bench.kernel_family("bsr_spmv") == "bsr_spmv"
+
+
+def test_storage_accounts_of_the_pages():
+    """The format page's section 1 example (10^6 rows, 10^7 fp64 entries, int32
+    indices): COO 16 bytes per entry = 160 MB; CSR 12 bytes per entry plus 4 MB
+    of row pointers = 124 MB (the page counts 10^6 pointers, the end pointer
+    adds 4 bytes); fp16 values bring CSR to 6 bytes per entry.  Its section 5:
+    one 4-byte index per 16 x 16 block is 0.0156 bytes per value.  The LSMR
+    page's section 4: values and indices of the CSR + CSC pair at nnz =
+    19,747,202 are about 301 MiB."""
+    assert bench.coo_storage_bytes(10 ** 7) == 160 * 10 ** 6
+    assert bench.csr_storage_bytes(10 ** 6, 10 ** 7) == 124 * 10 ** 6 + 4
+    assert bench.csr_storage_bytes(10 ** 6, 10 ** 7, val_bytes=2) - 4 * (10 ** 6 + 1) == 6 * 10 ** 7
+    assert round(bench.block_index_bytes_per_value(16), 4) == 0.0156
+    assert bench.block_index_bytes_per_value(16) == 4 / 256
+    mib = bench.dual_value_index_bytes(19747202) / 2 ** 20
+    assert abs(mib - 301.3) < 0.05
+    assert bench.dual_storage_bytes(10, 20, 7) == 2 * 8 * 7 + 4 * 11 + 4 * 21
+
+
+def test_gather_aware_spmm_bound():
+    # every entry reads at least a 128-byte line of B, or its 4N-byte row segment
+    assert bench.spmm_gather_bytes(3, 5, 8) == 8 * 5 + 4 * 4 + 5 * 128 + 4 * 3 * 8
+    assert bench.spmm_gather_bytes(3, 5, 64) == 8 * 5 + 4 * 4 + 5 * 256 + 4 * 3 * 64
+
+
+def test_workload_names_and_cpu_row_ranges():
+    import numpy as np
+    assert bench.parse_workload("spmm_lognormal_N128") == ("spmm_lognormal", 128)
+    assert bench.parse_workload("spmm_clustered_N32") == ("spmm_clustered", 32)
+    assert bench.parse_workload("stencil27") == ("stencil27", None)
+    assert bench.ALL_WORKLOADS[0] == bench.HEADLINE
+    rp = np.array([0, 3, 3, 10, 12, 20], np.int64)
+    # ranges of about equal entry counts, covering [0, hi) once, none empty
+    for hi in range(1, 6):
+        for parts in (1, 2, 3, 8):
+            r = bench._ranges(rp, hi, parts)
+            assert r[0][0] == 0 and r[-1][1] == hi
+            assert all(a < b for a, b in r) and all(r[i][1] == r[i + 1][0] for i in range(len(r) - 1))
+    # the row sample stops before the flop budget is exceeded (all rows when they fit)
+    assert bench._sample_rows(rp, 2, 25) == 4 and rp[4] * 2 <= 25
+    assert bench._sample_rows(rp, 2, 40) == 5
+    assert 1 <= bench.cpu_threads() <= 16
