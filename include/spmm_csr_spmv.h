@@ -78,6 +78,21 @@ int csr_build_from_coo(int64_t m, int64_t n, int64_t nnz,
                        int32_t* row_ptr, int32_t* col_idx, float* val,
                        void* work, size_t work_bytes, void* stream);
 
+/* COO -> CSR as csr_build_from_coo, for callers that cannot allocate device
+ * memory (code whose harness forbids hipMalloc, loops that must not allocate):
+ * no workspace argument; the scratch is a static 64 MiB device array that the
+ * library holds on every GPU it runs on until the process ends.  Sizes whose
+ * csr_build_from_coo_bufsize() exceeds 64 MiB (about 3.5 M entries with
+ * m = 1 M rows; 16 bytes per entry plus 24 per row) are refused with
+ * SP_ERR_WORKSPACE before any work is enqueued.  Every call on one GPU uses
+ * the same array: calls that overlap in time on one GPU (on other streams or
+ * from other host threads) race and must be ordered by the caller.
+ * Synchronises `stream` once, as csr_build_from_coo.  Allocates nothing.
+ * Errors: those of csr_build_from_coo, SP_ERR_WORKSPACE as above. */
+int csr_build_from_coo_noalloc(int64_t m, int64_t n, int64_t nnz,
+                               const int32_t* coo_row, const int32_t* coo_col, const float* coo_val,
+                               int32_t* row_ptr, int32_t* col_idx, float* val, void* stream);
+
 /* --------------------------------------------------------- CSR -> CSC
  * [LSMR] §2 and §4: the CSC of A is, array for array, the CSR of A^T; it is
  * built once, when the matrix is constructed.  Reading a CSC input as the

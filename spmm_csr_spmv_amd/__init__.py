@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     bsr_spmm,
     bsr_spmv,
     csr_build_from_coo,
+    csr_build_from_coo_noalloc,
     csr_to_bsr,
     csr_to_csc,
     csr_to_wcsr,

@@ -31,7 +31,8 @@ EXPORTS = ("sp_status_string", "sp_version", "csr_build_from_coo_bufsize", "csr_
            "csr_to_bsr_bufsize", "csr_to_bsr_analyze", "csr_to_bsr_fill", "bsr_spmv", "bsr_spmm_bufsize", "bsr_spmm",
            "sp_plan_dispatch_key", "sp_tune_cache_store", "sp_tune_cache_lookup", "sp_tune_cache_clear",
            "sp_tune_cache_size", "sp_autotune_workspace_size", "sp_autotune_spmv", "csr_to_wcsr_bufsize",
-           "csr_to_wcsr_analyze", "csr_to_wcsr_fill", "wcsr_spmm", "sp_plan_view_create")
+           "csr_to_wcsr_analyze", "csr_to_wcsr_fill", "wcsr_spmm", "sp_plan_view_create",
+           "csr_build_from_coo_noalloc")
 
 
 class SparseError(RuntimeError):
@@ -90,6 +91,7 @@ def lib():
         L.sp_version.restype = ctypes.c_int
         L.csr_build_from_coo_bufsize.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
         L.csr_build_from_coo.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
+        L.csr_build_from_coo_noalloc.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p]
         L.csr_to_csc_bufsize.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
         L.csr_to_csc.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
         L.sp_plan_options_default.argtypes = [ctypes.POINTER(sp_plan_options)]
@@ -196,6 +198,23 @@ def csr_build_from_coo(m, n, coo_row, coo_col, coo_val, stream=None):
     _check("csr_build_from_coo",
            L.csr_build_from_coo(m, n, nnz, _ptr(coo_row), _ptr(coo_col), _ptr(coo_val), _ptr(row_ptr), _ptr(col_idx),
                                 _ptr(val), _ptr(work), size.value, _stream(stream)))
+    return row_ptr, col_idx, val
+
+
+def csr_build_from_coo_noalloc(m, n, coo_row, coo_col, coo_val, stream=None):
+    """COO -> CSR like csr_build_from_coo, the library's static per-GPU scratch
+    instead of a workspace (the outputs are still allocated here)."""
+    L = lib()
+    _dev(coo_row, torch.int32, "coo_row"), _dev(coo_col, torch.int32, "coo_col"), _dev(coo_val, torch.float32, "coo_val")
+    nnz = coo_row.numel()
+    dev = coo_row.device
+    with _on(stream):
+        row_ptr = torch.empty(m + 1, dtype=torch.int32, device=dev)
+        col_idx = torch.empty(nnz, dtype=torch.int32, device=dev)
+        val = torch.empty(nnz, dtype=torch.float32, device=dev)
+    _check("csr_build_from_coo_noalloc",
+           L.csr_build_from_coo_noalloc(m, n, nnz, _ptr(coo_row), _ptr(coo_col), _ptr(coo_val), _ptr(row_ptr),
+                                        _ptr(col_idx), _ptr(val), _stream(stream)))
     return row_ptr, col_idx, val
 
 

@@ -1029,6 +1029,14 @@ int csr_build_from_coo(int64_t m, int64_t n, int64_t nnz, const int32_t* coo_row
                                   (hipStream_t)stream);
 }
 
+int csr_build_from_coo_noalloc(int64_t m, int64_t n, int64_t nnz, const int32_t* coo_row, const int32_t* coo_col,
+                               const float* coo_val, int32_t* row_ptr, int32_t* col_idx, float* val, void* stream) {
+    int rc = check_dims(m, n, nnz);
+    if (rc) return rc;
+    if (!row_ptr || (nnz > 0 && (!coo_row || !coo_col || !coo_val || !col_idx || !val))) return SP_ERR_NULL;
+    return spx::coo_to_csr_noalloc(m, n, nnz, coo_row, coo_col, coo_val, row_ptr, col_idx, val, (hipStream_t)stream);
+}
+
 int csr_to_csc_bufsize(int64_t m, int64_t n, int64_t nnz, size_t* bytes) {
     if (!bytes) return SP_ERR_NULL;
     const int rc = check_dims(m, n, nnz);

@@ -24,6 +24,7 @@
 #include "device_common.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace spx {
 
@@ -731,6 +732,54 @@ int csr_to_csc_device(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr,
     hipLaunchKernelGGL(gather_out, dim3(grid_for(nnz)), dim3(kBlock), 0, s, nnz, keys, val, row_idx, cval);
     SPX_LAUNCH();
     return SP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// COO -> CSR for callers that cannot allocate device memory: the same
+// conversion, its scratch taken from `scratch`, a static device array of
+// kNoallocScratchBytes on every GPU the library runs on (held until the
+// process ends).  Each region of it that the conversion reads is first
+// written by the same call (counts and flags by fill kernels, cursors by the
+// classification, keys by the scatter), so whatever a previous call left
+// there does not matter.  All calls on one GPU share the array: two calls
+// that overlap in time on one GPU (other streams, other host threads) race.
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+constexpr int kNoallocMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kNoallocMaxDevices] = {};
+}  // namespace
+
+// Device address of `scratch` on the current device.  The name of the array
+// in host code is only a host-side stand-in: its device address is looked up
+// once per device, with that device current, and kept.
+static int scratch_on_current_device(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SP_ERR_HIP;
+    if (dev < 0 || dev >= kNoallocMaxDevices) return SP_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SP_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SP_OK;
+}
+
+size_t coo_build_noalloc_limit() { return kNoallocScratchBytes; }
+
+int coo_to_csr_noalloc(int64_t m, int64_t n, int64_t nnz, const int32_t* coo_row, const int32_t* coo_col,
+                       const float* coo_val, int32_t* row_ptr, int32_t* col_idx, float* val, hipStream_t s) {
+    if (coo_build_bytes(m, n, nnz) > kNoallocScratchBytes) return SP_ERR_WORKSPACE;
+    void* ws = nullptr;
+    const int rc = scratch_on_current_device(&ws);
+    if (rc != SP_OK) return rc;
+    return coo_to_csr_device(m, n, nnz, coo_row, coo_col, coo_val, row_ptr, col_idx, val, ws, kNoallocScratchBytes,
+                             s);
 }
 
 }  // namespace spx

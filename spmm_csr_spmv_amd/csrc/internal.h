@@ -123,6 +123,12 @@ int csr_to_csc_device(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr,
                       const float* val, int32_t* col_ptr, int32_t* row_idx, float* cval, void* work,
                       size_t work_bytes, hipStream_t s);
 
+// COO -> CSR with the scratch in the library's static per-GPU array
+// (convert.hip); SP_ERR_WORKSPACE when coo_build_bytes() exceeds its size.
+size_t coo_build_noalloc_limit();
+int coo_to_csr_noalloc(int64_t m, int64_t n, int64_t nnz, const int32_t* coo_row, const int32_t* coo_col,
+                       const float* coo_val, int32_t* row_ptr, int32_t* col_idx, float* val, hipStream_t s);
+
 // Inclusive prefix sum of a[0..n) in place; sums is scratch of scan_work_bytes(n) (convert.hip).
 size_t scan_work_bytes(int64_t n);
 int scan_inclusive_i32(int32_t* a, int64_t n, int32_t* sums, hipStream_t s);

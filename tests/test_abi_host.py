@@ -238,3 +238,13 @@ def test_view_argument_errors():
     assert L.sp_plan_view_create(None, ctypes.byref(v)) == 1
     assert L.sp_plan_view_create(FAKE, None) == 1
     assert L.sp_plan_destroy(None) == 0
+
+
+def test_noalloc_conversion_refuses_before_work():
+    L = sp.lib()
+    b = SZ()
+    # the static scratch holds 64 MiB: a conversion needing more is refused
+    assert L.csr_build_from_coo_bufsize(1000, 1000, 5_000_000, ctypes.byref(b)) == 0 and b.value > 64 << 20
+    assert L.csr_build_from_coo_noalloc(1000, 1000, 5_000_000, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 4
+    assert L.csr_build_from_coo_noalloc(-1, 4, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert L.csr_build_from_coo_noalloc(4, 4, 3, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == 1
