@@ -173,6 +173,25 @@ int csr_to_csc(int64_t m, int64_t n, int64_t nnz,
  * returns SP_ERR_UNSUPPORTED for an explicit b that needs more than 256
  * windows.  Column indices outside [0, n) make sp_plan_create return
  * SP_ERR_INDEX whenever either stream is built.
+ *
+ * Phase-swept SpMM ([GEN] §3.1: with few right-hand sides the cost is the
+ * B-row reads; §2.5: gathers that leave the cache are the real cost): with
+ * spmm_phase_bits = b, sp_plan_bind builds a copy of A in which the columns
+ * are cut into phases of 2^b columns and, for every block of 2048 rows cut
+ * into 8 row ranges of about equal entry counts, each range's entries are
+ * stored phase by phase (at most 2^21 columns).  spmm with
+ * N in {4, 8, 16} (B and C rows 16-byte aligned) then runs one workgroup per
+ * block that keeps the block's C rows in LDS and sweeps the phases in order,
+ * so the B rows every XCD reads at a time form one slice of 2^b rows that
+ * stays in its L2; each C row is summed by one wave in a fixed order.  The
+ * default (-1) builds it when max_N (of the bind) is 4..16, B (n * max_N
+ * floats) exceeds 8 MiB, no row is longer than 8192 entries and a sample of
+ * rows shows columns spread over more than a quarter of the range and the
+ * matrix has at most 2^21 columns, with 2^b * max_N * 4 bytes = 512 KiB
+ * slices.
+ * An explicit b above 21 is taken as 21.  The copy costs 8 bytes per entry
+ * plus 4 bytes per (block, range, phase); sp_plan_bind reads the row pointer
+ * and column indices back once to lay it out.
  */
 typedef struct sp_plan sp_plan;
 
@@ -187,6 +206,7 @@ typedef struct sp_plan_options {
     int32_t xcd_remap;   /* 1 (default): consecutive groups go to one XCD     */
     int32_t col_panels;  /* -1 auto (default), 0 off, or 1, 2, 4, 8 panels    */
     int32_t x_window_bits; /* -1 auto (default), 0 off, or 5..15: x windows of 2^bits columns */
+    int32_t spmm_phase_bits; /* -1 auto (default), 0 off, or 5..24: SpMM phases of 2^bits columns */
 } sp_plan_options;
 
 /* Row-length profile and bin sizes of one direction of a plan. */
@@ -202,6 +222,8 @@ typedef struct sp_profile {
     int64_t sell_slots;          /* padded SELL slots (0 without SELL)         */
     int64_t col_panels;          /* panels of the column-panel stream (0: off)  */
     int64_t x_window_bits;       /* window bits of the x-window stream (0: off) */
+    int64_t spmm_phase_bits;     /* phase bits of the phase-swept SpMM copy, set by
+                                    sp_plan_bind (0: off)                       */
 } sp_profile;
 
 /* Fills *opt with the defaults listed above. */

@@ -47,7 +47,7 @@ class sp_plan_options(ctypes.Structure):
     _fields_ = [("group_nnz", ctypes.c_int32), ("wave_min", ctypes.c_int32), ("block_min", ctypes.c_int32),
                 ("split_min", ctypes.c_int32), ("split_seg", ctypes.c_int32), ("use_sell", ctypes.c_int32),
                 ("sell_sigma", ctypes.c_int32), ("xcd_remap", ctypes.c_int32), ("col_panels", ctypes.c_int32),
-                ("x_window_bits", ctypes.c_int32)]
+                ("x_window_bits", ctypes.c_int32), ("spmm_phase_bits", ctypes.c_int32)]
 
 
 class sp_profile(ctypes.Structure):
@@ -59,7 +59,8 @@ class sp_profile(ctypes.Structure):
                 ("wave_rows", ctypes.c_int64), ("wave_nnz", ctypes.c_int64),
                 ("block_rows", ctypes.c_int64), ("block_nnz", ctypes.c_int64),
                 ("split_rows", ctypes.c_int64), ("split_segments", ctypes.c_int64), ("split_nnz", ctypes.c_int64),
-                ("sell_slots", ctypes.c_int64), ("col_panels", ctypes.c_int64), ("x_window_bits", ctypes.c_int64)]
+                ("sell_slots", ctypes.c_int64), ("col_panels", ctypes.c_int64), ("x_window_bits", ctypes.c_int64),
+                ("spmm_phase_bits", ctypes.c_int64)]
 
 
 class sp_dispatch_key(ctypes.Structure):

@@ -78,6 +78,10 @@ struct Dir {
     std::vector<int4> xw_split_rows;   // {row, partial_base, nseg, 0}
     std::vector<int32_t> xw_pos;       // [nnz] stream position of each CSR entry
     int64_t xw_total = 0, xw_n_partials = 0;
+    // phase-swept SpMM copy (host side; see spmm.hip): decided per bind from max_N
+    bool col_spread = false;           // sampled rows spread over > 1/4 of the columns
+    mutable int32_t sw_pb = 0, sw_P = 0, sw_nblk = 0;
+    mutable size_t off_sw_off = 0, off_sw_wrow = 0, off_sw_pk = 0, off_sw_pv = 0;
     sp_profile prof{};
     DirDevice dev{};
     // workspace offsets (byte offsets into the bound workspace)
@@ -289,8 +293,38 @@ void build_sell(const std::vector<int32_t>& hptr, const sp_plan_options& o, Dir&
 
 int64_t ps_ystride(int64_t rows) { return (rows + 63) / 64 * 64; }
 
-size_t dir_layout(const Dir& d, const sp_plan_options& o, int32_t max_N, size_t base) {
+// Phase width (bits) of the phase-swept SpMM copy for a bind with max_N, or 0
+// for none (the rule is in the public header, sp_plan_options).
+int32_t sweep_bits(const Dir& d, const sp_plan_options& o, int32_t max_N) {
+    if (!d.present || d.rows == 0 || d.nnz == 0 || o.spmm_phase_bits == 0) return 0;
+    if (d.nnz > kI32Max) return 0;
+    if (d.cols > (1 << spx::kSwColBits)) return 0;  // columns are stored in kSwColBits bits
+    if (o.spmm_phase_bits > 0) return std::min(o.spmm_phase_bits, spx::kSwColBits);
+    if (max_N < 4 || max_N > 16) return 0;
+    if ((int64_t)d.cols * max_N * 4 <= ((int64_t)8 << 20)) return 0;
+    if (d.prof.max_len > spx::kSwMaxRowLen || !d.col_spread) return 0;
+    int32_t b = 5;
+    while (b < spx::kSwColBits && ((int64_t)1 << (b + 1)) * max_N * 4 <= spx::kSwSliceBytes) ++b;
+    return ((int64_t)d.cols + ((int64_t)1 << b) - 1) >> b >= 2 ? b : 0;
+}
+
+size_t dir_layout(const Dir& d, const sp_plan_options& o, int32_t max_N, size_t base, bool forward) {
     size_t off = base;
+    d.sw_pb = forward ? sweep_bits(d, o, max_N) : 0;  // spmm runs on A only
+    if (d.sw_pb > 0) {
+        d.sw_P = (int32_t)(((int64_t)d.cols + ((int64_t)1 << d.sw_pb) - 1) >> d.sw_pb);
+        d.sw_nblk = (int32_t)(((int64_t)d.rows + spx::kSwRows - 1) / spx::kSwRows);
+        d.off_sw_off = off;
+        off = align256(off + ((size_t)d.sw_nblk * d.sw_P * spx::kSwWaves + 1) * sizeof(int32_t));
+        d.off_sw_wrow = off;
+        off = align256(off + ((size_t)d.sw_nblk * spx::kSwWaves + 1) * sizeof(int32_t));
+        d.off_sw_pk = off;
+        off = align256(off + (size_t)d.nnz * sizeof(uint32_t));
+        d.off_sw_pv = off;
+        off = align256(off + (size_t)d.nnz * sizeof(float));
+    } else {
+        d.sw_P = d.sw_nblk = 0;
+    }
     d.off_tasks = off;
     off = align256(off + d.tasks.size() * sizeof(int4));
     d.off_split_rows = off;
@@ -370,8 +404,8 @@ constexpr size_t kMiscBytes = 256;
 
 size_t plan_layout(const sp_plan* p, int32_t max_N) {
     size_t off = kMiscBytes;
-    if (p->fwd.present) off = dir_layout(p->fwd, p->opt, max_N, off);
-    if (p->tr.present) off = dir_layout(p->tr, p->opt, max_N, off);
+    if (p->fwd.present) off = dir_layout(p->fwd, p->opt, max_N, off, true);
+    if (p->tr.present) off = dir_layout(p->tr, p->opt, max_N, off, false);
     return off < 256 ? 256 : off;
 }
 
@@ -444,6 +478,8 @@ int check_options_impl(const sp_plan_options& o) {
     if (o.x_window_bits != -1 && o.x_window_bits != 0 &&
         (o.x_window_bits < spx::kXwMinBits || o.x_window_bits > spx::kXwMaxBits))
         return SP_ERR_UNSUPPORTED;
+    if (o.spmm_phase_bits != -1 && o.spmm_phase_bits != 0 && (o.spmm_phase_bits < 5 || o.spmm_phase_bits > 24))
+        return SP_ERR_UNSUPPORTED;
     return SP_OK;
 }
 
@@ -452,9 +488,22 @@ int check_options_impl(const sp_plan_options& o) {
 // tasks must show columns spread over more than a quarter of the column range
 // (median over the sample of max col - min col).  Reads the sampled column
 // ranges back: synchronises.
+int column_spread(const Dir& d, hipStream_t s, bool* spread);
+
 int scattered_columns(const Dir& d, hipStream_t s, int32_t* P) {
     *P = 0;
     if ((int64_t)d.cols * 4 <= (int64_t)8 << 20) return SP_OK;
+    bool spread = false;
+    const int rc = column_spread(d, s, &spread);
+    if (rc == SP_OK && spread) *P = 8;
+    return rc;
+}
+
+// A sample of up to 64 evenly spaced group tasks: is the median over the
+// sample of (max col - min col) more than a quarter of the column range?
+// Reads the sampled column ranges back: synchronises.
+int column_spread(const Dir& d, hipStream_t s, bool* spread) {
+    *spread = false;
     const int32_t first = d.n_split + d.n_block + d.n_wave;
     const int32_t nsample = std::min<int32_t>(64, d.n_group);
     std::vector<std::vector<int32_t>> cols((size_t)nsample);
@@ -474,7 +523,7 @@ int scattered_columns(const Dir& d, hipStream_t s, int32_t* P) {
     }
     if (spans.empty()) return SP_OK;
     std::nth_element(spans.begin(), spans.begin() + spans.size() / 2, spans.end());
-    if (spans[spans.size() / 2] * 4 > d.cols) *P = 8;
+    *spread = spans[spans.size() / 2] * 4 > d.cols;
     return SP_OK;
 }
 
@@ -779,7 +828,7 @@ int build_xwin(const std::vector<int32_t>& hptr, int32_t bits, Dir& d, hipStream
 }
 
 int setup_dir(Dir& d, int64_t rows, int64_t cols, int64_t nnz, const int32_t* ptr, const int32_t* idx, const float* val,
-              const sp_plan_options& o, hipStream_t s) {
+              const sp_plan_options& o, hipStream_t s, bool forward) {
     d.present = true;
     d.rows = (int32_t)rows;
     d.cols = (int32_t)cols;
@@ -846,6 +895,79 @@ int setup_dir(Dir& d, int64_t rows, int64_t cols, int64_t nnz, const int32_t* pt
     }
     d.prof.col_panels = d.ps_P;
     d.prof.x_window_bits = d.xw_bits;
+    // column spread for the phase-swept SpMM's automatic rule (B of 8 MiB at
+    // N = 16 at the least)
+    d.col_spread = false;
+    if (forward && o.spmm_phase_bits == -1 && d.rows > 0 && d.n_group > 0 && d.prof.max_len <= spx::kSwMaxRowLen &&
+        (int64_t)d.cols * 16 * 4 > ((int64_t)8 << 20)) {
+        const int rc = column_spread(d, s, &d.col_spread);
+        if (rc != SP_OK) return rc;
+    }
+    return SP_OK;
+}
+
+// Phase-swept SpMM copy (spmm.hip) of d for the bind's layout: the table of
+// first entries of every (block, wave, phase) and, in d.sw_pk, the CSR entry
+// of every stream slot, which the build kernel turns into the packed words
+// and values.  Reads the row pointer and column indices back (synchronises).
+int build_sweep(Dir& d, char* ws, hipStream_t s) {
+    std::vector<int32_t> hptr((size_t)d.rows + 1), hidx;
+    if (hipMemcpyAsync(hptr.data(), d.ptr, hptr.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return SP_ERR_HIP;
+    int rc = fetch_columns(d, s, hidx);  // synchronises
+    if (rc != SP_OK) return rc;
+    const int32_t pb = d.sw_pb, P = d.sw_P, nblk = d.sw_nblk;
+    constexpr int W = spx::kSwWaves;
+    const size_t ncell = (size_t)nblk * P * W;
+    // wave row ranges: each block's rows cut into W contiguous ranges of about
+    // equal entry counts (cut k at the first row whose entries before it in
+    // the block reach k/W of the block's entries)
+    std::vector<int32_t> wrow((size_t)nblk * W + 1);
+    for (int64_t g = 0; g < nblk; ++g) {
+        const int64_t rb = g * spx::kSwRows, re = std::min<int64_t>(d.rows, rb + spx::kSwRows);
+        const int64_t base = hptr[(size_t)rb], tot = (int64_t)hptr[(size_t)re] - base;
+        int64_t r = rb;
+        for (int w = 0; w < W; ++w) {
+            const int64_t goal = base + (tot * w + W - 1) / W;
+            while (r < re && hptr[(size_t)r] < goal) ++r;
+            wrow[(size_t)g * W + (size_t)w] = (int32_t)r;
+        }
+    }
+    wrow[(size_t)nblk * W] = (int32_t)d.rows;
+    std::vector<int32_t> off(ncell + 1, 0);
+    // counts of every (block, wave, phase) cell; blocks are independent
+    parallel_for(nblk, [&](int64_t g) {
+        for (int w = 0; w < W; ++w) {
+            const int64_t r0 = wrow[(size_t)g * W + (size_t)w], r1 = wrow[(size_t)g * W + (size_t)w + 1];
+            const size_t cell = ((size_t)g * W + (size_t)w) * P;
+            for (int64_t r = r0; r < r1; ++r)
+                for (int32_t q = hptr[(size_t)r]; q < hptr[(size_t)r + 1]; ++q)
+                    ++off[cell + (size_t)(hidx[(size_t)q] >> pb) + 1];
+        }
+    });
+    for (size_t k = 1; k <= ncell; ++k) off[k] += off[k - 1];
+    std::vector<int32_t> src((size_t)d.nnz);
+    parallel_for(nblk, [&](int64_t g) {
+        std::vector<int32_t> cur((size_t)P);
+        for (int w = 0; w < W; ++w) {
+            const size_t cell = ((size_t)g * W + (size_t)w) * P;
+            for (size_t k = 0; k < cur.size(); ++k) cur[k] = off[cell + k];
+            const int64_t r0 = wrow[(size_t)g * W + (size_t)w], r1 = wrow[(size_t)g * W + (size_t)w + 1];
+            for (int64_t r = r0; r < r1; ++r)
+                for (int32_t q = hptr[(size_t)r]; q < hptr[(size_t)r + 1]; ++q)
+                    src[(size_t)cur[(size_t)(hidx[(size_t)q] >> pb)]++] = q;
+        }
+    });
+    // the uploads must not outlive the host vectors: synchronise after the build
+    if (hipMemcpyAsync(ws + d.off_sw_off, off.data(), off.size() * sizeof(int32_t), hipMemcpyHostToDevice, s) !=
+            hipSuccess ||
+        hipMemcpyAsync(ws + d.off_sw_wrow, wrow.data(), wrow.size() * sizeof(int32_t), hipMemcpyHostToDevice, s) !=
+            hipSuccess ||
+        hipMemcpyAsync(ws + d.off_sw_pk, src.data(), src.size() * sizeof(int32_t), hipMemcpyHostToDevice, s) !=
+            hipSuccess)
+        return SP_ERR_HIP;
+    if (spx::launch_sweep_build(d.dev, d.nnz, s) != hipSuccess) return SP_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return SP_ERR_HIP;
     return SP_OK;
 }
 
@@ -947,6 +1069,15 @@ int upload_dir(Dir& d, char* ws, const sp_plan_options& o, hipStream_t s) {
         if (!d.xw_split_rows.empty() &&
             spx::launch_fill_i32(v.xw_counters, (int64_t)d.xw_split_rows.size(), 0, s) != hipSuccess)
             return SP_ERR_HIP;
+    }
+    v.sw_pb = d.sw_pb;
+    if (d.sw_pb > 0) {
+        v.sw_P = d.sw_P;
+        v.sw_nblk = d.sw_nblk;
+        v.sw_off = reinterpret_cast<const int32_t*>(ws + d.off_sw_off);
+        v.sw_wrow = reinterpret_cast<const int32_t*>(ws + d.off_sw_wrow);
+        v.sw_pk = reinterpret_cast<uint32_t*>(ws + d.off_sw_pk);
+        v.sw_pv = reinterpret_cast<float*>(ws + d.off_sw_pv);
     }
     if (d.use_sell) {
         v.use_sell = 1;
@@ -1066,6 +1197,7 @@ int sp_plan_options_default(sp_plan_options* o) {
     o->use_sell = -1;
     o->col_panels = -1;
     o->x_window_bits = -1;
+    o->spmm_phase_bits = -1;
     o->sell_sigma = 1024;
     o->xcd_remap = 1;
     return SP_OK;
@@ -1100,7 +1232,7 @@ int sp_plan_create(sp_plan** plan, int64_t m, int64_t n, int64_t nnz, const int3
     p->nnz = nnz;
     p->opt = o;
     hipStream_t s = (hipStream_t)stream;
-    rc = setup_dir(p->fwd, m, n, nnz, row_ptr, col_idx, val, o, s);
+    rc = setup_dir(p->fwd, m, n, nnz, row_ptr, col_idx, val, o, s, true);
     if (rc == SP_OK && !opt) {
         // no options given: a tuned winner cached for this matrix's dispatch key
         // (SpMV, version 0) replaces the defaults
@@ -1112,10 +1244,10 @@ int sp_plan_create(sp_plan** plan, int64_t m, int64_t n, int64_t nnz, const int3
             o = tuned;
             p->opt = o;
             p->fwd = Dir{};
-            rc = setup_dir(p->fwd, m, n, nnz, row_ptr, col_idx, val, o, s);
+            rc = setup_dir(p->fwd, m, n, nnz, row_ptr, col_idx, val, o, s, true);
         }
     }
-    if (rc == SP_OK && has_t) rc = setup_dir(p->tr, n, m, nnz, col_ptr, row_idx, cval, o, s);
+    if (rc == SP_OK && has_t) rc = setup_dir(p->tr, n, m, nnz, col_ptr, row_idx, cval, o, s, false);
     if (rc != SP_OK) {
         delete p;
         return rc;
@@ -1217,7 +1349,9 @@ int sp_plan_bind(sp_plan* plan, void* work, size_t work_bytes, int32_t max_N, vo
     int rc = SP_OK;
     if (plan->fwd.present) rc = upload_dir(plan->fwd, ws, plan->opt, s);
     if (rc == SP_OK && plan->tr.present) rc = upload_dir(plan->tr, ws, plan->opt, s);
+    if (rc == SP_OK && plan->fwd.present && plan->fwd.sw_pb > 0) rc = build_sweep(plan->fwd, ws, s);
     if (rc != SP_OK) return rc;
+    plan->fwd.prof.spmm_phase_bits = plan->fwd.sw_pb;
     // arrival counters start at zero; the kernels put them back to zero
     for (Dir* d : {&plan->fwd, &plan->tr}) {
         if (!d->present || d->split_rows.empty()) continue;
@@ -1275,9 +1409,11 @@ int spmm(const sp_plan* plan, int32_t N, float alpha, const float* B, int64_t ld
     if (!tables_of(plan)->fwd.split_rows.empty() && N > plan->bound_max_N) return SP_ERR_SIZE;
     if ((plan->n > 0 && !B) || (plan->m > 0 && !C)) return SP_ERR_NULL;
     if (plan->m == 0) return SP_OK;
-    return spx::launch_spmm(dir_dev(plan, 0), N, alpha, B, ldb, beta, C, ldc, (hipStream_t)stream) == hipSuccess
-               ? SP_OK
-               : SP_ERR_HIP;
+    const DirDevice& d = dir_dev(plan, 0);
+    hipError_t e = spx::spmm_sweep_ok(d, N, B, ldb, C, ldc)
+                       ? spx::launch_spmm_sweep(d, N, alpha, B, ldb, beta, C, ldc, (hipStream_t)stream)
+                       : spx::launch_spmm(d, N, alpha, B, ldb, beta, C, ldc, (hipStream_t)stream);
+    return e == hipSuccess ? SP_OK : SP_ERR_HIP;
 }
 
 // ------------------------------------------------------------------ CSR -> BSR, BSR SpMV

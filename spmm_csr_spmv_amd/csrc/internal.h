@@ -24,6 +24,12 @@ constexpr int kXwMaxBits = 15;       // x-window stream: widest window, 2^15 col
 constexpr int kXwPiece = 32768;      // x-window stream: window entries per product workgroup
 constexpr int kXwPieceRuns = 1024;   // x-window stream: chunks per product workgroup
 constexpr int kXwProdGrid = 256;     // x-window stream: product workgroups (one per CU, 32 per XCD)
+constexpr int kSwWaves = 8;          // phase-swept SpMM: waves per workgroup
+constexpr int kSwRows = 2048;        // phase-swept SpMM: rows per workgroup (C rows in LDS)
+constexpr int kSwRowBits = 11;       // phase-swept SpMM: row within the workgroup's rows
+constexpr int kSwColBits = 21;       // phase-swept SpMM: column bits (at most 2^21 columns)
+constexpr int kSwMaxRowLen = 8192;   // phase-swept SpMM: longest row the automatic rule accepts
+constexpr int kSwSliceBytes = 512 << 10;  // phase-swept SpMM: B slice of one phase (automatic rule)
 
 // Task tables of one direction (A or A^T), laid out in device memory as one
 // int4 array: [split tasks | block tasks | wave tasks | group tasks].
@@ -83,6 +89,17 @@ struct DirDevice {
     const int4* xw_split_rows;       // {row, partial_base, nseg, 0}
     float* xw_partials;
     int32_t* xw_counters;            // [n_split_rows] arrival counters (self-resetting)
+    // optional phase-swept copy for SpMM with small N (spmm.hip): columns cut
+    // into sw_P phases of 2^sw_pb columns; blocks of kSwRows rows, cut into
+    // kSwWaves wave ranges of about equal entry counts; per (block, wave,
+    // phase) the wave's entries of that phase, rows then columns ascending:
+    // word (row - block's first row) << kSwColBits | column, and the value
+    int32_t sw_pb;                   // 0 = off
+    int32_t sw_P, sw_nblk;
+    const int32_t* sw_off;           // [(g kSwWaves + w) P + p] first entry; last = nnz
+    const int32_t* sw_wrow;          // [g kSwWaves + w] first row of each wave; last = rows
+    uint32_t* sw_pk;
+    float* sw_pv;
     // optional SELL-C-sigma copy of the group rows
     int32_t use_sell;
     int32_t sell_slices;
@@ -112,6 +129,14 @@ hipError_t launch_spmv_xwin(const DirDevice& d, float alpha, const float* x, flo
 // Writes the stream copies of d from pos[q] (chunk-major stream position of
 // CSR entry q), which the caller uploaded.
 hipError_t launch_xwin_build(const DirDevice& d, const int32_t* pos, hipStream_t s);
+
+// Phase-swept SpMM (spmm.hip): true when the call can take it (N in {4, 8, 16},
+// 16-byte aligned B and C rows); the build writes the stream from src[s] (the
+// CSR entry of stream slot s), which the caller uploaded into d.sw_pk.
+bool spmm_sweep_ok(const DirDevice& d, int32_t N, const float* B, int64_t ldb, const float* C, int64_t ldc);
+hipError_t launch_spmm_sweep(const DirDevice& d, int32_t N, float alpha, const float* B, int64_t ldb, float beta,
+                             float* C, int64_t ldc, hipStream_t s);
+hipError_t launch_sweep_build(const DirDevice& d, int64_t nnz, hipStream_t s);
 
 // Conversions: workspace sizes and the two builders (host driver in convert.hip).
 size_t coo_build_bytes(int64_t m, int64_t n, int64_t nnz);

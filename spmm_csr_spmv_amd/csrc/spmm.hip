@@ -14,6 +14,8 @@
 // their (column, value) pairs through LDS; wave / block rows spread a row's
 // entries over the sub-groups and reduce across them; split rows write
 // per-segment partial tiles that the last segment adds in fixed order.
+#include <algorithm>
+
 #include "device_common.h"
 
 namespace spx {
@@ -238,7 +240,176 @@ __global__ __launch_bounds__(kBlock) void spmm_bins_kernel(
     spmm_group<V>(x, tasks[n_split + n_block + n_wave + g], G, n0, lcol, lval);
 }
 
+// ---- phase-swept SpMM (small N) ---------------------------------------------
+// 「通用稀疏矩阵乘法CUDA算子实现」 §3.1: with few right-hand sides each entry's B
+// row segment is short, and the B reads, not the arithmetic, set the time;
+// §2.5: reads that leave the cache are the cost.  Here the columns are cut into
+// phases of 2^pb columns (a B slice of 2^pb rows) and every wave sweeps the
+// phases in the same order, so that at any time the waves of an XCD read about
+// one slice, which its L2 holds.  A workgroup owns kSwRows consecutive rows of
+// C, kept in LDS, cut into one contiguous row range per wave with about equal
+// entry counts (so that the waves move through the phases at the same pace).
+// A wave's entries are stored contiguously, phase by phase, rows then columns
+// ascending inside a phase, as a word (row within the workgroup's rows) <<
+// kSwColBits | column, and the value, and are read in steps of EPS = 64 / NV
+// entries: NV lanes per entry, four columns each (N = 4 NV), U steps with their
+// loads and gathers in flight together.  The products of a step are summed per
+// (phase, row) by a segmented scan over the step (that key never decreases
+// along the stream), and the last entry of each run adds the run's sum to its
+// row in LDS, phase by phase.  Only one wave touches a row, in program order,
+// so every C element is a sum in a fixed order: results are reproducible bit
+// for bit, with no floating-point atomics and no partial sums in memory.
+constexpr uint32_t kSwColMask = (1u << kSwColBits) - 1u;
+
+template <int NV, int U>
+__global__ __launch_bounds__(kSwWaves * 64) void spmm_sweep_kernel(int P, int pb,
+                                                                   const int32_t* __restrict__ off,
+                                                                   const int32_t* __restrict__ wrow,
+                                                                   const uint32_t* __restrict__ pk,
+                                                                   const float* __restrict__ pv,
+                                                                   const float* __restrict__ B, int64_t ldb,
+                                                                   float alpha, float beta, float* __restrict__ C,
+                                                                   int64_t ldc) {
+    constexpr int N = 4 * NV;
+    constexpr int EPS = 64 / NV;
+    __shared__ __attribute__((aligned(16))) float csh[kSwRows * N];
+    const int g = blockIdx.x, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int j = lane / NV, h = lane - j * NV;
+    const int rb = g * kSwRows;                  // first row of the workgroup
+    const int row0 = wrow[g * kSwWaves + w];     // the wave's rows [row0, row1)
+    const int nrows = wrow[g * kSwWaves + w + 1] - row0;
+    float* cw = csh + (row0 - rb) * N;
+    for (int k = lane; k < nrows * NV; k += 64)
+        *reinterpret_cast<float4*>(cw + 4 * k) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    const int64_t cell = ((int64_t)g * kSwWaves + w) * P;
+    const int wb = off[cell], we = off[cell + P];  // the wave's entries, phase by phase
+    const float* __restrict__ bh = B + 4 * h;
+    for (int e = wb; e < we; e += U * EPS) {
+        uint32_t word[U];
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int q = e + u * EPS + j;
+            word[u] = 0u;
+            v[u] = 0.0f;
+            if (q < we) {
+                word[u] = __builtin_nontemporal_load(pk + q);
+                v[u] = __builtin_nontemporal_load(pv + q);
+            }
+        }
+        float4 b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            b[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (e + u * EPS + j < we)
+                b[u] = *reinterpret_cast<const float4*>(bh + (int64_t)(word[u] & kSwColMask) * ldb);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool valid = e + u * EPS + j < we;
+            const int row = (int)(word[u] >> kSwColBits);
+            // run key: (phase, row); entries past the end get keys of their own
+            const int key = valid ? (int)(((word[u] & kSwColMask) >> pb) << kSwRowBits) | row : -1 - j;
+            float4 a = make_float4(v[u] * b[u].x, v[u] * b[u].y, v[u] * b[u].z, v[u] * b[u].w);
+#pragma unroll
+            for (int d = 1; d < EPS; d <<= 1) {
+                const int ks = __shfl_up(key, d * NV, 64);
+                const float sx = __shfl_up(a.x, d * NV, 64), sy = __shfl_up(a.y, d * NV, 64);
+                const float sz = __shfl_up(a.z, d * NV, 64), sw = __shfl_up(a.w, d * NV, 64);
+                if (j >= d && ks == key) {
+                    a.x += sx;
+                    a.y += sy;
+                    a.z += sz;
+                    a.w += sw;
+                }
+            }
+            const int kn = __shfl_down(key, NV, 64);
+            const bool last = valid && (j == EPS - 1 || kn != key);
+            // A step can hold runs of one row from several phases: their adds
+            // go in rounds, one phase per round, lowest first (the stream is in
+            // phase order, so the lowest pending lane has the lowest phase);
+            // inside a phase every run has a row of its own.
+            const int ph = key >> kSwRowBits;
+            uint64_t pend = __ballot(last);
+            while (pend) {
+                const int p0 = __shfl(ph, __ffsll((unsigned long long)pend) - 1, 64);
+                const bool mine = last && ph == p0;
+                if (mine) {
+                    float4* c = reinterpret_cast<float4*>(csh + row * N + 4 * h);
+                    float4 o = *c;
+                    o.x += a.x;
+                    o.y += a.y;
+                    o.z += a.z;
+                    o.w += a.w;
+                    *c = o;
+                }
+                pend &= ~__ballot(mine);
+            }
+        }
+    }
+    // the wave's rows of C, with the axpby epilogue
+    for (int k = lane; k < nrows * NV; k += 64) {
+        const int rr = k / NV, hh = k - rr * NV;
+        const float4 acc = *reinterpret_cast<const float4*>(cw + rr * N + 4 * hh);
+        Acc<4> t;
+        t.v[0] = acc.x;
+        t.v[1] = acc.y;
+        t.v[2] = acc.z;
+        t.v[3] = acc.w;
+        store_tile<4>(C + (int64_t)(row0 + rr) * ldc + 4 * hh, t, alpha, beta);
+    }
+}
+
+// Turns the slot -> CSR entry map that the host uploaded into d.sw_pk into the
+// packed words (row within its workgroup's rows, column) and the values.  Slot
+// s is read and written by one thread only.
+__global__ __launch_bounds__(kBlock) void sweep_build_kernel(int rows, int64_t nnz, const int32_t* __restrict__ ptr,
+                                                             const int32_t* __restrict__ idx,
+                                                             const float* __restrict__ val, uint32_t* pk, float* pv) {
+    for (int64_t s = (int64_t)blockIdx.x * kBlock + threadIdx.x; s < nnz; s += (int64_t)gridDim.x * kBlock) {
+        const int q = (int)pk[s];
+        int lo = 0, hi = rows;  // ptr[lo] <= q < ptr[hi]: the row of entry q is the last such lo
+        while (hi - lo > 1) {
+            const int mid = lo + ((hi - lo) >> 1);
+            if (ptr[mid] <= q)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        pk[s] = ((uint32_t)(lo % kSwRows) << kSwColBits) | ((uint32_t)idx[q] & kSwColMask);
+        pv[s] = val[q];
+    }
+}
+
 }  // namespace
+
+bool spmm_sweep_ok(const DirDevice& d, int32_t N, const float* B, int64_t ldb, const float* C, int64_t ldc) {
+    return d.sw_pb > 0 && (N == 4 || N == 8 || N == 16) && ldb % 4 == 0 && ldc % 4 == 0 &&
+           (reinterpret_cast<uintptr_t>(B) & 15) == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0;
+}
+
+hipError_t launch_spmm_sweep(const DirDevice& d, int32_t N, float alpha, const float* B, int64_t ldb, float beta,
+                             float* C, int64_t ldc, hipStream_t s) {
+    const dim3 grid((unsigned)d.sw_nblk), block(kSwWaves * 64);
+    if (N == 4)
+        hipLaunchKernelGGL((spmm_sweep_kernel<1, 4>), grid, block, 0, s, d.sw_P, d.sw_pb, d.sw_off, d.sw_wrow,
+                           d.sw_pk, d.sw_pv, B, ldb, alpha, beta, C, ldc);
+    else if (N == 8)
+        hipLaunchKernelGGL((spmm_sweep_kernel<2, 4>), grid, block, 0, s, d.sw_P, d.sw_pb, d.sw_off, d.sw_wrow,
+                           d.sw_pk, d.sw_pv, B, ldb, alpha, beta, C, ldc);
+    else
+        hipLaunchKernelGGL((spmm_sweep_kernel<4, 4>), grid, block, 0, s, d.sw_P, d.sw_pb, d.sw_off, d.sw_wrow,
+                           d.sw_pk, d.sw_pv, B, ldb, alpha, beta, C, ldc);
+    return hipGetLastError();
+}
+
+hipError_t launch_sweep_build(const DirDevice& d, int64_t nnz, hipStream_t s) {
+    if (nnz == 0) return hipSuccess;
+    const int64_t grid = std::min<int64_t>((nnz + kBlock - 1) / kBlock, 8192);
+    hipLaunchKernelGGL(sweep_build_kernel, dim3((unsigned)grid), dim3(kBlock), 0, s, d.rows, nnz, d.ptr, d.idx,
+                       d.val, d.sw_pk, d.sw_pv);
+    return hipGetLastError();
+}
 
 hipError_t launch_spmm(const DirDevice& d, int32_t N, float alpha, const float* B, int64_t ldb, float beta,
                        float* C, int64_t ldc, hipStream_t s) {

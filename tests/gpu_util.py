@@ -31,6 +31,8 @@ BINS = {
     # x-window stream (products with x windows in LDS, then row sums in CSR order)
     "xw8": dict(use_sell=0, x_window_bits=8),
     "xw15": dict(use_sell=0, x_window_bits=15),
+    # phase-swept SpMM copy (SpMM with N in {4, 8, 16}; SpMV is unaffected)
+    "sweep8": dict(spmm_phase_bits=8),
 }
 
 

@@ -44,6 +44,7 @@ def test_option_defaults():
     o = sp.plan_options()
     assert (o.group_nnz, o.wave_min, o.block_min, o.split_min, o.split_seg) == (2048, 256, 4096, 32768, 8192)
     assert (o.use_sell, o.sell_sigma, o.xcd_remap, o.col_panels, o.x_window_bits) == (-1, 1024, 1, -1, -1)
+    assert o.spmm_phase_bits == -1
 
 
 SZ = ctypes.c_size_t

@@ -127,6 +127,8 @@ def test_spmm_lognormal_all_rows(lognormal, N):
         np.testing.assert_array_equal(host(g_rp), rp)
         np.testing.assert_array_equal(host(g_c), c)
     plan = sp.Plan(coo.m, coo.n, g_rp, g_c, g_v, max_N=N)
+    # N = 8 takes the phase-swept copy (B of 32 MiB in 512 KiB slices), wider N the row bins
+    assert plan.profile()["spmm_phase_bits"] == (14 if N == 8 else 0)
     B = gen.dense_matrix(coo.n, N, 0)
     dB = dev(B)
     C = torch.full((coo.m, N), float("nan"), device="cuda")

@@ -89,8 +89,8 @@ def test_spmv_nonfinite_x(path):
     assert 0 < hit_t < coo.n
 
 
-@pytest.mark.parametrize("N", [3, 8, 32])
-@pytest.mark.parametrize("bins", ["default", "all_wave", "all_split", "mixed_small"])
+@pytest.mark.parametrize("N", [3, 8, 16, 32])
+@pytest.mark.parametrize("bins", ["default", "all_wave", "all_split", "mixed_small", "sweep8"])
 def test_spmm_nonfinite_b(bins, N):
     say("nonfinite spmm", bins, N)
     coo, (rp, c, v), _ = matrix()

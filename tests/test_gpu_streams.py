@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 # paths whose products use per-call scratch: split partials + counters, the
 # panel sums, the x-window products and long-row partials
-VIEW_BINS = ["all_split", "mixed_small", "ps8_split", "xw8", "xw15", "default"]
+VIEW_BINS = ["all_split", "mixed_small", "ps8_split", "xw8", "xw15", "default", "sweep8"]
 
 
 def _matrix(seed=1):
