@@ -335,7 +335,6 @@ def prepare(name, args, opts):
         brp, bcol, bval, fill = sp.csr_to_bsr(m, n, rp, ci, vv, bs, min_fill=0.5)
         torch.cuda.synchronize()
         w.setup["csr_to_bsr_ms"] = (time.time() - t1) * 1e3
-        del rp, ci, vv
         nnzb = bcol.numel()
         x = _to_dev(torch, gen.dense_vector(n, 0, 1))
         y = torch.zeros(m, device="cuda")
@@ -346,9 +345,31 @@ def prepare(name, args, opts):
         w.step, w.out_tensor, w.graph = step, y, 20
         w.flops = 2 * nnzb * bs * bs
         w.nbytes = bsr_spmv_bytes(m, n, bs, nnzb)
+        # the BCSR page's two thread mappings (section 2.1 whole blocks, 2.2
+        # whole columns), at 64 x 64 and at 4 x 4 blocks of the same matrix
+        # (section 3 compares them): mean kernel time of 20 graph-free launches
+        cmp = {}
+        b4 = sp.csr_to_bsr(m, n, rp, ci, vv, 4)
+        for name_b, (bsx, arr) in (("64x64", (64, (brp, bcol, bval))), ("4x4", (4, b4[:3]))):
+            for strat, rw in (("whole_blocks", False), ("rows", True)):
+                for _ in range(3):
+                    sp.bsr_spmv(m, n, bsx, *arr, 1.0, x, 0.0, y, rowwise=rw)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(20):
+                    sp.bsr_spmv(m, n, bsx, *arr, 1.0, x, 0.0, y, rowwise=rw)
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / 20
+                nb = arr[1].numel()
+                cmp["%s_%s" % (name_b, strat)] = dict(
+                    ms=round(ms, 5), gflops=round(2 * nb * bsx * bsx / (ms * 1e-3) / 1e9, 1),
+                    gbs=round(bsr_spmv_bytes(m, n, bsx, nb) / (ms * 1e-3) / 1e9, 1))
+        del b4
         w.launches = 1
         w.dtype = "f32"
-        w.config = dict(workload=name, M=m, K=n, block=bs, nnz=coo.nnz, nnz_blocks=nnzb, fill_ratio=fill)
+        w.config = dict(workload=name, M=m, K=n, block=bs, nnz=coo.nnz, nnz_blocks=nnzb, fill_ratio=fill,
+                        strategies=cmp)
         w.bound, w.peak, w.unit = "hbm", PEAK_HBM_GBS, "GB/s"
         if not args.no_cpu_baseline:
             import oracle
@@ -357,6 +378,7 @@ def prepare(name, args, opts):
                              lambda lo, h: oracle.bsr_spmv(m, n, bs, h_brp, h_bcol, h_bval, h_x))],
                            w.flops, w.nbytes, "full passes of y = A x over the 64 x 64-block BSR (fp64 accumulation, "
                                               "one call per pass)", max_threads=1)
+        del rp, ci, vv
         return w
     if base == "spmm_clustered":
         coo = gen.clustered_coo(seed=0)

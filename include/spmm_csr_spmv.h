@@ -408,6 +408,16 @@ int csr_to_bsr_fill(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, c
 int bsr_spmv(int64_t m, int64_t n, int32_t bs, int64_t nnzb, const int32_t* brow_ptr, const int32_t* bcol,
              const float* bval, float alpha, const float* x, float beta, float* y, void* stream);
 
+/* The same product by the other thread mapping of [BCSR] §2 (§2.2, a warp
+ * covers whole columns, where bsr_spmv follows §2.1, a warp covers whole
+ * blocks): each block row is served by bs lanes, lane r owning element row r,
+ * which walks the row's blocks reading its own row of each block and ends
+ * with the row's whole sum (no reduction across lanes).  [BCSR] §3 compares
+ * the two; bench.py reports both on the 64 x 64-block workload.  Arguments,
+ * layout, alignment and errors as bsr_spmv; deterministic. */
+int bsr_spmv_rowwise(int64_t m, int64_t n, int32_t bs, int64_t nnzb, const int32_t* brow_ptr, const int32_t* bcol,
+                     const float* bval, float alpha, const float* x, float beta, float* y, void* stream);
+
 /* --------------------------------------------------------- windowed rows (WCSR), windowed SpMM
  * [ASYNC] §2.2.2: rows are grouped into windows of a fixed height; per window
  * the union of its rows' column indices is kept (padding columns carry -1)

@@ -32,7 +32,7 @@ EXPORTS = ("sp_status_string", "sp_version", "csr_build_from_coo_bufsize", "csr_
            "sp_plan_dispatch_key", "sp_tune_cache_store", "sp_tune_cache_lookup", "sp_tune_cache_clear",
            "sp_tune_cache_size", "sp_autotune_workspace_size", "sp_autotune_spmv", "csr_to_wcsr_bufsize",
            "csr_to_wcsr_analyze", "csr_to_wcsr_fill", "wcsr_spmm", "sp_plan_view_create",
-           "csr_build_from_coo_noalloc")
+           "csr_build_from_coo_noalloc", "bsr_spmv_rowwise")
 
 
 class SparseError(RuntimeError):
@@ -111,6 +111,7 @@ def lib():
                                          ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double), _p, _sz, _p]
         L.csr_to_bsr_fill.argtypes = [_i64, _i64, _i64, _p, _p, _p, _i32, _p, _i64, _p, _p, _i32, _p]
         L.bsr_spmv.argtypes = [_i64, _i64, _i32, _i64, _p, _p, _p, _f, _p, _f, _p, _p]
+        L.bsr_spmv_rowwise.argtypes = [_i64, _i64, _i32, _i64, _p, _p, _p, _f, _p, _f, _p, _p]
         L.bsr_spmm_bufsize.argtypes = [_i64, _i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
         L.csr_to_wcsr_bufsize.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
         L.csr_to_wcsr_analyze.argtypes = [_i64, _i64, _i64, _p, _p, _i32, _p, ctypes.POINTER(_i64),
@@ -512,14 +513,16 @@ def spmm(plan, alpha, B, beta, C, stream=None):
     return C
 
 
-def bsr_spmv(m, n, bs, brow_ptr, bcol, bval, alpha, x, beta, y, stream=None):
-    """y = alpha * A x + beta * y (in place on y) with A in BSR, fp32 bs x bs blocks."""
+def bsr_spmv(m, n, bs, brow_ptr, bcol, bval, alpha, x, beta, y, stream=None, rowwise=False):
+    """y = alpha * A x + beta * y (in place on y) with A in BSR, fp32 bs x bs blocks.
+    rowwise=True calls bsr_spmv_rowwise (one lane per element row) instead."""
     _dev(brow_ptr, torch.int32, "brow_ptr"), _dev(bcol, torch.int32, "bcol"), _dev(bval, torch.float32, "bval")
     _dev(x, torch.float32, "x"), _dev(y, torch.float32, "y")
     if x.numel() != n or y.numel() != m:
         raise ValueError("x must have n entries and y m entries")
-    _check("bsr_spmv", lib().bsr_spmv(m, n, bs, bcol.numel(), _ptr(brow_ptr), _ptr(bcol), _ptr(bval), float(alpha),
-                                      _ptr(x), float(beta), _ptr(y), _stream(stream)))
+    fn = "bsr_spmv_rowwise" if rowwise else "bsr_spmv"
+    _check(fn, getattr(lib(), fn)(m, n, bs, bcol.numel(), _ptr(brow_ptr), _ptr(bcol), _ptr(bval), float(alpha),
+                                  _ptr(x), float(beta), _ptr(y), _stream(stream)))
     return y
 
 

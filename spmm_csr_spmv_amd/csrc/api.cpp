@@ -1481,6 +1481,19 @@ int bsr_spmv(int64_t m, int64_t n, int32_t bs, int64_t nnzb, const int32_t* brow
     return spx::bsr_spmv_device(m, n, bs, nnzb, brow_ptr, bcol, bval, alpha, x, beta, y, (hipStream_t)stream);
 }
 
+int bsr_spmv_rowwise(int64_t m, int64_t n, int32_t bs, int64_t nnzb, const int32_t* brow_ptr, const int32_t* bcol,
+                     const float* bval, float alpha, const float* x, float beta, float* y, void* stream) {
+    int rc = check_dims(m, n, 0);
+    if (rc) return rc;
+    if (!bsr_block_ok(bs)) return SP_ERR_UNSUPPORTED;
+    if (nnzb < 0 || nnzb > kI32Max) return SP_ERR_SIZE;
+    if (m == 0) return SP_OK;
+    if (!brow_ptr || !y || (nnzb > 0 && (!bcol || !bval || (n > 0 && !x)))) return SP_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(bval) & 15) return SP_ERR_UNSUPPORTED;
+    if (bs >= 4 && (reinterpret_cast<uintptr_t>(x) & 15)) return SP_ERR_UNSUPPORTED;
+    return spx::bsr_spmv_rows_device(m, n, bs, nnzb, brow_ptr, bcol, bval, alpha, x, beta, y, (hipStream_t)stream);
+}
+
 // ------------------------------------------------------------------ CSR -> WCSR, windowed SpMM
 static bool wcsr_pad_ok(int32_t pad) { return pad == 1 || pad == 2 || pad == 4 || pad == 8 || pad == 16 || pad == 32; }
 

@@ -22,7 +22,8 @@
 // element step).  For bs >= 16 a lane's column slice is the same in every
 // step of a block, so the 4 x values it needs are loaded once per block; the
 // per-row partial sums are reduced across the lanes of a row at the end (the
-// reading of the page's "warp covers whole blocks" strategy on wave64).  For
+// reading of the page's "warp covers whole blocks" strategy on wave64; its
+// "warp covers whole columns" strategy is bsr_spmv_rows_kernel below).  For
 // bs >= 16 the sixteen waves of a workgroup take the blocks of one block row
 // in turn and their row sums are added in wave order; for bs <= 8 each wave
 // serves one block row.
@@ -295,6 +296,73 @@ __global__ __launch_bounds__(kBlock) void bsr_spmv_small(int64_t m, int64_t n, i
     }
 }
 
+// The page's second strategy (§2.2, a warp covers whole columns), on wave64:
+// each block row is served by a group of BS lanes (64 / BS block rows per
+// wave), lane r of the group owns element row r of its block row and walks
+// the row's blocks, reading only its own row of each block (BS contiguous
+// values, 16-byte loads) and the block column's x segment, so every lane holds
+// sums of its own row only and no lanes are reduced together.  As in the
+// whole-block kernel, the W waves of a workgroup share the blocks of the same
+// block rows (wave w takes every W-th block) and their row sums are added in
+// wave order at the end, so that both mappings run with the same parallelism
+// and differ only in how a wave reads the blocks.  With 64 x 64 blocks the
+// block column is the same for the whole wave, so the x segment is one
+// broadcast per block.  The page's trade-off holds: no reduction inside a
+// wave, but a lane's block reads are strided by a block row's length.
+template <int BS, int W>
+__global__ __launch_bounds__(64 * W) void bsr_spmv_rows_kernel(int64_t m, int64_t n, int32_t mb, int32_t kb,
+                                                               int64_t nnzb, const int32_t* __restrict__ brow_ptr,
+                                                               const int32_t* __restrict__ bcol,
+                                                               const float* __restrict__ bval, float alpha,
+                                                               const float* __restrict__ x, float beta,
+                                                               float* __restrict__ y) {
+    constexpr int G = 64 / BS;  // block rows per workgroup (one per lane group)
+    __shared__ float red[W][64];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, k = lane / BS, r = lane % BS;
+    const int64_t I = (int64_t)blockIdx.x * G + k;
+    float acc = 0.0f;
+    if (I < mb) {
+        const int kb0 = (int)min<int64_t>(max(brow_ptr[I], 0), nnzb);
+        const int kb1 = (int)min<int64_t>(max(brow_ptr[I + 1], 0), nnzb);
+        for (int b = kb0 + w; b < kb1; b += W) {
+            int J = bcol[b];
+            if constexpr (BS == 64) J = __builtin_amdgcn_readfirstlane(J);  // one block row per wave
+            if (J < 0 || J >= kb) continue;
+            const float* __restrict__ arow = bval + (int64_t)b * BS * BS + (int64_t)r * BS;
+            const int64_t j0 = (int64_t)J * BS;
+            if constexpr (BS >= 4) {
+#pragma unroll
+                for (int c = 0; c < BS; c += 4)
+                    acc = dot4(acc, ldg4_nt(arow + c), load_x4(x, j0 + c, n), j0 + c, n);
+            } else {
+#pragma unroll
+                for (int c = 0; c < BS; ++c)
+                    if (j0 + c < n) acc += arow[c] * x[j0 + c];
+            }
+        }
+    }
+    red[w][lane] = acc;
+    __syncthreads();
+    if (w == 0) {
+        float t = red[0][lane];
+#pragma unroll
+        for (int q = 1; q < W; ++q) t += red[q][lane];
+        const int64_t row = I * BS + r;
+        if (I < mb && row < m) store_axpby(y, (int)row, t, alpha, beta);
+    }
+}
+
+template <int BS>
+int spmv_rows_bs(int64_t m, int64_t n, int64_t nnzb, const int32_t* brow_ptr, const int32_t* bcol, const float* bval,
+                 float alpha, const float* x, float beta, float* y, hipStream_t s) {
+    const int64_t mb = (m + BS - 1) / BS, kb = (n + BS - 1) / BS;
+    if (mb == 0) return SP_OK;
+    constexpr int W = 16, G = 64 / BS;
+    hipLaunchKernelGGL((bsr_spmv_rows_kernel<BS, W>), dim3((unsigned)((mb + G - 1) / G)), dim3(64 * W), 0, s, m, n,
+                       (int32_t)mb, (int32_t)kb, nnzb, brow_ptr, bcol, bval, alpha, x, beta, y);
+    return hipGetLastError() == hipSuccess ? SP_OK : SP_ERR_HIP;
+}
+
 template <int BS>
 int analyze_bs(int64_t m, int64_t n, const int32_t* ptr, const int32_t* idx, int32_t* brow_ptr, int32_t* flags,
                int32_t* sums, hipStream_t s) {
@@ -396,6 +464,20 @@ int bsr_spmv_device(int64_t m, int64_t n, int32_t bs, int64_t nnzb, const int32_
         case 16: return spmv_bs<16>(m, n, nnzb, brow_ptr, bcol, bval, alpha, x, beta, y, s);
         case 32: return spmv_bs<32>(m, n, nnzb, brow_ptr, bcol, bval, alpha, x, beta, y, s);
         case 64: return spmv_bs<64>(m, n, nnzb, brow_ptr, bcol, bval, alpha, x, beta, y, s);
+        default: return SP_ERR_UNSUPPORTED;
+    }
+}
+
+int bsr_spmv_rows_device(int64_t m, int64_t n, int32_t bs, int64_t nnzb, const int32_t* brow_ptr, const int32_t* bcol,
+                         const float* bval, float alpha, const float* x, float beta, float* y, hipStream_t s) {
+    switch (bs) {
+        case 1: return spmv_rows_bs<1>(m, n, nnzb, brow_ptr, bcol, bval, alpha, x, beta, y, s);
+        case 2: return spmv_rows_bs<2>(m, n, nnzb, brow_ptr, bcol, bval, alpha, x, beta, y, s);
+        case 4: return spmv_rows_bs<4>(m, n, nnzb, brow_ptr, bcol, bval, alpha, x, beta, y, s);
+        case 8: return spmv_rows_bs<8>(m, n, nnzb, brow_ptr, bcol, bval, alpha, x, beta, y, s);
+        case 16: return spmv_rows_bs<16>(m, n, nnzb, brow_ptr, bcol, bval, alpha, x, beta, y, s);
+        case 32: return spmv_rows_bs<32>(m, n, nnzb, brow_ptr, bcol, bval, alpha, x, beta, y, s);
+        case 64: return spmv_rows_bs<64>(m, n, nnzb, brow_ptr, bcol, bval, alpha, x, beta, y, s);
         default: return SP_ERR_UNSUPPORTED;
     }
 }

@@ -168,6 +168,8 @@ int csr_to_bsr_fill_device(int64_t m, int64_t n, const int32_t* row_ptr, const i
                            hipStream_t s);
 int bsr_spmv_device(int64_t m, int64_t n, int32_t bs, int64_t nnzb, const int32_t* brow_ptr, const int32_t* bcol,
                     const float* bval, float alpha, const float* x, float beta, float* y, hipStream_t s);
+int bsr_spmv_rows_device(int64_t m, int64_t n, int32_t bs, int64_t nnzb, const int32_t* brow_ptr, const int32_t* bcol,
+                         const float* bval, float alpha, const float* x, float beta, float* y, hipStream_t s);
 
 // CSR -> WCSR and the windowed SpMM (wcsr.hip); windows of 64 rows.
 size_t wcsr_convert_work_bytes(int64_t m);

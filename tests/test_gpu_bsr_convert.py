@@ -56,9 +56,10 @@ def test_five_by_five_bsr2_exact(golden_dir):
                       np.float32)
     np.testing.assert_array_equal(host(bval), blocks)
     assert fill == pytest.approx(1.0 / 3.0)
-    y = torch.full((5,), float("nan"), device="cuda")
-    sp.bsr_spmv(5, 5, 2, brp, bcol, bval, 1.0, dev(np.arange(1, 6, dtype=np.float32)), 0.0, y)
-    assert host(y).tolist() == [7, 6, 54, 21, 40]
+    for rowwise in (False, True):
+        y = torch.full((5,), float("nan"), device="cuda")
+        sp.bsr_spmv(5, 5, 2, brp, bcol, bval, 1.0, dev(np.arange(1, 6, dtype=np.float32)), 0.0, y, rowwise=rowwise)
+        assert host(y).tolist() == [7, 6, 54, 21, 40]
 
 
 @pytest.mark.parametrize("bs", BLOCKS)
@@ -80,10 +81,11 @@ def test_conversion_bit_exact(name, bs):
         assert fill == pytest.approx(c.size / (nnzb * bs * bs) if nnzb else 1.0, rel=1e-12)
 
 
+@pytest.mark.parametrize("rowwise", [False, True], ids=["whole_blocks", "rows"])
 @pytest.mark.parametrize("bs", BLOCKS)
 @pytest.mark.parametrize("name", list(cases()))
-def test_bsr_spmv(name, bs):
-    say("bsr_spmv", name, bs)
+def test_bsr_spmv(name, bs, rowwise):
+    say("bsr_spmv", name, bs, rowwise)
     coo, (rp, c, v) = case(name)
     erp, ecol, eval32 = oracle.csr_to_bsr(coo.m, coo.n, rp, c, v, bs)
     brp, bcol, bval = dev(erp), dev(ecol), dev(eval32)
@@ -91,7 +93,7 @@ def test_bsr_spmv(name, bs):
     for alpha, beta in AB:
         y0 = gen.dense_vector(coo.m, 13)
         y = dev(y0) if beta != 0.0 else torch.full((coo.m,), float("nan"), device="cuda")
-        sp.bsr_spmv(coo.m, coo.n, bs, brp, bcol, bval, alpha, dev(x), beta, y)
+        sp.bsr_spmv(coo.m, coo.n, bs, brp, bcol, bval, alpha, dev(x), beta, y, rowwise=rowwise)
         ref, scale = oracle.bsr_spmv(coo.m, coo.n, bs, erp, ecol, eval32, x, alpha, beta, y0)
         assert_close(host(y), ref, scale, what="bsr_spmv %s bs=%d a=%g b=%g" % (name, bs, alpha, beta))
         # the CSR route computes the same product up to the fp32 sums of
@@ -100,16 +102,17 @@ def test_bsr_spmv(name, bs):
         assert_close(ref, ref_csr, scale, what="BSR and CSR routes of the oracle")
 
 
+@pytest.mark.parametrize("rowwise", [False, True], ids=["whole_blocks", "rows"])
 @pytest.mark.parametrize("bs", [4, 64])
-def test_bsr_spmv_bitwise_deterministic(bs):
-    say("bsr_spmv determinism", bs)
+def test_bsr_spmv_bitwise_deterministic(bs, rowwise):
+    say("bsr_spmv determinism", bs, rowwise)
     coo, (rp, c, v) = case("ragged_long")
     brp, bcol, bval, _ = sp.csr_to_bsr(coo.m, coo.n, dev(rp), dev(c), dev(v), bs)
     x = dev(gen.dense_vector(coo.n, 21))
     outs = []
     for _ in range(3):
         y = torch.zeros(coo.m, device="cuda")
-        sp.bsr_spmv(coo.m, coo.n, bs, brp, bcol, bval, 1.0, x, 0.0, y)
+        sp.bsr_spmv(coo.m, coo.n, bs, brp, bcol, bval, 1.0, x, 0.0, y, rowwise=rowwise)
         outs.append(host(y).view(np.uint32).copy())
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
@@ -159,7 +162,8 @@ def test_block_sparse_workload_full():
     np.testing.assert_array_equal(host(bcol), ecol)
     np.testing.assert_array_equal(host(bval).view(np.uint32), eval32.view(np.uint32))
     x = gen.dense_vector(coo.n, 0, 1)
-    y = torch.full((coo.m,), float("nan"), device="cuda")
-    sp.bsr_spmv(coo.m, coo.n, 64, brp, bcol, bval, 1.0, dev(x), 0.0, y)
     ref, scale = oracle.bsr_spmv(coo.m, coo.n, 64, erp, ecol, eval32, x)
-    assert_close(host(y), ref, scale, what="bsr_spmv full")
+    for rowwise in (False, True):
+        y = torch.full((coo.m,), float("nan"), device="cuda")
+        sp.bsr_spmv(coo.m, coo.n, 64, brp, bcol, bval, 1.0, dev(x), 0.0, y, rowwise=rowwise)
+        assert_close(host(y), ref, scale, what="bsr_spmv full, rowwise=%s" % rowwise)

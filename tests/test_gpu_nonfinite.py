@@ -105,8 +105,9 @@ def test_spmm_nonfinite_b(bins, N):
     assert check_class(host(C), ref, scale, "spmm %s N=%d" % (bins, N)) > 0
 
 
+@pytest.mark.parametrize("rowwise", [False, True], ids=["whole_blocks", "rows"])
 @pytest.mark.parametrize("bs", [4, 64])
-def test_bsr_spmv_nonfinite_x(bs):
+def test_bsr_spmv_nonfinite_x(bs, rowwise):
     """Blocks keep their explicit zeros, so 0 * Inf = NaN inside a stored block
     on both sides; columns past n of the padded last block column are never read."""
     say("nonfinite bsr spmv", bs)
@@ -119,7 +120,7 @@ def test_bsr_spmv_nonfinite_x(bs):
     xpad[:coo.n] = x
     dx = dev(xpad)
     y = torch.full((coo.m,), float("nan"), device="cuda")
-    sp.bsr_spmv(coo.m, coo.n, bs, dev(brp), dev(bcol), dev(bval), 1.0, dx[:coo.n], 0.0, y)
+    sp.bsr_spmv(coo.m, coo.n, bs, dev(brp), dev(bcol), dev(bval), 1.0, dx[:coo.n], 0.0, y, rowwise=rowwise)
     ref, scale = oracle.bsr_spmv(coo.m, coo.n, bs, brp, bcol, bval, x)
     assert check_class(host(y), ref, scale, "bsr_spmv bs=%d" % bs) > 0
 
