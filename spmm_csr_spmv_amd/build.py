@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libspmm_csr_spmv.so")
 PROBE_LIB = os.path.join(HERE, "libspx_probe.so")
 PROBE_SOURCES = ["probe.hip"]
 
-SOURCES = ["api.cpp", "tune.cpp", "convert.hip", "spmv.hip", "pstream.hip", "spmm.hip", "bsr.hip", "bsr_convert.hip", "wcsr.hip", "xwin.hip"]
+SOURCES = ["api.cpp", "plan_host.cpp", "tune.cpp", "convert.hip", "spmv.hip", "pstream.hip", "spmm.hip", "bsr.hip", "bsr_convert.hip", "wcsr.hip", "xwin.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -7,29 +7,9 @@
 #include <stddef.h>
 
 #include "spmm_csr_spmv.h"
+#include "layout.h"
 
 namespace spx {
-
-constexpr int kBlock = 256;          // threads per workgroup for every kernel
-constexpr int kGroupMaxNnz = 4096;   // LDS capacity of a group task (entries)
-constexpr int kGroupMaxRows = 1024;  // rows per group task
-constexpr int kXcds = 8;             // MI355X: workgroups go round-robin to 8 XCDs
-constexpr int kPsEntries = 4096;     // column-panel stream: entries per chunk (16 per thread)
-constexpr int kPsMaxRows = 2048;     // column-panel stream: rows per chunk (LDS row sums)
-constexpr int kXwChunk = 15360;      // x-window stream: entries per row chunk (LDS products)
-constexpr int kXwMaxRows = 1536;     // x-window stream: rows per row chunk
-constexpr int kXwMaxWindows = 256;   // x-window stream: windows of x
-constexpr int kXwMinBits = 5;        // x-window stream: narrowest window, 2^5 columns
-constexpr int kXwMaxBits = 15;       // x-window stream: widest window, 2^15 columns = 128 KB of LDS
-constexpr int kXwPiece = 32768;      // x-window stream: window entries per product workgroup
-constexpr int kXwPieceRuns = 1024;   // x-window stream: chunks per product workgroup
-constexpr int kXwProdGrid = 256;     // x-window stream: product workgroups (one per CU, 32 per XCD)
-constexpr int kSwWaves = 8;          // phase-swept SpMM: waves per workgroup
-constexpr int kSwRows = 2048;        // phase-swept SpMM: rows per workgroup (C rows in LDS)
-constexpr int kSwRowBits = 11;       // phase-swept SpMM: row within the workgroup's rows
-constexpr int kSwColBits = 21;       // phase-swept SpMM: column bits (at most 2^21 columns)
-constexpr int kSwMaxRowLen = 8192;   // phase-swept SpMM: longest row the automatic rule accepts
-constexpr int kSwSliceBytes = 512 << 10;  // phase-swept SpMM: B slice of one phase (automatic rule)
 
 // Task tables of one direction (A or A^T), laid out in device memory as one
 // int4 array: [split tasks | block tasks | wave tasks | group tasks].
