@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 from concurrent.futures import ThreadPoolExecutor
@@ -350,7 +351,7 @@ def prepare(name, args, opts):
         # (section 3 compares them): mean kernel time of 20 graph-free launches
         cmp = {}
         b4 = sp.csr_to_bsr(m, n, rp, ci, vv, 4)
-        for name_b, (bsx, arr) in (("64x64", (64, (brp, bcol, bval))), ("4x4", (4, b4[:3]))):
+        for name_b, (bsx, arr) in () if args.counter_run else (("64x64", (64, (brp, bcol, bval))), ("4x4", (4, b4[:3]))):
             for strat, rw in (("whole_blocks", False), ("rows", True)):
                 for _ in range(3):
                     sp.bsr_spmv(m, n, bsx, *arr, 1.0, x, 0.0, y, rowwise=rw)
@@ -406,17 +407,18 @@ def prepare(name, args, opts):
                         wcsr_bytes=4 * total_cols * 64 + 4 * total_cols + 4 * total_cols * N + 4 * m * N)
         w.bound, w.peak, w.unit = "hbm", PEAK_HBM_GBS, "GB/s"
         # the CSR SpMM on the same matrix, for comparison
-        plan_c = sp.Plan(m, n, rp, ci, vv, max_N=N)
-        for _ in range(3):
-            sp.spmm(plan_c, 1.0, B, 0.0, C)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(10):
-            sp.spmm(plan_c, 1.0, B, 0.0, C)
-        e1.record()
-        torch.cuda.synchronize()
-        w.config["csr_spmm_ms_same_matrix"] = round(e0.elapsed_time(e1) / 10, 5)
-        del plan_c
+        if not args.counter_run:
+            plan_c = sp.Plan(m, n, rp, ci, vv, max_N=N)
+            for _ in range(3):
+                sp.spmm(plan_c, 1.0, B, 0.0, C)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                sp.spmm(plan_c, 1.0, B, 0.0, C)
+            e1.record()
+            torch.cuda.synchronize()
+            w.config["csr_spmm_ms_same_matrix"] = round(e0.elapsed_time(e1) / 10, 5)
+            del plan_c
         if not args.no_cpu_baseline:
             import oracle
             h_rp, h_ci, h_vv = (t.cpu().numpy() for t in (rp, ci, vv))
@@ -564,6 +566,250 @@ def prepare(name, args, opts):
 
 
 # --------------------------------------------------------------------------
+# Traffic between the L2s and memory, from rocprofv3 counters
+# --------------------------------------------------------------------------
+# Every read that misses an XCD's L2 goes to the memory side (the MALL, then
+# HBM) as one request of 32, 64 or 128 bytes, counted by size; writes leave as
+# 32- or 64-byte requests.  So the bytes are the request counts times their
+# sizes, with no scale factor.  (FETCH_SIZE is not used: its expression takes
+# every request that is neither a 32-byte one nor a TCC_BUBBLE as 64 bytes,
+# and on this chip the 128-byte requests are counted apart, so it reads half
+# of a streaming kernel's bytes.)  A 256 MiB device copy is profiled the same
+# way as a check of the method.  The MALL sits on the memory side of these
+# counters, so the bytes are what the XCDs move, wherever in memory it is
+# served from.
+COUNTER_PASSES = (
+    ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum"),
+    ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_RDREQ_DRAM_sum", "TCC_EA0_WRREQ_DRAM_sum"),
+    ("TCC_HIT_sum", "TCC_MISS_sum", "TCC_BUBBLE_sum"),
+)
+COUNTER_STEPS, COUNTER_WARMUP = 5, 1
+
+
+def _child_args(name):
+    if name == "copy":
+        return ["--copy-calibration"]
+    base, N = parse_workload(name)
+    a = ["--config", base] + (["--N", str(N)] if N is not None else [])
+    return a + ["--counter-run", "--steps", str(COUNTER_STEPS), "--warmup", str(COUNTER_WARMUP)]
+
+
+def _rocprof(prof_args, name, outdir):
+    """One rocprofv3 run over a child bench.py (started from /tmp, the program
+    itself right after '--'); returns the child's last stdout line."""
+    import subprocess
+    cmd = ["timeout", "-s", "KILL", "240", "rocprofv3"] + prof_args + [
+        "--output-format", "csv", "-d", outdir, "-o", "run", "--", sys.executable, os.path.join(HERE, "bench.py")
+    ] + _child_args(name)
+    env = dict(os.environ, TMPDIR="/tmp")
+    r = subprocess.run(cmd, cwd="/tmp", env=env, capture_output=True, text=True)
+    # rocprofv3 may end with SIGSEGV after the program finished and wrote its results
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    if r.returncode not in (0, 139, -11) or not lines:
+        raise RuntimeError("%s failed (%d): %s" % (" ".join(cmd), r.returncode, (r.stderr or "")[-2000:]))
+    shown = ["rocprofv3"] + prof_args + ["--output-format", "csv", "-d", "<out>", "-o", "run", "--", "python3",
+                                          "<repo>/bench.py"] + _child_args(name)
+    return json.loads(lines[-1]), " ".join(shown)
+
+
+def _csv_rows(outdir, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(outdir, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise RuntimeError("no %s under %s" % (suffix, outdir))
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _short_kernel(name):
+    """'void spx::(anonymous namespace)::bsr_spmm_dma<256>(int const*, ...)' -> 'bsr_spmm_dma<256>'"""
+    head = name.replace("(anonymous namespace)::", "").split("(")[0].strip()
+    if head.startswith("void "):
+        head = head[5:]
+    lt = head.find("<")
+    base, targs = (head, "") if lt < 0 else (head[:lt], head[lt:])
+    return base.split("::")[-1] + targs
+
+
+def _dispatches(rows):
+    """[(dispatch id, kernel name, {counter: value})] of one counter pass, in
+    dispatch order."""
+    out = {}
+    for r in rows:
+        d = int(r["Dispatch_Id"])
+        out.setdefault(d, (r["Kernel_Name"], {}))[1][r["Counter_Name"]] = float(r["Counter_Value"])
+    return [(d, k, v) for d, (k, v) in sorted(out.items())]
+
+
+def _call_dispatches(disp, calls):
+    """The dispatches of the last `calls` library calls of a counter run: the
+    timed steps come last, each call dispatching each of its kernels once, so
+    walking back from the end until a kernel repeats gives one call's kernels."""
+    lib = [x for x in disp if "spx::" in x[1]]
+    names = []
+    for _, k, _ in reversed(lib):
+        if k in names:
+            break
+        names.append(k)
+    tail = lib[-calls * len(names):]
+    if len(tail) != calls * len(names) or any(k not in names for _, k, _ in tail):
+        raise RuntimeError("the last %d calls do not repeat the kernels %s" % (calls, names))
+    return names[::-1], tail
+
+
+def _request_bytes(c):
+    """Read and write bytes of one dispatch's (or one launch's) counters."""
+    n = c["TCC_EA0_RDREQ_sum"]
+    n32, n64, n128 = c["TCC_EA0_RDREQ_32B_sum"], c["TCC_EA0_RDREQ_64B_sum"], c["TCC_EA0_RDREQ_128B_sum"]
+    other = max(0.0, n - n32 - n64 - n128)
+    read = 32 * n32 + 64 * (n64 + other) + 128 * n128
+    w, w64 = c["TCC_EA0_WRREQ_sum"], c["TCC_EA0_WRREQ_64B_sum"]
+    write = 32 * (w - w64) + 64 * w64
+    return read, write, other
+
+
+def collect_traffic(names_arg, out, summarize_only=False):
+    """Runs the counter passes (and a kernel trace) of the copy check and of
+    each workload, keeping the raw CSVs, the child's record and the commands
+    under out/raw, then writes the summaries from them."""
+    names = ALL_WORKLOADS if names_arg == "all" else names_arg.split(",")
+    out = os.path.abspath(out)  # the profiler runs from /tmp
+    raw = os.path.join(out, "raw")
+    os.makedirs(raw, exist_ok=True)
+    if not summarize_only:
+        for name in ["copy"] + names:
+            cmds = []
+            for i, ctrs in enumerate(COUNTER_PASSES):
+                rec, shown = _rocprof(["--pmc"] + list(ctrs), name, os.path.join(raw, "%s_p%d" % (name, i)))
+                cmds.append(shown)
+                log("counters", name, "pass", i, "done")
+            if name != "copy":
+                rec, shown = _rocprof(["--kernel-trace", "--stats"], name, os.path.join(raw, "%s_kt" % name))
+                cmds.append(shown)
+                log("kernel trace", name, "done")
+            with open(os.path.join(raw, "%s_run.json" % name), "w") as f:
+                json.dump(dict(record=rec, commands=cmds), f)
+    summarize_traffic(names, out)
+
+
+def _pass_counters(raw, name, calls):
+    """Per-launch counter values over the last `calls` calls, and the call's
+    kernels."""
+    total, kernels, by_kernel = {}, None, {}
+    for i in range(len(COUNTER_PASSES)):
+        disp = _dispatches(_csv_rows(os.path.join(raw, "%s_p%d" % (name, i)), "counter_collection.csv"))
+        if calls is None:  # the copy check: the run's last dispatch is its last copy
+            names, tail = [disp[-1][1]], [disp[-1]]
+            n = 1
+        else:
+            names, tail = _call_dispatches(disp, calls)
+            n = calls
+        if kernels is not None and names != kernels:
+            raise RuntimeError("passes disagree on the call's kernels: %s / %s" % (kernels, names))
+        kernels = names
+        for _, kn, v in tail:
+            for c, x in v.items():
+                total[c] = total.get(c, 0.0) + x / n
+                by_kernel.setdefault(kn, {})[c] = by_kernel.get(kn, {}).get(c, 0.0) + x / n
+    return kernels, total, by_kernel
+
+
+def summarize_traffic(names, out):
+    raw = os.path.join(out, "raw")
+    with open(os.path.join(raw, "copy_run.json")) as f:
+        run = json.load(f)
+    rec = run["record"]
+    kernels, c, _ = _pass_counters(raw, "copy", None)
+    rd, wr, _ = _request_bytes(c)
+    check = dict(kernel=_short_kernel(kernels[0]), bytes_read=rec["copy_bytes_read"],
+                 bytes_written=rec["copy_bytes_written"], counted_read=int(rd), counted_write=int(wr),
+                 read_ratio=round(rd / rec["copy_bytes_read"], 4), write_ratio=round(wr / rec["copy_bytes_written"], 4),
+                 requests_128B_share=round(c["TCC_EA0_RDREQ_128B_sum"] / c["TCC_EA0_RDREQ_sum"], 4),
+                 commands=run["commands"])
+    with open(os.path.join(out, "traffic_copy_check.json"), "w") as f:
+        json.dump(check, f, indent=1)
+
+    for name in names:
+        with open(os.path.join(raw, "%s_run.json" % name)) as f:
+            run = json.load(f)
+        rec, cmds = run["record"], run["commands"]
+        calls = (COUNTER_WARMUP + COUNTER_STEPS) * rec.get("launches_per_step", 1)
+        call, per_launch, by_kernel = _pass_counters(raw, name, calls)
+        rd, wr, other = _request_bytes(per_launch)
+        split = {}
+        for k in call:
+            krd, kwr, _ = _request_bytes(by_kernel[k])
+            kh, km = by_kernel[k]["TCC_HIT_sum"], by_kernel[k]["TCC_MISS_sum"]
+            split[_short_kernel(k)] = dict(read_bytes=int(krd), write_bytes=int(kwr),
+                                           l2_hit_rate=round(kh / max(1.0, kh + km), 4))
+        fetch_equiv = (128 * per_launch["TCC_BUBBLE_sum"] + 64 * (per_launch["TCC_EA0_RDREQ_sum"] -
+                       per_launch["TCC_BUBBLE_sum"] - per_launch["TCC_EA0_RDREQ_32B_sum"]) +
+                       32 * per_launch["TCC_EA0_RDREQ_32B_sum"])
+        hits, miss = per_launch["TCC_HIT_sum"], per_launch["TCC_MISS_sum"]
+        roof = rec.get("roofline", {})
+        t = dict(workload=name, kernels=[_short_kernel(k) for k in call], kernel_names=call,
+                 kernel_fingerprint=kernel_fingerprint(name), launches=calls,
+                 read_bytes_per_launch=int(rd), write_bytes_per_launch=int(wr), bytes_per_launch=int(rd + wr),
+                 algorithmic_bytes_per_launch=roof.get("algorithmic_bytes_per_launch"),
+                 requests_per_launch={k.replace("TCC_", "").replace("_sum", ""): round(v, 1)
+                                      for k, v in sorted(per_launch.items())},
+                 read_requests_unsized_per_launch=round(other, 1),
+                 fetch_size_bytes_per_launch=int(fetch_equiv),
+                 l2_hit_rate=round(hits / max(1.0, hits + miss), 4), per_kernel=split,
+                 method="read = 32 x RDREQ_32B + 64 x RDREQ_64B + 128 x RDREQ_128B, write = 32 x (WRREQ - "
+                        "WRREQ_64B) + 64 x WRREQ_64B (TCC_EA0 counters summed over the L2 channels), per launch "
+                        "over the dispatches of the last %d calls; no scale factor (copy check: read x%.4f, "
+                        "write x%.4f of a 256 MiB copy)" % (calls, check["read_ratio"], check["write_ratio"]),
+                 commands=cmds,
+                 note="run from /tmp with TMPDIR=/tmp; <repo> is the repository root; one launch = one library "
+                      "call = one dispatch of each kernel listed")
+        with open(os.path.join(out, "traffic_%s.json" % name), "w") as f:
+            json.dump(t, f, indent=1)
+        kt = _csv_rows(os.path.join(raw, "%s_kt" % name), "kernel_stats.csv")
+        _kernel_summary(out, name, t, kt, rec, cmds[-1])
+        log("traffic", name, "%.1f MB read + %.1f MB written per launch" % (rd / 1e6, wr / 1e6))
+
+
+def _kernel_summary(out, name, t, kt, rec, kt_cmd):
+    roof = rec.get("roofline", {})
+    rows = sorted(kt, key=lambda r: -float(r["TotalDurationNs"]))
+    main = re.sub(r"[^A-Za-z0-9_]", "", "_".join(k.split("<")[0] for k in t["kernels"][:2]))
+    lines = ["# %s on %s" % (", ".join(t["kernels"]), name), "",
+             "Written by `python3 <repo>/bench.py --collect-traffic %s --traffic-out <dir>` (`<repo>` is the "
+             "repository root), which runs each rocprofv3 pass below as a child process from /tmp with "
+             "TMPDIR=/tmp, and `traffic_%s.json` beside this file." % (name, name), "",
+             "Kernel trace:", "",
+             "```", kt_cmd, "```", "",
+             "| kernel | calls | total us | average us | % |", "|---|---|---|---|---|"]
+    for r in rows[:12]:
+        lines.append("| %s | %s | %.1f | %.2f | %.1f |" % (
+            _short_kernel(r["Name"])[:70], r["Calls"], float(r["TotalDurationNs"]) / 1e3, float(r["AverageNs"]) / 1e3,
+            float(r["Percentage"])))
+    lines += ["", "The same run's events (bench.py, plain launches, per launch): %.2f us; algorithmic bytes per "
+              "launch %s." % (
+        1e3 * roof.get("kernel_ms", float("nan")), roof.get("algorithmic_bytes_per_launch")), "",
+        "Traffic between the L2s and memory per launch (counter passes below, averaged over the last %d "
+        "launches):" % t["launches"], "",
+        "| quantity | value |", "|---|---|",
+        "| read bytes | %d |" % t["read_bytes_per_launch"],
+        "| write bytes | %d |" % t["write_bytes_per_launch"],
+        "| total / algorithmic | %.3f |" % (t["bytes_per_launch"] / max(1, t["algorithmic_bytes_per_launch"] or 1)),
+        "| L2 hit rate | %.3f |" % t["l2_hit_rate"],
+        "| FETCH_SIZE (as ROCm defines it), bytes | %d |" % t["fetch_size_bytes_per_launch"]]
+    for k, v in t["requests_per_launch"].items():
+        lines.append("| %s | %.0f |" % (k, v))
+    if len(t["per_kernel"]) > 1:
+        lines += ["", "| kernel | read bytes | write bytes | L2 hit rate |", "|---|---|---|---|"]
+        for k, v in t["per_kernel"].items():
+            lines.append("| %s | %d | %d | %.3f |" % (k, v["read_bytes"], v["write_bytes"], v["l2_hit_rate"]))
+    lines += ["", "Counter passes:", "", "```"] + t["commands"][:-1] + ["```", "",
+              "Method: " + t["method"] + ".", ""]
+    with open(os.path.join(out, "%s_%s.md" % (main, name)), "w") as f:
+        f.write("\n".join(lines))
+
+
+# --------------------------------------------------------------------------
 # GPU measurement
 # --------------------------------------------------------------------------
 def copy_rate_gbs():
@@ -653,6 +899,46 @@ def gather_probe(col, nnz, n):
     return res
 
 
+def feed_probe():
+    """Rates at which the memory side fills LDS through global_load_lds (see
+    csrc/probe.hip): a buffer resident in an XCD's L2, a 64 MiB buffer read
+    many times per launch and once per launch (held by the MALL between
+    launches), and a 1 GiB one (HBM).  Medians of 3 timed launches."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    from spmm_csr_spmv_amd import build as b
+    if not os.path.exists(b.PROBE_LIB):
+        raise ImportError("%s is not built" % b.PROBE_LIB)
+    L = ctypes.CDLL(b.PROBE_LIB)
+    L.spx_feed_probe_waves.restype = ctypes.c_int64
+    L.spx_probe_feed.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    waves = int(L.spx_feed_probe_waves())
+    src = torch.ones(1 << 28, device="cuda")  # 1 GiB
+    out = torch.empty(512 * 256, device="cuda")
+    s = torch.cuda.current_stream()
+    cases = {"l2_2MiB_tbs": (2048, 2048, 7919), "mall_64MiB_reread_tbs": (65536, 2048, 7919),
+             "mall_64MiB_once_tbs": (65536, 65536 // waves, 0), "hbm_1GiB_tbs": (1 << 20, 2048, 7919)}
+    res = {}
+    for key, (pieces, iters, stride) in cases.items():
+        ts = []
+        for _ in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            rc = L.spx_probe_feed(ctypes.c_void_p(src.data_ptr()), pieces, iters, stride,
+                                  ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(s.cuda_stream))
+            e1.record(s)
+            if rc != 0:
+                raise RuntimeError("spx_probe_feed failed: %d" % rc)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        res[key] = round(waves * iters * 1024 / (float(np.median(ts[1:])) * 1e-3) / 1e12, 2)
+    del src, out
+    return res
+
+
 def measure(w, args, stream):
     """Warm-up, then exactly args.steps timed steps; returns the record."""
     import numpy as np
@@ -721,7 +1007,7 @@ def measure(w, args, stream):
                 flops_per_launch=int(per_launch_flops), event_ms_median=round(float(np.median(ev_ms)), 5),
                 event_ms_min=round(float(np.min(ev_ms)), 5))
     if tr is not None:
-        for k in ("hbm_read_bytes_per_launch", "mall_read_bytes_per_launch", "write_bytes_per_launch", "method"):
+        for k in ("read_bytes_per_launch", "write_bytes_per_launch", "l2_hit_rate", "method"):
             if k in tr:
                 roof["traffic_" + k.replace("_per_launch", "")] = tr[k]
     if w.bound == "mfma":
@@ -762,6 +1048,8 @@ def measure(w, args, stream):
                          unit=w.unit, frac=round(cold_achieved / w.peak, 4),
                          warm_single_ms_median=round(float(np.median(single_ms)), 5))
     r["setup"] = {k: round(v, 2) for k, v in w.setup.items()}
+    if args.counter_run:
+        r["launches_per_step"] = w.launches
     return r
 
 
@@ -791,10 +1079,28 @@ def main():
                     help="SpMV workloads: time the default candidate plans (sp_autotune_spmv), then build the plan "
                          "from the tuning cache; the candidates' times are reported under 'autotune'")
     ap.add_argument("--no-gather-probe", dest="gather_probe", action="store_false",
-                    help="skip the gather-rate probe over the power-law matrix's columns")
+                    help="skip the probes (the gather rate over the power-law matrix's columns, the LDS feed "
+                         "rates beside bsr_blocks)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (5 launches) to calibrate HBM byte counters")
+    ap.add_argument("--counter-run", action="store_true",
+                    help="the run a counter pass profiles: warm-up and timed steps as plain launches, nothing else "
+                         "on the GPU but the workload's setup (no probes, comparisons or CPU baseline)")
+    ap.add_argument("--collect-traffic", default=None, metavar="NAMES",
+                    help="comma-separated workloads (or 'all'): run rocprofv3 counter and kernel-trace passes over "
+                         "'--counter-run' children and write traffic_<workload>.json and a kernel summary per "
+                         "workload to --traffic-out")
+    ap.add_argument("--traffic-out", default=None, metavar="DIR")
+    ap.add_argument("--summarize-only", action="store_true",
+                    help="with --collect-traffic: rewrite the summaries from DIR/raw without profiling")
     args = ap.parse_args()
+    if args.collect_traffic:
+        if not args.traffic_out:
+            ap.error("--collect-traffic needs --traffic-out")
+        collect_traffic(args.collect_traffic, args.traffic_out, args.summarize_only)
+        return
+    if args.counter_run:
+        args.no_cpu_baseline, args.gather_probe, args.graph_batch, args.cold = True, False, 0, 0
     if args.copy_calibration:
         import torch
         n = 64 << 20  # floats: 256 MiB per buffer
@@ -826,7 +1132,8 @@ def main():
     else:
         names = [args.config]
     copy_gbs = copy_rate_gbs()
-    warm_library()
+    if not args.counter_run:  # (a counter run counts every dispatch of the call's kernels)
+        warm_library()
     records = {}
     for i, name in enumerate(names):
         log("workload", name)
@@ -845,6 +1152,11 @@ def main():
             rec["roofline"]["measured_gather_rate"] = p["gather_2MiB_slice_gps"]
             rec["roofline"]["one_pass_gather_floor_ms"] = round(floor_ms, 5)
             rec["roofline"]["frac_of_gather_floor"] = round(floor_ms / rec["roofline"]["kernel_ms"], 4)
+        if w.name == "bsr_blocks" and args.gather_probe:
+            rec["feed_probe"] = feed_probe()
+            tb = rec["roofline"].get("traffic")
+            if tb:  # what the call moves between the L2s and memory, per second
+                rec["roofline"]["traffic_tbs"] = round(tb / (rec["roofline"]["kernel_ms"] * 1e-3) / 1e12, 2)
         if w.cpu is not None:
             secs = args.cpu_seconds if i == 0 else args.cpu_seconds_other
             rec["cpu_baseline"] = cpu_baseline(w.cpu, secs)

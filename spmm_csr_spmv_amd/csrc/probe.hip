@@ -60,6 +60,37 @@ __global__ __launch_bounds__(kThreads) void gather_probe_kernel(const i32x4* __r
     out[(int64_t)blockIdx.x * kThreads + threadIdx.x] = acc;
 }
 
+// Feed probe: the rate at which the memory side fills LDS, the operand feed of
+// the BSR SpMM (「通用稀疏矩阵乘法CUDA算子实现」 §3.4 stages A and B tiles
+// through on-chip memory).  Each wave copies 1 KB pieces into its own
+// 16-piece LDS ring with global_load_lds (16 bytes per lane, whole-wave
+// coalesced), waiting only when 16 pieces are in flight; nothing is computed.
+// Piece i of wave g is (g * stride + i) & mask of a buffer of mask + 1
+// pieces: stride 0 gives each wave its own consecutive pieces (a buffer of
+// exactly waves x iters pieces is then read once per launch), an odd stride
+// spreads the waves over the buffer so that every piece is read many times.
+constexpr int kFeedDepth = 16;
+
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+__global__ __launch_bounds__(kThreads) void feed_probe_kernel(const uint8_t* __restrict__ src, int64_t mask,
+                                                              int iters, int64_t stride, float* __restrict__ out) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kThreads / 64][kFeedDepth][1024];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t g = (int64_t)blockIdx.x * (kThreads / 64) + w;
+    const int64_t first = stride == 0 ? g * iters : g * stride;
+    for (int i = 0; i < iters; ++i) {
+        const uint8_t* p = src + ((first + i) & mask) * 1024 + lane * 16;
+        __builtin_amdgcn_global_load_lds((const void*)p,
+                                         (__attribute__((address_space(3))) void*)&ring[w][i % kFeedDepth][0], 16,
+                                         0, 0);
+        __builtin_amdgcn_s_waitcnt(vm_wait(kFeedDepth - 1));
+    }
+    __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    __syncthreads();
+    out[(int64_t)blockIdx.x * kThreads + threadIdx.x] = (float)ring[w][lane & (kFeedDepth - 1)][lane];
+}
+
 }  // namespace
 
 extern "C" {
@@ -82,6 +113,20 @@ int spx_probe_gather(const int32_t* col, const float* val, int64_t nnz, const fl
     hipLaunchKernelGGL(gather_probe_kernel, dim3(256 * 8), dim3(kThreads), 0, (hipStream_t)stream,
                        reinterpret_cast<const i32x4*>(col), reinterpret_cast<const f32x4*>(val), chunks, x, mask,
                        mode, out);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Grid of the feed probe: 2 workgroups of 4 waves per CU on 256 CUs.
+int64_t spx_feed_probe_waves(void) { return (int64_t)512 * (kThreads / 64); }
+
+// Runs the feed probe once: every wave copies `iters` 1 KB pieces of a buffer
+// of `pieces` KB (a power of two; src holds pieces * 1024 bytes, device) as
+// described above; out holds 512 * 256 floats.  Returns 0, 1 for a bad
+// argument, 2 for a failed launch.
+int spx_probe_feed(const uint8_t* src, int64_t pieces, int iters, int64_t stride, float* out, void* stream) {
+    if (!src || !out || pieces <= 0 || (pieces & (pieces - 1)) != 0 || iters <= 0 || stride < 0) return 1;
+    hipLaunchKernelGGL(feed_probe_kernel, dim3(512), dim3(kThreads), 0, (hipStream_t)stream, src, pieces - 1, iters,
+                       stride, out);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

@@ -101,3 +101,49 @@ def test_workload_names_and_cpu_row_ranges():
     assert bench._sample_rows(rp, 2, 25) == 4 and rp[4] * 2 <= 25
     assert bench._sample_rows(rp, 2, 40) == 5
     assert 1 <= bench.cpu_threads() <= 16
+
+
+def test_counter_traffic_accounting():
+    # ROCm's FETCH_SIZE expression, written out: it counts a 128-byte request
+    # as 64 bytes unless TCC_BUBBLE counts it
+    def fetch_size(c):
+        return (128 * c["TCC_BUBBLE_sum"] + 64 * (c["TCC_EA0_RDREQ_sum"] - c["TCC_BUBBLE_sum"]
+                - c["TCC_EA0_RDREQ_32B_sum"]) + 32 * c["TCC_EA0_RDREQ_32B_sum"])
+    stream = dict(TCC_EA0_RDREQ_sum=1000.0, TCC_EA0_RDREQ_32B_sum=0.0, TCC_EA0_RDREQ_64B_sum=0.0,
+                  TCC_EA0_RDREQ_128B_sum=1000.0, TCC_EA0_WRREQ_sum=1000.0, TCC_EA0_WRREQ_64B_sum=1000.0,
+                  TCC_BUBBLE_sum=0.0)
+    rd, wr, other = bench._request_bytes(stream)
+    assert (rd, wr, other) == (128000.0, 64000.0, 0.0)
+    assert fetch_size(stream) * 2 == rd  # the factor a streaming copy shows
+    mixed = dict(stream, TCC_EA0_RDREQ_sum=10.0, TCC_EA0_RDREQ_32B_sum=3.0, TCC_EA0_RDREQ_64B_sum=2.0,
+                 TCC_EA0_RDREQ_128B_sum=4.0, TCC_EA0_WRREQ_sum=5.0, TCC_EA0_WRREQ_64B_sum=2.0)
+    rd, wr, other = bench._request_bytes(mixed)
+    # one request of no listed size is taken as 64 bytes, as FETCH_SIZE does
+    assert other == 1.0 and rd == 3 * 32 + 3 * 64 + 4 * 128 and wr == 3 * 32 + 2 * 64
+
+
+def test_kernel_short_names():
+    assert bench._short_kernel("void spx::(anonymous namespace)::bsr_spmm_dma<256>(int const*, float)") == \
+        "bsr_spmm_dma<256>"
+    assert bench._short_kernel("spx::(anonymous namespace)::xw_rows_kernel(spx::(anonymous namespace)::A)") == \
+        "xw_rows_kernel"
+    assert bench._short_kernel("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
+
+
+def test_counter_run_call_selection():
+    # setup kernels first (one of them as often as the call's kernels), then
+    # 3 calls of two kernels, the last call of one kernel shared by two calls
+    # per step; only the last calls' dispatches are taken
+    k = lambda n: "void spx::(anonymous namespace)::%s(int)" % n
+    setup = [(i, k("sort"), {"x": 1.0}) for i in range(3)] + [(3, "torch_fill", {"x": 9.0})]
+    calls = []
+    for c in range(3):
+        calls += [(10 + 2 * c, k("products"), {"x": 2.0}), (11 + 2 * c, k("rows"), {"x": 3.0})]
+    names, tail = bench._call_dispatches(setup + calls, 3)
+    assert names == [k("products"), k("rows")] and len(tail) == 6 and tail[0][0] == 10
+    one = [(i, k("sell"), {"x": 1.0}) for i in range(4)]
+    names, tail = bench._call_dispatches(setup + one, 4)
+    assert names == [k("sell")] and len(tail) == 4
+    import pytest
+    with pytest.raises(RuntimeError):
+        bench._call_dispatches(setup + calls, 4)  # a setup kernel inside the span
