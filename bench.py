@@ -271,6 +271,17 @@ class Workload:
         self.cpu = None       # CpuLeg or None
         self.extra = {}       # roofline extras (e.g. a gather-aware bound)
         self.keep = []        # device tensors to free afterwards
+        self.digest = None    # fingerprint of the generated inputs
+
+
+def _digest(*arrays):
+    """SHA-256 (first 16 hex digits) of the generator's arrays, in order: a
+    fingerprint of the inputs a run used."""
+    import numpy as np
+    h = hashlib.sha256()
+    for a in arrays:
+        h.update(np.ascontiguousarray(a).view(np.uint8).reshape(-1))
+    return h.hexdigest()[:16]
 
 
 def _to_dev(torch, a):
@@ -306,6 +317,7 @@ def prepare(name, args, opts):
         d_B = _to_dev(torch, Bh.view(np.int16))
         C = torch.empty(b.mb * b.bs, N, device="cuda")
         w.setup["generate_s"] = time.time() - t0
+        w.digest = _digest(b.brow_ptr, b.bcol, b.bval, Bh)
 
         def step():
             sp.bsr_spmm(b.mb, b.kb, b.bs, d_brow, d_bcol, d_bval, d_B, 1.0, 0.0, C)
@@ -330,6 +342,7 @@ def prepare(name, args, opts):
         bs = 64
         coo = gen.block_sparse_coo(seed=0)
         w.setup["generate_s"] = time.time() - t0
+        w.digest = _digest(coo.row, coo.col, coo.val)
         m, n = coo.m, coo.n
         rp, ci, vv = _csr_from_coo(w, sp, torch, coo)
         t1 = time.time()
@@ -384,6 +397,7 @@ def prepare(name, args, opts):
     if base == "spmm_clustered":
         coo = gen.clustered_coo(seed=0)
         w.setup["generate_s"] = time.time() - t0
+        w.digest = _digest(coo.row, coo.col, coo.val)
         m, n, nnz = coo.m, coo.n, coo.nnz
         rp, ci, vv = _csr_from_coo(w, sp, torch, coo)
         t1 = time.time()
@@ -436,6 +450,7 @@ def prepare(name, args, opts):
            "stencil27": lambda: gen.stencil27_coo(seed=0),
            "spmm_lognormal": lambda: gen.lognormal_coo(seed=0)}[base]()
     w.setup["generate_s"] = time.time() - t0
+    w.digest = _digest(coo.row, coo.col, coo.val)
     m, n, nnz = coo.m, coo.n, coo.nnz
     rp, ci, vv = _csr_from_coo(w, sp, torch, coo)
     del coo
@@ -994,6 +1009,8 @@ def measure(w, args, stream):
     r["ms_per_step"] = round(ms_per_step, 5)
     r["dtype"] = w.dtype
     r["config"] = w.config
+    if w.digest:
+        r["config"]["input_sha256"] = w.digest
     per_launch_bytes = w.nbytes / w.launches
     per_launch_flops = w.flops / w.launches
     if w.bound == "hbm":
@@ -1021,12 +1038,15 @@ def measure(w, args, stream):
     r["roofline"] = roof
     r["gflops_event"] = round(per_launch_flops / (launch_ms * 1e-3) / 1e9, 2)
 
-    if args.cold > 0:
+    # cold-cache reps: asked for, or by default where the working set is under
+    # the 256 MB MALL (so that warm numbers read part of it from there)
+    cold_reps = args.cold if args.cold >= 0 else (10 if per_launch_bytes < (256 << 20) else 0)
+    if cold_reps > 0:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.cold)]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(cold_reps)]
         # each rep: flush, one timed step (cold), then one more timed step the
         # same way (warm: what the flushed step left in the caches)
-        for i in range(args.cold):
+        for i in range(cold_reps):
             if w.restore:
                 w.restore()  # before the flush, so the copy leaves nothing in the caches
             flush.fill_(i & 255)
@@ -1043,7 +1063,7 @@ def measure(w, args, stream):
             cold_achieved = per_launch_bytes / (med * 1e-3) / 1e9
         else:
             cold_achieved = per_launch_flops / (med * 1e-3) / 1e12
-        r["cold"] = dict(reps=args.cold, flush_bytes=512 << 20, kernel_ms_median=round(med, 5),
+        r["cold"] = dict(reps=cold_reps, flush_bytes=512 << 20, kernel_ms_median=round(med, 5),
                          kernel_ms_min=round(float(np.min(cold_ms)), 5), achieved=round(cold_achieved, 2),
                          unit=w.unit, frac=round(cold_achieved / w.peak, 4),
                          warm_single_ms_median=round(float(np.median(single_ms)), 5))
@@ -1065,9 +1085,11 @@ def main():
                     help="steps per replay of a captured HIP graph in the timed region (0: one plain launch per "
                          "step; -1: 20 for workloads whose step is a single short kernel, else 0)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold", type=int, default=0, metavar="R",
+    ap.add_argument("--cold", type=int, default=-1, metavar="R",
                     help="after the timed region, also time R single steps each preceded by writing a 512 MiB "
-                         "buffer (evicts the L2s and the 256 MB MALL): cold-cache numbers, reported under 'cold'")
+                         "buffer (evicts the L2s and the 256 MB MALL): cold-cache numbers, reported under 'cold'; "
+                         "-1 (default): 10 for workloads whose algorithmic bytes per launch are under 256 MiB, "
+                         "else none")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="oracle time of the headline's CPU baseline (half on all threads, half on one)")
     ap.add_argument("--cpu-seconds-other", type=float, default=2.0,
