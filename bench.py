@@ -165,7 +165,7 @@ def parse_workload(name):
 # --------------------------------------------------------------------------
 def cpu_threads():
     """Threads the oracle baseline uses: the cores this process may run on,
-    at most 16 (the GPU machine's CPU share per GPU)."""
+    at most 16 (the host's CPU share per GPU on an MI355X node)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
