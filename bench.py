@@ -602,10 +602,14 @@ COUNTER_STEPS, COUNTER_WARMUP = 5, 1
 
 
 def _child_args(name):
+    """bench.py arguments of one counter run; a workload name may carry plan
+    options after a '+', separated by ':' (spmv_powerlaw+col_panels=8:wave_min=64)."""
     if name == "copy":
         return ["--copy-calibration"]
+    name, _, opts = name.partition("+")
     base, N = parse_workload(name)
     a = ["--config", base] + (["--N", str(N)] if N is not None else [])
+    a += ["--options", opts.replace(":", ",")] if opts else []
     return a + ["--counter-run", "--steps", str(COUNTER_STEPS), "--warmup", str(COUNTER_WARMUP)]
 
 
@@ -1109,7 +1113,8 @@ def main():
                     help="the run a counter pass profiles: warm-up and timed steps as plain launches, nothing else "
                          "on the GPU but the workload's setup (no probes, comparisons or CPU baseline)")
     ap.add_argument("--collect-traffic", default=None, metavar="NAMES",
-                    help="comma-separated workloads (or 'all'): run rocprofv3 counter and kernel-trace passes over "
+                    help="comma-separated workloads (or 'all'; plan options after '+', e.g. "
+                         "spmv_powerlaw+col_panels=8): run rocprofv3 counter and kernel-trace passes over "
                          "'--counter-run' children and write traffic_<workload>.json and a kernel summary per "
                          "workload to --traffic-out")
     ap.add_argument("--traffic-out", default=None, metavar="DIR")
