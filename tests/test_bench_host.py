@@ -147,3 +147,30 @@ def test_counter_run_call_selection():
     import pytest
     with pytest.raises(RuntimeError):
         bench._call_dispatches(setup + calls, 4)  # a setup kernel inside the span
+
+
+def test_probe_library_loads_and_refuses_bad_arguments():
+    # the measurement probes bench.py loads (not part of the product ABI);
+    # argument checks return before any launch
+    import ctypes
+    import os
+
+    from spmm_csr_spmv_amd import build as b
+    if not os.path.exists(b.PROBE_LIB):
+        import pytest
+        pytest.skip("probe library not built")
+    L = ctypes.CDLL(b.PROBE_LIB)
+    for name in ("spx_probe_out_bytes", "spx_probe_entries", "spx_probe_gather", "spx_feed_probe_waves",
+                 "spx_probe_feed"):
+        assert hasattr(L, name), name
+    L.spx_probe_entries.restype = ctypes.c_int64
+    L.spx_probe_entries.argtypes = [ctypes.c_int64]
+    assert L.spx_probe_entries(5000) == 4096 and L.spx_probe_entries(-3) == 0
+    L.spx_feed_probe_waves.restype = ctypes.c_int64
+    assert L.spx_feed_probe_waves() == 2048
+    L.spx_probe_feed.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    fake = ctypes.c_void_p(256)
+    assert L.spx_probe_feed(fake, 3, 10, 0, fake, None) == 1      # not a power of two
+    assert L.spx_probe_feed(None, 1024, 10, 0, fake, None) == 1   # null source
+    assert L.spx_probe_feed(fake, 1024, 0, 0, fake, None) == 1    # no pieces per wave
