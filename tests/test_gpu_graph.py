@@ -41,13 +41,16 @@ def _replays_match(run, outs, replays=3):
 @pytest.mark.parametrize("bins", [dict(), dict(use_sell=0, col_panels=4, wave_min=8, block_min=20, split_min=40,
                                                split_seg=16), dict(use_sell=1, sell_sigma=64),
                                   dict(use_sell=0, x_window_bits=6),
-                                  dict(wave_min=0, block_min=0, split_min=0, split_seg=16)])
+                                  dict(wave_min=0, block_min=0, split_min=0, split_seg=16),
+                                  dict(spmm_phase_bits=6)])  # SpMM through the phase-swept copy
 def test_spmv_spmv_t_spmm_graph_replays(bins):
     say("graph replays", bins)
     coo = gen.ragged_coo(1500, 900, seed=2, max_len=30, long_rows=(300, 800, 257))
     rp, c, v = sp.csr_build_from_coo(coo.m, coo.n, dev(coo.row), dev(coo.col), dev(coo.val))
     csc = sp.csr_to_csc(coo.m, coo.n, rp, c, v)
     plan = sp.Plan(coo.m, coo.n, rp, c, v, csc=csc, max_N=8, **bins)
+    if "spmm_phase_bits" in bins:
+        assert plan.profile()["spmm_phase_bits"] == bins["spmm_phase_bits"]
     x = dev(gen.dense_vector(coo.n, 1))
     u = dev(gen.dense_vector(coo.m, 2))
     B = dev(gen.dense_matrix(coo.n, 8, 3))
