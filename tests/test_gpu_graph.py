@@ -123,3 +123,33 @@ def test_wcsr_spmm_graph_replays():
         sp.wcsr_spmm(coo.m, coo.n, wp, wc, vals, 1.0, B, 0.0, C)
 
     _replays_match(run, [C])
+
+
+def test_view_products_graph_replays():
+    """A view's products (its own scratch: split partials and counters, x-window
+    products) captured and replayed like the plan's."""
+    say("graph replays on a view")
+    coo = gen.ragged_coo(1500, 900, seed=5, max_len=30, long_rows=(300, 800, 257))
+    rp, c, v = sp.csr_build_from_coo(coo.m, coo.n, dev(coo.row), dev(coo.col), dev(coo.val))
+    csc = sp.csr_to_csc(coo.m, coo.n, rp, c, v)
+    for bins in (dict(use_sell=0, x_window_bits=6), dict(wave_min=0, block_min=0, split_min=0, split_seg=16)):
+        plan = sp.Plan(coo.m, coo.n, rp, c, v, csc=csc, max_N=8, **bins)
+        view = plan.view(max_N=8)
+        x = dev(gen.dense_vector(coo.n, 1))
+        u = dev(gen.dense_vector(coo.m, 2))
+        B = dev(gen.dense_matrix(coo.n, 8, 3))
+        y = torch.empty(coo.m, device="cuda")
+        z = torch.empty(coo.n, device="cuda")
+        C = torch.empty(coo.m, 8, device="cuda")
+
+        def run():
+            sp.spmv(view, 1.0, x, 0.0, y)
+            sp.spmv_t(view, 2.0, u, 0.0, z)
+            sp.spmm(view, 1.0, B, 0.0, C)
+
+        _replays_match(run, [y, z, C])
+        hrp, hc, hv = oracle.coo_to_csr(coo.m, coo.n, coo.row, coo.col, coo.val)
+        ref, scale = oracle.spmv(hrp, hc, hv, x.cpu().numpy())
+        assert np.all(np.abs(y.cpu().numpy() - ref) <= 1e-5 * scale + 1e-30)
+        view.destroy()
+        plan.destroy()
