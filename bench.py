@@ -493,6 +493,10 @@ def prepare(name, args, opts):
     if tune is not None:
         w.config["autotune"] = tune
         w.config["col_panels"] = prof["col_panels"]
+    if base == "spmv_powerlaw" and not args.counter_run and not opts and tune is None:
+        # the entry-balanced one-kernel stream against the binned dispatcher and
+        # the other paths on this matrix (mean of 20 graph-free calls each)
+        w.config["strategies"] = compare_spmv_paths(sp, torch, m, n, rp, ci, vv, x_dev=_to_dev(torch, gen.dense_vector(n, 0, 1)))
     w.bound, w.peak, w.unit = "hbm", PEAK_HBM_GBS, "GB/s"
     w.dtype = "f32"
     want_cpu = not args.no_cpu_baseline
@@ -956,6 +960,30 @@ def feed_probe():
         res[key] = round(waves * iters * 1024 / (float(np.median(ts[1:])) * 1e-3) / 1e12, 2)
     del src, out
     return res
+
+
+def compare_spmv_paths(sp, torch, m, n, rp, ci, vv, x_dev):
+    """Call time of y = A x through each SpMV path on one matrix: the default
+    plan's choice, the row bins (no SELL, no streams), the entry-balanced
+    one-kernel stream (one column panel) and eight column panels."""
+    paths = {"x_window_stream": dict(), "row_bins": dict(use_sell=0, col_panels=0, x_window_bits=0),
+             "entry_balanced_stream": dict(use_sell=0, col_panels=1, x_window_bits=0),
+             "column_panels_8": dict(use_sell=0, col_panels=8, x_window_bits=0)}
+    y = torch.empty(m, device="cuda")
+    out = {}
+    for key, o in paths.items():
+        plan = sp.Plan(m, n, rp, ci, vv, **o)
+        for _ in range(3):
+            sp.spmv(plan, 1.0, x_dev, 0.0, y)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            sp.spmv(plan, 1.0, x_dev, 0.0, y)
+        e1.record()
+        torch.cuda.synchronize()
+        out[key] = dict(ms=round(e0.elapsed_time(e1) / 20, 5), options=o)
+        del plan
+    return out
 
 
 def measure(w, args, stream):
