@@ -37,14 +37,17 @@ def test_powerlaw_conversion_bit_exact(powerlaw):
     np.testing.assert_array_equal(host(g_v).view(np.uint32), v.view(np.uint32))
 
 
-@pytest.mark.parametrize("opts", [dict(), dict(col_panels=8)], ids=["default_x_windows", "panels8"])
-def test_powerlaw_spmv_all_rows(powerlaw, opts):
+@pytest.mark.parametrize("opts,path", [(dict(), (15, 0)), (dict(col_panels=8), (0, 8)),
+                                       (dict(use_sell=0, col_panels=1, x_window_bits=0), (0, 1)),
+                                       (dict(use_sell=0, col_panels=0, x_window_bits=0), (0, 0))],
+                         ids=["default_x_windows", "panels8", "entry_balanced_stream", "row_bins"])
+def test_powerlaw_spmv_all_rows(powerlaw, opts, path):
     coo, (rp, c, v), (g_rp, g_c, g_v) = powerlaw
     say("powerlaw plan", opts)
     plan = sp.Plan(coo.m, coo.n, g_rp, g_c, g_v, **opts)
     prof = plan.profile()
     # the default picks the x-window stream for these scattered columns
-    assert (prof["x_window_bits"], prof["col_panels"]) == ((15, 0) if not opts else (0, 8))
+    assert (prof["x_window_bits"], prof["col_panels"]) == path
     exp = oracle.row_profile(rp)
     assert (prof["p95"], prof["p99"], prof["max_len"], prof["empty_rows"]) == (exp["p95"], exp["p99"], exp["max"],
                                                                                exp["empty"])
