@@ -95,12 +95,14 @@ def test_stencil_conversions_bit_exact(stencil):
     np.testing.assert_array_equal(host(g_cv).view(np.uint32), cv.view(np.uint32))
 
 
-def test_stencil_operator_pair(stencil):
+@pytest.mark.parametrize("opts", [dict(), dict(use_sell=0)], ids=["default_sell", "row_bins"])
+def test_stencil_operator_pair(stencil, opts):
     """u <- A v - alpha u through the CSR, then v <- A^T u - beta v through the CSC."""
     coo, (rp, c, v), (g_rp, g_c, g_v) = stencil
     csc = sp.csr_to_csc(coo.m, coo.n, g_rp, g_c, g_v)
     cp, ri, cv = (host(t) for t in csc)
-    plan = sp.Plan(coo.m, coo.n, g_rp, g_c, g_v, csc=csc)
+    plan = sp.Plan(coo.m, coo.n, g_rp, g_c, g_v, csc=csc, **opts)
+    assert (plan.profile()["sell_slots"] > 0) == (not opts)
     u0 = gen.dense_vector(coo.m, 0, 2)
     v0 = gen.dense_vector(coo.n, 0, 3)
     alpha, beta = np.random.default_rng(5).uniform(0.5, 2.0, size=2)
