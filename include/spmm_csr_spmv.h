@@ -465,7 +465,10 @@ int wcsr_spmm(int64_t m, int64_t n, const int32_t* window_ptr, const int32_t* wi
  *
  * C (mb*bs x N fp32, row-major, ldc >= N) = alpha * A B + beta * C, with
  * B (kb*bs x N bf16 bit patterns, row-major, ldb >= N).  Supported: bs == 64,
- * N % 64 == 0, ldb % 8 == 0, ldc % 4 == 0, B and C 16-byte aligned.
+ * N % 8 == 0, ldb % 8 == 0, ldc % 4 == 0, B and C 16-byte aligned.  Widths
+ * that are multiples of 256 (or of 128) take the pipelined kernels; other
+ * widths a plain 64-column-tile kernel whose last tile reads no B column and
+ * writes no C column at or past N.
  * work: at least bsr_spmm_bufsize() bytes (may be 0 bytes: then NULL is fine).
  * The block structure is not validated (no synchronisation): block pointers
  * are clamped to [0, nnzb], and a block whose column index lies outside

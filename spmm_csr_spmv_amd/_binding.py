@@ -539,6 +539,9 @@ def bsr_spmm(mb, kb, bs, brow_ptr, bcol, bval, B, alpha, beta, C, stream=None, w
     _dev(C, torch.float32, "C")
     nnzb = bcol.numel()
     N = B.shape[1]
+    if (B.dim() != 2 or C.dim() != 2 or B.shape[0] != kb * bs or tuple(C.shape) != (mb * bs, N)
+            or brow_ptr.numel() != mb + 1 or bval.numel() != nnzb * bs * bs):
+        raise ValueError("shape mismatch: B must be (kb*bs, N), C (mb*bs, N), brow_ptr mb + 1, bval nnzb*bs*bs")
     size = _sz()
     _check("bsr_spmm_bufsize", L.bsr_spmm_bufsize(mb, kb, bs, nnzb, N, ctypes.byref(size)))
     if size.value > 0 and work is None:

@@ -1055,7 +1055,7 @@ int bsr_spmm(int64_t mb, int64_t kb, int32_t bs, int64_t nnzb, const int32_t* br
     if (bs != 64) return SP_ERR_UNSUPPORTED;
     if (mb * 64 > kI32Max || kb * 64 > kI32Max) return SP_ERR_SIZE;
     if (ldb < N || ldc < N) return SP_ERR_SIZE;
-    if (N % 64 != 0 || ldb % 8 != 0 || ldc % 4 != 0) return SP_ERR_UNSUPPORTED;
+    if (N % 8 != 0 || ldb % 8 != 0 || ldc % 4 != 0) return SP_ERR_UNSUPPORTED;
     if (mb > 0 && N > 0 && (!brow_ptr || !C)) return SP_ERR_NULL;
     if (nnzb > 0 && N > 0 && (!bcol || !bval || !B)) return SP_ERR_NULL;
     if ((reinterpret_cast<uintptr_t>(B) & 15) || (reinterpret_cast<uintptr_t>(C) & 15) ||

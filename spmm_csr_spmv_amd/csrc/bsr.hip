@@ -13,7 +13,8 @@
 //                 ring, B operands by LDS transpose reads, copy waves apart
 //                 from MFMA waves);
 //   N % 128 == 0: register-prefetch kernel, B repacked into k-pair words;
-//   N % 64 == 0:  plain kernel, one 64 x 64 tile, no prefetch.
+//   otherwise:    plain kernel, one 64 x 64 tile, no prefetch; the last
+//                 tile's columns past N (N % 8 == 0) are neither read nor written.
 // Each block contributes A_blk B[J*64 : J*64+64, tile] to its block row's tile.
 #include "device_common.h"
 
@@ -43,14 +44,16 @@ __device__ __forceinline__ void pair_rows(const u32x4 lo, const u32x4 hi, u32x4&
 }
 
 // ---------------------------------------------------------------------------
-// Simple kernel for N % 64 == 0 (tile 64 x 64, one 32 x 32 MFMA tile per
-// wave, no prefetch).  Serves the widths the pipelined kernel does not.
+// Simple kernel for any N % 8 == 0 (tile 64 x 64, one 32 x 32 MFMA tile per
+// wave, no prefetch).  Serves the widths the pipelined kernels do not; in the
+// last tile the 8-column chunks of B at or past N load as zeros and those
+// columns of C are not stored ([GEN] §6.1 pads B to the tile width instead).
 __global__ __launch_bounds__(kBlock) void bsr_spmm_n64(const int32_t* __restrict__ brow_ptr,
                                                        const int32_t* __restrict__ bcol,
                                                        const uint16_t* __restrict__ bval,
                                                        const uint16_t* __restrict__ B, int64_t ldb, float alpha,
                                                        float beta, float* __restrict__ C, int64_t ldc, int nnzb,
-                                                       int kb_count) {
+                                                       int kb_count, int N) {
     constexpr int NT = 64;
     __shared__ __attribute__((aligned(16))) uint16_t lA[kBs * kArow];
     __shared__ __attribute__((aligned(16))) uint32_t lB[(kBs / 2) * NT];
@@ -73,9 +76,10 @@ __global__ __launch_bounds__(kBlock) void bsr_spmm_n64(const int32_t* __restrict
         const uint16_t* b_src = B + (int64_t)J * kBs * ldb + n_base;
         for (int c = tid; c < (kBs / 2) * (NT / 8); c += kBlock) {
             const int p = c / (NT / 8), ch = c % (NT / 8);
-            u32x4 o0, o1;
-            pair_rows(*reinterpret_cast<const u32x4*>(b_src + (int64_t)(2 * p) * ldb + ch * 8),
-                      *reinterpret_cast<const u32x4*>(b_src + (int64_t)(2 * p + 1) * ldb + ch * 8), o0, o1);
+            u32x4 o0 = {0u, 0u, 0u, 0u}, o1 = {0u, 0u, 0u, 0u};
+            if (n_base + ch * 8 < N)  // whole 8-column chunks (N % 8 == 0)
+                pair_rows(*reinterpret_cast<const u32x4*>(b_src + (int64_t)(2 * p) * ldb + ch * 8),
+                          *reinterpret_cast<const u32x4*>(b_src + (int64_t)(2 * p + 1) * ldb + ch * 8), o0, o1);
             *reinterpret_cast<u32x4*>(lB + p * NT + ch * 8) = o0;
             *reinterpret_cast<u32x4*>(lB + p * NT + ch * 8 + 4) = o1;
         }
@@ -93,6 +97,7 @@ __global__ __launch_bounds__(kBlock) void bsr_spmm_n64(const int32_t* __restrict
     }
     // D layout of the 32x32 MFMA: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
     const int col = n_base + w_col + (l & 31);
+    if (col >= N) return;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int row = I * kBs + w_row + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
@@ -510,8 +515,8 @@ int bsr_spmm_device(int64_t mb, int64_t kb, int32_t bs, int64_t nnzb, const int3
     } else if (N % 128 == 0) {
         err = launch_pipelined<128>(mb, kb, nnzb, brow_ptr, bcol, bval, N, B, ldb, alpha, beta, C, ldc, s);
     } else {
-        hipLaunchKernelGGL(bsr_spmm_n64, dim3((unsigned)mb, (unsigned)(N / 64)), dim3(kBlock), 0, s, brow_ptr, bcol,
-                           bval, B, ldb, alpha, beta, C, ldc, (int)nnzb, (int)kb);
+        hipLaunchKernelGGL(bsr_spmm_n64, dim3((unsigned)mb, (unsigned)((N + 63) / 64)), dim3(kBlock), 0, s, brow_ptr,
+                           bcol, bval, B, ldb, alpha, beta, C, ldc, (int)nnzb, (int)kb, (int)N);
         err = hipGetLastError();
     }
     return err == hipSuccess ? SP_OK : SP_ERR_HIP;

@@ -129,7 +129,7 @@ def test_bsr_argument_errors():
                           a["ldb"], a["alpha"], a["beta"], a["C"], a["ldc"], None, 0, None)
 
     assert call(bs=16) == 5
-    assert call(N=96, ldb=96, ldc=96) == 5        # N not a multiple of 64
+    assert call(N=100, ldb=104, ldc=104) == 5     # N not a multiple of 8
     assert call(ldb=132) == 5                     # ldb not a multiple of 8
     assert call(ldb=100) == 2                     # ldb < N
     assert call(ldc=64) == 2                      # ldc < N

@@ -271,7 +271,9 @@ def test_spmm_n1_equals_spmv():
                                              # long block rows: 94..96 half-block stages, every tail length
                                              (4, 48, 512, 0.98), (4, 47, 256, 1.0),
                                              # several column tiles per block row
-                                             (3, 5, 768, 0.6), (2, 7, 1024, 1.0)])
+                                             (3, 5, 768, 0.6), (2, 7, 1024, 1.0),
+                                             # widths with a partial last 64-column tile
+                                             (3, 4, 8, 0.5), (4, 5, 72, 0.6), (5, 3, 200, 0.4), (2, 6, 264, 1.0)])
 def test_bsr_spmm(mb, kb, N, density):
     say("bsr", mb, kb, N, density)
     b = gen.block_sparse_bsr(mb=mb, kb=kb, bs=64, density=density, std=0.02, seed=mb * 100 + kb)
