@@ -520,6 +520,8 @@ def bsr_spmv(m, n, bs, brow_ptr, bcol, bval, alpha, x, beta, y, stream=None, row
     _dev(x, torch.float32, "x"), _dev(y, torch.float32, "y")
     if x.numel() != n or y.numel() != m:
         raise ValueError("x must have n entries and y m entries")
+    if bs > 0 and (brow_ptr.numel() != (m + bs - 1) // bs + 1 or bval.numel() != bcol.numel() * bs * bs):
+        raise ValueError("brow_ptr must have ceil(m / bs) + 1 entries and bval nnzb * bs * bs")
     fn = "bsr_spmv_rowwise" if rowwise else "bsr_spmv"
     _check(fn, getattr(lib(), fn)(m, n, bs, bcol.numel(), _ptr(brow_ptr), _ptr(bcol), _ptr(bval), float(alpha),
                                   _ptr(x), float(beta), _ptr(y), _stream(stream)))
