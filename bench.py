@@ -1049,7 +1049,10 @@ def measure(w, args, stream):
         achieved = per_launch_bytes / (launch_ms * 1e-3) / 1e9
     else:
         achieved = per_launch_flops / (launch_ms * 1e-3) / 1e12
-    tr = load_traffic_record(w.name)
+    # the committed counters were taken on the default plan: not for a run
+    # with other plan options or an autotuned plan
+    default_plan = not (w.config.get("plan_options") or w.config.get("autotune"))
+    tr = load_traffic_record(w.name) if default_plan else None
     roof = dict(bound=w.bound, achieved=round(achieved, 2), peak=w.peak, unit=w.unit, frac=round(achieved / w.peak, 4),
                 traffic=None if tr is None else tr.get("bytes_per_launch"),
                 kernel_ms=round(launch_ms, 5), algorithmic_bytes_per_launch=int(per_launch_bytes),
