@@ -24,6 +24,7 @@ from .oracle import (  # noqa: F401
     bsr_spmv,
     csr_to_wcsr,
     wcsr_spmm,
+    wcsr_tasks,
     row_profile,
     sell_build,
     sell_spmv,

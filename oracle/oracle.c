@@ -557,6 +557,47 @@ void oracle_wcsr_spmm(int64_t m, int64_t H, const int32_t* window_ptr, const int
 }
 
 /* ------------------------------------------------------------------------ */
+/* WCSR task split ([ASYNC] §4.2: a window whose compressed columns exceed a  */
+/* threshold is cut along its columns into pieces of a fixed width, and a     */
+/* workgroup is launched per piece; each piece names its window, its first    */
+/* compressed column and its width).  A window of c <= T columns is one task  */
+/* covering [window_ptr[w], window_ptr[w+1]); a window of c > T columns is    */
+/* ceil(c / T) tasks of T columns each, the last one shorter.  Tasks are      */
+/* numbered window by window.  The tasks of the split windows take partial    */
+/* slots 0, 1, 2, ... in task order; a task of an unsplit window has slot -1.  */
+/* tasks[4k .. 4k+3] = {window, first column, end column, slot};              */
+/* winfo[2w], winfo[2w+1] = first slot of window w (-1 if not split), tasks. */
+/* Returns the number of tasks and stores the number of slots in *nslots;     */
+/* with tasks == NULL and winfo == NULL it only counts.                       */
+/* ------------------------------------------------------------------------ */
+int64_t oracle_wcsr_tasks(int64_t nw, const int32_t* window_ptr, int64_t T, int32_t* tasks, int32_t* winfo,
+                          int64_t* nslots)
+{
+    int64_t k = 0, slot = 0;
+    for (int64_t w = 0; w < nw; ++w) {
+        int64_t q0 = window_ptr[w], q1 = window_ptr[w + 1];
+        int64_t c = q1 - q0;
+        int64_t nt = c <= T ? 1 : (c + T - 1) / T;
+        if (winfo) {
+            winfo[2 * w] = nt > 1 ? (int32_t)slot : -1;
+            winfo[2 * w + 1] = (int32_t)nt;
+        }
+        for (int64_t t = 0; t < nt; ++t, ++k) {
+            if (!tasks) continue;
+            int64_t b = nt > 1 ? q0 + t * T : q0;
+            int64_t e = nt > 1 ? (b + T < q1 ? b + T : q1) : q1;
+            tasks[4 * k] = (int32_t)w;
+            tasks[4 * k + 1] = (int32_t)b;
+            tasks[4 * k + 2] = (int32_t)e;
+            tasks[4 * k + 3] = nt > 1 ? (int32_t)(slot + t) : -1;
+        }
+        if (nt > 1) slot += nt;
+    }
+    *nslots = slot;
+    return k;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Row-length profile ([GEN] §4 dispatch key: average, p95 and maximum row    */
 /* length and the coefficient of variation; [LSMR] §5.3: l_i = row_ptr[i+1] - */
 /* row_ptr[i], its mean, variance and tail).  Percentiles use the nearest-    */

@@ -82,6 +82,8 @@ def _declare(lib):
     lib.oracle_csr_to_wcsr_count.restype = _i64
     lib.oracle_csr_to_wcsr_fill.argtypes = [_i64, _p, _p, _p, _i64, _p, _p, _p]
     lib.oracle_csr_to_wcsr_fill.restype = None
+    lib.oracle_wcsr_tasks.argtypes = [_i64, _p, _i64, _p, _p, ctypes.POINTER(_i64)]
+    lib.oracle_wcsr_tasks.restype = _i64
     lib.oracle_wcsr_spmm.argtypes = [_i64, _i64, _p, _p, _p, _i64, _p, _i64, _d, _d, _p, _i64, _p, _p]
     lib.oracle_wcsr_spmm.restype = None
     lib.oracle_row_profile.argtypes = [_i64, _p, _p]
@@ -291,6 +293,20 @@ def csr_to_wcsr(m, n, row_ptr, col, val, H, pad):
     lib.oracle_csr_to_wcsr_fill(m, _ptr(row_ptr), _ptr(col), _ptr(val), H, _ptr(window_ptr), _ptr(window_col),
                                 _ptr(values))
     return window_ptr, window_col, values
+
+
+def wcsr_tasks(window_ptr, task_cols):
+    """Task split of the windows: (tasks int32[T, 4] = {window, first column, end
+    column, slot or -1}, winfo int32[nw, 2] = {first slot or -1, tasks}, slots)."""
+    lib = _load()
+    window_ptr = _c(window_ptr, np.int32)
+    nw = window_ptr.size - 1
+    slots = ctypes.c_int64()
+    T = lib.oracle_wcsr_tasks(nw, _ptr(window_ptr), int(task_cols), None, None, ctypes.byref(slots))
+    tasks = np.empty((T, 4), np.int32)
+    winfo = np.empty((nw, 2), np.int32)
+    lib.oracle_wcsr_tasks(nw, _ptr(window_ptr), int(task_cols), _ptr(tasks), _ptr(winfo), ctypes.byref(slots))
+    return tasks, winfo, slots.value
 
 
 def wcsr_spmm(m, H, window_ptr, window_col, values, B, alpha=1.0, beta=0.0, C=None):

@@ -541,3 +541,63 @@ def test_csr_to_wcsr_brute_force(case, H, pad, seed):
     C, sc = oracle.wcsr_spmm(m, H, wp, wc, vals, B, alpha, beta, C0)
     np.testing.assert_array_equal(C, alpha * (d32.astype(np.float64) @ B) + beta * C0)
     np.testing.assert_array_equal(sc, abs(alpha) * (np.abs(d32).astype(np.float64) @ np.abs(B)) + abs(beta) * np.abs(C0))
+
+
+# --------------------------------------------------------------------------
+# WCSR task split ([ASYNC] §4.2)
+# --------------------------------------------------------------------------
+def test_wcsr_tasks_hand_derivation():
+    # windows of 40, 0, 1060, 60, 1540, 512 and 513 compressed columns, T = 512:
+    # 1060 -> 512 + 512 + 36, 1540 -> 512 * 3 + 4, 512 stays whole, 513 -> 512 + 1
+    wp = [0, 40, 40, 1100, 1160, 2700, 3212, 3725]
+    tasks, winfo, slots = oracle.wcsr_tasks(np.array(wp, np.int32), 512)
+    assert tasks.tolist() == [[0, 0, 40, -1], [1, 40, 40, -1],
+                              [2, 40, 552, 0], [2, 552, 1064, 1], [2, 1064, 1100, 2],
+                              [3, 1100, 1160, -1],
+                              [4, 1160, 1672, 3], [4, 1672, 2184, 4], [4, 2184, 2696, 5], [4, 2696, 2700, 6],
+                              [5, 2700, 3212, -1],
+                              [6, 3212, 3724, 7], [6, 3724, 3725, 8]]
+    assert winfo.tolist() == [[-1, 1], [-1, 1], [0, 3], [-1, 1], [3, 4], [-1, 1], [7, 2]]
+    assert slots == 9
+    tasks, winfo, slots = oracle.wcsr_tasks(np.zeros(1, np.int32), 32)
+    assert tasks.shape == (0, 4) and winfo.shape == (0, 2) and slots == 0
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.lists(st.integers(0, 300), min_size=1, max_size=40), st.sampled_from([1, 3, 32, 64]),
+       st.integers(0, 2 ** 31 - 1))
+def test_wcsr_tasks_cover_each_window_once(widths, T, seed):
+    wp = np.concatenate([[0], np.cumsum(widths)]).astype(np.int32)
+    tasks, winfo, slots = oracle.wcsr_tasks(wp, T)
+    nw = len(widths)
+    # tasks run window by window; each window's tasks tile its range in order
+    k = 0
+    next_slot = 0
+    for w in range(nw):
+        c = widths[w]
+        nt = 1 if c <= T else -(-c // T)
+        mine = tasks[k:k + nt]
+        assert (mine[:, 0] == w).all()
+        assert mine[0, 1] == wp[w] and mine[-1, 2] == wp[w + 1]
+        assert (mine[1:, 1] == mine[:-1, 2]).all()
+        if nt == 1:
+            assert mine[0, 3] == -1 and winfo[w].tolist() == [-1, 1]
+        else:
+            assert ((mine[:, 2] - mine[:, 1]) <= T).all() and ((mine[:-1, 2] - mine[:-1, 1]) == T).all()
+            assert mine[-1, 2] - mine[-1, 1] >= 1
+            assert mine[:, 3].tolist() == list(range(next_slot, next_slot + nt))
+            assert winfo[w].tolist() == [next_slot, nt]
+            next_slot += nt
+        k += nt
+    assert k == len(tasks) and slots == next_slot
+    # the sum of the tasks' partial products is the product of the whole window
+    rng = np.random.default_rng(seed)
+    total = int(wp[-1])
+    H, N = 3, 2
+    vals = rng.integers(-3, 4, size=(total, H)).astype(np.float64)
+    Bq = rng.integers(-3, 4, size=(total, N)).astype(np.float64)  # B row of each compressed column
+    whole = np.stack([vals[wp[w]:wp[w + 1]].T @ Bq[wp[w]:wp[w + 1]] for w in range(nw)])
+    parts = np.zeros_like(whole)
+    for w, b, e, _ in tasks:
+        parts[w] += vals[b:e].T @ Bq[b:e]
+    np.testing.assert_array_equal(parts, whole)
