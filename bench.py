@@ -12,7 +12,8 @@ workload, each timed in this run the same way:
   spmv_uniform (4096^2, rows of 1..16 entries), stencil27 (u <- A v - a u,
   v <- A^T u - b v per step through the CSR and the CSC), spmm_lognormal_N8 /
   _N32 / _N128, bsr_blocks (bf16 64 x 64 blocks on MFMA), and the extra paths
-  bsr_spmv (fp32 64 x 64 blocks) and spmm_clustered_N32 (windowed rows).
+  bsr_spmv (fp32 64 x 64 blocks), spmm_clustered_N32 (windowed rows) and
+  spmm_skewed_N32 (windowed rows of very different widths, task split).
 --config NAME runs only that workload (as the headline), for profiling.
 
 CPU baseline ("cpu_baseline" of each record): the oracle (plain C, fp64
@@ -35,9 +36,12 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 METRIC = "SpMV/SpMM GFLOP/s + achieved HBM GB/s vs MI355X peak (fp32), 1 GPU"
 HEADLINE = "spmv_powerlaw"
+# compressed columns per task of the skewed-window SpMM (a window of more is
+# split); tasks run widest first
+SKEWED_TASK_COLS = 2048
 # every workload of a default run, in order (the headline first)
 ALL_WORKLOADS = ["spmv_powerlaw", "spmv_uniform", "stencil27", "spmm_lognormal_N8", "spmm_lognormal_N32",
-                 "spmm_lognormal_N128", "bsr_blocks", "bsr_spmv", "spmm_clustered_N32"]
+                 "spmm_lognormal_N128", "bsr_blocks", "bsr_spmv", "spmm_clustered_N32", "spmm_skewed_N32"]
 # Sources whose code decides the kernels each workload runs (a committed
 # traffic summary is used only while these are unchanged).
 _CSRC = "spmm_csr_spmv_amd/csrc/"
@@ -120,7 +124,7 @@ def block_index_bytes_per_value(bs, idx_bytes=4):
 def kernel_family(workload):
     if workload == "bsr_spmv":
         return "bsr_spmv"
-    if workload.startswith("spmm_clustered"):
+    if workload.startswith("spmm_clustered") or workload.startswith("spmm_skewed"):
         return "wcsr"
     return "bsr" if workload.startswith("bsr") else ("spmm" if workload.startswith("spmm") else "spmv")
 
@@ -154,7 +158,7 @@ def load_traffic(workload, launches_bytes=None):
 
 def parse_workload(name):
     """'spmm_lognormal_N32' -> ('spmm_lognormal', 32); others -> (name, None)."""
-    for base in ("spmm_lognormal", "spmm_clustered"):
+    for base in ("spmm_lognormal", "spmm_clustered", "spmm_skewed"):
         if name.startswith(base + "_N"):
             return base, int(name[len(base) + 2:])
     return name, None
@@ -442,6 +446,70 @@ def prepare(name, args, opts):
                            2 * int(h_rp[hi]) * N, spmm_bytes(m, n, nnz, N) * int(h_rp[hi]) / max(1, nnz),
                            "rows [0, %d) of %d of C = A B over the CSR (fp64 accumulation)" % (hi, m))
         w.keep = [rp, ci, vv, wp, wc, wv]
+        return w
+
+    if base == "spmm_skewed":
+        coo = gen.skewed_windows_coo(seed=0)
+        w.setup["generate_s"] = time.time() - t0
+        w.digest = _digest(coo.row, coo.col, coo.val)
+        m, n, nnz = coo.m, coo.n, coo.nnz
+        rp, ci, vv = _csr_from_coo(w, sp, torch, coo)
+        del coo
+        t1 = time.time()
+        wp, wc, wv, fill = sp.csr_to_wcsr(m, n, rp, ci, vv, pad=8)
+        torch.cuda.synchronize()
+        w.setup["csr_to_wcsr_ms"] = (time.time() - t1) * 1e3
+        total_cols = wc.numel()
+        T = SKEWED_TASK_COLS
+        t1 = time.time()
+        tasks = sp.wcsr_tasks(m, wp, total_cols, task_cols=T)
+        w.setup["wcsr_tasks_ms"] = (time.time() - t1) * 1e3
+        B = _to_dev(torch, gen.dense_matrix(n, N, 0))
+        C = torch.empty(m, N, device="cuda")
+        work = torch.empty(max(tasks.workspace_bytes(N), 1), dtype=torch.uint8, device="cuda")
+
+        def step():
+            sp.wcsr_spmm_tasks(m, n, tasks, wc, wv, 1.0, B, 0.0, C, work=work)
+
+        w.step, w.out_tensor = step, C
+        w.flops = 2 * nnz * N
+        w.nbytes = spmm_bytes(m, n, nnz, N)
+        w.launches = 1  # one library call: the task kernel and the partial sums
+        w.dtype = "f32"
+        widths = (wp[1:] - wp[:-1]).cpu().numpy()
+        w.config = dict(workload=name, M=m, K=n, nnz=nnz, N=N, window=64, compressed_columns=total_cols,
+                        window_fill=round(fill, 4), widest_window=int(widths.max()),
+                        median_window=float(np.median(widths)), task_cols=T, tasks=tasks.ntasks,
+                        partial_slots=tasks.nslots, partial_bytes=2 * tasks.workspace_bytes(N),
+                        mfma_flops=2 * total_cols * 64 * N,
+                        wcsr_bytes=4 * total_cols * 64 + 4 * total_cols + 4 * total_cols * N + 4 * m * N)
+        w.bound, w.peak, w.unit = "hbm", PEAK_HBM_GBS, "GB/s"
+        # the same product with one workgroup per window, and through the CSR
+        if not args.counter_run:
+            def ms_of(fn, reps=10):
+                for _ in range(2):
+                    fn()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                return round(e0.elapsed_time(e1) / reps, 5)
+
+            w.config["one_workgroup_per_window_ms"] = ms_of(lambda: sp.wcsr_spmm(m, n, wp, wc, wv, 1.0, B, 0.0, C))
+            plan_c = sp.Plan(m, n, rp, ci, vv, max_N=N)
+            w.config["csr_spmm_ms_same_matrix"] = ms_of(lambda: sp.spmm(plan_c, 1.0, B, 0.0, C))
+            del plan_c
+        if not args.no_cpu_baseline:
+            import oracle
+            h_rp, h_ci, h_vv = (t.cpu().numpy() for t in (rp, ci, vv))
+            Bh = B.cpu().numpy()
+            hi = _sample_rows(h_rp, 2 * N, args.cpu_sample_gflop * 1e9)
+            w.cpu = CpuLeg([(h_rp, hi, lambda lo, h: oracle.spmm(h_rp, h_ci, h_vv, Bh, rows=np.arange(lo, h)))],
+                           2 * int(h_rp[hi]) * N, spmm_bytes(m, n, nnz, N) * int(h_rp[hi]) / max(1, nnz),
+                           "rows [0, %d) of %d of C = A B over the CSR (fp64 accumulation)" % (hi, m))
+        w.keep = [rp, ci, vv, wp, wc, wv, tasks.table, work]
         return w
 
     # CSR workloads through a plan
@@ -1113,8 +1181,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default=None, choices=ALL_WORKLOADS + ["spmm_lognormal", "spmm_clustered"],
-                    help="run only this workload (spmm_lognormal / spmm_clustered take --N)")
+    ap.add_argument("--config", default=None,
+                    choices=ALL_WORKLOADS + ["spmm_lognormal", "spmm_clustered", "spmm_skewed"],
+                    help="run only this workload (spmm_lognormal / spmm_clustered / spmm_skewed take --N)")
     ap.add_argument("--N", type=int, default=32, help="right-hand-side columns for --config spmm_lognormal")
     ap.add_argument("--graph-batch", type=int, default=-1,
                     help="steps per replay of a captured HIP graph in the timed region (0: one plain launch per "
@@ -1185,7 +1254,7 @@ def main():
     stream = torch.cuda.current_stream()
     if args.config is None:
         names = ALL_WORKLOADS
-    elif args.config in ("spmm_lognormal", "spmm_clustered"):
+    elif args.config in ("spmm_lognormal", "spmm_clustered", "spmm_skewed"):
         names = ["%s_N%d" % (args.config, args.N)]
     else:
         names = [args.config]

@@ -20,6 +20,7 @@ from .workloads import (  # noqa: F401
     block_sparse_bsr,
     block_sparse_coo,
     clustered_coo,
+    skewed_windows_coo,
     bf16_matrix,
     ragged_coo,
     dense_vector,

@@ -257,6 +257,32 @@ def clustered_coo(m=1 << 20, n=1 << 20, H=64, pool=128, mu=2.5, sigma=1.0, seed=
     return Coo(m, n, row, col, val)
 
 
+def skewed_windows_coo(m=1 << 20, n=1 << 20, H=64, pool_median=64, pool_sigma=1.5, pool_max=16384,
+                       frac=(0.05, 0.3), seed=0):
+    """Windows of H rows whose column pools vary widely in size: window w
+    draws P_w = floor(pool_median * exp(pool_sigma Z)) clipped to [1,
+    pool_max] columns uniformly from [0, n) (with replacement, duplicates
+    dropped, so at most P_w distinct); every row of the window draws a rate
+    f in U[frac) and keeps each pool column with probability f; values
+    U[-1, 1].  Rows come out sorted by column."""
+    rng = _rng(seed, 80)
+    nw = (m + H - 1) // H
+    sizes = np.clip(np.floor(pool_median * np.exp(pool_sigma * rng.standard_normal(nw))), 1, pool_max)
+    rows, cols = [], []
+    for w in range(nw):
+        r0, r1 = w * H, min(m, w * H + H)
+        pool = np.unique(rng.integers(0, n, size=int(sizes[w])))
+        f = rng.uniform(frac[0], frac[1], size=r1 - r0)
+        keep = rng.random((r1 - r0, pool.size)) < f[:, None]
+        rr, pp = np.nonzero(keep)
+        rows.append((rr + r0).astype(np.int32))
+        cols.append(pool[pp].astype(np.int32))
+    row = np.concatenate(rows) if rows else np.zeros(0, np.int32)
+    col = np.concatenate(cols) if cols else np.zeros(0, np.int32)
+    val = _rng(seed, 81).uniform(-1.0, 1.0, size=row.size).astype(np.float32)
+    return Coo(m, n, row, col, val)
+
+
 def bf16_matrix(rows, cols, seed, stream=51, std=1.0):
     """bf16 (uint16 bits) matrix with N(0, std) entries."""
     a = _rng(seed, stream).normal(0.0, std, size=(rows, cols)).astype(np.float32)

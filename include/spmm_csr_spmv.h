@@ -456,6 +456,52 @@ int wcsr_spmm(int64_t m, int64_t n, const int32_t* window_ptr, const int32_t* wi
               int32_t N, float alpha, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
               void* stream);
 
+/* Task split of the windowed SpMM ([ASYNC] §4.2): a window of more than
+ * task_cols compressed columns is cut into tasks of task_cols columns (the
+ * last one shorter); every other window is one task.  One workgroup per task
+ * and column tile of C, so a few very wide windows no longer hold the tail of
+ * the launch.  The tasks of a split window store partial tiles in slots of
+ * the caller's workspace, and a second kernel adds each split window's
+ * partials in task order and writes C.  The page adds the parts with
+ * atomics; here the order is fixed: results are reproducible, equal bit for
+ * bit to wcsr_spmm on windows that are not split, and within fp32 rounding
+ * of it on the others.
+ *
+ * wcsr_tasks_bufsize: bytes of the task table for m rows, total_cols
+ * compressed columns (from csr_to_wcsr_analyze) and task_cols, a positive
+ * multiple of 32.
+ * wcsr_tasks_build: reads window_ptr (device) back to the host, builds the
+ * task table there and writes it to `table` (device, caller-allocated,
+ * 16-byte aligned; built once per matrix, read-only afterwards); returns, on
+ * the host, the number of tasks and of partial slots.  Synchronises `stream`.
+ * SP_ERR_INDEX when window_ptr is not nondecreasing inside [0, total_cols].
+ * Table layout, nw = ceil(m / 64): int32 {tasks, slots, 0, split windows} at
+ * byte 0; int32 quadruples {window, first slot, tasks, 0} per split window,
+ * in window order, at byte 256; int32 quadruples {window, first column, end
+ * column, slot or -1} per task at byte 256 + 16 nw rounded up to a multiple
+ * of 256.  A split window's tasks take consecutive slots in column order,
+ * the split windows one after another in window order.  Tasks are stored
+ * widest first (end - first column decreasing; equal widths in window order,
+ * then column order): workgroups start roughly in index order, so the
+ * longest tasks start first and the short ones fill in behind them.
+ * wcsr_spmm_tasks_bufsize: workspace bytes of one call with nslots slots and
+ * N columns (nslots * 64 * N * 4; 0 when nslots == 0).
+ * wcsr_spmm_tasks: C = alpha * A B + beta * C as wcsr_spmm (same operands,
+ * layouts and requirements), over a table built for the same m; ntasks and
+ * nslots are the build's results.  work: device, 16-byte aligned, >=
+ * wcsr_spmm_tasks_bufsize() bytes, may be NULL when nslots == 0; its contents
+ * on entry do not matter, and calls that share one workspace must not
+ * overlap.  Never allocates, never synchronises.  A table that needs more
+ * slots than nslots makes the call write nothing.
+ */
+int wcsr_tasks_bufsize(int64_t m, int64_t total_cols, int32_t task_cols, size_t* bytes);
+int wcsr_tasks_build(int64_t m, const int32_t* window_ptr, int64_t total_cols, int32_t task_cols, void* table,
+                     size_t table_bytes, int64_t* ntasks, int64_t* nslots, void* stream);
+int wcsr_spmm_tasks_bufsize(int64_t nslots, int32_t N, size_t* bytes);
+int wcsr_spmm_tasks(int64_t m, int64_t n, const void* table, int64_t ntasks, int64_t nslots,
+                    const int32_t* window_col, const float* values, int32_t N, float alpha, const float* B,
+                    int64_t ldb, float beta, float* C, int64_t ldc, void* work, size_t work_bytes, void* stream);
+
 /* --------------------------------------------------------- BSR SpMM
  * [BCSR] §1 and [ASYNC] §2.2.1: block row pointer brow_ptr[mb+1], block column
  * index bcol[nnzb] (increasing within a block row), and the nnzb dense

@@ -25,6 +25,9 @@ from ._binding import (  # noqa: F401
     csr_to_csc,
     csr_to_wcsr,
     wcsr_spmm,
+    wcsr_spmm_tasks,
+    wcsr_tasks,
+    WcsrTasks,
     lib,
     options_dict,
     plan_options,

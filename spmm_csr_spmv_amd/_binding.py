@@ -32,7 +32,8 @@ EXPORTS = ("sp_status_string", "sp_version", "csr_build_from_coo_bufsize", "csr_
            "sp_plan_dispatch_key", "sp_tune_cache_store", "sp_tune_cache_lookup", "sp_tune_cache_clear",
            "sp_tune_cache_size", "sp_autotune_workspace_size", "sp_autotune_spmv", "csr_to_wcsr_bufsize",
            "csr_to_wcsr_analyze", "csr_to_wcsr_fill", "wcsr_spmm", "sp_plan_view_create",
-           "csr_build_from_coo_noalloc", "bsr_spmv_rowwise")
+           "csr_build_from_coo_noalloc", "bsr_spmv_rowwise", "wcsr_tasks_bufsize", "wcsr_tasks_build",
+           "wcsr_spmm_tasks_bufsize", "wcsr_spmm_tasks")
 
 
 class SparseError(RuntimeError):
@@ -118,6 +119,11 @@ def lib():
                                           ctypes.POINTER(ctypes.c_double), _p, _sz, _p]
         L.csr_to_wcsr_fill.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _i64, _p, _p, _p]
         L.wcsr_spmm.argtypes = [_i64, _i64, _p, _p, _p, _i32, _f, _p, _i64, _f, _p, _i64, _p]
+        L.wcsr_tasks_bufsize.argtypes = [_i64, _i64, _i32, ctypes.POINTER(_sz)]
+        L.wcsr_tasks_build.argtypes = [_i64, _p, _i64, _i32, _p, _sz, ctypes.POINTER(_i64), ctypes.POINTER(_i64), _p]
+        L.wcsr_spmm_tasks_bufsize.argtypes = [_i64, _i32, ctypes.POINTER(_sz)]
+        L.wcsr_spmm_tasks.argtypes = [_i64, _i64, _p, _i64, _i64, _p, _p, _i32, _f, _p, _i64, _f, _p, _i64, _p, _sz,
+                                      _p]
         _key = ctypes.POINTER(sp_dispatch_key)
         _opt = ctypes.POINTER(sp_plan_options)
         L.sp_plan_dispatch_key.argtypes = [_p, _i32, _i32, ctypes.c_uint64, _key]
@@ -299,6 +305,55 @@ def wcsr_spmm(m, n, window_ptr, window_col, values, alpha, B, beta, C, stream=No
         raise ValueError("shape mismatch")
     _check("wcsr_spmm", lib().wcsr_spmm(m, n, _ptr(window_ptr), _ptr(window_col), _ptr(values), N, float(alpha),
                                         _ptr(B), N, float(beta), _ptr(C), N, _stream(stream)))
+    return C
+
+
+class WcsrTasks:
+    """Task table of a windowed matrix (windows of more than task_cols compressed
+    columns cut into tasks of task_cols); built once, read-only afterwards."""
+
+    def __init__(self, m, table, ntasks, nslots, task_cols):
+        self.m, self.table, self.ntasks, self.nslots, self.task_cols = m, table, ntasks, nslots, task_cols
+
+    def workspace_bytes(self, N):
+        size = _sz()
+        _check("wcsr_spmm_tasks_bufsize", lib().wcsr_spmm_tasks_bufsize(self.nslots, int(N), ctypes.byref(size)))
+        return size.value
+
+
+def wcsr_tasks(m, window_ptr, total_cols, task_cols=2048, stream=None):
+    """Builds the task table of a WCSR matrix (synchronises once)."""
+    L = lib()
+    _dev(window_ptr, torch.int32, "window_ptr")
+    size = _sz()
+    _check("wcsr_tasks_bufsize", L.wcsr_tasks_bufsize(m, int(total_cols), int(task_cols), ctypes.byref(size)))
+    with _on(stream):
+        table = _workspace(size.value, window_ptr.device)
+    ntasks, nslots = _i64(), _i64()
+    _check("wcsr_tasks_build",
+           L.wcsr_tasks_build(m, _ptr(window_ptr), int(total_cols), int(task_cols), _ptr(table), size.value,
+                              ctypes.byref(ntasks), ctypes.byref(nslots), _stream(stream)))
+    return WcsrTasks(m, table, ntasks.value, nslots.value, int(task_cols))
+
+
+def wcsr_spmm_tasks(m, n, tasks, window_col, values, alpha, B, beta, C, work=None, stream=None):
+    """C = alpha * A B + beta * C over a task table from wcsr_tasks; `work` is a uint8
+    device tensor of at least tasks.workspace_bytes(N) bytes (allocated when None)."""
+    _dev(window_col, torch.int32, "window_col"), _dev(values, torch.float32, "values")
+    _dev(B, torch.float32, "B"), _dev(C, torch.float32, "C")
+    N = B.shape[1]
+    if B.shape[0] != n or C.shape[0] != m or C.shape[1] != N or tasks.m != m:
+        raise ValueError("shape mismatch")
+    need = tasks.workspace_bytes(N)
+    if work is None:
+        with _on(stream):
+            work = _workspace(need, C.device)
+    elif work.numel() * work.element_size() < need:
+        raise ValueError("workspace of %d bytes, %d needed" % (work.numel() * work.element_size(), need))
+    _check("wcsr_spmm_tasks",
+           lib().wcsr_spmm_tasks(m, n, _ptr(tasks.table), tasks.ntasks, tasks.nslots, _ptr(window_col),
+                                 _ptr(values), N, float(alpha), _ptr(B), N, float(beta), _ptr(C), N, _ptr(work),
+                                 need, _stream(stream)))
     return C
 
 

@@ -1039,6 +1039,64 @@ int wcsr_spmm(int64_t m, int64_t n, const int32_t* window_ptr, const int32_t* wi
                                  (hipStream_t)stream);
 }
 
+static int wcsr_task_args(int64_t m, int64_t total_cols, int32_t task_cols) {
+    if (m < 0 || m > kI32Max || total_cols < 0 || total_cols > kI32Max) return SP_ERR_SIZE;
+    if (task_cols < 32 || task_cols % 32 != 0) return SP_ERR_UNSUPPORTED;
+    return SP_OK;
+}
+
+int wcsr_tasks_bufsize(int64_t m, int64_t total_cols, int32_t task_cols, size_t* bytes) {
+    if (!bytes) return SP_ERR_NULL;
+    const int rc = wcsr_task_args(m, total_cols, task_cols);
+    if (rc) return rc;
+    *bytes = spx::wcsr_task_table_bytes(m, total_cols, task_cols);
+    return SP_OK;
+}
+
+int wcsr_tasks_build(int64_t m, const int32_t* window_ptr, int64_t total_cols, int32_t task_cols, void* table,
+                     size_t table_bytes, int64_t* ntasks, int64_t* nslots, void* stream) {
+    const int rc = wcsr_task_args(m, total_cols, task_cols);
+    if (rc) return rc;
+    if (!ntasks || !nslots) return SP_ERR_NULL;
+    *ntasks = *nslots = 0;
+    if (m == 0) return SP_OK;
+    if (!window_ptr || !table) return SP_ERR_NULL;
+    if (table_bytes < spx::wcsr_task_table_bytes(m, total_cols, task_cols)) return SP_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(table) & 15) return SP_ERR_UNSUPPORTED;
+    int32_t head[4] = {0, 0, 0, 0};
+    const int r = spx::wcsr_tasks_build_device(m, window_ptr, total_cols, task_cols, table, (hipStream_t)stream, head);
+    if (r != SP_OK) return r;
+    *ntasks = head[0];
+    *nslots = head[1];
+    return SP_OK;
+}
+
+int wcsr_spmm_tasks_bufsize(int64_t nslots, int32_t N, size_t* bytes) {
+    if (!bytes) return SP_ERR_NULL;
+    if (nslots < 0 || nslots > kI32Max || N < 0) return SP_ERR_SIZE;
+    *bytes = spx::wcsr_spmm_tasks_work_bytes(nslots, N);
+    return SP_OK;
+}
+
+int wcsr_spmm_tasks(int64_t m, int64_t n, const void* table, int64_t ntasks, int64_t nslots,
+                    const int32_t* window_col, const float* values, int32_t N, float alpha, const float* B,
+                    int64_t ldb, float beta, float* C, int64_t ldc, void* work, size_t work_bytes, void* stream) {
+    int rc = check_dims(m, n, 0);
+    if (rc) return rc;
+    if (N < 0 || ldb < N || ldc < N) return SP_ERR_SIZE;
+    if (m == 0 || N == 0) return SP_OK;
+    // every window is at least one task
+    if (ntasks < (m + 63) / 64 || ntasks > kI32Max || nslots < 0 || nslots > kI32Max) return SP_ERR_SIZE;
+    if (!table || !C || (n > 0 && !B) || (nslots > 0 && !work)) return SP_ERR_NULL;
+    if (work_bytes < spx::wcsr_spmm_tasks_work_bytes(nslots, N)) return SP_ERR_WORKSPACE;
+    if (N % 4 != 0 || ldb % 4 != 0) return SP_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(B) & 15) || (reinterpret_cast<uintptr_t>(values) & 15) ||
+        (reinterpret_cast<uintptr_t>(table) & 15) || (reinterpret_cast<uintptr_t>(work) & 15))
+        return SP_ERR_UNSUPPORTED;
+    return spx::wcsr_spmm_tasks_device(m, table, ntasks, nslots, window_col, values, N, B, ldb, alpha, beta, C, ldc,
+                                       work, (hipStream_t)stream);
+}
+
 // ------------------------------------------------------------------ BSR
 int bsr_spmm_bufsize(int64_t mb, int64_t kb, int32_t bs, int64_t nnzb, int32_t N, size_t* bytes) {
     if (!bytes) return SP_ERR_NULL;

@@ -160,6 +160,16 @@ int csr_to_wcsr_fill_device(int64_t m, int64_t n, const int32_t* row_ptr, const 
 int wcsr_spmm_device(int64_t m, const int32_t* window_ptr, const int32_t* window_col, const float* values,
                      int32_t N, const float* B, int64_t ldb, float alpha, float beta, float* C, int64_t ldc,
                      hipStream_t s);
+// Task split of the windowed SpMM: the task table (built on the host once per
+// matrix, synchronises) and the product over it; head_host receives {tasks,
+// slots, 0, split windows}.
+size_t wcsr_task_table_bytes(int64_t m, int64_t total_cols, int32_t task_cols);
+int wcsr_tasks_build_device(int64_t m, const int32_t* window_ptr, int64_t total_cols, int32_t task_cols, void* table,
+                            hipStream_t s, int32_t* head_host);
+size_t wcsr_spmm_tasks_work_bytes(int64_t nslots, int32_t N);
+int wcsr_spmm_tasks_device(int64_t m, const void* table, int64_t ntasks, int64_t nslots, const int32_t* window_col,
+                           const float* values, int32_t N, const float* B, int64_t ldb, float alpha, float beta,
+                           float* C, int64_t ldc, void* work, hipStream_t s);
 
 // Plan option validation (api.cpp); dispatch key and tuning cache (tune.cpp).
 int check_plan_options(const sp_plan_options& o);

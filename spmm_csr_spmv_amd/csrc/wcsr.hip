@@ -24,10 +24,15 @@
 // v_mfma_f32_32x32x2_f32 on its 32 x 32 part of the tile (fp32 in, fp32
 // accumulate: the products are the plain fp32 ones of the CSR kernels, only
 // the order of the sum differs).  The next chunk is loaded into registers
-// while the current one is multiplied.  The page splits large windows into
-// tasks and adds their parts with atomics; here a window is one workgroup and
-// the many windows of a matrix balance the GPU, so every output is written
-// once and the result is reproducible.
+// while the current one is multiplied.  wcsr_spmm_device runs one workgroup
+// per window: with many windows of similar width the dispatcher balances the
+// GPU and every output is written once.  For windows of very different
+// widths, the task split below cuts the wide ones into tasks, as the page
+// does, but adds their parts in a fixed order instead of with atomics.
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
 #include "device_common.h"
 
 namespace spx {
@@ -173,21 +178,15 @@ __device__ __forceinline__ void store_chunk(const Chunk<NT>& c, float* As, float
 }
 
 // Waves: 2, 4 or 8 (NT = 32, 64, 128); wave v owns rows 32 (v % 2) .. +32
-// and columns 32 (v / 2) .. +32 of the tile.
+// and columns 32 (v / 2) .. +32 of the tile.  Compressed columns [q0, q1) of
+// window w times the B tile starting at column n0, summed chunk by chunk in
+// column order.
 template <int NT>
-__global__ __launch_bounds__(4 * NT) void wcsr_spmm_kernel(int64_t m, int64_t nw, const int32_t* __restrict__ window_ptr,
-                                                           const int32_t* __restrict__ window_col,
-                                                           const float* __restrict__ values, int32_t N,
-                                                           const float* __restrict__ B, int64_t ldb, float alpha,
-                                                           float beta, float* __restrict__ C, int64_t ldc) {
-    // As[k][r], Bs[k][c]: chunk column k (32) by window row r (64) / tile column c (NT)
-    __shared__ __attribute__((aligned(16))) float As[kKc * kWin];
-    __shared__ __attribute__((aligned(16))) float Bs[kKc * NT];
-    const int64_t w = blockIdx.x;
-    const int n0 = blockIdx.y * NT;
+__device__ __forceinline__ f32x16 window_tile(int q0, int q1, int n0, const int32_t* __restrict__ window_col,
+                                              const float* __restrict__ values, int32_t N,
+                                              const float* __restrict__ B, int64_t ldb, float* As, float* Bs) {
     const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int wr = 32 * (wv & 1), wc = 32 * (wv >> 1);
-    const int q0 = window_ptr[w], q1 = window_ptr[w + 1];
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
@@ -206,18 +205,113 @@ __global__ __launch_bounds__(4 * NT) void wcsr_spmm_kernel(int64_t m, int64_t nw
         }
         __syncthreads();
     }
-    // D layout of the 32 x 32 MFMA: lane l, register r -> row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
-    const int col = n0 + wc + (l & 31);
+    return acc;
+}
+
+// D layout of the 32 x 32 MFMA: lane l, register r -> row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+__device__ __forceinline__ int tile_row(int r) {
+    const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    return 32 * (wv & 1) + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+}
+__device__ __forceinline__ int tile_col(int n0) {
+    const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    return n0 + 32 * (wv >> 1) + (l & 31);
+}
+
+template <int NT>
+__global__ __launch_bounds__(4 * NT) void wcsr_spmm_kernel(int64_t m, int64_t nw, const int32_t* __restrict__ window_ptr,
+                                                           const int32_t* __restrict__ window_col,
+                                                           const float* __restrict__ values, int32_t N,
+                                                           const float* __restrict__ B, int64_t ldb, float alpha,
+                                                           float beta, float* __restrict__ C, int64_t ldc) {
+    // As[k][r], Bs[k][c]: chunk column k (32) by window row r (64) / tile column c (NT)
+    __shared__ __attribute__((aligned(16))) float As[kKc * kWin];
+    __shared__ __attribute__((aligned(16))) float Bs[kKc * NT];
+    const int64_t w = blockIdx.x;
+    const int n0 = blockIdx.y * NT;
+    const f32x16 acc = window_tile<NT>(window_ptr[w], window_ptr[w + 1], n0, window_col, values, N, B, ldb, As, Bs);
+    const int col = tile_col(n0);
     if (col >= N) return;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int64_t row = w * kWin + wr + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+        const int64_t row = w * kWin + tile_row(r);
         if (row < m) {
             float* cp = C + row * ldc + col;
             float o = alpha * acc[r];
             if (beta != 0.0f) o = fmaf(beta, *cp, o);
             *cp = o;
         }
+    }
+}
+
+// ---- task split ([ASYNC] §4.2).  A window of more than `task_cols`
+// compressed columns is cut into tasks of task_cols columns (the last one
+// shorter), one workgroup each.  Each task of such a window stores its
+// partial tile in a slot of its own; a second kernel adds a split window's
+// partials in task order and writes C.  The page adds the parts with atomics;
+// here the order of the sum is fixed, so results are reproducible.  The
+// kernel boundary orders the partial stores before their reads: a
+// completion counter inside one kernel would need a device-scope release per
+// task (an L2 write-back), which costs more than the second launch.  The
+// task table is built on the host, once per matrix (wcsr_tasks_build_device).
+
+// One workgroup per (task, column tile).  head = {tasks, slots, -, -} of the
+// table: a workgroup past the table's tasks, or every workgroup when the
+// table needs more slots than `slots`, writes nothing.
+template <int NT>
+__global__ __launch_bounds__(4 * NT) void wcsr_task_kernel(int64_t m, const int32_t* __restrict__ head, int64_t slots,
+                                                           const int4* __restrict__ tasks, float* __restrict__ partials,
+                                                           const int32_t* __restrict__ window_col,
+                                                           const float* __restrict__ values, int32_t N,
+                                                           const float* __restrict__ B, int64_t ldb, float alpha,
+                                                           float beta, float* __restrict__ C, int64_t ldc) {
+    __shared__ __attribute__((aligned(16))) float As[kKc * kWin];
+    __shared__ __attribute__((aligned(16))) float Bs[kKc * NT];
+    if ((int)blockIdx.x >= head[0] || head[1] > slots) return;
+    const int4 t = tasks[blockIdx.x];
+    const int64_t w = t.x;
+    const int n0 = blockIdx.y * NT;
+    const f32x16 acc = window_tile<NT>(t.y, t.z, n0, window_col, values, N, B, ldb, As, Bs);
+    const int col = tile_col(n0);
+    if (col >= N) return;
+    if (t.w < 0) {  // the window's only task: as the one-workgroup-per-window kernel
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t row = w * kWin + tile_row(r);
+            if (row < m) {
+                float* cp = C + row * ldc + col;
+                float o = alpha * acc[r];
+                if (beta != 0.0f) o = fmaf(beta, *cp, o);
+                *cp = o;
+            }
+        }
+    } else {  // slot t.w: 64 rows x N columns, row-major
+        float* p = partials + (int64_t)t.w * kWin * N + col;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[(int64_t)tile_row(r) * N] = acc[r];
+    }
+}
+
+// One workgroup per split window (the grid is a bound: head[3] of them are
+// real): C = alpha * (sum of the window's partial tiles in task order) + beta C.
+__global__ __launch_bounds__(kBlock) void wcsr_partials_reduce_kernel(int64_t m, const int32_t* __restrict__ head,
+                                                                      int64_t slots, const int4* __restrict__ splits,
+                                                                      const float* __restrict__ partials, int32_t N,
+                                                                      float alpha, float beta, float* __restrict__ C,
+                                                                      int64_t ldc) {
+    if ((int)blockIdx.x >= head[3] || head[1] > slots) return;
+    const int4 sp = splits[blockIdx.x];  // {window, first slot, tasks, 0}
+    const int64_t tile = (int64_t)kWin * N;
+    const float* p0 = partials + (int64_t)sp.y * tile;
+    for (int64_t e = threadIdx.x; e < tile; e += kBlock) {
+        const int64_t row = (int64_t)sp.x * kWin + e / N;
+        if (row >= m) break;  // e grows: every later element is past m too
+        float s = p0[e];
+        for (int k = 1; k < sp.z; ++k) s += p0[k * tile + e];
+        float* cp = C + row * ldc + e % N;
+        float o = alpha * s;
+        if (beta != 0.0f) o = fmaf(beta, *cp, o);
+        *cp = o;
     }
 }
 
@@ -268,6 +362,107 @@ int wcsr_spmm_device(int64_t m, const int32_t* window_ptr, const int32_t* window
                            nw, window_ptr, window_col, values, N, B, ldb, alpha, beta, C, ldc);
     }
     return hipGetLastError() == hipSuccess ? SP_OK : SP_ERR_HIP;
+}
+
+// Task table in device memory: head {tasks, slots, 0, split windows} (256
+// B), splits int4[nw] {window, first slot, tasks, 0}, tasks int4[nw +
+// total_cols / task_cols] {window, first column, end column, slot or -1} (a
+// bound: a window of c columns has at most 1 + c / task_cols tasks).  Where
+// head, splits and tasks start depends on m alone.
+namespace {
+constexpr size_t kTaskHead = 256;
+size_t up256(size_t b) { return (b + 255) / 256 * 256; }
+int64_t task_bound(int64_t nw, int64_t total_cols, int32_t task_cols) { return nw + total_cols / task_cols; }
+struct TaskTable {
+    int32_t* head;
+    int4* splits;
+    int4* tasks;
+};
+TaskTable task_table(void* base, int64_t nw) {
+    char* p = static_cast<char*>(base);
+    return {reinterpret_cast<int32_t*>(p), reinterpret_cast<int4*>(p + kTaskHead),
+            reinterpret_cast<int4*>(p + kTaskHead + up256(16 * (size_t)nw))};
+}
+}  // namespace
+
+size_t wcsr_task_table_bytes(int64_t m, int64_t total_cols, int32_t task_cols) {
+    const int64_t nw = (m + kWin - 1) / kWin;
+    return kTaskHead + up256(16 * (size_t)nw) + up256(16 * (size_t)task_bound(nw, total_cols, task_cols));
+}
+
+// Windows of at most task_cols columns are one task; wider ones are cut into
+// tasks of task_cols columns, whose partial slots are numbered in window
+// order.  The tasks are then ordered widest first (equal widths in window and
+// column order): workgroups start roughly in index order, so the longest
+// tasks start first and the short ones fill in behind them.
+int wcsr_tasks_build_device(int64_t m, const int32_t* window_ptr, int64_t total_cols, int32_t task_cols, void* table,
+                            hipStream_t s, int32_t* head_host) {
+    const int64_t nw = (m + kWin - 1) / kWin;
+    std::vector<int32_t> wp((size_t)nw + 1);
+    if (hipMemcpyAsync(wp.data(), window_ptr, wp.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return SP_ERR_HIP;
+    for (int64_t w = 0; w < nw; ++w)
+        if (wp[w] < 0 || wp[w + 1] < wp[w] || wp[w + 1] > total_cols) return SP_ERR_INDEX;
+    std::vector<int4> tasks, splits;
+    tasks.reserve((size_t)task_bound(nw, total_cols, task_cols));
+    int32_t slots = 0;
+    for (int64_t w = 0; w < nw; ++w) {
+        const int32_t q0 = wp[w], q1 = wp[w + 1];
+        if (q1 - q0 <= task_cols) {
+            tasks.push_back(make_int4((int)w, q0, q1, -1));
+            continue;
+        }
+        const int32_t nt = (q1 - q0 + task_cols - 1) / task_cols;
+        splits.push_back(make_int4((int)w, slots, nt, 0));
+        for (int32_t t = 0; t < nt; ++t) {
+            const int64_t b = q0 + (int64_t)t * task_cols;
+            tasks.push_back(make_int4((int)w, (int)b, (int)std::min<int64_t>(b + task_cols, q1), slots + t));
+        }
+        slots += nt;
+    }
+    std::stable_sort(tasks.begin(), tasks.end(), [](const int4& a, const int4& b) { return a.z - a.y > b.z - b.y; });
+    const size_t tasks_at = kTaskHead + up256(16 * (size_t)nw);
+    std::vector<char> img(tasks_at + 16 * tasks.size(), 0);
+    const int32_t head[4] = {(int32_t)tasks.size(), slots, 0, (int32_t)splits.size()};
+    std::memcpy(img.data(), head, sizeof(head));
+    if (!splits.empty()) std::memcpy(img.data() + kTaskHead, splits.data(), 16 * splits.size());
+    if (!tasks.empty()) std::memcpy(img.data() + tasks_at, tasks.data(), 16 * tasks.size());
+    if (hipMemcpyAsync(table, img.data(), img.size(), hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return SP_ERR_HIP;
+    std::memcpy(head_host, head, sizeof(head));
+    return SP_OK;
+}
+
+size_t wcsr_spmm_tasks_work_bytes(int64_t nslots, int32_t N) { return (size_t)nslots * kWin * (size_t)N * sizeof(float); }
+
+int wcsr_spmm_tasks_device(int64_t m, const void* table, int64_t ntasks, int64_t nslots, const int32_t* window_col,
+                           const float* values, int32_t N, const float* B, int64_t ldb, float alpha, float beta,
+                           float* C, int64_t ldc, void* work, hipStream_t s) {
+    const int64_t nw = (m + kWin - 1) / kWin;
+    if (nw == 0 || N == 0) return SP_OK;
+    const TaskTable t = task_table(const_cast<void*>(table), nw);
+    const int NT = N <= 32 ? 32 : N <= 64 ? 64 : 128;
+    float* partials = static_cast<float*>(work);
+    const dim3 grid((unsigned)ntasks, (unsigned)((N + NT - 1) / NT));
+    if (NT == 32)
+        hipLaunchKernelGGL(wcsr_task_kernel<32>, grid, dim3(128), 0, s, m, t.head, nslots, t.tasks, partials,
+                           window_col, values, N, B, ldb, alpha, beta, C, ldc);
+    else if (NT == 64)
+        hipLaunchKernelGGL(wcsr_task_kernel<64>, grid, dim3(256), 0, s, m, t.head, nslots, t.tasks, partials,
+                           window_col, values, N, B, ldb, alpha, beta, C, ldc);
+    else
+        hipLaunchKernelGGL(wcsr_task_kernel<128>, grid, dim3(512), 0, s, m, t.head, nslots, t.tasks, partials,
+                           window_col, values, N, B, ldb, alpha, beta, C, ldc);
+    if (hipGetLastError() != hipSuccess) return SP_ERR_HIP;
+    // a split window has at least two slots: nslots / 2 bounds the split windows
+    if (nslots >= 2) {
+        hipLaunchKernelGGL(wcsr_partials_reduce_kernel, dim3((unsigned)(nslots / 2)), dim3(kBlock), 0, s, m, t.head,
+                           nslots, t.splits, partials, N, alpha, beta, C, ldc);
+        if (hipGetLastError() != hipSuccess) return SP_ERR_HIP;
+    }
+    return SP_OK;
 }
 
 }  // namespace spx

@@ -233,6 +233,40 @@ def test_wcsr_argument_errors():
     assert L.wcsr_spmm(10, 10, None, FAKE, FAKE, 8, 1.0, FAKE, 8, 0.0, FAKE, 8, None) == 1
 
 
+def test_wcsr_task_split_argument_errors():
+    L = sp.lib()
+    b = SZ()
+    nt, ns = ctypes.c_int64(), ctypes.c_int64()
+    assert L.wcsr_tasks_bufsize(100, 1000, 512, ctypes.byref(b)) == 0 and b.value > 0
+    assert L.wcsr_tasks_bufsize(100, 1000, 48, ctypes.byref(b)) == 5   # not a multiple of 32
+    assert L.wcsr_tasks_bufsize(100, 1000, 0, ctypes.byref(b)) == 5
+    assert L.wcsr_tasks_bufsize(100, -1, 32, ctypes.byref(b)) == 2
+    assert L.wcsr_tasks_bufsize(100, 1000, 32, None) == 1
+    assert L.wcsr_tasks_build(0, None, 0, 32, None, 0, ctypes.byref(nt), ctypes.byref(ns), None) == 0
+    assert (nt.value, ns.value) == (0, 0)
+    assert L.wcsr_tasks_build(100, None, 1000, 32, FAKE, 1 << 20, ctypes.byref(nt), ctypes.byref(ns), None) == 1
+    assert L.wcsr_tasks_build(100, FAKE, 1000, 32, FAKE, 16, ctypes.byref(nt), ctypes.byref(ns), None) == 4
+    assert L.wcsr_tasks_build(100, FAKE, 1000, 32, ctypes.c_void_p(0x1008), 1 << 20, ctypes.byref(nt),
+                              ctypes.byref(ns), None) == 5        # table not 16-byte aligned
+    assert L.wcsr_tasks_build(100, FAKE, 1000, 32, FAKE, 1 << 20, None, ctypes.byref(ns), None) == 1
+    assert L.wcsr_spmm_tasks_bufsize(0, 32, ctypes.byref(b)) == 0 and b.value == 0
+    assert L.wcsr_spmm_tasks_bufsize(3, 32, ctypes.byref(b)) == 0 and b.value >= 3 * 64 * 32 * 4
+    assert L.wcsr_spmm_tasks_bufsize(-1, 32, ctypes.byref(b)) == 2
+
+    def call(m=100, ntasks=2, nslots=0, N=8, ldb=8, table=FAKE, work=None, wbytes=0, B=FAKE):
+        return L.wcsr_spmm_tasks(m, 10, table, ntasks, nslots, FAKE, FAKE, N, 1.0, B, ldb, 0.0, FAKE, N, work,
+                                 wbytes, None)
+
+    assert call(m=0) == 0                       # no rows: no-op
+    assert call(N=6, ldb=6) == 5                # N % 4 != 0
+    assert call(ldb=4) == 2                     # ldb < N
+    assert call(ntasks=1) == 2                  # fewer tasks than the 2 windows of 100 rows
+    assert call(table=None) == 1
+    assert call(nslots=2) == 1                  # slots but no workspace
+    assert call(nslots=2, work=FAKE, wbytes=100) == 4
+    assert call(B=ctypes.c_void_p(0x1004)) == 5
+
+
 def test_view_argument_errors():
     L = sp.lib()
     v = ctypes.c_void_p()

@@ -88,6 +88,8 @@ def test_workload_names_and_cpu_row_ranges():
     import numpy as np
     assert bench.parse_workload("spmm_lognormal_N128") == ("spmm_lognormal", 128)
     assert bench.parse_workload("spmm_clustered_N32") == ("spmm_clustered", 32)
+    assert bench.parse_workload("spmm_skewed_N32") == ("spmm_skewed", 32)
+    assert bench.kernel_family("spmm_skewed_N32") == bench.kernel_family("spmm_clustered_N32") == "wcsr"
     assert bench.parse_workload("stencil27") == ("stencil27", None)
     assert bench.ALL_WORKLOADS[0] == bench.HEADLINE
     rp = np.array([0, 3, 3, 10, 12, 20], np.int64)

@@ -125,6 +125,24 @@ def test_wcsr_spmm_graph_replays():
     _replays_match(run, [C])
 
 
+def test_wcsr_spmm_tasks_graph_replays():
+    """The task-split windowed SpMM (counter clear and product) captured and replayed."""
+    say("graph replays, WCSR task split")
+    coo = gen.skewed_windows_coo(m=1500, n=40000, pool_median=48, pool_sigma=1.5, pool_max=4000, seed=3)
+    rp, c, v = sp.csr_build_from_coo(coo.m, coo.n, dev(coo.row), dev(coo.col), dev(coo.val))
+    wp, wc, vals, _ = sp.csr_to_wcsr(coo.m, coo.n, rp, c, v)
+    t = sp.wcsr_tasks(coo.m, wp, wc.numel(), task_cols=64)
+    assert t.nslots > 0
+    B = dev(gen.dense_matrix(coo.n, 32, 6))
+    C = torch.empty(coo.m, 32, device="cuda")
+    work = torch.empty(t.workspace_bytes(32), dtype=torch.uint8, device="cuda")
+
+    def run():
+        sp.wcsr_spmm_tasks(coo.m, coo.n, t, wc, vals, 1.0, B, 0.0, C, work=work)
+
+    _replays_match(run, [C])
+
+
 def test_view_products_graph_replays():
     """A view's products (its own scratch: split partials and counters, x-window
     products) captured and replayed like the plan's."""

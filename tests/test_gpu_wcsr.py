@@ -133,3 +133,154 @@ def test_clustered_workload_full():
     sp.wcsr_spmm(coo.m, coo.n, wp, wc, vals, 1.0, dev(B), 0.0, C)
     ref, scale = oracle.wcsr_spmm(coo.m, 64, ewp, ewc, evals, B)
     assert_close(host(C), ref, scale, what="wcsr_spmm full")
+
+
+# --------------------------------------------------------------------------
+# task split ([ASYNC] §4.2)
+# --------------------------------------------------------------------------
+def skewed():
+    return gen.skewed_windows_coo(m=1500, n=40000, pool_median=48, pool_sigma=1.5, pool_max=4000, seed=3)
+
+
+def task_case(name):
+    if name == "skewed":
+        if name not in _cache:
+            coo = skewed()
+            _cache[name] = (coo, oracle.coo_to_csr(coo.m, coo.n, coo.row, coo.col, coo.val))
+        return _cache[name]
+    return case(name)
+
+
+TASK_CASES = list(cases()) + ["skewed"]
+
+
+def table_parts(t, nw):
+    """(head, splits, tasks) read from the task table as the header lays it out."""
+    raw = host(t.table)
+    head = raw[:16].view(np.int32)
+    splits = raw[256:256 + 16 * int(head[3])].view(np.int32).reshape(-1, 4)
+    off = 256 + (16 * nw + 255) // 256 * 256
+    tasks = raw[off:off + 16 * t.ntasks].view(np.int32).reshape(-1, 4)
+    return head, splits, tasks
+
+
+@pytest.mark.parametrize("task_cols", [32, 96, 512])
+@pytest.mark.parametrize("name", TASK_CASES)
+def test_task_table_bit_exact(name, task_cols):
+    say("wcsr task table", name, task_cols)
+    coo, (rp, c, v) = task_case(name)
+    ewp, ewc, evals = oracle.csr_to_wcsr(coo.m, coo.n, rp, c, v, 64, 8)
+    etasks, ewinfo, eslots = oracle.wcsr_tasks(ewp, task_cols)
+    t = sp.wcsr_tasks(coo.m, dev(ewp), ewc.size, task_cols=task_cols)
+    assert (t.ntasks, t.nslots) == (len(etasks), eslots)
+    nw = ewp.size - 1
+    head, splits, tasks = table_parts(t, nw)
+    esplit = [[w, p, k, 0] for w, (p, k) in enumerate(ewinfo.tolist()) if p >= 0]
+    assert head.tolist() == [len(etasks), eslots, 0, len(esplit)]
+    assert splits.tolist() == esplit
+    # launch order: widest first, equal widths in the oracle's (window, column) order
+    order = np.argsort(-(etasks[:, 2] - etasks[:, 1]), kind="stable")
+    np.testing.assert_array_equal(tasks, etasks[order])
+
+
+@pytest.mark.parametrize("task_cols", [32, 512, 2048])
+@pytest.mark.parametrize("N", [4, 32, 100, 192])
+@pytest.mark.parametrize("name", TASK_CASES)
+def test_wcsr_spmm_tasks(name, N, task_cols):
+    say("wcsr_spmm_tasks", name, N, task_cols)
+    coo, (rp, c, v) = task_case(name)
+    ewp, ewc, evals = oracle.csr_to_wcsr(coo.m, coo.n, rp, c, v, 64, 8)
+    wp, wc, vals = dev(ewp), dev(ewc), dev(evals)
+    t = sp.wcsr_tasks(coo.m, wp, ewc.size, task_cols=task_cols)
+    _, ewinfo, _ = oracle.wcsr_tasks(ewp, task_cols)
+    whole = np.repeat(ewinfo[:, 0] < 0, 64)[:coo.m]  # rows of windows that are one task
+    B = gen.dense_matrix(coo.n, N, 3)
+    for alpha, beta in AB:
+        C0 = gen.dense_matrix(coo.m, N, 4)
+        C = dev(C0) if beta != 0.0 else torch.full((coo.m, N), float("nan"), device="cuda")
+        sp.wcsr_spmm_tasks(coo.m, coo.n, t, wc, vals, alpha, dev(B), beta, C)
+        ref, scale = oracle.wcsr_spmm(coo.m, 64, ewp, ewc, evals, B, alpha, beta, C0)
+        got = host(C)
+        assert_close(got, ref, scale, what="wcsr_spmm_tasks %s N=%d T=%d a=%g b=%g" % (name, N, task_cols, alpha,
+                                                                                        beta))
+        # windows that are one task: bit for bit the one-workgroup-per-window kernel
+        C1 = dev(C0) if beta != 0.0 else torch.full((coo.m, N), float("nan"), device="cuda")
+        sp.wcsr_spmm(coo.m, coo.n, wp, wc, vals, alpha, dev(B), beta, C1)
+        np.testing.assert_array_equal(got[whole].view(np.uint32), host(C1)[whole].view(np.uint32))
+    # reproducible: the same bits on a second call with a reused workspace
+    work = torch.empty(max(t.workspace_bytes(N), 1), dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(2):
+        C = torch.zeros(coo.m, N, device="cuda")
+        sp.wcsr_spmm_tasks(coo.m, coo.n, t, wc, vals, 1.0, dev(B), 0.0, C, work=work)
+        outs.append(host(C).view(np.uint32).copy())
+    np.testing.assert_array_equal(outs[0], outs[1])
+
+
+def test_wcsr_tasks_errors():
+    say("wcsr task split errors")
+    coo, (rp, c, v) = task_case("skewed")
+    ewp, ewc, evals = oracle.csr_to_wcsr(coo.m, coo.n, rp, c, v, 64, 8)
+    wp, wc, vals = dev(ewp), dev(ewc), dev(evals)
+    for bad_cols in (0, 48, -32):
+        with pytest.raises(sp.SparseError) as e:
+            sp.wcsr_tasks(coo.m, wp, ewc.size, task_cols=bad_cols)
+        assert e.value.code == 5
+    bad = ewp.copy()
+    bad[3], bad[4] = bad[4], bad[3] - 1  # a window that ends before it starts
+    with pytest.raises(sp.SparseError) as e:
+        sp.wcsr_tasks(coo.m, dev(bad), ewc.size, task_cols=32)
+    assert e.value.code == 3
+    with pytest.raises(sp.SparseError) as e:  # window_ptr past total_cols
+        sp.wcsr_tasks(coo.m, wp, ewc.size - 8, task_cols=32)
+    assert e.value.code == 3
+    t = sp.wcsr_tasks(coo.m, wp, ewc.size, task_cols=64)
+    assert t.nslots > 0
+    L = sp.lib()
+    B = dev(gen.dense_matrix(coo.n, 32, 1))
+    C = torch.full((coo.m, 32), float("nan"), device="cuda")
+    need = t.workspace_bytes(32)
+    work = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def call(ntasks=t.ntasks, nslots=t.nslots, wbytes=need, work_ptr=work.data_ptr()):
+        return L.wcsr_spmm_tasks(coo.m, coo.n, t.table.data_ptr(), ntasks, nslots, wc.data_ptr(), vals.data_ptr(),
+                                 32, 1.0, B.data_ptr(), 32, 0.0, C.data_ptr(), 32, work_ptr, wbytes, None)
+
+    assert call(wbytes=need - 1) == 4
+    assert call(work_ptr=None) == 1
+    assert call(ntasks=(coo.m + 63) // 64 - 1) == 2
+    # a workspace sized for fewer slots than the table needs: nothing is written
+    fewer = t.nslots - 1
+    assert call(nslots=fewer, wbytes=t.workspace_bytes(32)) == 0
+    torch.cuda.synchronize()
+    assert torch.isnan(C).all()
+    assert call() == 0
+    torch.cuda.synchronize()
+    assert not torch.isnan(C).any()
+
+
+def test_skewed_workload_task_split_sampled():
+    """The 2^20-row skewed-window matrix (windows of 1 to 16384 compressed
+    columns): task split with 2048 columns per task, N = 32 (the benchmarked
+    call), checked against the oracle on every split window and on 200 sampled
+    others."""
+    say("wcsr task split, skewed workload")
+    coo = gen.skewed_windows_coo(seed=0)
+    rp, c, v = sp.csr_build_from_coo(coo.m, coo.n, dev(coo.row), dev(coo.col), dev(coo.val))
+    wp, wc, vals, fill = sp.csr_to_wcsr(coo.m, coo.n, rp, c, v, pad=8)
+    t = sp.wcsr_tasks(coo.m, wp, wc.numel(), task_cols=2048)
+    N = 32
+    B = gen.dense_matrix(coo.n, N, 0)
+    C = torch.full((coo.m, N), float("nan"), device="cuda")
+    sp.wcsr_spmm_tasks(coo.m, coo.n, t, wc, vals, 1.0, dev(B), 0.0, C)
+    hwp, hwc, hvals, got = host(wp), host(wc), host(vals), host(C)
+    _, winfo, _ = oracle.wcsr_tasks(hwp, 2048)
+    split = np.flatnonzero(winfo[:, 0] >= 0)
+    assert split.size > 100
+    rng = np.random.default_rng(0)
+    others = rng.choice(np.flatnonzero(winfo[:, 0] < 0), size=200, replace=False)
+    for w in np.concatenate([split, others]):
+        q0, q1 = hwp[w], hwp[w + 1]
+        r0, r1 = 64 * w, min(coo.m, 64 * w + 64)
+        ref, scale = oracle.wcsr_spmm(r1 - r0, 64, np.array([0, q1 - q0], np.int32), hwc[q0:q1], hvals[q0:q1], B)
+        assert_close(got[r0:r1], ref, scale, what="skewed window %d" % w)
