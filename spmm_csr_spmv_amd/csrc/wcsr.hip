@@ -60,14 +60,31 @@ __device__ __forceinline__ int col_at(const int32_t* __restrict__ idx, int q, in
     return (c >= 0 && c < n) ? c : kNoCol;
 }
 
+// A window of more than kWideEntries entries is converted by one workgroup
+// of its own (wcsr_wide_kernel): the wave merge below takes one dependent
+// load per compressed column, so a window of thousands of columns would hold
+// the whole conversion for milliseconds.
+constexpr int kWideEntries = 4096;
+constexpr int kWideThreads = 1024;
+constexpr int kWideBits = 19;                        // columns per pass: 2^19, a 64 KB bitmap
+constexpr int kWideWords = (1 << kWideBits) / 32;
+constexpr int kWideGroups = kWideWords / 8;          // set-bit counts kept per group of 8 words
+constexpr int64_t kWideMaxCols = 8LL << kWideBits;   // wider matrices keep the wave merge
+
+__device__ __forceinline__ bool wide_window(const int32_t* __restrict__ ptr, int64_t m, int64_t w, int32_t n) {
+    const int64_t r0 = w * kWin, r1 = min(m, r0 + kWin);
+    return (int64_t)ptr[r1] - ptr[r0] > kWideEntries && n <= kWideMaxCols;
+}
+
 // flags[0] |= 1: a column outside [0, n);  |= 2: a row not sorted by column.
-// Four windows per workgroup, one per wave.
+// Four windows per workgroup, one per wave; wide windows are left to
+// wcsr_wide_kernel.
 __global__ __launch_bounds__(kBlock) void wcsr_analyze_kernel(int64_t m, int32_t n, int64_t nw, int32_t pad,
                                                               const int32_t* __restrict__ ptr,
                                                               const int32_t* __restrict__ idx,
                                                               int32_t* __restrict__ counts, int32_t* __restrict__ flags) {
     const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (w >= nw) return;
+    if (w >= nw || wide_window(ptr, m, w, n)) return;
     const int l = threadIdx.x & 63;
     const int64_t i = w * kWin + l;
     const bool in = i < m;
@@ -99,7 +116,7 @@ __global__ __launch_bounds__(kBlock) void wcsr_fill_kernel(int64_t m, int32_t n,
                                                            int32_t* __restrict__ window_col,
                                                            float* __restrict__ values) {
     const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (w >= nw) return;
+    if (w >= nw || wide_window(ptr, m, w, n)) return;
     const int l = threadIdx.x & 63;
     const int64_t i = w * kWin + l;
     const bool in = i < m;
@@ -129,6 +146,144 @@ __global__ __launch_bounds__(kBlock) void wcsr_fill_kernel(int64_t m, int32_t n,
     for (; q < qend; ++q) {
         if (l == 0) window_col[q] = -1;
         values[(int64_t)q * kWin + l] = 0.0f;
+    }
+}
+
+// Exclusive prefix sum over the 1024 threads of a workgroup; *total gets the sum.
+__device__ int block_exclusive_scan(int v, int* wsum, int* total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[wv] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int acc = 0;
+        for (int k = 0; k < kWideThreads / 64; ++k) {
+            const int u = wsum[k];
+            wsum[k] = acc;
+            acc += u;
+        }
+        *total = acc;
+    }
+    __syncthreads();
+    return x - v + wsum[wv];
+}
+
+// The window row holding entry e: the r with rps[r] <= e < rps[r + 1]
+// (rps[0] <= e < rps[rows]).
+__device__ __forceinline__ int entry_row(const int32_t* rps, int rows, int e) {
+    int lo = 0, hi = rows;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (rps[mid] <= e) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Rank of column bit (k, bit) among the set bits of the bitmap.
+__device__ __forceinline__ int bit_rank(const uint32_t* bm, const int32_t* gp, int k, int bit) {
+    int r = gp[k >> 3];
+    for (int j = k & ~7; j < k; ++j) r += __popc(bm[j]);
+    return r + __popc(bm[k] & ((1u << bit) - 1u));
+}
+
+// One workgroup per wide window (the grid covers every window; the others
+// exit).  Pass by pass over 2^19 columns, the window's entries set their
+// column's bit in an LDS bitmap; the set bits are the window's distinct
+// columns in ascending order.  Analyze: their count, rounded up to pad, and
+// the same flags as wcsr_analyze_kernel.  Fill: the window's values cleared
+// and its columns set to -1 first; then every set bit writes its column at
+// its rank, and the first entry of each run of equal columns in a row adds
+// the run in CSR order and writes the sum at that rank (the wave merge's
+// values, bit for bit).
+template <bool FILL>
+__global__ __launch_bounds__(kWideThreads) void wcsr_wide_kernel(int64_t m, int32_t n, int32_t pad,
+                                                                 const int32_t* __restrict__ ptr,
+                                                                 const int32_t* __restrict__ idx,
+                                                                 const float* __restrict__ val,
+                                                                 int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ flags,
+                                                                 const int32_t* __restrict__ window_ptr,
+                                                                 int32_t* __restrict__ window_col,
+                                                                 float* __restrict__ values) {
+    __shared__ uint32_t bm[kWideWords];
+    __shared__ int32_t gp[kWideGroups];  // set bits before each group of 8 words
+    __shared__ int32_t wsum[kWideThreads / 64];
+    __shared__ int32_t pass_total;
+    __shared__ int32_t rps[kWin + 1];  // the window's row pointers
+    const int64_t w = blockIdx.x;
+    if (!wide_window(ptr, m, w, n)) return;
+    const int t = threadIdx.x;
+    const int64_t r0 = w * kWin;
+    const int rows = (int)(min(m, r0 + kWin) - r0);
+    if (t <= rows) rps[t] = ptr[r0 + t];
+    int q = 0, qend = 0;
+    if (FILL) {
+        q = window_ptr[w];
+        qend = window_ptr[w + 1];
+        for (int64_t k = (int64_t)q * kWin + t; k < (int64_t)qend * kWin; k += kWideThreads) values[k] = 0.0f;
+        for (int k = q + t; k < qend; k += kWideThreads) window_col[k] = -1;
+    }
+    __syncthreads();
+    const int e0 = rps[0], e1 = rps[rows];
+    int bad = 0, done = 0;
+    for (int64_t base = 0; base < n; base += 1 << kWideBits) {
+        const int64_t lim = min((int64_t)n, base + (1 << kWideBits));
+        for (int k = t; k < kWideWords; k += kWideThreads) bm[k] = 0u;
+        __syncthreads();
+        for (int e = e0 + t; e < e1; e += kWideThreads) {
+            const int c = idx[e];
+            if (!FILL && base == 0) {
+                if (c < 0 || c >= n) bad |= 1;
+                if (e > rps[entry_row(rps, rows, e)] && c < idx[e - 1]) bad |= 2;
+            }
+            if (c >= base && c < lim) atomicOr(&bm[(c - base) >> 5], 1u << (c & 31));
+        }
+        __syncthreads();
+        int c0 = 0, c1 = 0;  // thread t owns groups 2t and 2t + 1
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            c0 += __popc(bm[16 * t + k]);
+            c1 += __popc(bm[16 * t + 8 + k]);
+        }
+        const int excl = block_exclusive_scan(c0 + c1, wsum, &pass_total);
+        gp[2 * t] = excl;
+        gp[2 * t + 1] = excl + c0;
+        __syncthreads();
+        if (FILL) {
+            for (int k = t; k < kWideWords; k += kWideThreads) {
+                uint32_t b = bm[k];
+                int r = bit_rank(bm, gp, k, 0);
+                while (b) {
+                    const int bit = __ffs(b) - 1;
+                    b &= b - 1u;
+                    const int64_t qq = (int64_t)q + done + r++;
+                    if (qq < qend) window_col[qq] = (int)(base + 32 * k + bit);
+                }
+            }
+            for (int e = e0 + t; e < e1; e += kWideThreads) {
+                const int c = idx[e];
+                if (c < base || c >= lim) continue;
+                const int r = entry_row(rps, rows, e);
+                const int p0 = rps[r], p1 = rps[r + 1];
+                if (e > p0 && idx[e - 1] == c) continue;
+                float v = val[e];
+                for (int f = e + 1; f < p1 && idx[f] == c; ++f) v = v + val[f];
+                const int64_t qq = (int64_t)q + done + bit_rank(bm, gp, (int)((c - base) >> 5), c & 31);
+                if (qq < qend) values[qq * kWin + r] = v;
+            }
+        }
+        done += pass_total;
+        __syncthreads();  // the next pass clears the bitmap
+    }
+    if (!FILL) {
+        if (bad) atomicOr(flags, bad);
+        if (t == 0) counts[w] = (done + pad - 1) / pad * pad;
     }
 }
 
@@ -329,6 +484,8 @@ int csr_to_wcsr_analyze_device(int64_t m, int64_t n, const int32_t* row_ptr, con
     if (nw > 0) {
         hipLaunchKernelGGL(wcsr_analyze_kernel, dim3((unsigned)((nw + 3) / 4)), dim3(kBlock), 0, s, m, (int32_t)n, nw,
                            pad, row_ptr, col_idx, window_ptr + 1, flags);
+        hipLaunchKernelGGL(wcsr_wide_kernel<false>, dim3((unsigned)nw), dim3(kWideThreads), 0, s, m, (int32_t)n, pad,
+                           row_ptr, col_idx, nullptr, window_ptr + 1, flags, nullptr, nullptr, nullptr);
         if (hipGetLastError() != hipSuccess) return SP_ERR_HIP;
         const int rc = scan_inclusive_i32(window_ptr + 1, nw, sums, s);
         if (rc != SP_OK) return rc;
@@ -343,6 +500,8 @@ int csr_to_wcsr_fill_device(int64_t m, int64_t n, const int32_t* row_ptr, const 
     if (nw == 0) return SP_OK;
     hipLaunchKernelGGL(wcsr_fill_kernel, dim3((unsigned)((nw + 3) / 4)), dim3(kBlock), 0, s, m, (int32_t)n, nw,
                        row_ptr, col_idx, val, window_ptr, window_col, values);
+    hipLaunchKernelGGL(wcsr_wide_kernel<true>, dim3((unsigned)nw), dim3(kWideThreads), 0, s, m, (int32_t)n, 1, row_ptr,
+                       col_idx, val, nullptr, nullptr, window_ptr, window_col, values);
     return hipGetLastError() == hipSuccess ? SP_OK : SP_ERR_HIP;
 }
 

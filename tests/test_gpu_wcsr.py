@@ -90,6 +90,35 @@ def test_wcsr_spmm(name, N):
     assert_close(ref_w, ref_csr, scale_w, what="WCSR and CSR routes of the oracle")
 
 
+WIDE = {
+    # windows of about 5000 entries (one workgroup each, a column bitmap in 4 passes of 2^19 columns)
+    "wide_multipass": lambda: gen.ragged_coo(200, 3 * 2 ** 19 + 7, seed=11, max_len=160, empty_frac=0.1,
+                                             dup_frac=0.05),
+    # as wide, but more columns than the bitmap path takes: the wave merge
+    "wide_huge_n": lambda: gen.ragged_coo(130, 5_000_000, seed=12, max_len=160, empty_frac=0.1, dup_frac=0.05),
+}
+
+
+@pytest.mark.parametrize("pad", [1, 8])
+@pytest.mark.parametrize("name", list(WIDE))
+def test_wide_window_conversion(name, pad):
+    say("csr_to_wcsr wide windows", name, pad)
+    coo = WIDE[name]()
+    rp, c, v = oracle.coo_to_csr(coo.m, coo.n, coo.row, coo.col, coo.val)
+    per_window = rp[np.minimum(np.arange(1, (coo.m + 63) // 64 + 1) * 64, coo.m)] - rp[np.arange(0, coo.m, 64)]
+    assert (per_window > 4096).sum() >= 2
+    ewp, ewc, evals = oracle.csr_to_wcsr(coo.m, coo.n, rp, c, v, 64, pad)
+    wp, wc, vals, fill = sp.csr_to_wcsr(coo.m, coo.n, dev(rp), dev(c), dev(v), pad=pad)
+    np.testing.assert_array_equal(host(wp), ewp)
+    np.testing.assert_array_equal(host(wc), ewc)
+    np.testing.assert_array_equal(host(vals).view(np.uint32), evals.view(np.uint32))
+    B = gen.dense_matrix(coo.n, 4, 3)
+    C = torch.full((coo.m, 4), float("nan"), device="cuda")
+    sp.wcsr_spmm(coo.m, coo.n, wp, wc, vals, 1.0, dev(B), 0.0, C)
+    ref, scale = oracle.wcsr_spmm(coo.m, 64, ewp, ewc, evals, B)
+    assert_close(host(C), ref, scale, what="wcsr_spmm %s" % name)
+
+
 def test_wcsr_bitwise_deterministic_and_errors():
     say("wcsr determinism and errors")
     coo, (rp, c, v) = case("clustered")
@@ -113,6 +142,22 @@ def test_wcsr_bitwise_deterministic_and_errors():
     bad[-1] = -1
     with pytest.raises(sp.SparseError) as e:
         sp.csr_to_wcsr(coo2.m, coo2.n, dev(rp2), dev(bad), dev(v2))
+    assert e.value.code == 3
+    # the same checks inside a window of more than 4096 entries (converted by a workgroup of its own)
+    coo3 = WIDE["wide_multipass"]()
+    rp3, c3, v3 = oracle.coo_to_csr(coo3.m, coo3.n, coo3.row, coo3.col, coo3.val)
+    i = 5
+    assert rp3[i + 1] - rp3[i] >= 2 and rp3[64] - rp3[0] > 4096
+    bad = c3.copy()
+    bad[rp3[i]], bad[rp3[i] + 1] = c3[rp3[i] + 1], c3[rp3[i]]
+    if bad[rp3[i]] != bad[rp3[i] + 1]:
+        with pytest.raises(sp.SparseError) as e:
+            sp.csr_to_wcsr(coo3.m, coo3.n, dev(rp3), dev(bad), dev(v3))
+        assert e.value.code == 5
+    bad = c3.copy()
+    bad[rp3[i]] = coo3.n
+    with pytest.raises(sp.SparseError) as e:
+        sp.csr_to_wcsr(coo3.m, coo3.n, dev(rp3), dev(bad), dev(v3))
     assert e.value.code == 3
 
 
@@ -268,6 +313,12 @@ def test_skewed_workload_task_split_sampled():
     coo = gen.skewed_windows_coo(seed=0)
     rp, c, v = sp.csr_build_from_coo(coo.m, coo.n, dev(coo.row), dev(coo.col), dev(coo.val))
     wp, wc, vals, fill = sp.csr_to_wcsr(coo.m, coo.n, rp, c, v, pad=8)
+    # the conversion, bit for bit (windows of up to 180 k entries take the wide-window kernel)
+    ewp, ewc, evals = oracle.csr_to_wcsr(coo.m, coo.n, host(rp), host(c), host(v), 64, 8)
+    np.testing.assert_array_equal(host(wp), ewp)
+    np.testing.assert_array_equal(host(wc), ewc)
+    np.testing.assert_array_equal(host(vals).view(np.uint32), evals.view(np.uint32))
+    del ewc, evals
     t = sp.wcsr_tasks(coo.m, wp, wc.numel(), task_cols=2048)
     N = 32
     B = gen.dense_matrix(coo.n, N, 0)
