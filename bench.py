@@ -42,16 +42,17 @@ SKEWED_TASK_COLS = 2048
 # every workload of a default run, in order (the headline first)
 ALL_WORKLOADS = ["spmv_powerlaw", "spmv_uniform", "stencil27", "spmm_lognormal_N8", "spmm_lognormal_N32",
                  "spmm_lognormal_N128", "bsr_blocks", "bsr_spmv", "spmm_clustered_N32", "spmm_skewed_N32"]
-# Sources whose code decides the kernels each workload runs (a committed
-# traffic summary is used only while these are unchanged).
+# Sources whose code decides the kernels each workload runs and the layouts
+# they stream (a committed traffic summary is used only while these are
+# unchanged).
 _CSRC = "spmm_csr_spmv_amd/csrc/"
 KERNEL_SOURCES = {
     "spmv": [_CSRC + f for f in ("spmv.hip", "pstream.hip", "xwin.hip", "seg_rows.h", "device_common.h", "internal.h",
-                                 "api.cpp")],
-    "spmm": [_CSRC + f for f in ("spmm.hip", "device_common.h", "internal.h", "api.cpp")],
-    "bsr": [_CSRC + f for f in ("bsr.hip", "device_common.h", "internal.h")],
-    "bsr_spmv": [_CSRC + f for f in ("bsr_convert.hip", "device_common.h", "internal.h")],
-    "wcsr": [_CSRC + f for f in ("wcsr.hip", "device_common.h", "internal.h")],
+                                 "layout.h", "api.cpp", "plan_host.cpp")],
+    "spmm": [_CSRC + f for f in ("spmm.hip", "device_common.h", "internal.h", "layout.h", "api.cpp", "plan_host.cpp")],
+    "bsr": [_CSRC + f for f in ("bsr.hip", "device_common.h", "internal.h", "layout.h")],
+    "bsr_spmv": [_CSRC + f for f in ("bsr_convert.hip", "device_common.h", "internal.h", "layout.h")],
+    "wcsr": [_CSRC + f for f in ("wcsr.hip", "device_common.h", "internal.h", "layout.h", "plan_host.cpp")],
 }
 
 

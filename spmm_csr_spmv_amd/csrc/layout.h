@@ -129,6 +129,15 @@ int build_xwin_layout(const std::vector<int32_t>& hptr, const std::vector<int32_
 void build_sweep_layout(const std::vector<int32_t>& hptr, const std::vector<int32_t>& hidx, int64_t rows, int32_t pb,
                         int32_t P, int32_t nblk, std::vector<int32_t>& wrow, std::vector<int32_t>& off,
                         std::vector<int32_t>& src);
+// WCSR task split (wcsr.hip), from the window pointer wp (nw + 1 entries): a
+// window of at most task_cols compressed columns is one task, a wider one
+// ceil(cols / task_cols) tasks of task_cols columns (the last shorter) whose
+// partial slots follow each other, the split windows in window order.
+// tasks = {window, first column, end column, slot or -1}, widest first (equal
+// widths in window, then column order); splits = {window, first slot, tasks,
+// 0}.  SP_ERR_INDEX when wp is not nondecreasing inside [0, total_cols].
+int build_wcsr_tasks(const std::vector<int32_t>& wp, int64_t total_cols, int32_t task_cols, std::vector<int4>& tasks,
+                     std::vector<int4>& splits, int32_t& slots);
 
 }  // namespace host
 }  // namespace spx

@@ -1,12 +1,13 @@
 // Host side of the plan (declarations and the layout of each structure in
 // layout.h): row profile, row bins, SELL-C-sigma order, column-panel and
-// x-window streams, phase-swept SpMM copy.  Plain C++ without HIP, so that it
+// x-window streams, phase-swept SpMM copy; and the WCSR task table.  Plain C++ without HIP, so that it
 // runs under the host sanitizers; api.cpp moves the arrays to and from the
 // device.
 //
 // 「通用稀疏矩阵乘法CUDA算子实现」 §4: the profile of the matrix (row lengths with
 // their mean, variance and tail, 「CUDA LSMR 专栏（二）」 §5.3) decides which kernel
 // serves which rows.
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -512,6 +513,38 @@ void build_sweep_layout(const std::vector<int32_t>& hptr, const std::vector<int3
                     src[(size_t)cur[(size_t)(hidx[(size_t)q] >> pb)]++] = q;
         }
     });
+}
+
+// The AsyncSparse summary page §4.2: windows whose compressed columns pass a
+// threshold are cut into pieces of a fixed width, one workgroup each.
+// Workgroups start roughly in index order, so the widest tasks go first and
+// the short ones fill in behind them.
+int build_wcsr_tasks(const std::vector<int32_t>& wp, int64_t total_cols, int32_t task_cols, std::vector<int4>& tasks,
+                     std::vector<int4>& splits, int32_t& slots) {
+    const int64_t nw = (int64_t)wp.size() - 1;
+    tasks.clear();
+    splits.clear();
+    slots = 0;
+    for (int64_t w = 0; w < nw; ++w)
+        if (wp[(size_t)w] < 0 || wp[(size_t)w + 1] < wp[(size_t)w] || wp[(size_t)w + 1] > total_cols)
+            return SP_ERR_INDEX;
+    tasks.reserve((size_t)(nw + total_cols / task_cols));
+    for (int64_t w = 0; w < nw; ++w) {
+        const int32_t q0 = wp[(size_t)w], q1 = wp[(size_t)w + 1];
+        if (q1 - q0 <= task_cols) {
+            tasks.push_back(make_int4((int32_t)w, q0, q1, -1));
+            continue;
+        }
+        const int32_t nt = (int32_t)(((int64_t)q1 - q0 + task_cols - 1) / task_cols);
+        splits.push_back(make_int4((int32_t)w, slots, nt, 0));
+        for (int32_t t = 0; t < nt; ++t) {
+            const int64_t b = q0 + (int64_t)t * task_cols;
+            tasks.push_back(make_int4((int32_t)w, (int32_t)b, (int32_t)std::min<int64_t>(b + task_cols, q1), slots + t));
+        }
+        slots += nt;
+    }
+    std::stable_sort(tasks.begin(), tasks.end(), [](const int4& a, const int4& b) { return a.z - a.y > b.z - b.y; });
+    return SP_OK;
 }
 
 }  // namespace host

@@ -15,7 +15,8 @@
 //
 // Conversion: one wave per window merges its 64 sorted rows by wave-wide
 // minima of the current column (analyze counts, fill writes one compressed
-// column of 64 values per round, coalesced).
+// column of 64 values per round, coalesced); a window of more than 4096
+// entries gets a workgroup that marks its columns in an LDS bitmap instead.
 //
 // SpMM: one workgroup per (window, column tile of C: 32 columns when N <= 32,
 // 64 when N <= 64, else 128), one wave per 32 x 32 part of the tile.  Chunks of
@@ -29,7 +30,6 @@
 // GPU and every output is written once.  For windows of very different
 // widths, the task split below cuts the wide ones into tasks, as the page
 // does, but adds their parts in a fixed order instead of with atomics.
-#include <algorithm>
 #include <cstring>
 #include <vector>
 
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(4 * NT) void wcsr_spmm_kernel(int64_t m, int64_t nw
 // kernel boundary orders the partial stores before their reads: a
 // completion counter inside one kernel would need a device-scope release per
 // task (an L2 write-back), which costs more than the second launch.  The
-// task table is built on the host, once per matrix (wcsr_tasks_build_device).
+// task table is built on the host, once per matrix (plan_host.cpp).
 
 // One workgroup per (task, column tile).  head = {tasks, slots, -, -} of the
 // table: a workgroup past the table's tasks, or every workgroup when the
@@ -549,11 +549,7 @@ size_t wcsr_task_table_bytes(int64_t m, int64_t total_cols, int32_t task_cols) {
     return kTaskHead + up256(16 * (size_t)nw) + up256(16 * (size_t)task_bound(nw, total_cols, task_cols));
 }
 
-// Windows of at most task_cols columns are one task; wider ones are cut into
-// tasks of task_cols columns, whose partial slots are numbered in window
-// order.  The tasks are then ordered widest first (equal widths in window and
-// column order): workgroups start roughly in index order, so the longest
-// tasks start first and the short ones fill in behind them.
+// The table is built on the host (spx::host::build_wcsr_tasks) and uploaded.
 int wcsr_tasks_build_device(int64_t m, const int32_t* window_ptr, int64_t total_cols, int32_t task_cols, void* table,
                             hipStream_t s, int32_t* head_host) {
     const int64_t nw = (m + kWin - 1) / kWin;
@@ -561,26 +557,10 @@ int wcsr_tasks_build_device(int64_t m, const int32_t* window_ptr, int64_t total_
     if (hipMemcpyAsync(wp.data(), window_ptr, wp.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)
         return SP_ERR_HIP;
-    for (int64_t w = 0; w < nw; ++w)
-        if (wp[w] < 0 || wp[w + 1] < wp[w] || wp[w + 1] > total_cols) return SP_ERR_INDEX;
-    std::vector<int4> tasks, splits;
-    tasks.reserve((size_t)task_bound(nw, total_cols, task_cols));
+    std::vector<host::int4> tasks, splits;
     int32_t slots = 0;
-    for (int64_t w = 0; w < nw; ++w) {
-        const int32_t q0 = wp[w], q1 = wp[w + 1];
-        if (q1 - q0 <= task_cols) {
-            tasks.push_back(make_int4((int)w, q0, q1, -1));
-            continue;
-        }
-        const int32_t nt = (q1 - q0 + task_cols - 1) / task_cols;
-        splits.push_back(make_int4((int)w, slots, nt, 0));
-        for (int32_t t = 0; t < nt; ++t) {
-            const int64_t b = q0 + (int64_t)t * task_cols;
-            tasks.push_back(make_int4((int)w, (int)b, (int)std::min<int64_t>(b + task_cols, q1), slots + t));
-        }
-        slots += nt;
-    }
-    std::stable_sort(tasks.begin(), tasks.end(), [](const int4& a, const int4& b) { return a.z - a.y > b.z - b.y; });
+    const int rc = host::build_wcsr_tasks(wp, total_cols, task_cols, tasks, splits, slots);
+    if (rc != SP_OK) return rc;
     const size_t tasks_at = kTaskHead + up256(16 * (size_t)nw);
     std::vector<char> img(tasks_at + 16 * tasks.size(), 0);
     const int32_t head[4] = {(int32_t)tasks.size(), slots, 0, (int32_t)splits.size()};

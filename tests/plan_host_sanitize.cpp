@@ -6,9 +6,10 @@
 // On seeded random CSR matrices (empty rows, rows longer than a chunk, m != n)
 // it runs the row profile, the row bins under several option sets, the
 // SELL-C-sigma order, the column-panel stream (1, 2, 4, 8 panels), the x-window
-// stream (several window widths) and the phase-swept SpMM copy, and checks
-// their structural invariants with plain loops written here: every row served
-// once, every entry placed once inside its chunk, window run or cell, tables
+// stream (several window widths), the phase-swept SpMM copy and the WCSR
+// task table, and checks their structural invariants with plain loops
+// written here: every row served once, every entry placed once inside its
+// chunk, window run or cell, every window column in one task, tables
 // monotone, sizes consistent.  A sanitizer report or a failed check ends the
 // run with a non-zero status.
 #include <algorithm>
@@ -282,6 +283,62 @@ static void check_sweep(const Csr& a, int32_t pb) {
     for (char f : seen) CHECK(f == 1);
 }
 
+// WCSR task table: every window's range tiled once by its tasks in column
+// order, each split window's tasks task_cols wide but the last, slots
+// consecutive in window order, tasks sorted widest first with ties in
+// (window, column) order; bad window pointers refused.
+static void check_wcsr_tasks(std::mt19937_64& rng, int32_t task_cols) {
+    std::uniform_int_distribution<int32_t> nwd(0, 300), wd(0, 3 * task_cols), big(0, 9);
+    const int32_t nw = nwd(rng);
+    std::vector<int32_t> wp(1, 0);
+    for (int32_t w = 0; w < nw; ++w) wp.push_back(wp.back() + (big(rng) == 0 ? 10 * wd(rng) : wd(rng) / 4));
+    std::vector<spx::host::int4> tasks, splits;
+    int32_t slots = -1;
+    CHECK(spx::host::build_wcsr_tasks(wp, wp.back(), task_cols, tasks, splits, slots) == SP_OK);
+    for (size_t k = 1; k < tasks.size(); ++k) {
+        const int32_t wa = tasks[k - 1].z - tasks[k - 1].y, wb = tasks[k].z - tasks[k].y;
+        CHECK(wa > wb || (wa == wb && (tasks[k - 1].x < tasks[k].x ||
+                                       (tasks[k - 1].x == tasks[k].x && tasks[k - 1].y < tasks[k].y))));
+    }
+    std::vector<std::vector<spx::host::int4>> by_window((size_t)nw);
+    for (const auto& t : tasks) {
+        CHECK(t.x >= 0 && t.x < nw);
+        by_window[(size_t)t.x].push_back(t);
+    }
+    int32_t next_slot = 0;
+    size_t si = 0;
+    for (int32_t w = 0; w < nw; ++w) {
+        auto& v = by_window[(size_t)w];
+        std::sort(v.begin(), v.end(), [](const spx::host::int4& a, const spx::host::int4& b) { return a.y < b.y; });
+        const int32_t c = wp[(size_t)w + 1] - wp[(size_t)w];
+        CHECK(!v.empty() && v.front().y == wp[(size_t)w] && v.back().z == wp[(size_t)w + 1]);
+        for (size_t k = 1; k < v.size(); ++k) CHECK(v[k].y == v[k - 1].z);
+        if (c <= task_cols) {
+            CHECK(v.size() == 1 && v[0].w == -1);
+            continue;
+        }
+        CHECK((int64_t)v.size() == ((int64_t)c + task_cols - 1) / task_cols);
+        for (size_t k = 0; k < v.size(); ++k) {
+            CHECK(v[k].w == next_slot + (int32_t)k);
+            CHECK(k + 1 == v.size() ? v[k].z - v[k].y >= 1 : v[k].z - v[k].y == task_cols);
+        }
+        CHECK(si < splits.size() && splits[si].x == w && splits[si].y == next_slot &&
+              splits[si].z == (int32_t)v.size() && splits[si].w == 0);
+        ++si;
+        next_slot += (int32_t)v.size();
+    }
+    CHECK(si == splits.size() && slots == next_slot);
+    CHECK((int64_t)tasks.size() <= (int64_t)nw + wp.back() / task_cols);
+    if (nw >= 2) {
+        std::vector<int32_t> bad(wp);
+        std::swap(bad[1], bad[2]);
+        if (bad[1] > bad[2]) CHECK(spx::host::build_wcsr_tasks(bad, wp.back(), task_cols, tasks, splits, slots) ==
+                                   SP_ERR_INDEX);
+        CHECK(spx::host::build_wcsr_tasks(wp, (int64_t)wp.back() - 1, task_cols, tasks, splits, slots) ==
+              SP_ERR_INDEX);
+    }
+}
+
 int main(int argc, char** argv) {
     const int cases = argc > 1 ? std::atoi(argv[1]) : 40;
     std::mt19937_64 rng(12345);
@@ -300,6 +357,7 @@ int main(int argc, char** argv) {
         for (int32_t P : {1, 2, 4, 8}) check_pstream(a, c % 2 ? o1 : o2, P);
         for (int32_t bits : {5, 8, 11, 15}) check_xwin(a, bits);
         for (int32_t pb : {5, 9, 16}) check_sweep(a, pb);
+        for (int32_t T : {32, 64, 2048}) check_wcsr_tasks(rng, T);
         if (g_fail) {
             std::fprintf(stderr, "case %d (m=%d n=%d nnz=%zu) failed\n", c, m, n, a.col.size());
             return 1;

@@ -2,8 +2,8 @@
 UndefinedBehaviorSanitizer.
 
 spmm_csr_spmv_amd/csrc/plan_host.cpp holds the row profile, the row bins, the
-SELL-C-sigma order, the column-panel and x-window stream layouts and the
-phase-swept SpMM copy: plain C++ with no HIP.  tests/plan_host_sanitize.cpp
+SELL-C-sigma order, the column-panel and x-window stream layouts, the
+phase-swept SpMM copy and the WCSR task table: plain C++ with no HIP.  tests/plan_host_sanitize.cpp
 runs them on seeded random matrices and checks their structural invariants;
 built here with g++ and the sanitizers, any out-of-bounds access, leak,
 overflow, data race visible to the sanitizers or failed check ends the run
