@@ -443,7 +443,10 @@ int bsr_spmv_rowwise(int64_t m, int64_t n, int32_t bs, int64_t nnzb, const int32
  * wcsr_spmm: C = alpha * A B + beta * C with B n x N and C m x N row-major
  * (fp32, device); N % 4 == 0, ldb % 4 == 0, B and values 16-byte aligned;
  * window_col and values may be NULL when total_cols == 0.  Deterministic;
- * never allocates, never synchronises.
+ * never allocates, never synchronises.  The product runs over the stored
+ * window tiles, zeros included (0 * Inf is NaN where a row of the window has
+ * no entry at a column whose B row holds Inf or NaN); padding columns (-1)
+ * are skipped and never read from B.
  */
 int csr_to_wcsr_bufsize(int64_t m, int64_t n, int64_t nnz, size_t* bytes);
 int csr_to_wcsr_analyze(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,

@@ -140,3 +140,31 @@ def test_bsr_spmm_nonfinite_b(N):
                 0.0, C)
     ref, scale = oracle.spmm_bf16(rp, colx, v64, B)
     assert check_class(host(C), ref, scale, "bsr_spmm N=%d" % N) > 0
+
+
+@pytest.mark.parametrize("N", [4, 32, 128])
+@pytest.mark.parametrize("path", ["window", "tasks"])
+def test_wcsr_spmm_nonfinite_b(path, N):
+    """Window tiles are dense: a row of the window without an entry at a
+    compressed column holds a stored 0 there, so 0 * Inf = NaN on both sides
+    (the oracle sums over the stored tile); padding columns (-1) are skipped,
+    never read from B."""
+    say("nonfinite wcsr spmm", path, N)
+    coo = gen.skewed_windows_coo(m=700, n=30000, pool_median=40, pool_sigma=1.2, pool_max=3000, seed=9)
+    rp, c, v = oracle.coo_to_csr(coo.m, coo.n, coo.row, coo.col, coo.val)
+    wp, wc, vals = oracle.csr_to_wcsr(coo.m, coo.n, rp, c, v, 64, 8)
+    B = gen.dense_matrix(coo.n, N, 7).astype(np.float32)
+    rng = np.random.default_rng(9)
+    used = np.unique(c)
+    for k, r in enumerate(rng.choice(used, size=30, replace=False)):
+        B[r, k % N] = (np.inf, -np.inf, np.nan)[k % 3]
+    B[0, :] = np.nan  # row 0 of B: read only where column 0 is stored
+    C = torch.full((coo.m, N), float("nan"), device="cuda")
+    if path == "window":
+        sp.wcsr_spmm(coo.m, coo.n, dev(wp), dev(wc), dev(vals), 1.0, dev(B), 0.0, C)
+    else:
+        t = sp.wcsr_tasks(coo.m, dev(wp), wc.size, task_cols=64)
+        assert t.nslots > 0
+        sp.wcsr_spmm_tasks(coo.m, coo.n, t, dev(wc), dev(vals), 1.0, dev(B), 0.0, C)
+    ref, scale = oracle.wcsr_spmm(coo.m, 64, wp, wc, vals, B)
+    assert check_class(host(C), ref, scale, "wcsr %s N=%d" % (path, N)) > 0

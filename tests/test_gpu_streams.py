@@ -127,3 +127,42 @@ def test_view_lifetime_rules():
     assert e.value.code == 2
     view.destroy()
     plan.destroy()
+
+
+def test_wcsr_task_split_two_streams():
+    """One WCSR task table (read-only after the build) on two streams at the
+    same time, each with its own partial-tile workspace: every repetition
+    equals the single-stream result bit for bit and the oracle within
+    tolerance."""
+    say("wcsr task split, two streams")
+    coo = gen.skewed_windows_coo(m=1500, n=40000, pool_median=48, pool_sigma=1.5, pool_max=4000, seed=3)
+    rp, c, v = oracle.coo_to_csr(coo.m, coo.n, coo.row, coo.col, coo.val)
+    wp, wc, vals = oracle.csr_to_wcsr(coo.m, coo.n, rp, c, v, 64, 8)
+    dwp, dwc, dvals = dev(wp), dev(wc), dev(vals)
+    t = sp.wcsr_tasks(coo.m, dwp, wc.size, task_cols=64)
+    assert t.nslots > 0
+    N = 32
+    Bs = [gen.dense_matrix(coo.n, N, 70 + k) for k in range(2)]
+    dB = [dev(b) for b in Bs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    works = [torch.empty(t.workspace_bytes(N), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    single = []
+    for k in range(2):
+        C = torch.empty(coo.m, N, device="cuda")
+        sp.wcsr_spmm_tasks(coo.m, coo.n, t, dwc, dvals, 1.0, dB[k], 0.0, C, work=works[k])
+        single.append(host(C).view(np.uint32).copy())
+    reps = 6
+    Cs = [[torch.empty(coo.m, N, device="cuda") for _ in range(reps)] for _ in range(2)]
+    torch.cuda.synchronize()
+    for r in range(reps):
+        for k in range(2):
+            with torch.cuda.stream(streams[k]):
+                sp.wcsr_spmm_tasks(coo.m, coo.n, t, dwc, dvals, 1.0, dB[k], 0.0, Cs[k][r], work=works[k],
+                                   stream=streams[k])
+    torch.cuda.synchronize()
+    for k in range(2):
+        ref, scale = oracle.wcsr_spmm(coo.m, 64, wp, wc, vals, Bs[k])
+        for r in range(reps):
+            got = host(Cs[k][r])
+            assert np.array_equal(got.view(np.uint32), single[k]), "stream %d rep %d differs" % (k, r)
+        assert_close(host(Cs[k][0]), ref, scale, what="wcsr tasks stream %d" % k)
