@@ -416,7 +416,7 @@ def prepare(name, args, opts):
         def step():
             sp.wcsr_spmm(m, n, wp, wc, wv, 1.0, B, 0.0, C)
 
-        w.step, w.out_tensor = step, C
+        w.step, w.out_tensor, w.graph = step, C, 20
         w.flops = 2 * nnz * N
         w.nbytes = spmm_bytes(m, n, nnz, N)
         w.launches = 1
@@ -472,7 +472,7 @@ def prepare(name, args, opts):
         def step():
             sp.wcsr_spmm_tasks(m, n, tasks, wc, wv, 1.0, B, 0.0, C, work=work)
 
-        w.step, w.out_tensor = step, C
+        w.step, w.out_tensor, w.graph = step, C, 20
         w.flops = 2 * nnz * N
         w.nbytes = spmm_bytes(m, n, nnz, N)
         w.launches = 1  # one library call: the task kernel and the partial sums
@@ -591,6 +591,7 @@ def prepare(name, args, opts):
             v.copy_(v0)
 
         w.step, w.restore = step, restore
+        w.graph = 0  # its alpha/beta change every step and the iterates are put back every 8 steps
         w.flops = 2 * spmv_flops(m, nnz, True)
         w.nbytes = 2 * spmv_bytes(m, n, nnz, True)  # per step (two launches)
         w.launches = 2
@@ -620,7 +621,7 @@ def prepare(name, args, opts):
         def step():
             sp.spmm(plan, 1.0, B, 0.0, C)
 
-        w.step, w.out_tensor = step, C
+        w.step, w.out_tensor, w.graph = step, C, 20
         w.flops = 2 * nnz * N
         w.nbytes = spmm_bytes(m, n, nnz, N)
         w.launches = 1
@@ -640,7 +641,7 @@ def prepare(name, args, opts):
         w.flops = spmv_flops(m, nnz)
         w.nbytes = spmv_bytes(m, n, nnz)
         w.launches = 1
-        w.graph = 20 if base == "spmv_uniform" else 0
+        w.graph = 20  # (the stencil pair below stays graph-free)
         if want_cpu:
             hx = x.cpu().numpy()
             # the 4096-row matrix is too small to split among threads
