@@ -335,3 +335,32 @@ def test_skewed_workload_task_split_sampled():
         r0, r1 = 64 * w, min(coo.m, 64 * w + 64)
         ref, scale = oracle.wcsr_spmm(r1 - r0, 64, np.array([0, q1 - q0], np.int32), hwc[q0:q1], hvals[q0:q1], B)
         assert_close(got[r0:r1], ref, scale, what="skewed window %d" % w)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_wcsr_tasks_random(seed):
+    """Random shapes, pads, task widths, N and alpha / beta: the task table
+    against the oracle's (widest first) and the product against the oracle."""
+    rng = np.random.default_rng(100 + seed)
+    m, n = int(rng.integers(1, 2500)), int(rng.integers(1, 6000))
+    coo = gen.skewed_windows_coo(m=m, n=n, pool_median=int(rng.integers(4, 80)), pool_sigma=float(rng.uniform(0.5, 2.0)),
+                                 pool_max=int(min(n, rng.integers(64, 4000))), seed=seed)
+    pad = int(rng.choice([1, 2, 8, 32]))
+    T = 32 * int(rng.integers(1, 33))
+    N = 4 * int(rng.integers(1, 65))
+    alpha, beta = float(rng.uniform(-2, 2)), float(rng.choice([0.0, rng.uniform(-2, 2)]))
+    say("wcsr tasks random", seed, m, n, coo.nnz, pad, T, N)
+    rp, c, v = oracle.coo_to_csr(coo.m, coo.n, coo.row, coo.col, coo.val)
+    ewp, ewc, evals = oracle.csr_to_wcsr(coo.m, coo.n, rp, c, v, 64, pad)
+    etasks, ewinfo, eslots = oracle.wcsr_tasks(ewp, T)
+    t = sp.wcsr_tasks(coo.m, dev(ewp), ewc.size, task_cols=T)
+    assert (t.ntasks, t.nslots) == (len(etasks), eslots)
+    _, splits, tasks = table_parts(t, ewp.size - 1)
+    order = np.argsort(-(etasks[:, 2] - etasks[:, 1]), kind="stable")
+    np.testing.assert_array_equal(tasks, etasks[order])
+    B = gen.dense_matrix(coo.n, N, seed)
+    C0 = gen.dense_matrix(coo.m, N, seed + 1)
+    C = dev(C0) if beta != 0.0 else torch.full((coo.m, N), float("nan"), device="cuda")
+    sp.wcsr_spmm_tasks(coo.m, coo.n, t, dev(ewc), dev(evals), alpha, dev(B), beta, C)
+    ref, scale = oracle.wcsr_spmm(coo.m, 64, ewp, ewc, evals, B, alpha, beta, C0)
+    assert_close(host(C), ref, scale, what="wcsr tasks random seed %d" % seed)
