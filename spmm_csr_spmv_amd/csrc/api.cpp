@@ -1071,9 +1071,14 @@ int wcsr_tasks_build(int64_t m, const int32_t* window_ptr, int64_t total_cols, i
     return SP_OK;
 }
 
+// nslots partial tiles of 64 x N floats must be addressable in size_t
+static bool wcsr_slots_fit(int64_t nslots, int32_t N) {
+    return nslots == 0 || N == 0 || (uint64_t)N <= (uint64_t)SIZE_MAX / (256u * (uint64_t)nslots);
+}
+
 int wcsr_spmm_tasks_bufsize(int64_t nslots, int32_t N, size_t* bytes) {
     if (!bytes) return SP_ERR_NULL;
-    if (nslots < 0 || nslots > kI32Max || N < 0) return SP_ERR_SIZE;
+    if (nslots < 0 || nslots > kI32Max || N < 0 || !wcsr_slots_fit(nslots, N)) return SP_ERR_SIZE;
     *bytes = spx::wcsr_spmm_tasks_work_bytes(nslots, N);
     return SP_OK;
 }
@@ -1086,7 +1091,8 @@ int wcsr_spmm_tasks(int64_t m, int64_t n, const void* table, int64_t ntasks, int
     if (N < 0 || ldb < N || ldc < N) return SP_ERR_SIZE;
     if (m == 0 || N == 0) return SP_OK;
     // every window is at least one task
-    if (ntasks < (m + 63) / 64 || ntasks > kI32Max || nslots < 0 || nslots > kI32Max) return SP_ERR_SIZE;
+    if (ntasks < (m + 63) / 64 || ntasks > kI32Max || nslots < 0 || nslots > kI32Max || !wcsr_slots_fit(nslots, N))
+        return SP_ERR_SIZE;
     if (!table || !C || (n > 0 && !B) || (nslots > 0 && !work)) return SP_ERR_NULL;
     if (work_bytes < spx::wcsr_spmm_tasks_work_bytes(nslots, N)) return SP_ERR_WORKSPACE;
     if (N % 4 != 0 || ldb % 4 != 0) return SP_ERR_UNSUPPORTED;

@@ -252,6 +252,8 @@ def test_wcsr_task_split_argument_errors():
     assert L.wcsr_spmm_tasks_bufsize(0, 32, ctypes.byref(b)) == 0 and b.value == 0
     assert L.wcsr_spmm_tasks_bufsize(3, 32, ctypes.byref(b)) == 0 and b.value >= 3 * 64 * 32 * 4
     assert L.wcsr_spmm_tasks_bufsize(-1, 32, ctypes.byref(b)) == 2
+    # 2^31 - 1 slots of 64 x (2^31 - 1) floats do not fit in size_t
+    assert L.wcsr_spmm_tasks_bufsize(2 ** 31 - 1, 2 ** 31 - 1, ctypes.byref(b)) == 2
 
     def call(m=100, ntasks=2, nslots=0, N=8, ldb=8, table=FAKE, work=None, wbytes=0, B=FAKE):
         return L.wcsr_spmm_tasks(m, 10, table, ntasks, nslots, FAKE, FAKE, N, 1.0, B, ldb, 0.0, FAKE, N, work,
