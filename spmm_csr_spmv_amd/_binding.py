@@ -354,6 +354,7 @@ def wcsr_spmm_tasks(m, n, tasks, window_col, values, alpha, B, beta, C, work=Non
            lib().wcsr_spmm_tasks(m, n, _ptr(tasks.table), tasks.ntasks, tasks.nslots, _ptr(window_col),
                                  _ptr(values), N, float(alpha), _ptr(B), N, float(beta), _ptr(C), N, _ptr(work),
                                  need, _stream(stream)))
+    _used_on(tasks.table, stream)  # the table may have been allocated on another stream
     return C
 
 
