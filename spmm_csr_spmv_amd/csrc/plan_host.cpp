@@ -1,8 +1,8 @@
 // Host side of the plan (declarations and the layout of each structure in
 // layout.h): row profile, row bins, SELL-C-sigma order, column-panel and
-// x-window streams, phase-swept SpMM copy; and the WCSR task table.  Plain C++ without HIP, so that it
-// runs under the host sanitizers; api.cpp moves the arrays to and from the
-// device.
+// x-window streams, phase-swept SpMM copy; and the WCSR task table.  Plain
+// C++ without HIP, so that it runs under the host sanitizers; api.cpp and
+// wcsr.hip move the arrays to and from the device.
 //
 // 「通用稀疏矩阵乘法CUDA算子实现」 §4: the profile of the matrix (row lengths with
 // their mean, variance and tail, 「CUDA LSMR 专栏（二）」 §5.3) decides which kernel
@@ -176,7 +176,9 @@ void build_sell(const std::vector<int32_t>& hptr, const sp_plan_options& o, Host
 
 int check_columns(const std::vector<int32_t>& hidx, int64_t cols) {
     const int64_t nnz = (int64_t)hidx.size();
-    constexpr int64_t kBlockEntries = 1 << 20;
+    // blocks small enough that parallel_for spreads them over its threads
+    // (it takes at most one thread per 64 blocks)
+    constexpr int64_t kBlockEntries = 1 << 14;
     const int64_t blocks = (nnz + kBlockEntries - 1) / kBlockEntries;
     std::vector<char> bad((size_t)blocks, 0);
     parallel_for(blocks, [&](int64_t b) {
