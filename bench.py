@@ -499,6 +499,15 @@ def prepare(name, args, opts):
                 return round(e0.elapsed_time(e1) / reps, 5)
 
             w.config["one_workgroup_per_window_ms"] = ms_of(lambda: sp.wcsr_spmm(m, n, wp, wc, wv, 1.0, B, 0.0, C))
+            # the same call with other task widths (tables built here, widest first)
+            widths = {}
+            for Tw in (512, 1024, 2048, 4096):
+                tw = sp.wcsr_tasks(m, wp, total_cols, task_cols=Tw)
+                ww = torch.empty(max(tw.workspace_bytes(N), 1), dtype=torch.uint8, device="cuda")
+                widths[str(Tw)] = dict(ms=ms_of(lambda: sp.wcsr_spmm_tasks(m, n, tw, wc, wv, 1.0, B, 0.0, C, work=ww)),
+                                       tasks=tw.ntasks, partial_slots=tw.nslots)
+                del tw, ww
+            w.config["task_widths"] = widths
             plan_c = sp.Plan(m, n, rp, ci, vv, max_N=N)
             w.config["csr_spmm_ms_same_matrix"] = ms_of(lambda: sp.spmm(plan_c, 1.0, B, 0.0, C))
             del plan_c
