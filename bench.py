@@ -1190,7 +1190,7 @@ def measure(w, args, stream):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=None,
                     choices=ALL_WORKLOADS + ["spmm_lognormal", "spmm_clustered", "spmm_skewed"],
